@@ -1,0 +1,168 @@
+"""Benchmark: fused error-feedback Top-1% + 8-bit QSGD on a 7e9-element fp32 gradient.
+
+One step = one gc_ef_topk call with QSGD (s = 127, groups of 64) over the whole flat
+gradient: c = g + r, exact Top-k (k = 1% = 7e7), ordered compaction, QSGD of the kept
+values and the residual update.  Inputs live in HBM before the timed region starts.
+
+Workload (synthetic, generated on the GPU): 32 layers of 218,750,000 elements, each
+t(3) times a per-layer lognormal(-7, 1) scale; three step gradients g_1..g_3 (step t
+cycles through them), the residual carried from step to step starting at 0, QSGD seed
+500 + t.
+
+Printed: one JSON line.  value = input fp32 GB/s (4 n bytes per step / step time);
+roofline = the streaming pass (the dominant kernel), 12 algorithmic bytes per element,
+timed with HIP events recorded by the library on the launch stream inside the timed
+region; cpu_baseline = the numpy oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "EF-Top-1%+int8 compress GB/s of fp32 grad input; % of HBM peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=12)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--layer-len", type=int, default=218_750_000)
+    ap.add_argument("--ratio", type=float, default=0.01)
+    ap.add_argument("--cpu-sample-log2", type=int, default=25,
+                    help="elements in the oracle's sample (2^N, split over the same 32 layers)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return ap.parse_args()
+
+
+def cpu_baseline(args, n_layers):
+    """Time the oracle (as it stands) on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+    import workloads
+    n_s = 1 << args.cpu_sample_log2
+    layer_len = n_s // n_layers
+    g, _ = workloads.big_layers_host(n_layers, layer_len, step=1)
+    r = np.zeros_like(g)
+    k = int(g.size * args.ratio)
+    t0 = time.perf_counter()
+    oracle.ef_topk_qsgd(g, r, k, levels=127, group=64, seed=501)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(4.0 * g.size / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{g.size} elements ({n_layers} layers x {layer_len}) of the same layered t(3) x "
+                   f"lognormal recipe drawn on the host, k = {k} (1%), one EF-Top-k + QSGD-127 step; "
+                   f"{dt:.2f} s on one core (numpy sort-based oracle); host has {os.cpu_count()} cpus"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the compression kernels run per GPU; no collectives are built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gradient_compression_ddp_amd as gc
+    import workloads
+
+    dev = torch.device("cuda:0")
+    L, LL = args.layers, args.layer_len
+    n = L * LL
+    k = int(n * args.ratio)
+    print(f"[bench] generating 3 step gradients of {n} elements on the GPU", file=sys.stderr, flush=True)
+    grads = [workloads.layered_torch(L, LL, step=t, device=dev) for t in (1, 2, 3)]
+    res = torch.zeros(n, dtype=torch.float32, device=dev)
+    out_idx = torch.empty(k, dtype=torch.int64, device=dev)
+    out_codes = torch.empty(k, dtype=torch.int8, device=dev)
+    out_norms = torch.empty((k + 63) // 64, dtype=torch.float32, device=dev)
+    ws = torch.empty(gc.workspace_size(gc.OP_EF_TOPK, n, k, 127), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        t = i % 3
+        gc.ef_topk(grads[t], res, k, qsgd_levels=127, qsgd_group=64, qsgd_seed=501 + t,
+                   out_idx=out_idx, out_codes=out_codes, out_norms=out_norms, want_values=False,
+                   workspace=ws)
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    gc.profile_collect()              # discard anything recorded before the timed region
+    gc.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, args.warmup + args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    gc.profile_enable(False)
+    calls, ms_before, ms_pass, ms_after = gc.profile_collect()
+    print(f"[bench] timed {args.steps} steps in {elapsed:.4f} s", file=sys.stderr, flush=True)
+
+    ms_step = elapsed / args.steps * 1e3
+    in_bytes = 4.0 * n
+    alg_step = 12.0 * n + 8.0 * k + 1.0 * k + 4.0 * ((k + 63) // 64)
+    value = in_bytes / (ms_step / 1e3) / 1e9
+    pass_ms = ms_pass / max(calls, 1)
+    pass_bytes = 12.0 * n
+    achieved = pass_bytes / (pass_ms / 1e3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "ef_topk_1pct_qsgd8_7e9",
+            "elements": n, "layers": L, "layer_len": LL, "k": k,
+            "qsgd_levels": 127, "qsgd_group": 64, "step_gradients": 3,
+            "parallelism": "single GPU",
+        },
+        "hbm_frac_step": round(alg_step / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": alg_step,
+        "stage_ms_per_step": {"before_pass": round(ms_before / max(calls, 1), 4),
+                              "streaming_pass": round(pass_ms, 4),
+                              "after_pass": round(ms_after / max(calls, 1), 4)},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_ef_cand (fused c = g + r, write c, candidate extraction)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": pass_bytes,
+            "avg_launch_ms": round(pass_ms, 4),
+        },
+    }
+    if not args.no_cpu:
+        del grads, res, ws
+        torch.cuda.empty_cache()
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(args, L)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,242 @@
+"""Python binding of libgc.so, the MI355X (gfx950) gradient-compression library.
+
+Marshalling only: each function checks tensor dtypes/devices, allocates the outputs
+and the workspace with torch when the caller does not pass them, and forwards raw
+device pointers and the current HIP stream to the C ABI declared in include/gc.h.
+Every step of the computation runs in the library's HIP kernels; there is no CPU
+fallback.  Importing this package fails loudly if libgc.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "lib_path", "GCError", "workspace_size", "ef_topk", "quant_minmax", "qsgd", "terngrad",
+    "powersgd_step", "decompress_scatter", "KIND_F32", "KIND_MINMAX8", "KIND_MINMAX4",
+    "KIND_QSGD", "KIND_TERN", "OP_EF_TOPK", "OP_QUANT_MINMAX", "OP_QSGD", "OP_TERNGRAD",
+    "OP_POWERSGD", "OP_DECOMPRESS", "profile_enable", "profile_collect",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libgc.so")
+
+GC_OK, GC_EINVAL, GC_EWORKSPACE, GC_EUNSUPPORTED, GC_EHIP = 0, 1, 2, 3, 4
+OP_EF_TOPK, OP_QUANT_MINMAX, OP_QSGD, OP_TERNGRAD, OP_POWERSGD, OP_DECOMPRESS = 1, 2, 3, 4, 5, 6
+KIND_F32, KIND_MINMAX8, KIND_MINMAX4, KIND_QSGD, KIND_TERN = 0, 1, 2, 3, 4
+
+if not os.path.exists(lib_path):
+    raise ImportError(
+        f"{lib_path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+        "or `python gradient_compression_ddp_amd/build.py` (needs hipcc for gfx950)")
+
+_lib = ctypes.CDLL(lib_path)
+
+_p, _i64, _u64, _i32, _f32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_int,
+                                   ctypes.c_float, ctypes.c_size_t)
+_SIGS = {
+    "gc_status_string": ([_i32], ctypes.c_char_p),
+    "gc_last_error": ([], ctypes.c_char_p),
+    "gc_version": ([], _i32),
+    "gc_workspace_size": ([_i32, _i64, _i64, _i64, ctypes.POINTER(_sz)], _i32),
+    "gc_ef_topk": ([_p, _p, _i64, _i64, _i64, _p, _p, _i32, _i64, _u64, _p, _p, _p, _sz, _p], _i32),
+    "gc_quant_minmax": ([_p, _p, _i64, _i64, _i32, _p, _p, _p, _p, _sz, _p], _i32),
+    "gc_qsgd": ([_p, _p, _i64, _i64, _i32, _u64, _i64, _p, _p, _p], _i32),
+    "gc_terngrad": ([_p, _p, _i32, _p, _u64, _i64, _p, _p, _p, _sz, _p], _i32),
+    "gc_powersgd_step": ([_p, _p, _i64, _i64, _i32, _p, _p, _p, _sz, _p], _i32),
+    "gc_decompress_scatter": ([_i32, _p, _i64, _i64, _p, _p, _p, _i64, _i32, _f32, _i32, _p, _i64, _p],
+                              _i32),
+    "gc_profile_enable": ([_i32], _i32),
+    "gc_profile_collect": ([ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double),
+                            ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)], _i32),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+
+class GCError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = _lib.gc_last_error().decode(errors="replace")
+        kind = _lib.gc_status_string(status).decode()
+        super().__init__(f"{where}: {kind}: {msg}")
+        self.status = status
+
+
+def _check(status: int, where: str):
+    if status != GC_OK:
+        raise GCError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t: torch.Tensor, dtype, name: str):
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def workspace_size(op: int, n: int, k: int = 0, aux: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    _check(_lib.gc_workspace_size(op, n, k, aux, ctypes.byref(out)), "gc_workspace_size")
+    return int(out.value)
+
+
+def _workspace(op, n, k, aux, device, workspace):
+    need = workspace_size(op, n, k, aux)
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel()
+
+
+def ef_topk(grad, residual, k, index_base=0, *, qsgd_levels=0, qsgd_group=64, qsgd_seed=0,
+            out_idx=None, out_val=None, out_codes=None, out_norms=None, want_values=True,
+            workspace=None, stream=None):
+    """Error-feedback Top-K; with qsgd_levels > 0 also QSGD on the kept values.
+
+    Updates ``residual`` in place.  Returns ``(idx, val)`` for pure Top-K, or
+    ``(idx, codes, norms, val)`` with QSGD (``val`` is None when ``want_values`` is False).
+    """
+    _dev(grad, torch.float32, "grad")
+    _dev(residual, torch.float32, "residual")
+    n = grad.numel()
+    if residual.numel() != n:
+        raise ValueError("grad and residual differ in size")
+    dev = grad.device
+    if out_idx is None:
+        out_idx = torch.empty(k, dtype=torch.int64, device=dev)
+    quant = qsgd_levels > 0
+    if out_val is None and (want_values or not quant):
+        out_val = torch.empty(k, dtype=torch.float32, device=dev)
+    if quant:
+        if out_codes is None:
+            out_codes = torch.empty(k, dtype=torch.int8, device=dev)
+        if out_norms is None:
+            out_norms = torch.empty((k + qsgd_group - 1) // qsgd_group, dtype=torch.float32, device=dev)
+    ws, ws_bytes = _workspace(OP_EF_TOPK, n, k, qsgd_levels, dev, workspace)
+    _check(_lib.gc_ef_topk(_ptr(grad), _ptr(residual), n, k, index_base, _ptr(out_idx), _ptr(out_val),
+                           qsgd_levels, qsgd_group, qsgd_seed, _ptr(out_codes), _ptr(out_norms),
+                           _ptr(ws), ws_bytes, _stream(stream)), "gc_ef_topk")
+    if quant:
+        return out_idx, out_codes, out_norms, out_val
+    return out_idx, out_val
+
+
+def quant_minmax(x, group, bits, residual=None, *, codes=None, mins=None, scales=None,
+                 workspace=None, stream=None):
+    """Min-max quantization; returns (codes uint8, mins, scales).  int4 codes are packed."""
+    _dev(x, torch.float32, "x")
+    if residual is not None:
+        _dev(residual, torch.float32, "residual")
+    n = x.numel()
+    g = n if group == 0 else group
+    ng = 0 if n == 0 else (n + g - 1) // g
+    dev = x.device
+    if codes is None:
+        codes = torch.empty(n if bits == 8 else (n + 1) // 2, dtype=torch.uint8, device=dev)
+    if mins is None:
+        mins = torch.empty(ng, dtype=torch.float32, device=dev)
+    if scales is None:
+        scales = torch.empty(ng, dtype=torch.float32, device=dev)
+    ws, ws_bytes = _workspace(OP_QUANT_MINMAX, n, group, 0, dev, workspace)
+    _check(_lib.gc_quant_minmax(_ptr(x), _ptr(residual), n, group, bits, _ptr(codes), _ptr(mins),
+                                _ptr(scales), _ptr(ws), ws_bytes, _stream(stream)), "gc_quant_minmax")
+    return codes, mins, scales
+
+
+def qsgd(x, group, levels, seed, index_base=0, residual=None, *, codes=None, norms=None, stream=None):
+    """QSGD; returns (codes int8, norms)."""
+    _dev(x, torch.float32, "x")
+    if residual is not None:
+        _dev(residual, torch.float32, "residual")
+    n = x.numel()
+    dev = x.device
+    if codes is None:
+        codes = torch.empty(n, dtype=torch.int8, device=dev)
+    if norms is None:
+        norms = torch.empty((n + group - 1) // group, dtype=torch.float32, device=dev)
+    _check(_lib.gc_qsgd(_ptr(x), _ptr(residual), n, group, levels, seed, index_base, _ptr(codes),
+                        _ptr(norms), _stream(stream)), "gc_qsgd")
+    return codes, norms
+
+
+def terngrad(x, seg_offsets, seed, index_base=0, residual=None, *, packed=None, scales=None,
+             workspace=None, stream=None):
+    """TernGrad over segments; seg_offsets is a host sequence of nseg+1 int64 offsets.
+    Returns (packed uint8, scales)."""
+    import numpy as np
+    _dev(x, torch.float32, "x")
+    if residual is not None:
+        _dev(residual, torch.float32, "residual")
+    off = np.ascontiguousarray(np.asarray(seg_offsets, dtype=np.int64))
+    nseg = off.size - 1
+    lens = np.diff(off)
+    nbytes = int(((lens + 3) // 4).sum()) if nseg > 0 else 0
+    dev = x.device
+    if packed is None:
+        packed = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(max(nseg, 0), dtype=torch.float32, device=dev)
+    ws, ws_bytes = _workspace(OP_TERNGRAD, int(off[-1]) if nseg > 0 else 0, nseg, 0, dev, workspace)
+    _check(_lib.gc_terngrad(_ptr(x), _ptr(residual), nseg, off.ctypes.data_as(ctypes.c_void_p), seed,
+                            index_base, _ptr(packed), _ptr(scales), _ptr(ws), ws_bytes,
+                            _stream(stream)), "gc_terngrad")
+    return packed, scales
+
+
+def powersgd_step(grad, residual, Q, *, P=None, workspace=None, stream=None):
+    """One PowerSGD step on a rows x cols matrix; Q (cols x rank) is updated in place.
+    Returns P (rows x rank)."""
+    _dev(grad, torch.float32, "grad")
+    if residual is not None:
+        _dev(residual, torch.float32, "residual")
+    _dev(Q, torch.float32, "Q")
+    rows, cols = grad.shape
+    rank = Q.shape[1]
+    if P is None:
+        P = torch.empty((rows, rank), dtype=torch.float32, device=grad.device)
+    ws, ws_bytes = _workspace(OP_POWERSGD, rows, cols, rank, grad.device, workspace)
+    _check(_lib.gc_powersgd_step(_ptr(grad), _ptr(residual), rows, cols, rank, _ptr(Q), _ptr(P), _ptr(ws),
+                                 ws_bytes, _stream(stream)), "gc_powersgd_step")
+    return P
+
+
+def decompress_scatter(kind, codes, count, out, *, idx=None, index_base=0, meta0=None, meta1=None,
+                       group=0, levels=0, alpha=1.0, accumulate=False, stream=None):
+    """Decode `count` payload entries into `out` (dense, or scattered through idx)."""
+    _dev(out, torch.float32, "out")
+    _check(_lib.gc_decompress_scatter(kind, _ptr(idx), count, index_base, _ptr(codes), _ptr(meta0),
+                                      _ptr(meta1), group, levels, alpha, 1 if accumulate else 0, _ptr(out),
+                                      out.numel(), _stream(stream)), "gc_decompress_scatter")
+    return out
+
+
+def profile_enable(on: bool = True) -> None:
+    """Record HIP events around the stages of every ef_topk call (see gc.h)."""
+    _check(_lib.gc_profile_enable(1 if on else 0), "gc_profile_enable")
+
+
+def profile_collect():
+    """Wait for the recorded events; returns (calls, ms_before_pass, ms_pass, ms_after_pass)."""
+    calls = ctypes.c_int64(0)
+    a, b, c = ctypes.c_double(0), ctypes.c_double(0), ctypes.c_double(0)
+    _check(_lib.gc_profile_collect(ctypes.byref(calls), ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)),
+           "gc_profile_collect")
+    return int(calls.value), a.value, b.value, c.value

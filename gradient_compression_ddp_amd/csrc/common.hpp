@@ -1,0 +1,153 @@
+// Device-side building blocks shared by the gfx950 kernels: the Philox4x32-10 counter
+// RNG, wave64 reductions and scans, and the float <-> ordered-integer encodings used by
+// the min/max and Top-K code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gc {
+
+constexpr int kWave = 64;
+
+// Native 4 x fp32 vector (usable with the nontemporal load/store builtins).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11).  One block: counter
+// (c0, c1, 0, 0) under key (k0, k1).  Each round forms the two 32x32->64 products
+// M0*x0 and M1*x2 and the new state (hi1^x1^k0, lo1, hi0^x3^k1, lo0); the key is
+// bumped by the Weyl constants between rounds.  The key is wave-uniform (the seed), so
+// its schedule stays in scalar registers.
+// ---------------------------------------------------------------------------------
+struct Words4 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ Words4 philox10(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1) {
+  constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+  constexpr uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+  uint32_t x0 = c0, x1 = c1, x2 = 0u, x3 = 0u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)M0 * (uint64_t)x0;
+    const uint64_t p1 = (uint64_t)M1 * (uint64_t)x2;
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    x0 = hi1 ^ x1 ^ k0;
+    x1 = lo1;
+    x2 = hi0 ^ x3 ^ k1;
+    x3 = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+  Words4 o;
+  o.w[0] = x0; o.w[1] = x1; o.w[2] = x2; o.w[3] = x3;
+  return o;
+}
+
+// Block holding element indices [4*ctr, 4*ctr+4) of the stream keyed by `seed`.
+__device__ __forceinline__ Words4 philox_block(uint64_t seed, uint64_t ctr) {
+  return philox10((uint32_t)ctr, (uint32_t)(ctr >> 32), (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+// 24-bit uniform in [0,1): (word >> 8) * 2^-24, exact in fp32.
+__device__ __forceinline__ float u24(uint32_t w) {
+  return (float)(w >> 8) * 5.9604644775390625e-08f;
+}
+
+// Uniforms of the four consecutive element indices e0..e0+3 (any alignment).  When
+// e0 % 4 == 0 this is one Philox block; otherwise two blocks are stitched.
+__device__ __forceinline__ void uniforms4(uint64_t seed, uint64_t e0, float u[4]) {
+  const uint64_t c = e0 >> 2;
+  const uint32_t sh = (uint32_t)(e0 & 3u);
+  const Words4 a = philox_block(seed, c);
+  if (sh == 0) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) u[m] = u24(a.w[m]);
+  } else {
+    const Words4 b = philox_block(seed, c + 1);
+    uint32_t w[8];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) { w[m] = a.w[m]; w[4 + m] = b.w[m]; }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      // select w[sh + m] without dynamic register indexing
+      uint32_t v = w[m + 1];
+      v = (sh == 2) ? w[m + 2] : v;
+      v = (sh == 3) ? w[m + 3] : v;
+      u[m] = u24(v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Float encodings.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t fbits(float f) { return __float_as_uint(f); }
+__device__ __forceinline__ float bitsf(uint32_t u) { return __uint_as_float(u); }
+
+// Magnitude key: bit pattern with the sign cleared.
+__device__ __forceinline__ uint32_t mag_key(float f) { return fbits(f) & 0x7FFFFFFFu; }
+
+// Monotone map float -> uint32 for the total order -inf < ... < -0 < +0 < ... < +inf.
+__device__ __forceinline__ uint32_t ord_enc(float f) {
+  const uint32_t b = fbits(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float ord_dec(uint32_t e) {
+  return bitsf((e & 0x80000000u) ? (e & 0x7FFFFFFFu) : ~e);
+}
+
+// ---------------------------------------------------------------------------------
+// Wave64 helpers.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+// Number of set bits of `mask` in lanes below this one.
+__device__ __forceinline__ uint32_t mbcnt(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+template <typename T>
+__device__ __forceinline__ T shfl_xor(T v, int m) { return __shfl_xor(v, m, kWave); }
+
+// Butterfly min/max of ordered-encoded values over aligned segments of `width` lanes.
+__device__ __forceinline__ uint32_t seg_min_u32(uint32_t v, int width) {
+  for (int m = 1; m < width; m <<= 1) v = min(v, (uint32_t)shfl_xor((int)v, m));
+  return v;
+}
+__device__ __forceinline__ uint32_t seg_max_u32(uint32_t v, int width) {
+  for (int m = 1; m < width; m <<= 1) v = max(v, (uint32_t)shfl_xor((int)v, m));
+  return v;
+}
+
+// Float sum over aligned segments of `width` lanes as a balanced pairwise tree in lane
+// order: the xor butterfly with offsets 1, 2, 4, ... adds exactly the pairs of the
+// tree (a + b and b + a are the same IEEE result), and every lane ends with the sum.
+__device__ __forceinline__ float seg_tree_sum(float v, int width) {
+  for (int m = 1; m < width; m <<= 1) v = v + shfl_xor(v, m);
+  return v;
+}
+
+// Inclusive scan (sum) of 64-bit counts across the wave.
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint64_t o = __shfl_up(v, d, kWave);
+    if (l >= d) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+}  // namespace gc

@@ -1,0 +1,60 @@
+// Host-side launchers of the gfx950 kernels.  capi.cpp validates every argument
+// before calling these; the launchers only size grids and enqueue work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gc {
+
+// Round a byte count up to the 256-byte alignment used for every workspace carve-out.
+inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// ---- min-max -------------------------------------------------------------------
+// Small groups (power of two in [4,256]): one pass, a group spans group/4 lanes.
+hipError_t launch_minmax_small(const float* x, float* res, int64_t n, int64_t group, int bits,
+                               uint8_t* codes, float* mins, float* scales, hipStream_t s);
+// Large groups (> 256, or the whole tensor): reduce, finalize, quantize.
+size_t minmax_large_workspace(int64_t n, int64_t group);
+hipError_t launch_minmax_large(const float* x, float* res, int64_t n, int64_t group, int bits,
+                               uint8_t* codes, float* mins, float* scales, void* ws,
+                               hipStream_t s);
+
+// ---- QSGD ----------------------------------------------------------------------
+hipError_t launch_qsgd(const float* x, float* res, int64_t n, int64_t group, int levels,
+                       uint64_t seed, int64_t index_base, int8_t* codes, float* norms,
+                       hipStream_t s);
+
+// ---- TernGrad ------------------------------------------------------------------
+size_t terngrad_workspace(int64_t n, int nseg);
+hipError_t launch_terngrad(const float* x, float* res, int nseg, const int64_t* seg_offsets_host,
+                           uint64_t seed, int64_t index_base, uint8_t* packed, float* scales,
+                           void* ws, hipStream_t s);
+
+// ---- EF Top-K ------------------------------------------------------------------
+size_t ef_topk_workspace(int64_t n, int64_t k, int qsgd_levels);
+hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, int64_t index_base,
+                          int64_t* out_idx, float* out_val, int qsgd_levels, int64_t qsgd_group,
+                          uint64_t qsgd_seed, int8_t* out_codes, float* out_norms, void* ws,
+                          size_t ws_bytes, hipStream_t s);
+
+// ---- PowerSGD ------------------------------------------------------------------
+size_t powersgd_workspace(int64_t rows, int64_t cols, int rank);
+hipError_t launch_powersgd(const float* grad, float* res, int64_t rows, int64_t cols, int rank,
+                           float* Q, float* P, void* ws, hipStream_t s);
+
+// ---- decompress ----------------------------------------------------------------
+hipError_t launch_decompress(int kind, const int64_t* idx, int64_t count, int64_t index_base,
+                             const void* codes, const float* meta0, const float* meta1,
+                             int64_t group, int levels, float alpha, int accumulate, float* out,
+                             int64_t n_out, hipStream_t s);
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+// Stage timing of gc_ef_topk (see gc_profile_enable): stage 0 = call start, 1 = before the
+// streaming pass, 2 = after it, 3 = call end.  No-op unless profiling is enabled.
+void prof_mark(hipStream_t s, int stage);
+
+}  // namespace gc

@@ -1,0 +1,332 @@
+// Per-group min-max (linear) quantization with deterministic rounding, gfx950.
+//
+// Operation: zyxy.net/archives/25733 "分布式训练中的梯度压缩算法", section 二.1 (linear
+// quantization: scale = (max-min)/(2^b-1), q = round((g-min)/scale), g_hat = q*scale+min)
+// and section 三 (error compensation); grouping per hotdry.top
+// "gradient-compression-quantization-sparsification", section 1.2.
+//
+// Layout: each lane owns one aligned quad of 4 consecutive elements (one 16-byte load).
+// A group of G elements spans G/4 consecutive lanes, so for G <= 256 a group is
+// reduced inside one wave with a lane butterfly and everything happens in one pass:
+// 4 B read (+4 B read/write of the residual) and 1 B (int8) or 0.5 B (int4) written per
+// element, 8 B per group.  Larger groups (and the whole-tensor case) take a reduce pass
+// with ordered-integer atomics, a per-group finalize and a quantize pass.
+//
+// Every float operation is one IEEE binary32 operation (the library is compiled with
+// -ffp-contract=off); min/max use the total order -0 < +0 through an order-preserving
+// integer map, so the sign of a zero minimum is well defined.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace gc {
+namespace {
+
+constexpr int kBlock = 256;
+
+struct Quad {
+  float v[4];
+  bool ok[4];
+};
+
+template <bool EF>
+__device__ __forceinline__ Quad load_quad(const float* __restrict__ x, const float* __restrict__ res,
+                                          int64_t e0, int64_t n) {
+  Quad q;
+  if (e0 + 4 <= n) {
+    const float4 a = *reinterpret_cast<const float4*>(x + e0);
+    q.v[0] = a.x; q.v[1] = a.y; q.v[2] = a.z; q.v[3] = a.w;
+    if (EF) {
+      const float4 b = *reinterpret_cast<const float4*>(res + e0);
+      q.v[0] = q.v[0] + b.x; q.v[1] = q.v[1] + b.y; q.v[2] = q.v[2] + b.z; q.v[3] = q.v[3] + b.w;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) q.ok[m] = true;
+  } else {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      q.ok[m] = e0 + m < n;
+      float v = 0.f;
+      if (q.ok[m]) {
+        v = x[e0 + m];
+        if (EF) v = v + res[e0 + m];
+      }
+      q.v[m] = v;
+    }
+  }
+  return q;
+}
+
+// Quantize one element against (mn, scale); returns the code as float and g_hat.
+template <int BITS>
+__device__ __forceinline__ float quantize_one(float v, float mn, float scale, float* ghat) {
+  constexpr float L = (float)((1 << BITS) - 1);
+  float q = 0.f;
+  if (scale != 0.f) {
+    q = rintf((v - mn) / scale);
+    q = fminf(fmaxf(q, 0.f), L);
+  }
+  *ghat = q * scale + mn;
+  return q;
+}
+
+template <int BITS, bool EF>
+__device__ __forceinline__ void emit_quad(const Quad& qd, int64_t e0, int64_t n, const float mn[4],
+                                          const float sc[4], uint8_t* __restrict__ codes,
+                                          float* __restrict__ res) {
+  uint32_t c[4];
+  float gh[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) c[m] = (uint32_t)quantize_one<BITS>(qd.v[m], mn[m], sc[m], &gh[m]);
+  const bool full = e0 + 4 <= n;
+  if (BITS == 8) {
+    if (full) {
+      *reinterpret_cast<uint32_t*>(codes + e0) = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        if (qd.ok[m]) codes[e0 + m] = (uint8_t)c[m];
+    }
+  } else {
+    const int64_t b = e0 >> 1;
+    if (full) {
+      *reinterpret_cast<uint16_t*>(codes + b) = (uint16_t)(c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12));
+    } else {
+      if (qd.ok[0]) codes[b] = (uint8_t)(c[0] | ((qd.ok[1] ? c[1] : 0u) << 4));
+      if (qd.ok[2]) codes[b + 1] = (uint8_t)(c[2] | ((qd.ok[3] ? c[3] : 0u) << 4));
+    }
+  }
+  if (EF) {
+    if (full) {
+      float4 r;
+      r.x = qd.v[0] - gh[0]; r.y = qd.v[1] - gh[1]; r.z = qd.v[2] - gh[2]; r.w = qd.v[3] - gh[3];
+      *reinterpret_cast<float4*>(res + e0) = r;
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        if (qd.ok[m]) res[e0 + m] = qd.v[m] - gh[m];
+    }
+  }
+}
+
+// One pass for groups of 4..256 elements: a group is `lpg` = G/4 consecutive lanes.
+template <int BITS, bool EF>
+__global__ __launch_bounds__(kBlock) void k_minmax_small(const float* __restrict__ x,
+                                                         float* __restrict__ res, int64_t n,
+                                                         int lpg_log2, uint8_t* __restrict__ codes,
+                                                         float* __restrict__ mins,
+                                                         float* __restrict__ scales) {
+  constexpr float L = (float)((1 << BITS) - 1);
+  const int64_t nquads = (n + 3) >> 2;
+  const int lpg = 1 << lpg_log2;
+  const int lane = lane_id();
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  // The loop bound is uniform per block, so every lane of a wave takes part in the
+  // butterflies; lanes past the end carry neutral values.
+  for (int64_t base = (int64_t)blockIdx.x * kBlock; base < nquads; base += stride) {
+    const int64_t q = base + threadIdx.x;
+    const int64_t e0 = q << 2;
+    Quad qd;
+    if (q < nquads) {
+      qd = load_quad<EF>(x, res, e0, n);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) { qd.v[m] = 0.f; qd.ok[m] = false; }
+    }
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      if (qd.ok[m]) {
+        const uint32_t e = ord_enc(qd.v[m]);
+        lo = min(lo, e);
+        hi = max(hi, e);
+      }
+    lo = seg_min_u32(lo, lpg);
+    hi = seg_max_u32(hi, lpg);
+    if (q >= nquads) continue;
+    const float mn = ord_dec(lo), mx = ord_dec(hi);
+    const float scale = (mx - mn) / L;
+    const float mna[4] = {mn, mn, mn, mn}, sca[4] = {scale, scale, scale, scale};
+    emit_quad<BITS, EF>(qd, e0, n, mna, sca, codes, res);
+    if ((lane & (lpg - 1)) == 0) {
+      const int64_t g = e0 >> (lpg_log2 + 2);
+      mins[g] = mn;
+      scales[g] = scale;
+    }
+  }
+}
+
+// ---- large groups ----------------------------------------------------------------
+
+__global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t n, uint32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+__device__ __forceinline__ void flush_run(int64_t g, uint32_t lo, uint32_t hi, uint32_t* gmin,
+                                          uint32_t* gmax) {
+  if (g >= 0 && lane_id() == 0) {
+    atomicMin(gmin + g, lo);
+    atomicMax(gmax + g, hi);
+  }
+}
+
+// Each wave scans a contiguous run of 256-element tiles.  A tile touches at most two
+// groups (G >= 256); the wave keeps a running (group, min, max) and issues atomics only
+// when the group changes, so the whole-tensor case costs one atomic pair per wave.
+template <bool EF>
+__global__ __launch_bounds__(kBlock) void k_minmax_reduce(const float* __restrict__ x,
+                                                          const float* __restrict__ res, int64_t n,
+                                                          int64_t G, int64_t tiles_per_wave,
+                                                          uint32_t* __restrict__ gmin,
+                                                          uint32_t* __restrict__ gmax) {
+  const int lane = lane_id();
+  const int64_t wave = ((int64_t)blockIdx.x * kBlock + threadIdx.x) >> 6;
+  const int64_t ntiles = (n + 255) >> 8;
+  const int64_t t0 = wave * tiles_per_wave;
+  const int64_t t1 = min(ntiles, t0 + tiles_per_wave);
+  int64_t run_g = -1;
+  uint32_t run_lo = 0xFFFFFFFFu, run_hi = 0u;
+  for (int64_t t = t0; t < t1; ++t) {
+    const int64_t ef = t << 8;
+    const int64_t gA = ef / G;
+    const int64_t bnd = (gA + 1) * G;
+    const int64_t e0 = ef + 4 * lane;
+    Quad qd;
+    if (e0 < n) {
+      qd = load_quad<EF>(x, res, e0, n);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) { qd.v[m] = 0.f; qd.ok[m] = false; }
+    }
+    uint32_t loA = 0xFFFFFFFFu, hiA = 0u, loB = 0xFFFFFFFFu, hiB = 0u;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      if (qd.ok[m]) {
+        const uint32_t e = ord_enc(qd.v[m]);
+        if (e0 + m < bnd) { loA = min(loA, e); hiA = max(hiA, e); }
+        else { loB = min(loB, e); hiB = max(hiB, e); }
+      }
+    loA = seg_min_u32(loA, kWave);
+    hiA = seg_max_u32(hiA, kWave);
+    const bool hasB = min(ef + 256, n) > bnd;
+    if (gA == run_g) {
+      run_lo = min(run_lo, loA);
+      run_hi = max(run_hi, hiA);
+    } else {
+      flush_run(run_g, run_lo, run_hi, gmin, gmax);
+      run_g = gA; run_lo = loA; run_hi = hiA;
+    }
+    if (hasB) {
+      loB = seg_min_u32(loB, kWave);
+      hiB = seg_max_u32(hiB, kWave);
+      flush_run(run_g, run_lo, run_hi, gmin, gmax);
+      run_g = gA + 1; run_lo = loB; run_hi = hiB;
+    }
+  }
+  flush_run(run_g, run_lo, run_hi, gmin, gmax);
+}
+
+template <int BITS>
+__global__ void k_minmax_finalize(const uint32_t* __restrict__ gmin, const uint32_t* __restrict__ gmax,
+                                  int64_t ng, float* __restrict__ mins, float* __restrict__ scales) {
+  constexpr float L = (float)((1 << BITS) - 1);
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < ng;
+       g += (int64_t)gridDim.x * blockDim.x) {
+    const float mn = ord_dec(gmin[g]), mx = ord_dec(gmax[g]);
+    mins[g] = mn;
+    scales[g] = (mx - mn) / L;
+  }
+}
+
+template <int BITS, bool EF>
+__global__ __launch_bounds__(kBlock) void k_minmax_quant(const float* __restrict__ x,
+                                                         float* __restrict__ res, int64_t n, int64_t G,
+                                                         const float* __restrict__ mins,
+                                                         const float* __restrict__ scales,
+                                                         uint8_t* __restrict__ codes) {
+  const int lane = lane_id();
+  const int64_t ntiles = (n + 255) >> 8;
+  const int64_t waves = ((int64_t)gridDim.x * kBlock) >> 6;
+  for (int64_t t = ((int64_t)blockIdx.x * kBlock + threadIdx.x) >> 6; t < ntiles; t += waves) {
+    const int64_t ef = t << 8;
+    const int64_t gA = ef / G;
+    const int64_t bnd = (gA + 1) * G;
+    const int64_t e0 = ef + 4 * lane;
+    if (e0 >= n) continue;
+    const Quad qd = load_quad<EF>(x, res, e0, n);
+    const float mnA = mins[gA], scA = scales[gA];
+    const bool hasB = min(ef + 256, n) > bnd;
+    const float mnB = hasB ? mins[gA + 1] : mnA, scB = hasB ? scales[gA + 1] : scA;
+    float mn[4], sc[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const bool inA = e0 + m < bnd;
+      mn[m] = inA ? mnA : mnB;
+      sc[m] = inA ? scA : scB;
+    }
+    emit_quad<BITS, EF>(qd, e0, n, mn, sc, codes, res);
+  }
+}
+
+int grid_for(int64_t work_items, int per_block, int max_blocks) {
+  const int64_t b = (work_items + per_block - 1) / per_block;
+  return (int)(b < 1 ? 1 : (b > max_blocks ? max_blocks : b));
+}
+
+}  // namespace
+
+hipError_t launch_minmax_small(const float* x, float* res, int64_t n, int64_t group, int bits,
+                               uint8_t* codes, float* mins, float* scales, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  int lpg_log2 = 0;
+  while ((int64_t(4) << lpg_log2) < group) ++lpg_log2;
+  const int64_t nquads = (n + 3) / 4;
+  const int grid = grid_for(nquads, kBlock, device_cu_count() * 16);
+  if (bits == 8) {
+    if (res) hipLaunchKernelGGL((k_minmax_small<8, true>), grid, kBlock, 0, s, x, res, n, lpg_log2, codes, mins, scales);
+    else hipLaunchKernelGGL((k_minmax_small<8, false>), grid, kBlock, 0, s, x, res, n, lpg_log2, codes, mins, scales);
+  } else {
+    if (res) hipLaunchKernelGGL((k_minmax_small<4, true>), grid, kBlock, 0, s, x, res, n, lpg_log2, codes, mins, scales);
+    else hipLaunchKernelGGL((k_minmax_small<4, false>), grid, kBlock, 0, s, x, res, n, lpg_log2, codes, mins, scales);
+  }
+  return hipGetLastError();
+}
+
+size_t minmax_large_workspace(int64_t n, int64_t group) {
+  const int64_t G = group == 0 ? (n > 0 ? n : 1) : group;
+  const int64_t ng = n == 0 ? 0 : (n + G - 1) / G;
+  return 2 * align256((size_t)ng * sizeof(uint32_t));
+}
+
+hipError_t launch_minmax_large(const float* x, float* res, int64_t n, int64_t group, int bits,
+                               uint8_t* codes, float* mins, float* scales, void* ws, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int64_t G = group == 0 ? n : group;
+  const int64_t ng = (n + G - 1) / G;
+  uint32_t* gmin = reinterpret_cast<uint32_t*>(ws);
+  uint32_t* gmax = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) + align256((size_t)ng * 4));
+  const int cus = device_cu_count();
+  const int fill_grid = grid_for(ng, 256, cus * 8);
+  hipLaunchKernelGGL(k_fill_u32, fill_grid, 256, 0, s, gmin, ng, 0xFFFFFFFFu);
+  hipLaunchKernelGGL(k_fill_u32, fill_grid, 256, 0, s, gmax, ng, 0u);
+  const int64_t ntiles = (n + 255) / 256;
+  const int rgrid = grid_for(ntiles, kBlock / kWave, cus * 8);
+  const int64_t waves = (int64_t)rgrid * (kBlock / kWave);
+  const int64_t tpw = (ntiles + waves - 1) / waves;
+  if (res) hipLaunchKernelGGL((k_minmax_reduce<true>), rgrid, kBlock, 0, s, x, res, n, G, tpw, gmin, gmax);
+  else hipLaunchKernelGGL((k_minmax_reduce<false>), rgrid, kBlock, 0, s, x, res, n, G, tpw, gmin, gmax);
+  if (bits == 8) hipLaunchKernelGGL((k_minmax_finalize<8>), fill_grid, 256, 0, s, gmin, gmax, ng, mins, scales);
+  else hipLaunchKernelGGL((k_minmax_finalize<4>), fill_grid, 256, 0, s, gmin, gmax, ng, mins, scales);
+  const int qgrid = grid_for(ntiles, kBlock / kWave, cus * 16);
+  if (bits == 8) {
+    if (res) hipLaunchKernelGGL((k_minmax_quant<8, true>), qgrid, kBlock, 0, s, x, res, n, G, mins, scales, codes);
+    else hipLaunchKernelGGL((k_minmax_quant<8, false>), qgrid, kBlock, 0, s, x, res, n, G, mins, scales, codes);
+  } else {
+    if (res) hipLaunchKernelGGL((k_minmax_quant<4, true>), qgrid, kBlock, 0, s, x, res, n, G, mins, scales, codes);
+    else hipLaunchKernelGGL((k_minmax_quant<4, false>), qgrid, kBlock, 0, s, x, res, n, G, mins, scales, codes);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gc

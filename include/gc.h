@@ -1,0 +1,237 @@
+/*
+ * gc.h -- C ABI of the MI355X (gfx950) gradient-compression library (libgc.so).
+ *
+ * The library compresses one GPU's flat fp32 gradient bucket in HBM before it is sent
+ * anywhere: error-feedback Top-K, min-max int8/int4, QSGD, TernGrad, PowerSGD, and the
+ * matching decompression.
+ *
+ * Conventions for every call
+ *   - Data pointers are DEVICE pointers (HBM) unless a comment says "host".
+ *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.  Every call
+ *     only enqueues work on `stream` and returns; nothing is synchronized, nothing is
+ *     read back to the host, and no memory is allocated or freed by the library.
+ *   - The caller owns every buffer.  Scratch memory is passed in as `workspace` of
+ *     `workspace_bytes` bytes; gc_workspace_size() says how much a call needs.
+ *     A workspace may be reused by consecutive calls on one stream, not by calls that
+ *     can run concurrently.
+ *   - Outputs must not alias inputs, except the residual, which is updated in place.
+ *   - Sizes and indices are 64-bit.  fp32 arrays read with vector loads (grad, residual,
+ *     x) must be 16-byte aligned; torch allocations are.
+ *   - Arguments are checked on the host before anything is enqueued.  A failing check
+ *     returns GC_EINVAL / GC_EWORKSPACE / GC_EUNSUPPORTED and touches no memory; the
+ *     reason is available from gc_last_error() in the calling thread.  A failed launch
+ *     returns GC_EHIP.
+ *   - Floating point is IEEE binary32 with round-to-nearest-even, correctly rounded
+ *     division and square root, no fused multiply-add and no flush of denormals, so the
+ *     results are bit-reproducible and match a plain CPU implementation.  Non-finite
+ *     inputs produce unspecified (but finite-time, in-bounds) results, except in Top-K,
+ *     where NaN and Inf are ordered by their bit pattern.
+ *
+ * Random draws (QSGD, TernGrad) use Philox4x32-10 (Salmon et al., "Parallel Random
+ * Numbers: As Easy as 1, 2, 3", SC'11): element e takes word (e & 3) of the block at
+ * counter (e >> 2, 0) under key (seed_lo, seed_hi), and U = (word >> 8) * 2^-24.
+ * Rounding goes up when U < p.  The draw depends only on (seed, e), never on the
+ * launch configuration.
+ *
+ * Sources of the operations (web pages on gradient compression):
+ *   [P1] blog.hotdry.top, "gradient-compression-quantization-sparsification"
+ *   [P2] zyxy.net/archives/25733, "分布式训练中的梯度压缩算法：性能瓶颈、收敛性影响与实现细节"
+ *   [P3] 5688vip.com, "4、梯度累积与梯度压缩" (multi-GPU sync efficiency series, part 04)
+ *   [P4] aiqz.cc, "梯度聚合通信优化实战方案"
+ */
+#ifndef GC_H
+#define GC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum gc_status {
+  GC_OK = 0,
+  GC_EINVAL = 1,        /* bad argument: null pointer, size, k, bits, levels, group, alignment */
+  GC_EWORKSPACE = 2,    /* workspace missing or smaller than gc_workspace_size() */
+  GC_EUNSUPPORTED = 3,  /* valid request this build does not implement */
+  GC_EHIP = 4           /* a HIP runtime call or kernel launch failed */
+};
+
+/* Operation selectors for gc_workspace_size(). */
+enum gc_op {
+  GC_OP_EF_TOPK = 1,       /* n = elements, k = kept, aux = QSGD levels (0: none)       */
+  GC_OP_QUANT_MINMAX = 2,  /* n = elements, k = group (0: whole tensor), aux unused      */
+  GC_OP_QSGD = 3,          /* needs no workspace                                         */
+  GC_OP_TERNGRAD = 4,      /* n = total elements, k = number of segments                 */
+  GC_OP_POWERSGD = 5,      /* n = rows, k = cols, aux = rank                             */
+  GC_OP_DECOMPRESS = 6     /* needs no workspace                                         */
+};
+
+/* Payload kinds for gc_decompress_scatter(). */
+enum gc_kind {
+  GC_KIND_F32 = 0,      /* codes: float[count] values                                   */
+  GC_KIND_MINMAX8 = 1,  /* codes: uint8[count]; meta0 = mins, meta1 = scales per group   */
+  GC_KIND_MINMAX4 = 2,  /* codes: uint8[ceil(count/2)], entry 2j in the low nibble       */
+  GC_KIND_QSGD = 3,     /* codes: int8[count] = sign*level; meta0 = norms; `levels` = s   */
+  GC_KIND_TERN = 4      /* codes: uint8[ceil(count/4)], 2 bits each; meta0 = scales      */
+};
+
+/* Static string for a status value. Host only, never fails. */
+const char* gc_status_string(int status);
+
+/* Reason for the last non-GC_OK return in the calling thread ("" if none). */
+const char* gc_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int gc_version(void);
+
+/* Bytes of workspace the call selected by `op` needs for the given sizes (host only;
+ * no device call).  Returns GC_EINVAL for impossible sizes. */
+int gc_workspace_size(int op, int64_t n, int64_t k, int64_t aux, size_t* bytes);
+
+/*
+ * gc_ef_topk -- error-feedback Top-K sparsification, optionally followed by QSGD on
+ * the kept values.
+ *
+ * Operation ([P1] section 2 and 2.1; [P3] section 4.2.1 topk_compress and its error
+ * accumulation; [P4] "Python 演示" error_feedback_compress; hybrid with 8-bit
+ * quantization of what is sent: [P3] section 4.3):
+ *   c      = fl(grad + residual)                                  (every element)
+ *   key(c) = bit pattern of c with the sign bit cleared (31-bit unsigned magnitude)
+ *   S      = the k elements with the largest key; among equal keys the lower index wins
+ *   out_idx[j] = index_base + (j-th smallest index in S)          (strictly ascending)
+ *   pure Top-K (qsgd_levels == 0):
+ *       out_val[j]      = c[idx_j]            (bit-exact copy)
+ *       residual[idx_j] = +0.0,  residual[i] = c[i] elsewhere
+ *   with QSGD (qsgd_levels in [1,127]), applied to v = (c[idx_0], ..., c[idx_{k-1}]):
+ *       groups of qsgd_group consecutive kept values (power of two in [4,256]);
+ *       out_norms[g] = fl(sqrt(pairwise-tree sum of v^2 over group g)), float[ceil(k/group)];
+ *       out_codes[j] = sign(v_j) * level_j (int8), level from stochastic rounding of
+ *           fl(fl(|v_j|/nu)*s) with the Philox draw of element index j under qsgd_seed;
+ *       residual[idx_j] = fl(v_j - g_hat_j), g_hat_j = sign * fl(fl(nu*level)/s);
+ *       out_val may be NULL; if given it receives v.
+ *
+ * grad: const float[n], 16-byte aligned.  residual: float[n], 16-byte aligned, in: the
+ * previous residual (zeros on the first step), out: the new residual.  out_idx: int64[k].
+ * k == 0 performs only residual = c.  n == 0 is a no-op.  Requires 0 <= k <= n.
+ * Workspace: gc_workspace_size(GC_OP_EF_TOPK, n, k, qsgd_levels).
+ * The selection is exact for every input: an internal fast path keeps a candidate set
+ * above a sampled threshold, and falls back to a full exact selection on the device if
+ * the candidate set cannot contain the answer.
+ */
+int gc_ef_topk(const float* grad, float* residual, int64_t n, int64_t k, int64_t index_base,
+               int64_t* out_idx, float* out_val,
+               int qsgd_levels, int64_t qsgd_group, uint64_t qsgd_seed,
+               int8_t* out_codes, float* out_norms,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gc_quant_minmax -- per-group min-max (linear) quantization with deterministic
+ * rounding.
+ *
+ * Operation ([P2] section 二.1 linear quantization and section 三 error
+ * compensation; [P4] "Python 演示" quantize; grouping: [P1] section 1.2):
+ *   x'    = fl(x + residual) if residual != NULL, else x
+ *   per group: mn = min, mx = max, scale = fl(fl(mx - mn) / (2^bits - 1))
+ *   q     = scale == 0 ? 0 : clamp(rint(fl(fl(x' - mn) / scale)), 0, 2^bits - 1)
+ *   g_hat = fl(fl(q * scale) + mn);  residual := fl(x' - g_hat) if residual != NULL
+ * group: 0 (one group over all n), a power of two in [4,256], or any value > 256.  The
+ * last group may be partial.  bits: 8 -> codes uint8[n]; 4 -> codes uint8[ceil(n/2)],
+ * element 2j in the low nibble of byte j, an odd tail leaves the high nibble 0.
+ * mins, scales: float[ngroups].  x, residual: 16-byte aligned.
+ * Workspace: gc_workspace_size(GC_OP_QUANT_MINMAX, n, group, 0) (0 for small groups).
+ */
+int gc_quant_minmax(const float* x, float* residual, int64_t n, int64_t group, int bits,
+                    uint8_t* codes, float* mins, float* scales,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gc_qsgd -- QSGD stochastic quantization onto `levels` levels of the group L2 norm.
+ *
+ * Operation ([P1] section 1.1: stochastic rounding between levels, unbiased, used with
+ * error feedback; grouping [P1] section 1.2; levels of the norm as in the QSGD paper
+ * [P1] cites):
+ *   x' = fl(x + residual) if residual != NULL, else x
+ *   nu = fl(sqrt(sum of x'^2 over the group, balanced pairwise tree in index order))
+ *   u = fl(fl(|x'|/nu) * s), l = floor(u), p = u - l,
+ *   level = min(l + (U(seed, index_base + i) < p), s), code = (x' < 0 ? -level : level)
+ *   nu == 0 gives code 0.  residual := fl(x' - g_hat), g_hat = sign * fl(fl(nu*level)/s).
+ * group: power of two in [4,256].  levels: [1,127].  codes: int8[n]; norms: float[ngroups].
+ * index_base >= 0.  Needs no workspace.
+ */
+int gc_qsgd(const float* x, float* residual, int64_t n, int64_t group, int levels,
+            uint64_t seed, int64_t index_base, int8_t* codes, float* norms, void* stream);
+
+/*
+ * gc_terngrad -- TernGrad ternary codes with one scale per segment (layer).
+ *
+ * Operation ([P1] section 1.1: codes in {-1,0,+1}, layer-wise normalization; the scheme
+ * of the TernGrad paper [P1] cites):
+ *   x' = fl(x + residual) if residual != NULL, else x
+ *   per segment s: scale_s = max |x'|;  p = fl(|x'| / scale_s)
+ *   code = (U(seed, index_base + i) < p) ? (x' < 0 ? -1 : +1) : 0, for global position i
+ *   scale_s == 0 gives code 0.  residual := fl(x' - code*scale_s).
+ * seg_offsets: HOST int64[nseg+1], seg_offsets[0] == 0, nondecreasing; n = seg_offsets[nseg].
+ * packed: segment s occupies bytes [B_s, B_s + ceil(len_s/4)), B_s = sum_{j<s} ceil(len_j/4);
+ *   element t of the segment sits in bits 2(t%4)..2(t%4)+1 of byte B_s + t/4, with
+ *   0 -> 00, +1 -> 01, -1 -> 11; unused bits are 0.  scales: float[nseg].
+ * x, residual: 16-byte aligned.  index_base >= 0.
+ * Workspace: gc_workspace_size(GC_OP_TERNGRAD, n, nseg, 0).
+ */
+int gc_terngrad(const float* x, float* residual, int nseg, const int64_t* seg_offsets,
+                uint64_t seed, int64_t index_base, uint8_t* packed, float* scales,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gc_powersgd_step -- one PowerSGD power-iteration step with error feedback.
+ *
+ * Operation ([P1] section 3.1: low-rank approximation, only the two thin factors are
+ * sent, rebuilt at the receiver; [P4] "梯度压缩原理": run with error compensation; the
+ * step of the PowerSGD paper [P1] cites):
+ *   M = fl(grad + residual) (M = grad if residual == NULL)
+ *   P = M Q;  P^ = modified Gram-Schmidt of P's columns (norm-0 column -> 0)
+ *   Q' = M^T P^;  residual := M - P^ Q'^T  (skipped if residual == NULL)
+ * grad, residual: rows x cols row-major float, 16-byte aligned, cols % 4 == 0.
+ * Q: cols x rank row-major float, in: Q_{t-1}, out: Q'.  P: rows x rank row-major, out: P^.
+ * rank: [1,4].  Products accumulate in fp32; agreement with a float64 evaluation is to
+ * about 1e-6 relative (Frobenius).
+ * Workspace: gc_workspace_size(GC_OP_POWERSGD, rows, cols, rank).
+ */
+int gc_powersgd_step(const float* grad, float* residual, int64_t rows, int64_t cols, int rank,
+                     float* Q, float* P, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gc_decompress_scatter -- decode a payload and store or add it into a dense fp32 vector.
+ *
+ * Operation ([P2] section 四: the receiver decompresses before the update; section 二.2:
+ * the sparse gradient is dense with zeros off the kept set).  For entry j < count,
+ * g_hat_j is the dequantization of the payload kind (see enum gc_kind and the matching
+ * compressor above); group g = j / group (group 0: one group).  Then
+ *   pos_j = idx ? idx[j] - index_base : j
+ *   out[pos_j] = fl(alpha * g_hat_j)            (accumulate == 0)
+ *   out[pos_j] = fl(out[pos_j] + fl(alpha * g_hat_j))   (accumulate != 0)
+ * Entries whose pos_j falls outside [0, n_out) are skipped.  idx entries must be
+ * distinct (Top-K output is).  levels is used by GC_KIND_QSGD only.
+ */
+int gc_decompress_scatter(int kind, const int64_t* idx, int64_t count, int64_t index_base,
+                          const void* codes, const float* meta0, const float* meta1,
+                          int64_t group, int levels, float alpha, int accumulate,
+                          float* out, int64_t n_out, void* stream);
+
+/*
+ * Stage timing (profiling aid, not part of any operation).  While enabled, every
+ * gc_ef_topk call records four HIP events on its stream: call start, start and end of the
+ * full streaming pass (the fused add + candidate kernel), and call end.
+ * gc_profile_collect() waits for the recorded events, returns the number of calls and the
+ * summed milliseconds of [start, pass start), [pass start, pass end) and [pass end, end),
+ * and clears the record.  Host-side state, guarded by a mutex; events are created by the
+ * HIP runtime (no device memory is allocated by the library).
+ */
+int gc_profile_enable(int on);
+int gc_profile_collect(int64_t* calls, double* ms_before, double* ms_pass, double* ms_after);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GC_H */

@@ -21,13 +21,20 @@ Readings where the pages are open:
 * codes are unsigned, 0..2^b-1 (the demo's cast to int8 overflows above 127);
   int4 codes pack two per byte, element 2j in the low nibble;
 * metadata per group is (min, scale) in float32; the last group may be partial;
-  group 0 means one group over the whole tensor.
+  group 0 means one group over the whole tensor;
+* min and max follow the IEEE total order, in which -0 < +0, so the sign of a zero
+  minimum is defined.
 """
 from __future__ import annotations
 
 import numpy as np
 
 F32 = np.float32
+
+
+def _total_order_key(v: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(v, dtype=F32).view(np.uint32)
+    return np.where(b & np.uint32(0x80000000), ~b, b | np.uint32(0x80000000))
 
 
 def _groups(n: int, group: int):
@@ -57,8 +64,9 @@ def quant_minmax(x: np.ndarray, group: int, bits: int, residual: np.ndarray | No
     g_hat = np.zeros(n, dtype=F32)
     for j in range(ng):
         seg = x[j * g:(j + 1) * g]
-        mn = seg.min()
-        mx = seg.max()
+        key = _total_order_key(seg)
+        mn = seg[np.argmin(key)]
+        mx = seg[np.argmax(key)]
         rng = F32(mx - mn)
         scale = F32(rng / L)
         if scale == F32(0.0):

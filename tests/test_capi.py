@@ -1,0 +1,114 @@
+"""The C ABI without a GPU: the library loads, exports every symbol include/gc.h declares,
+and rejects bad arguments on the host before any HIP call (no compute is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gc_testlib import ROOT, ensure_built
+
+HEADER = os.path.join(ROOT, "include", "gc.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    path = ensure_built()
+    return ctypes.CDLL(path)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gc_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"gc_ef_topk", "gc_quant_minmax", "gc_qsgd", "gc_terngrad", "gc_powersgd_step",
+            "gc_decompress_scatter"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), f"libgc.so does not export {name}"
+
+
+def test_status_strings_and_version(lib):
+    lib.gc_status_string.restype = ctypes.c_char_p
+    lib.gc_last_error.restype = ctypes.c_char_p
+    assert lib.gc_status_string(0) == b"GC_OK"
+    assert b"EINVAL" in lib.gc_status_string(1)
+    assert b"unknown" in lib.gc_status_string(99)
+    assert lib.gc_version() >= 100
+
+
+def _ws(lib, op, n, k, aux):
+    out = ctypes.c_size_t(7)
+    st = lib.gc_workspace_size(op, ctypes.c_int64(n), ctypes.c_int64(k), ctypes.c_int64(aux), ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_sizes(lib):
+    st, b = _ws(lib, 1, 7_000_000_000, 70_000_000, 127)
+    assert st == 0 and 1 << 30 < b < 8 << 30          # a few GB of candidate pool for the 7e9 case
+    st, b = _ws(lib, 1, 1_000_000, 10_000, 0)
+    assert st == 0 and b > 0
+    assert _ws(lib, 1, 100, 0, 0) == (0, 0)
+    assert _ws(lib, 1, 100, 101, 0)[0] == 1            # k > n
+    assert _ws(lib, 2, 6_553_600, 64, 0) == (0, 0)     # small groups need no workspace
+    st, b = _ws(lib, 2, 1_000_000, 0, 0)
+    assert st == 0 and b >= 8
+    assert _ws(lib, 2, 100, 3, 0)[0] == 1              # group < 4
+    assert _ws(lib, 99, 1, 1, 1)[0] == 1
+
+
+VP = ctypes.c_void_p
+FAKE = VP(0x100000)     # never dereferenced: every call below fails validation first
+MISALIGNED = VP(0x100004)
+
+
+def test_ef_topk_rejects_bad_arguments(lib):
+    lib.gc_last_error.restype = ctypes.c_char_p
+    f = lib.gc_ef_topk
+    f.argtypes = [VP, VP, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, VP, VP, ctypes.c_int,
+                  ctypes.c_int64, ctypes.c_uint64, VP, VP, VP, ctypes.c_size_t, VP]
+    assert f(FAKE, FAKE, 10, 11, 0, FAKE, FAKE, 0, 64, 0, None, None, FAKE, 1 << 20, None) == 1
+    assert b"k must" in lib.gc_last_error()
+    assert f(None, FAKE, 10, 1, 0, FAKE, FAKE, 0, 64, 0, None, None, FAKE, 1 << 20, None) == 1
+    assert f(MISALIGNED, FAKE, 10, 1, 0, FAKE, FAKE, 0, 64, 0, None, None, FAKE, 1 << 20, None) == 1
+    assert f(FAKE, FAKE, 10, 1, 0, FAKE, None, 0, 64, 0, None, None, FAKE, 1 << 20, None) == 1
+    assert f(FAKE, FAKE, 10, 1, 0, FAKE, FAKE, 200, 64, 0, FAKE, FAKE, FAKE, 1 << 20, None) == 1
+    assert f(FAKE, FAKE, 10, 1, 0, FAKE, FAKE, 127, 48, 0, FAKE, FAKE, FAKE, 1 << 20, None) == 1
+    assert f(FAKE, FAKE, 10, 1, -1, FAKE, FAKE, 0, 64, 0, None, None, FAKE, 1 << 20, None) == 1
+    assert f(FAKE, FAKE, 10, 1, 0, FAKE, FAKE, 0, 64, 0, None, None, None, 0, None) == 2
+    assert f(FAKE, FAKE, 10, 1, 0, FAKE, FAKE, 0, 64, 0, None, None, FAKE, 16, None) == 2
+    assert f(FAKE, FAKE, -1, 0, 0, FAKE, FAKE, 0, 64, 0, None, None, None, 0, None) == 1
+    # n == 0 is a no-op that needs no pointers at all
+    assert f(None, None, 0, 0, 0, None, None, 0, 64, 0, None, None, None, 0, None) == 0
+
+
+def test_other_calls_reject_bad_arguments(lib):
+    q = lib.gc_quant_minmax
+    q.argtypes = [VP, VP, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, VP, VP, VP, VP, ctypes.c_size_t, VP]
+    assert q(FAKE, None, 100, 64, 7, FAKE, FAKE, FAKE, None, 0, None) == 1        # bits
+    assert q(FAKE, None, 100, 48, 8, FAKE, FAKE, FAKE, None, 0, None) == 1        # group not a power of two
+    assert q(FAKE, None, 100, 0, 8, FAKE, FAKE, FAKE, None, 0, None) == 2         # whole tensor needs workspace
+    s = lib.gc_qsgd
+    s.argtypes = [VP, VP, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_uint64, ctypes.c_int64, VP, VP, VP]
+    assert s(FAKE, None, 100, 64, 0, 7, 0, FAKE, FAKE, None) == 1                 # levels
+    assert s(FAKE, None, 100, 512, 15, 7, 0, FAKE, FAKE, None) == 1               # group too large
+    t = lib.gc_terngrad
+    t.argtypes = [VP, VP, ctypes.c_int, VP, ctypes.c_uint64, ctypes.c_int64, VP, VP, VP, ctypes.c_size_t, VP]
+    bad = (ctypes.c_int64 * 3)(0, 10, 5)
+    assert t(FAKE, None, 2, ctypes.cast(bad, VP), 3, 0, FAKE, FAKE, None, 0, None) == 1
+    first = (ctypes.c_int64 * 2)(1, 10)
+    assert t(FAKE, None, 1, ctypes.cast(first, VP), 3, 0, FAKE, FAKE, None, 0, None) == 1
+    p = lib.gc_powersgd_step
+    p.argtypes = [VP, VP, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, VP, VP, VP, ctypes.c_size_t, VP]
+    assert p(FAKE, None, 64, 62, 4, FAKE, FAKE, FAKE, 1 << 20, None) == 1         # cols % 4
+    assert p(FAKE, None, 64, 64, 5, FAKE, FAKE, FAKE, 1 << 20, None) == 1         # rank
+    d = lib.gc_decompress_scatter
+    d.argtypes = [ctypes.c_int, VP, ctypes.c_int64, ctypes.c_int64, VP, VP, VP, ctypes.c_int64, ctypes.c_int,
+                  ctypes.c_float, ctypes.c_int, VP, ctypes.c_int64, VP]
+    assert d(9, None, 10, 0, FAKE, FAKE, FAKE, 0, 0, 1.0, 0, FAKE, 10, None) == 1  # kind
+    assert d(0, None, 11, 0, FAKE, None, None, 0, 0, 1.0, 0, FAKE, 10, None) == 1  # dense overrun
+    assert d(3, None, 10, 0, FAKE, FAKE, None, 64, 0, 1.0, 0, FAKE, 10, None) == 1  # QSGD levels
+    assert d(1, None, 10, 0, FAKE, FAKE, None, 64, 0, 1.0, 0, FAKE, 10, None) == 1  # min-max meta1

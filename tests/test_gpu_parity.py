@@ -1,0 +1,287 @@
+"""GPU parity: every entry point against the CPU oracle on the same seeded inputs.
+
+Integer codes, indices and every float output are compared bit for bit (the library
+and the oracle perform the same binary32 operations in the same order).  Sizes span
+several tiles and ragged tails and finish in seconds on the CPU side.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gc_testlib import assert_bits_equal
+
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+
+
+@pytest.fixture(scope="module")
+def gc():
+    import torch  # noqa: F401
+    import gradient_compression_ddp_amd as lib
+    return lib
+
+
+def dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+# ---------------------------------------------------------------- min-max ----------
+
+MINMAX_CASES = [
+    (64 * 300 + 37, 64, 8), (64 * 300 + 37, 64, 4), (1000, 4, 8), (1003, 16, 4), (5000, 256, 8),
+    (5001, 128, 4), (70_001, 0, 8), (70_001, 0, 4), (300_000, 1000, 8), (300_003, 4097, 4),
+    (3, 64, 8), (1, 4, 4), (257, 257, 8),
+]
+
+
+@pytest.mark.parametrize("n,group,bits", MINMAX_CASES)
+@pytest.mark.parametrize("ef", [False, True])
+def test_minmax(gc, n, group, bits, ef):
+    x = workloads.bucket(n, seed=n % 97)
+    r = (workloads.bucket(n, seed=5) * F32(0.01)).astype(F32) if ef else None
+    codes, mins, scales, _, r_new = oracle.quant_minmax(x, group, bits, residual=r)
+    rd = dev(r) if ef else None
+    c_d, m_d, s_d = gc.quant_minmax(dev(x), group, bits, residual=rd)
+    want_codes = codes if bits == 8 else oracle.pack_int4(codes)
+    assert_bits_equal(host(c_d), want_codes, "codes")
+    assert_bits_equal(host(m_d), mins, "mins")
+    assert_bits_equal(host(s_d), scales, "scales")
+    if ef:
+        assert_bits_equal(host(rd), r_new, "residual")
+
+
+def test_minmax_demo_per_tensor_int8(gc):
+    g1, _ = workloads.ef_demo_gradients()
+    codes, mins, scales, _, _ = oracle.quant_minmax(g1, 0, 8)
+    c_d, m_d, s_d = gc.quant_minmax(dev(g1), 0, 8)
+    assert_bits_equal(host(c_d), codes, "codes")
+    assert_bits_equal(host(m_d), mins, "min")
+    assert_bits_equal(host(s_d), scales, "scale")
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_minmax_bucket_full_size(gc, bits):
+    x = workloads.bucket()
+    codes, mins, scales, _, _ = oracle.quant_minmax(x, 64, bits)
+    c_d, m_d, s_d = gc.quant_minmax(dev(x), 64, bits)
+    assert_bits_equal(host(c_d), codes if bits == 8 else oracle.pack_int4(codes), "codes")
+    assert_bits_equal(host(m_d), mins, "mins")
+    assert_bits_equal(host(s_d), scales, "scales")
+
+
+def test_minmax_signed_zero_and_constant_groups(gc):
+    x = np.zeros(64 * 4, F32)
+    x[0:64] = 0.0
+    x[5] = -0.0
+    x[64:128] = 3.5
+    x[128:192] = np.linspace(-1, 1, 64, dtype=F32)
+    x[192] = -0.0
+    x[193:256] = 0.0
+    for bits in (8, 4):
+        codes, mins, scales, _, _ = oracle.quant_minmax(x, 64, bits)
+        c_d, m_d, s_d = gc.quant_minmax(dev(x), 64, bits)
+        assert_bits_equal(host(c_d), codes if bits == 8 else oracle.pack_int4(codes), "codes")
+        assert_bits_equal(host(m_d), mins, "mins")
+        assert_bits_equal(host(s_d), scales, "scales")
+
+
+# ---------------------------------------------------------------- QSGD -------------
+
+@pytest.mark.parametrize("n,group,levels,base", [
+    (64 * 500 + 13, 64, 15, 0), (10_000, 4, 1, 0), (10_003, 256, 127, 3), (777, 32, 7, 1 << 33),
+    (5, 64, 15, 2), (64 * 64, 64, 127, 6),
+])
+@pytest.mark.parametrize("ef", [False, True])
+def test_qsgd(gc, n, group, levels, base, ef):
+    x = workloads.bucket(n, seed=n % 89)
+    r = (workloads.bucket(n, seed=6) * F32(0.01)).astype(F32) if ef else None
+    codes, norms, _, r_new = oracle.qsgd(x, group, levels, seed=7, index_base=base, residual=r)
+    rd = dev(r) if ef else None
+    c_d, n_d = gc.qsgd(dev(x), group, levels, 7, index_base=base, residual=rd)
+    assert_bits_equal(host(c_d), codes, "codes")
+    assert_bits_equal(host(n_d), norms, "norms")
+    if ef:
+        assert_bits_equal(host(rd), r_new, "residual")
+
+
+def test_qsgd_bucket_full_size(gc):
+    x = workloads.bucket()
+    codes, norms, _, _ = oracle.qsgd(x, 64, 15, seed=7)
+    c_d, n_d = gc.qsgd(dev(x), 64, 15, 7)
+    assert_bits_equal(host(c_d), codes, "codes")
+    assert_bits_equal(host(n_d), norms, "norms")
+
+
+# ---------------------------------------------------------------- TernGrad ---------
+
+@pytest.mark.parametrize("lens,base", [
+    ([1001, 1001, 1001], 0), ([14_583, 14_583, 14_583, 14_583], 0), ([5, 0, 3, 250, 252, 1], 0),
+    ([4096, 4096], 2), ([100_001, 7, 65_537], 1 << 33), ([1], 0),
+])
+@pytest.mark.parametrize("ef", [False, True])
+def test_terngrad(gc, lens, base, ef):
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    n = int(off[-1])
+    x = workloads.bucket(n, seed=len(lens)) if n else np.zeros(0, F32)
+    # vary the scale per segment as in the layered workload
+    for s in range(len(lens)):
+        x[off[s]:off[s + 1]] *= F32(10.0 ** (s % 3))
+    r = (workloads.bucket(n, seed=8) * F32(0.01)).astype(F32) if ef else None
+    packed, scales, _, _, r_new = oracle.terngrad(x, off, seed=3, index_base=base, residual=r)
+    rd = dev(r) if ef else None
+    p_d, s_d = gc.terngrad(dev(x), off, 3, index_base=base, residual=rd)
+    assert_bits_equal(host(p_d), packed, "packed codes")
+    assert_bits_equal(host(s_d), scales, "scales")
+    if ef:
+        assert_bits_equal(host(rd), r_new, "residual")
+
+
+def test_terngrad_layers_scaled(gc):
+    x, off = workloads.tern_layers(24, 145_833)        # lengths = 1 mod 4, as in the 350M case
+    packed, scales, _, _, _ = oracle.terngrad(x, off, seed=3)
+    p_d, s_d = gc.terngrad(dev(x), off, 3)
+    assert_bits_equal(host(p_d), packed, "packed codes")
+    assert_bits_equal(host(s_d), scales, "scales")
+
+
+# ---------------------------------------------------------------- EF Top-K ---------
+
+def run_topk(gc, g, r, k, base=0):
+    rd = dev(r)
+    idx, val = gc.ef_topk(dev(g), rd, k, index_base=base)
+    return host(idx), host(val), host(rd)
+
+
+def check_topk(gc, g, r, k, base=0):
+    o_idx, o_val, o_res = oracle.ef_topk(g, r, k, index_base=base)
+    idx, val, res = run_topk(gc, g, r, k, base)
+    assert_bits_equal(idx, o_idx, "idx")
+    assert_bits_equal(val, o_val, "values")
+    assert_bits_equal(res, o_res, "residual")
+    return res
+
+
+def test_topk_demo_two_steps(gc):
+    g1, g2 = workloads.ef_demo_gradients()
+    r = np.zeros_like(g1)
+    r = check_topk(gc, g1, r, workloads.DEMO_K)
+    check_topk(gc, g2, r, workloads.DEMO_K)
+
+
+@pytest.mark.parametrize("n,k", [(8192 * 3 + 77, 1), (8192 * 3 + 77, 100), (8192 * 3 + 77, 8192 * 3 + 77),
+                                 (1, 1), (7, 3), (8192, 8192), (100_000, 50_000), (2_500_001, 25_000),
+                                 (5_000_003, 4_000_000)])
+def test_topk_sizes(gc, n, k):
+    g = workloads.bucket(n, seed=11)
+    r = (workloads.bucket(n, seed=12) * F32(0.1)).astype(F32)
+    check_topk(gc, g, r, k)
+
+
+def test_topk_ties_and_specials(gc):
+    n = 50_000
+    g = np.full(n, 0.5, F32)                        # all ties: lowest indices win
+    check_topk(gc, g, np.zeros(n, F32), 1234)
+    g = np.zeros(n, F32)
+    g[::7] = -0.0
+    check_topk(gc, g, np.zeros(n, F32), 77)
+    rng = np.random.default_rng(3)
+    g = rng.choice(np.array([0.0, -0.0, 1.0, -1.0, 2.0, np.inf, -np.inf, np.nan, 1e-45], F32), n)
+    check_topk(gc, g, np.zeros(n, F32), 10_000)
+
+
+def test_topk_forced_fallback(gc):
+    # a huge tie block defeats the candidate bound: the pool overflows and the exact
+    # full-array path must still produce the oracle's answer
+    n = 3_000_000
+    g = np.full(n, 1.0, F32)
+    g[1_000_000:1_000_010] = 2.0
+    check_topk(gc, g, np.zeros(n, F32), 500_000)
+
+
+def test_topk_index_base_and_zero_k(gc):
+    g = workloads.bucket(40_000, seed=2)
+    r = np.zeros_like(g)
+    check_topk(gc, g, r, 400, base=(1 << 36) + 5)
+    idx, val, res = run_topk(gc, g, r, 0)
+    assert idx.size == 0
+    assert_bits_equal(res, (g + r).astype(F32), "k=0 residual")
+
+
+def test_topk_layered_three_steps_with_qsgd(gc):
+    import torch
+    n_layers, layer_len = 32, 65_537
+    r = np.zeros(n_layers * layer_len, F32)
+    rd = dev(r)
+    for t in (1, 2, 3):
+        g, _ = workloads.big_layers_host(n_layers, layer_len, step=t)
+        k = g.size // 100
+        o_idx, o_codes, o_norms, o_res, o_val = oracle.ef_topk_qsgd(g, r, k, levels=127, group=64,
+                                                                     seed=500 + t)
+        idx, codes, norms, val = gc.ef_topk(dev(g), rd, k, qsgd_levels=127, qsgd_group=64,
+                                            qsgd_seed=500 + t)
+        assert_bits_equal(host(idx), o_idx, f"step {t} idx")
+        assert_bits_equal(host(val), o_val, f"step {t} values")
+        assert_bits_equal(host(codes), o_codes, f"step {t} codes")
+        assert_bits_equal(host(norms), o_norms, f"step {t} norms")
+        assert_bits_equal(host(rd), o_res, f"step {t} residual")
+        r = o_res
+
+
+def test_topk_qsgd_without_values(gc):
+    g, _ = workloads.big_layers_host(4, 30_001, step=1)
+    r = np.zeros_like(g)
+    k = 1_203
+    o_idx, o_codes, o_norms, o_res, _ = oracle.ef_topk_qsgd(g, r, k, levels=15, group=16, seed=9)
+    rd = dev(r)
+    idx, codes, norms, val = gc.ef_topk(dev(g), rd, k, qsgd_levels=15, qsgd_group=16, qsgd_seed=9,
+                                        want_values=False)
+    assert val is None
+    assert_bits_equal(host(idx), o_idx, "idx")
+    assert_bits_equal(host(codes), o_codes, "codes")
+    assert_bits_equal(host(norms), o_norms, "norms")
+    assert_bits_equal(host(rd), o_res, "residual")
+
+
+# ---------------------------------------------------------------- decompress -------
+
+def test_decompress_all_kinds(gc):
+    import torch
+    x = workloads.bucket(64 * 40 + 9)
+    n = x.size
+    cases = []
+    c8, m8, s8, _, _ = oracle.quant_minmax(x, 64, 8)
+    cases.append((gc.KIND_MINMAX8, c8, m8, s8, 64, 0))
+    c4, m4, s4, _, _ = oracle.quant_minmax(x, 64, 4)
+    cases.append((gc.KIND_MINMAX4, oracle.pack_int4(c4), m4, s4, 64, 0))
+    cq, nq, _, _ = oracle.qsgd(x, 64, 15, seed=7)
+    cases.append((gc.KIND_QSGD, cq, nq, None, 64, 15))
+    pk, sc, _, _, _ = oracle.terngrad(x, [0, n], seed=3)
+    cases.append((gc.KIND_TERN, pk, sc, None, 0, 0))
+    cases.append((gc.KIND_F32, x, None, None, 0, 0))
+    base = np.linspace(-1, 1, 3 * n, dtype=F32)
+    idx = np.sort(np.random.default_rng(1).choice(3 * n, n, replace=False)).astype(np.int64) + 1000
+    for kind, codes, m0, m1, group, levels in cases:
+        for alpha, acc in ((1.0, 0), (0.125, 1)):
+            want = oracle.decompress_scatter(kind, None, n, 0, codes, m0, m1, group, levels, alpha, acc,
+                                             np.zeros(n, F32) + F32(0.25))
+            out = dev(np.zeros(n, F32) + F32(0.25))
+            gc.decompress_scatter(kind, dev(codes), n, out, meta0=None if m0 is None else dev(m0),
+                                  meta1=None if m1 is None else dev(m1), group=group, levels=levels,
+                                  alpha=alpha, accumulate=bool(acc))
+            assert_bits_equal(host(out), want, f"dense kind {kind}")
+            want = oracle.decompress_scatter(kind, idx, n, 1000, codes, m0, m1, group, levels, alpha, acc,
+                                             base.copy())
+            out = dev(base)
+            gc.decompress_scatter(kind, dev(codes), n, out, idx=dev(idx), index_base=1000,
+                                  meta0=None if m0 is None else dev(m0), meta1=None if m1 is None else dev(m1),
+                                  group=group, levels=levels, alpha=alpha, accumulate=bool(acc))
+            assert_bits_equal(host(out), want, f"scatter kind {kind}")
