@@ -15,14 +15,18 @@ the PowerSGD paper the page cites (Vogels et al., NeurIPS 2019):
 
 Readings where the pages are open: modified Gram-Schmidt in column order 0..r-1
 (for each j: subtract (p^_i . p_j) p^_i for i < j using the updated p_j, then divide
-by its norm); a column of norm exactly 0 becomes 0; only P is orthonormalized; Q'
-warm-starts the next step; matrices are row-major.
+by its norm); only P is orthonormalized; Q' warm-starts the next step; matrices are
+row-major.  A column that lies in the span of the previous ones becomes 0: in exact
+arithmetic its projected norm is 0, and in floating point we take "numerically in the
+span" to mean a projected norm of at most 1e-5 of the column's own norm (below that its
+direction is set by rounding, not by the data).
 """
 from __future__ import annotations
 
 import numpy as np
 
 F32 = np.float32
+DEPENDENT_REL = 1e-5
 
 
 def modified_gram_schmidt(P: np.ndarray) -> np.ndarray:
@@ -31,10 +35,11 @@ def modified_gram_schmidt(P: np.ndarray) -> np.ndarray:
     out = np.zeros_like(P)
     for j in range(r):
         v = P[:, j].copy()
+        own = np.sqrt(v @ v)
         for i in range(j):
             v = v - (out[:, i] @ v) * out[:, i]
         nrm = np.sqrt(v @ v)
-        out[:, j] = v / nrm if nrm > 0.0 else 0.0
+        out[:, j] = v / nrm if nrm > DEPENDENT_REL * own else 0.0
     return out
 
 

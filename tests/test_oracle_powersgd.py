@@ -68,3 +68,17 @@ def test_zero_column_stays_zero():
     out = oracle.powersgd_step(G, None, Q)
     assert np.allclose(out["P"][:, 1], 0.0)
     assert np.allclose(out["Q"][:, 1], 0.0)
+
+
+def test_numerically_dependent_column_becomes_zero():
+    # p_1 = 2 p_0 exactly in exact arithmetic; the float64 projection leaves only rounding
+    rng = np.random.default_rng(9)
+    G = np.zeros((64, 16), F32)
+    G[:, 0] = np.linspace(1, 2, 64, dtype=F32)
+    G[:, 1] = rng.standard_normal(64).astype(F32)
+    Q = np.zeros((16, 3), F32)
+    Q[0, 0], Q[0, 1], Q[1, 2] = 1.0, 3.0, 1.0
+    out = oracle.powersgd_step(G, None, Q)
+    assert np.all(out["P"][:, 1] == 0.0)
+    assert abs(np.linalg.norm(out["P"][:, 2]) - 1.0) < 1e-12      # an independent column survives
+    assert abs(out["P"][:, 0] @ out["P"][:, 2]) < 1e-12
