@@ -293,7 +293,7 @@ int gc_terngrad(const float* x, float* residual, int nseg, const int64_t* seg_of
 
 int gc_powersgd_step(const float* grad, float* residual, int64_t rows, int64_t cols, int rank,
                      float* Q, float* P, void* workspace, size_t workspace_bytes, void* stream) {
-  GC_REQUIRE(rows >= 1 && cols >= 1 && rows <= kMaxN && cols <= kMaxN && rows * cols <= kMaxN,
+  GC_REQUIRE(rows >= 1 && cols >= 1 && rows <= kMaxN && cols <= kMaxN && rows * cols <= kMaxN && rank <= cols,
              "rows and cols must be >= 1 with rows*cols <= 2^40");
   GC_REQUIRE(cols % 4 == 0, "cols must be a multiple of 4");
   GC_REQUIRE(rank >= 1 && rank <= 4, "rank must lie in [1, 4]");
