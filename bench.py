@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--cpu-sample-log2", type=int, default=25,
                     help="elements in the oracle's sample (2^N, split over the same 32 layers)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
+                    help="run one device-to-device copy of this many GiB before the timed region "
+                         "(a plain copy of known size for calibrating HBM byte counters)")
     return ap.parse_args()
 
 
@@ -97,6 +100,14 @@ def main():
                    out_idx=out_idx, out_codes=out_codes, out_norms=out_norms, want_values=False,
                    workspace=ws)
 
+    if args.copy_calibration_gib > 0:
+        nb = int(args.copy_calibration_gib * (1 << 30)) // 4
+        src = grads[0][:nb]
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy of {4 * nb} bytes done", file=sys.stderr, flush=True)
+        del dst
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)

@@ -12,21 +12,24 @@
 //  1. sample   key(g+r) at m <= 2^20 jittered positions;
 //  2. select   a conservative lower bound L on the k-th largest key from the sample
 //              (exact when the sample is the whole input);
-//  3. K1       the one full streaming pass: c = g + r written over r, and every element
-//              with key >= L appended to per-block pages of a candidate pool (a wave
-//              ballot and mbcnt give each candidate its slot; no inter-block waiting);
-//  4. scan     per-tile candidate counts -> per-tile offsets in index order;
-//              the device then picks the source: the candidates if they surely hold the
-//              answer (no pool overflow, count >= k), else the full c (exact fallback);
-//  5. reorder  candidates into one array in ascending index order;
-//  6. select   the exact k-th largest key T by three radix passes (11, 11, 9 bits) with
+//  3. K1       the one full streaming pass, one 4096-element tile per block: c = g + r
+//              written over r, and every element with key >= L appended to a candidate
+//              pool (a wave ballot and mbcnt give each candidate its slot; the tile claims
+//              its pool segment with one atomic on one of 32 interleaved region counters,
+//              so no block ever waits for another);
+//  4. decide   the candidates are used if they surely hold the answer (no pool overflow,
+//              count >= k); otherwise the exact fallback selects over the full c;
+//  5. select   the exact k-th largest key T by three radix passes (11, 11, 9 bits) with
 //              LDS histograms, and `need`, the number of entries with key == T to keep;
+//  6. reorder  the candidates into one array in index order (entry-parallel over batches
+//              of 128 tiles, taken grid-stride so dense layers spread over all blocks);
 //  7. count + scan + emit: ordered compaction of {key > T} plus the first `need` entries
-//              with key == T, writing idx (+index_base) and values; pure Top-K also sets
-//              the residual at kept positions to +0.0;
+//              with key == T (block-level ballot ranks over chunks of 4096 candidates);
+//              pure Top-K also sets the residual at kept positions to +0.0;
 //  8. QSGD     (optional) on the kept values, groups in kept order, RNG index = kept
-//              position, and residual[idx] = v - g_hat.
-// HBM traffic is 12 B per element in K1 (read g and r, write c) plus O(candidates).
+//              position, and the new residual v - g_hat scattered to the kept positions.
+// HBM traffic is 12 B per element in K1 (read g and r, write c) plus O(candidates) plus
+// the scattered residual update of the kept set (one 64-byte sector per isolated entry).
 #include "common.hpp"
 #include "internal.hpp"
 #include "qsgd_core.hpp"
@@ -36,66 +39,82 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / kWave;       // 4
-constexpr int kRounds = 8;                   // quads per thread per tile
-constexpr int64_t kTile = (int64_t)kBlock * 4 * kRounds;   // 8192 elements
-constexpr uint32_t kPage = 8192;             // pool page, >= the largest tile count
-constexpr int kMaxGrid = 2048;               // K1 blocks (each owns at most one open page)
+constexpr int kRounds = 4;                   // quads per thread per tile
+constexpr int64_t kTile = (int64_t)kBlock * 4 * kRounds;   // 4096 elements
+constexpr int kTileShift = 12;
+constexpr int kRegions = 32;                 // candidate-pool regions (tile % 32)
 constexpr int kSampleMax = 1 << 20;
 constexpr int kScanChunk = 1024;             // items per block in the multi-block scan
 constexpr int kBins = 2048;
-constexpr uint32_t kInvalid = 0xFFFFFFFFu;
 
 enum : uint32_t { MODE_CAND = 0, MODE_FULL = 1 };
 
 struct TopkCtrl {
   uint32_t L;              // candidate lower bound on the key
-  uint32_t page_next;      // next free pool page
-  uint32_t overflow;       // set when a block found no free page
+  uint32_t overflow;       // set when a region of the pool is full
   uint32_t mode;           // MODE_CAND or MODE_FULL
-  unsigned long long ncand;   // candidates found by K1
-  unsigned long long krem;    // rank still to locate inside the current prefix (1-based)
   uint32_t prefix;         // key bits fixed so far by the radix passes
   uint32_t T;              // the k-th largest key
+  uint32_t pad;
+  unsigned long long ncand;   // candidates found by K1
+  unsigned long long krem;    // rank still to locate inside the current prefix (1-based)
   unsigned long long need;    // entries with key == T to keep
-  unsigned long long nchunks; // compaction chunks of the selected source
+  unsigned long long nchunks; // tiles of the full fallback source
   unsigned long long hist[kBins];
+  uint32_t region_fill[kRegions];
 };
 
 struct Layout {
   TopkCtrl* ctrl;
   uint32_t* sample;        // [kSampleMax]
   uint32_t* tile_start;    // [ntiles] pool position of the tile's candidates
-  uint32_t* tile_count;    // [ntiles]
-  unsigned long long* tile_excl;  // [ntiles] exclusive prefix of tile counts
+  uint32_t* tile_count;    // [ntiles] candidates of the tile
+  unsigned long long* tile_excl;  // [ntiles] exclusive prefix of the candidate counts
   unsigned long long* scan_up;    // [2 * scan blocks] block sums, then their exclusive scan
-  uint32_t* page_fill;     // [cap_pages]
-  float* pool_val;         // [cap_pages * kPage]
-  uint16_t* pool_off;      // [cap_pages * kPage]
-  float* cand_val;         // [cap_pages * kPage] candidates in index order
-  int64_t* cand_idx;       // [cap_pages * kPage]
-  uint32_t* chunk_gt;      // [max_chunks]
-  uint32_t* chunk_eq;      // [max_chunks]
-  unsigned long long* chunk_gt_excl;  // [max_chunks]
-  unsigned long long* chunk_eq_excl;  // [max_chunks]
+  float* pool_val;         // [pool] candidate values, region by region
+  uint16_t* pool_off;      // [pool] offset of the candidate inside its tile
+  float* cand_val;         // [pool] candidates in index order
+  int64_t* cand_idx;       // [pool]
+  uint32_t* chunk_gt;      // [max_chunks] entries with key > T per chunk of the source
+  uint32_t* chunk_eq;      // [max_chunks] entries with key == T
+  unsigned long long* gt_excl;    // [max_chunks] exclusive prefixes
+  unsigned long long* eq_excl;    // [max_chunks]
   float* staging;          // [k] kept values (QSGD mode without out_val)
-  int64_t ntiles, cap_pages, max_chunks, scan_blocks;
+  int64_t ntiles, region_cap, pool, max_chunks, scan_blocks;
   size_t bytes;
 };
 
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Sample size and the sample rank whose key is taken as the candidate bound L.
+// The rank sits 2% above the expected sample rank plus 8 standard deviations, so the
+// candidates hold the k largest unless the sample is off by far more than sampling error.
+// A sample of the whole input gives the exact k-th key.
+int64_t sample_size(int64_t n) { return n < kSampleMax ? n : kSampleMax; }
+int64_t sample_rank(int64_t n, int64_t k) {
+  const int64_t m = sample_size(n);
+  if (m == n) return k;
+  const double expect = (double)k * (double)m / (double)n;
+  int64_t j = (int64_t)(1.02 * expect + 8.0 * __builtin_sqrt(expect) + 64.0) + 1;
+  return j > m ? m : j;
+}
+
 Layout make_layout(void* base, int64_t n, int64_t k, bool staging) {
   Layout l{};
   l.ntiles = cdiv(n, kTile);
-  const int64_t grid = l.ntiles < kMaxGrid ? l.ntiles : kMaxGrid;
-  int64_t cap = cdiv(2 * k, (int64_t)kPage) + grid + 1;
-  if (cap > l.ntiles) cap = l.ntiles;
-  const int64_t pool_max = (int64_t)0xFFFFFFFFu / kPage;   // pool positions fit in uint32
-  if (cap > pool_max) cap = pool_max;
-  l.cap_pages = cap;
-  l.max_chunks = l.ntiles > cap ? l.ntiles : cap;
-  const int64_t scan_items = l.max_chunks;
-  l.scan_blocks = cdiv(scan_items, kScanChunk);
+  // Room for twice the expected candidates (at least 2k) plus one full tile per region;
+  // positions stay in uint32.
+  const int64_t m = sample_size(n);
+  const double expect_cand = (double)sample_rank(n, k) * (double)n / (double)(m > 0 ? m : 1);
+  const int64_t want = expect_cand > (double)k ? (int64_t)expect_cand : k;
+  int64_t cap = 2 * want + (int64_t)kRegions * kTile;
+  const int64_t cap_max = (int64_t)0xFFFFFFFFu - (int64_t)kRegions * (kTile + 4);
+  if (cap > cap_max) cap = cap_max;
+  l.region_cap = cdiv(cdiv(cap, kRegions), 4) * 4;   // regions start 16-byte aligned
+  l.pool = l.region_cap * kRegions;
+  const int64_t pool_chunks = cdiv(l.pool, kTile);
+  l.max_chunks = l.ntiles > pool_chunks ? l.ntiles : pool_chunks;
+  l.scan_blocks = cdiv(l.max_chunks, kScanChunk);
   size_t off = 0;
   char* b = reinterpret_cast<char*>(base);
   auto take = [&](size_t bytes) -> void* {
@@ -109,23 +128,21 @@ Layout make_layout(void* base, int64_t n, int64_t k, bool staging) {
   l.tile_count = (uint32_t*)take(sizeof(uint32_t) * l.ntiles);
   l.tile_excl = (unsigned long long*)take(sizeof(unsigned long long) * l.ntiles);
   l.scan_up = (unsigned long long*)take(sizeof(unsigned long long) * 4 * (l.scan_blocks + 1));
-  l.page_fill = (uint32_t*)take(sizeof(uint32_t) * cap);
-  const int64_t pool = cap * (int64_t)kPage;
-  l.pool_val = (float*)take(sizeof(float) * pool);
-  l.pool_off = (uint16_t*)take(sizeof(uint16_t) * pool);
-  l.cand_val = (float*)take(sizeof(float) * pool);
-  l.cand_idx = (int64_t*)take(sizeof(int64_t) * pool);
+  l.pool_val = (float*)take(sizeof(float) * l.pool);
+  l.pool_off = (uint16_t*)take(sizeof(uint16_t) * l.pool);
+  l.cand_val = (float*)take(sizeof(float) * l.pool);
+  l.cand_idx = (int64_t*)take(sizeof(int64_t) * l.pool);
   l.chunk_gt = (uint32_t*)take(sizeof(uint32_t) * l.max_chunks);
   l.chunk_eq = (uint32_t*)take(sizeof(uint32_t) * l.max_chunks);
-  l.chunk_gt_excl = (unsigned long long*)take(sizeof(unsigned long long) * l.max_chunks);
-  l.chunk_eq_excl = (unsigned long long*)take(sizeof(unsigned long long) * l.max_chunks);
+  l.gt_excl = (unsigned long long*)take(sizeof(unsigned long long) * l.max_chunks);
+  l.eq_excl = (unsigned long long*)take(sizeof(unsigned long long) * l.max_chunks);
   l.staging = staging ? (float*)take(sizeof(float) * (k > 0 ? k : 1)) : nullptr;
   l.bytes = off;
   return l;
 }
 
 // ---------------------------------------------------------------------------------
-// Block-level ordered ranking.  A block handles 8192 entries as 8 rounds x 4 waves x
+// Block-level ordered ranking.  A block handles 4096 entries as 4 rounds x 4 waves x
 // 64 lanes x 4 entries; entry (j, w, lane, m) has index j*1024 + w*256 + lane*4 + m.
 // For a predicate held as one 4-bit mask per lane and round, rank_round() returns the
 // entry's rank among the lane's earlier set bits plus the earlier lanes of the wave, and
@@ -147,7 +164,7 @@ __device__ __forceinline__ void block_scan32(const uint32_t* s_cnt, uint32_t* s_
     uint32_t v = t < kRounds * kWaves ? s_cnt[t] : 0u;
     uint32_t inc = v;
 #pragma unroll
-    for (int d = 1; d < 32; d <<= 1) {
+    for (int d = 1; d < kRounds * kWaves; d <<= 1) {
       const uint32_t o = (uint32_t)__shfl_up((int)inc, d, kWave);
       if (t >= d) inc += o;
     }
@@ -156,20 +173,21 @@ __device__ __forceinline__ void block_scan32(const uint32_t* s_cnt, uint32_t* s_
   }
 }
 
+
 // ---------------------------------------------------------------------------------
 // Kernels
 // ---------------------------------------------------------------------------------
 __global__ void k_init(TopkCtrl* __restrict__ ctrl, unsigned long long krem) {
   for (int i = threadIdx.x; i < kBins; i += blockDim.x) ctrl->hist[i] = 0ull;
+  for (int i = threadIdx.x; i < kRegions; i += blockDim.x) ctrl->region_fill[i] = 0u;
   if (threadIdx.x == 0) {
     ctrl->L = 0u;
-    ctrl->page_next = 0u;
     ctrl->overflow = 0u;
     ctrl->mode = MODE_CAND;
-    ctrl->ncand = 0ull;
-    ctrl->krem = krem;
     ctrl->prefix = 0u;
     ctrl->T = 0u;
+    ctrl->ncand = 0ull;
+    ctrl->krem = krem;
     ctrl->need = 0ull;
     ctrl->nchunks = 0ull;
   }
@@ -188,22 +206,46 @@ __global__ void k_sample(const float* __restrict__ g, const float* __restrict__ 
                          uint32_t* __restrict__ keys) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < m;
        i += (int64_t)gridDim.x * blockDim.x) {
-    // i < 2^20 and n <= 2^40, so the products stay below 2^61
+    // i < 2^20 and n <= 2^40, so the products stay below 2^61, and hi - lo <= 2^20
     const int64_t lo = (int64_t)(((uint64_t)i * (uint64_t)n) / (uint64_t)m);
     const int64_t hi = (int64_t)(((uint64_t)(i + 1) * (uint64_t)n) / (uint64_t)m);
-    const int64_t p = lo + (int64_t)(mix64((uint64_t)i) % (uint64_t)(hi - lo));
+    const uint64_t h = mix64((uint64_t)i) >> 32;
+    const int64_t p = lo + (int64_t)((h * (uint64_t)(hi - lo)) >> 32);
     keys[i] = mag_key(g[p] + r[p]);
   }
 }
 
+
+__device__ __forceinline__ void hist_add(uint32_t* my, uint32_t key, uint32_t hshift, uint32_t want,
+                                         int shift, uint32_t mask) {
+  if ((key >> hshift) == want) atomicAdd(&my[(key >> shift) & mask], 1u);
+}
+
+// Histogram of nq quads plus a scalar tail of `count` floats starting at src (16-byte aligned).
+__device__ __forceinline__ void hist_span(const float* __restrict__ src, int64_t count, int64_t first,
+                                          int64_t stride, bool tail_owner, uint32_t* my,
+                                          uint32_t hshift, uint32_t want, int shift, uint32_t mask) {
+  const int64_t nq = count >> 2;
+  for (int64_t q = first; q < nq; q += stride) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(src + (q << 2));
+    hist_add(my, mag_key(v.x), hshift, want, shift, mask);
+    hist_add(my, mag_key(v.y), hshift, want, shift, mask);
+    hist_add(my, mag_key(v.z), hshift, want, shift, mask);
+    hist_add(my, mag_key(v.w), hshift, want, shift, mask);
+  }
+  if (tail_owner && threadIdx.x < (count & 3))
+    hist_add(my, mag_key(src[(nq << 2) + threadIdx.x]), hshift, want, shift, mask);
+}
+
 // Radix histogram pass over the key bits [shift, shift+bits) of the entries whose higher
-// bits equal the prefix fixed so far.  SRC 0: sample keys; SRC 1: candidates or full c.
+// bits equal the prefix fixed so far.  SRC 0: sample keys; SRC 1: the candidate pool
+// (region by region) or, in the fallback, the full c.
 template <int SRC>
 __global__ __launch_bounds__(kBlock) void k_hist(TopkCtrl* __restrict__ ctrl,
                                                  const uint32_t* __restrict__ sample_keys,
-                                                 int64_t sample_n, const float* __restrict__ cand,
-                                                 const float* __restrict__ full, int64_t n,
-                                                 int shift, int bits) {
+                                                 int64_t sample_n, const float* __restrict__ pool,
+                                                 int64_t region_cap, const float* __restrict__ full,
+                                                 int64_t n, int shift, int bits) {
   __shared__ uint32_t lh[kWaves][kBins];
   for (int i = threadIdx.x; i < kWaves * kBins; i += kBlock) (&lh[0][0])[i] = 0u;
   __syncthreads();
@@ -212,29 +254,15 @@ __global__ __launch_bounds__(kBlock) void k_hist(TopkCtrl* __restrict__ ctrl,
   const uint32_t mask = (1u << bits) - 1u;
   uint32_t* my = lh[threadIdx.x / kWave];
   const int64_t stride = (int64_t)gridDim.x * kBlock;
+  const int64_t first = (int64_t)blockIdx.x * kBlock + threadIdx.x;
   if (SRC == 0) {
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < sample_n; i += stride) {
-      const uint32_t key = sample_keys[i];
-      if ((key >> hshift) == want) atomicAdd(&my[(key >> shift) & mask], 1u);
-    }
+    for (int64_t i = first; i < sample_n; i += stride) hist_add(my, sample_keys[i], hshift, want, shift, mask);
+  } else if (ctrl->mode == MODE_CAND) {
+    for (int rg = 0; rg < kRegions; ++rg)
+      hist_span(pool + rg * region_cap, (int64_t)ctrl->region_fill[rg], first, stride,
+                blockIdx.x == (unsigned)(rg % gridDim.x), my, hshift, want, shift, mask);
   } else {
-    const bool use_cand = ctrl->mode == MODE_CAND;
-    const float* __restrict__ src = use_cand ? cand : full;
-    const int64_t cnt = use_cand ? (int64_t)ctrl->ncand : n;
-    const int64_t nq = cnt >> 2;
-    for (int64_t q = (int64_t)blockIdx.x * kBlock + threadIdx.x; q < nq; q += stride) {
-      const float4 v = *reinterpret_cast<const float4*>(src + (q << 2));
-      const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint32_t key = mag_key(vv[m]);
-        if ((key >> hshift) == want) atomicAdd(&my[(key >> shift) & mask], 1u);
-      }
-    }
-    if (blockIdx.x == 0 && threadIdx.x < (cnt & 3)) {
-      const uint32_t key = mag_key(src[(nq << 2) + threadIdx.x]);
-      if ((key >> hshift) == want) atomicAdd(&my[(key >> shift) & mask], 1u);
-    }
+    hist_span(full, n, first, stride, blockIdx.x == 0, my, hshift, want, shift, mask);
   }
   __syncthreads();
   for (int b = threadIdx.x; b < kBins; b += kBlock) {
@@ -294,17 +322,19 @@ __global__ __launch_bounds__(kBlock) void k_pick(TopkCtrl* __restrict__ ctrl, in
   }
 }
 
-// K1: the fused error-feedback add and candidate extraction.  Tiles are assigned
-// statically (tile = blockIdx.x + i*gridDim.x); each block appends its candidates to
-// its own open page and takes a new page with one atomic when the tile does not fit.
+
+// K1: the fused error-feedback add and candidate extraction, one tile per block.  The
+// non-persistent grid with 16-byte non-temporal loads and stores is the fastest
+// streaming shape measured on MI355X.  A tile with candidates claims its pool segment
+// with one atomic on the counter of region (tile % 32): few enough regions that a run of
+// consecutive tiles keeps its segments close together, enough to keep each counter cold.
 __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g, float* __restrict__ r,
-                                                    int64_t n, int64_t ntiles, TopkCtrl* __restrict__ ctrl,
+                                                    int64_t n, TopkCtrl* __restrict__ ctrl,
                                                     uint32_t* __restrict__ tile_start,
                                                     uint32_t* __restrict__ tile_count,
-                                                    uint32_t* __restrict__ page_fill,
                                                     float* __restrict__ pool_val,
                                                     uint16_t* __restrict__ pool_off,
-                                                    uint32_t cap_pages) {
+                                                    uint32_t region_cap) {
   __shared__ uint32_t s_cnt[kRounds * kWaves];
   __shared__ uint32_t s_off[kRounds * kWaves];
   __shared__ uint32_t s_total;
@@ -313,120 +343,121 @@ __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g,
   const uint32_t L = ctrl->L;
   const int w = threadIdx.x / kWave;
   const int lane = lane_id();
-  uint32_t page = kInvalid, fill = kPage;   // meaningful in thread 0 only
-  unsigned long long found = 0ull;          // thread 0 only
-  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int64_t base = tile * kTile;
-    float c[kRounds][4];
-    if (base + kTile <= n) {
-      f32x4 gv[kRounds], rv[kRounds];
-#pragma unroll
-      for (int j = 0; j < kRounds; ++j) {
-        const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4;
-        gv[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + e));
-        rv[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(r + e));
-      }
-#pragma unroll
-      for (int j = 0; j < kRounds; ++j) {
-        const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4;
-        f32x4 cv;
-        cv.x = gv[j].x + rv[j].x; cv.y = gv[j].y + rv[j].y;
-        cv.z = gv[j].z + rv[j].z; cv.w = gv[j].w + rv[j].w;
-        __builtin_nontemporal_store(cv, reinterpret_cast<f32x4*>(r + e));
-        c[j][0] = cv.x; c[j][1] = cv.y; c[j][2] = cv.z; c[j][3] = cv.w;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < kRounds; ++j) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4 + m;
-          float v = 0.f;
-          if (e < n) {
-            v = g[e] + r[e];
-            r[e] = v;
-          }
-          c[j][m] = v;
-        }
-      }
-    }
-    uint32_t nib[kRounds], pre[kRounds];
+  const int64_t tile = blockIdx.x;
+  const int64_t base = tile * kTile;
+  float c[kRounds][4];
+  if (base + kTile <= n) {
+    f32x4 gv[kRounds], rv[kRounds];
 #pragma unroll
     for (int j = 0; j < kRounds; ++j) {
-      uint32_t b = 0u;
+      const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4;
+      gv[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + e));
+      rv[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(r + e));
+    }
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4;
+      f32x4 cv;
+      cv.x = gv[j].x + rv[j].x; cv.y = gv[j].y + rv[j].y;
+      cv.z = gv[j].z + rv[j].z; cv.w = gv[j].w + rv[j].w;
+      __builtin_nontemporal_store(cv, reinterpret_cast<f32x4*>(r + e));
+      c[j][0] = cv.x; c[j][1] = cv.y; c[j][2] = cv.z; c[j][3] = cv.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4 + m;
-        b |= ((mag_key(c[j][m]) >= L) && e < n) ? (1u << m) : 0u;
-      }
-      nib[j] = b;
-      uint32_t wc;
-      pre[j] = rank_round(b, &wc);
-      if (lane == 0) s_cnt[j * kWaves + w] = wc;
-    }
-    __syncthreads();
-    block_scan32(s_cnt, s_off, &s_total);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const uint32_t total = s_total;
-      uint32_t start = 0u, ok = 1u;
-      if (total) {
-        if (fill + total > kPage) {
-          if (page < cap_pages) page_fill[page] = fill;
-          page = atomicAdd(&ctrl->page_next, 1u);
-          fill = 0u;
-          if (page >= cap_pages) atomicOr(&ctrl->overflow, 1u);
+        float v = 0.f;
+        if (e < n) {
+          v = g[e] + r[e];
+          r[e] = v;
         }
-        ok = page < cap_pages ? 1u : 0u;
-        start = ok ? page * kPage + fill : 0u;
-        fill += total;
+        c[j][m] = v;
       }
-      tile_start[tile] = start;
-      tile_count[tile] = total;
-      found += total;
-      s_base = start;
-      s_ok = ok;
     }
-    __syncthreads();
-    if (s_ok) {
+  }
+  uint32_t nib[kRounds], pre[kRounds];
 #pragma unroll
-      for (int j = 0; j < kRounds; ++j) {
-        if (nib[j]) {
-          uint32_t pos = s_base + s_off[j * kWaves + w] + pre[j];
+  for (int j = 0; j < kRounds; ++j) {
+    uint32_t b = 0u;
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            if (nib[j] & (1u << m)) {
-              pool_val[pos] = c[j][m];
-              pool_off[pos] = (uint16_t)(j * (kBlock * 4) + threadIdx.x * 4 + m);
-              ++pos;
-            }
+    for (int m = 0; m < 4; ++m) {
+      const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4 + m;
+      b |= ((mag_key(c[j][m]) >= L) && e < n) ? (1u << m) : 0u;
+    }
+    nib[j] = b;
+    uint32_t wc;
+    pre[j] = rank_round(b, &wc);
+    if (lane == 0) s_cnt[j * kWaves + w] = wc;
+  }
+  __syncthreads();
+  block_scan32(s_cnt, s_off, &s_total);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t total = s_total;
+    uint32_t start = 0u, ok = 1u;
+    if (total) {
+      const uint32_t region = (uint32_t)(tile & (kRegions - 1));
+      const uint32_t at = atomicAdd(&ctrl->region_fill[region], total);
+      if (at + total > region_cap) {
+        atomicOr(&ctrl->overflow, 1u);
+        ok = 0u;
+      } else {
+        start = region * region_cap + at;
+      }
+    }
+    tile_start[tile] = start;
+    tile_count[tile] = total;
+    s_base = start;
+    s_ok = ok;
+  }
+  __syncthreads();
+  if (s_ok) {
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      if (nib[j]) {
+        uint32_t pos = s_base + s_off[j * kWaves + w] + pre[j];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          if (nib[j] & (1u << m)) {
+            pool_val[pos] = c[j][m];
+            pool_off[pos] = (uint16_t)(j * (kBlock * 4) + threadIdx.x * 4 + m);
+            ++pos;
           }
         }
       }
     }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    if (page < cap_pages) page_fill[page] = fill;
-    atomicAdd(&ctrl->ncand, found);
   }
 }
 
-// Plain error-feedback add for k == 0: r = g + r.
-__global__ void k_ef_add(const float* __restrict__ g, float* __restrict__ r, int64_t n) {
-  const int64_t nq = n >> 2;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nq; q += stride) {
-    const float4 a = *reinterpret_cast<const float4*>(g + 4 * q);
-    float4 b = *reinterpret_cast<const float4*>(r + 4 * q);
-    b.x = a.x + b.x; b.y = a.y + b.y; b.z = a.z + b.z; b.w = a.w + b.w;
-    *reinterpret_cast<float4*>(r + 4 * q) = b;
-  }
-  if (blockIdx.x == 0 && threadIdx.x < (n & 3)) {
-    const int64_t e = 4 * nq + threadIdx.x;
-    r[e] = g[e] + r[e];
+
+// Plain error-feedback add for k == 0: r = g + r, in the same tile shape as K1.
+__global__ __launch_bounds__(kBlock) void k_ef_add(const float* __restrict__ g, float* __restrict__ r,
+                                                   int64_t n) {
+  const int64_t base = (int64_t)blockIdx.x * kTile;
+  if (base + kTile <= n) {
+    f32x4 gv[kRounds], rv[kRounds];
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4;
+      gv[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + e));
+      rv[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(r + e));
+    }
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4;
+      f32x4 cv;
+      cv.x = gv[j].x + rv[j].x; cv.y = gv[j].y + rv[j].y;
+      cv.z = gv[j].z + rv[j].z; cv.w = gv[j].w + rv[j].w;
+      __builtin_nontemporal_store(cv, reinterpret_cast<f32x4*>(r + e));
+    }
+  } else {
+    for (int64_t e = base + threadIdx.x; e < n; e += kBlock) r[e] = g[e] + r[e];
   }
 }
+
 
 // ---- multi-block exclusive scan of up to two uint32 count arrays ---------------------
 // Items are a[i] (and b[i] when b != nullptr); results are 64-bit exclusive prefixes.
@@ -525,22 +556,27 @@ __global__ __launch_bounds__(kBlock) void k_scan_down(const uint32_t* __restrict
   }
 }
 
+
 // Choose the source of the exact selection.  Candidates hold the answer iff the pool did
 // not overflow and at least k entries reached the bound L (then T >= L).
-__global__ void k_decide(TopkCtrl* __restrict__ ctrl, unsigned long long k, int64_t n) {
+__global__ void k_decide(TopkCtrl* __restrict__ ctrl, const unsigned long long* __restrict__ tile_excl,
+                         const uint32_t* __restrict__ tile_count, int64_t ntiles,
+                         unsigned long long k) {
   if (threadIdx.x == 0) {
-    const bool full = ctrl->overflow != 0u || ctrl->ncand < k;
+    const unsigned long long ncand = tile_excl[ntiles - 1] + tile_count[ntiles - 1];
+    ctrl->ncand = ncand;
+    const bool full = ctrl->overflow != 0u || ncand < k;
     ctrl->mode = full ? MODE_FULL : MODE_CAND;
-    const unsigned long long cnt = full ? (unsigned long long)n : ctrl->ncand;
-    ctrl->nchunks = (cnt + kTile - 1) / kTile;
+    ctrl->nchunks = full ? (unsigned long long)ntiles : (ncand + kTile - 1) / kTile;
   }
 }
 
-// Copy each tile's candidates from the pool into one array in index order.  Block b
-// handles the tiles it produced in K1 (b, b+G, ...); within a batch of up to 1024 such
-// tiles the entries are spread over threads and mapped back to (tile, offset) by binary
-// search over the batch's in-block prefix.
-__global__ __launch_bounds__(kBlock) void k_reorder(const TopkCtrl* __restrict__ ctrl, int64_t ntiles, int grid1,
+// Copy each tile's candidates from the pool into one array in index order.  Work is
+// cut into batches of 128 consecutive tiles, taken grid-stride so that runs of dense
+// tiles (a layer with a large scale can hold ten times the average) spread over all
+// blocks.  A batch's entries are spread over the threads and mapped back to
+// (tile, offset) by binary search over the in-batch prefix of the tile counts.
+__global__ __launch_bounds__(kBlock) void k_reorder(const TopkCtrl* __restrict__ ctrl, int64_t ntiles,
                                                     const uint32_t* __restrict__ tile_start,
                                                     const uint32_t* __restrict__ tile_count,
                                                     const unsigned long long* __restrict__ tile_excl,
@@ -548,72 +584,79 @@ __global__ __launch_bounds__(kBlock) void k_reorder(const TopkCtrl* __restrict__
                                                     const uint16_t* __restrict__ pool_off,
                                                     float* __restrict__ cand_val,
                                                     int64_t* __restrict__ cand_idx) {
-  constexpr int kB = 1024;
+  constexpr int kB = 128;
+  constexpr int kU = 8;      // independent entries per thread per iteration
   __shared__ uint32_t s_pre[kB + 1];
   __shared__ uint32_t s_start[kB];
   __shared__ unsigned long long s_excl[kB];
-  __shared__ uint32_t s_w[kWaves];
+  __shared__ uint32_t s_w[2];
   if (ctrl->mode != MODE_CAND) return;
-  const int w = threadIdx.x / kWave;
-  for (int b = blockIdx.x; b < grid1; b += gridDim.x) {
-    const int64_t my_tiles = b < ntiles ? cdiv(ntiles - b, grid1) : 0;
-    for (int64_t t0 = 0; t0 < my_tiles; t0 += kB) {
-      const int nt = (int)(my_tiles - t0 < kB ? my_tiles - t0 : kB);
-      // per-tile data and the in-batch exclusive prefix of the counts
-      uint32_t cnt4[4];
-      uint32_t local = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int li = threadIdx.x * 4 + i;
-        uint32_t cn = 0;
-        if (li < nt) {
-          const int64_t tile = b + (t0 + li) * (int64_t)grid1;
-          cn = tile_count[tile];
-          s_start[li] = tile_start[tile];
-          s_excl[li] = tile_excl[tile];
-        }
-        cnt4[i] = cn;
-        local += cn;
+  const int64_t nbatch = cdiv(ntiles, kB);
+  for (int64_t bt = blockIdx.x; bt < nbatch; bt += gridDim.x) {
+    const int64_t t0 = bt * kB;
+    const int nt = (int)(ntiles - t0 < kB ? ntiles - t0 : kB);
+    if (threadIdx.x < kB) {
+      const int li = threadIdx.x;
+      uint32_t cn = 0;
+      if (li < nt) {
+        cn = tile_count[t0 + li];
+        s_start[li] = tile_start[t0 + li];
+        s_excl[li] = tile_excl[t0 + li];
       }
-      uint32_t inc = local;
+      uint32_t inc = cn;
 #pragma unroll
       for (int d = 1; d < kWave; d <<= 1) {
         const uint32_t o = (uint32_t)__shfl_up((int)inc, d, kWave);
         if (lane_id() >= d) inc += o;
       }
-      if (lane_id() == kWave - 1) s_w[w] = inc;
-      __syncthreads();
-      uint32_t p = inc - local;
-      for (int i = 0; i < w; ++i) p += s_w[i];
+      if (lane_id() == kWave - 1) s_w[li / kWave] = inc;
+      s_pre[li] = inc - cn;   // exclusive within the wave; the second wave adds s_w[0] below
+    }
+    __syncthreads();
+    if (threadIdx.x >= kWave && threadIdx.x < kB) s_pre[threadIdx.x] += s_w[0];
+    const uint32_t total = s_w[0] + s_w[1];
+    // for nt < kB the padding entry s_pre[nt] (count 0) already holds the total
+    if (threadIdx.x == 0 && nt == kB) s_pre[kB] = total;
+    __syncthreads();
+    for (uint32_t j0 = 0; j0 < total; j0 += kBlock * kU) {
+      uint32_t src[kU];
+      unsigned long long dst[kU];
+      int64_t tbase[kU];
+      bool live[kU];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int li = threadIdx.x * 4 + i;
-        if (li < nt) s_pre[li] = p;
-        p += cnt4[i];
-      }
-      const uint32_t total = s_w[0] + s_w[1] + s_w[2] + s_w[3];
-      if (threadIdx.x == 0) s_pre[nt] = total;
-      __syncthreads();
-      for (uint32_t j = threadIdx.x; j < total; j += kBlock) {
-        // last tile whose prefix is <= j
+      for (int u = 0; u < kU; ++u) {
+        const uint32_t j = j0 + u * kBlock + threadIdx.x;
+        live[u] = j < total;
         int lo = 0, hi = nt;   // invariant: s_pre[lo] <= j < s_pre[hi]
         while (hi - lo > 1) {
           const int mid = (lo + hi) >> 1;
           if (s_pre[mid] <= j) lo = mid; else hi = mid;
         }
         const uint32_t o = j - s_pre[lo];
-        const uint32_t src = s_start[lo] + o;
-        const unsigned long long dst = s_excl[lo] + o;
-        const int64_t tile = b + (t0 + lo) * (int64_t)grid1;
-        cand_val[dst] = pool_val[src];
-        cand_idx[dst] = tile * kTile + pool_off[src];
+        src[u] = s_start[lo] + o;
+        dst[u] = s_excl[lo] + o;
+        tbase[u] = (t0 + lo) * kTile;
       }
-      __syncthreads();
+      float v[kU];
+      uint32_t off[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        v[u] = live[u] ? pool_val[src[u]] : 0.f;
+        off[u] = live[u] ? pool_off[src[u]] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (live[u]) {
+          cand_val[dst[u]] = v[u];
+          cand_idx[dst[u]] = tbase[u] + off[u];
+        }
     }
+    __syncthreads();
   }
 }
 
-// Per-chunk counts of key > T and key == T over the selected source.
+// Per-chunk counts of key > T and key == T over the selected source (the ordered
+// candidates, or the full c in the fallback).
 __global__ __launch_bounds__(kBlock) void k_count(const TopkCtrl* __restrict__ ctrl,
                                                   const float* __restrict__ cand,
                                                   const float* __restrict__ full, int64_t n,
@@ -631,10 +674,9 @@ __global__ __launch_bounds__(kBlock) void k_count(const TopkCtrl* __restrict__ c
 #pragma unroll
     for (int j = 0; j < kRounds; ++j) {
       const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4;
-      float v[4];
       if (e + 4 <= cnt) {
-        const float4 a = *reinterpret_cast<const float4*>(src + e);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(src + e);
+        const float v[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const uint32_t key = mag_key(v[m]);
@@ -692,7 +734,7 @@ __global__ __launch_bounds__(kBlock) void k_emit(const TopkCtrl* __restrict__ ct
     for (int j = 0; j < kRounds; ++j) {
       const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4;
       if (e + 4 <= cnt) {
-        const float4 a = *reinterpret_cast<const float4*>(src + e);
+        const f32x4 a = *reinterpret_cast<const f32x4*>(src + e);
         v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
       } else {
 #pragma unroll
@@ -764,7 +806,7 @@ __global__ __launch_bounds__(kBlock) void k_emit(const TopkCtrl* __restrict__ ct
 }
 
 // QSGD over the kept values (groups in kept order, RNG index = kept position) and the
-// residual fix-up r[idx] = v - g_hat.
+// residual update r[idx] = v - g_hat.
 __global__ __launch_bounds__(kBlock) void k_qsgd_kept(const float* __restrict__ vals, int64_t k,
                                                       int lpg_log2, float s, uint64_t seed,
                                                       int8_t* __restrict__ codes, float* __restrict__ norms,
@@ -781,7 +823,7 @@ __global__ __launch_bounds__(kBlock) void k_qsgd_kept(const float* __restrict__ 
     const bool full = e0 + 4 <= k;
     float v[4];
     if (live && full) {
-      const float4 a = *reinterpret_cast<const float4*>(vals + e0);
+      const f32x4 a = *reinterpret_cast<const f32x4*>(vals + e0);
       v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     } else {
 #pragma unroll
@@ -831,42 +873,36 @@ hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, i
   if (n == 0) return hipSuccess;
   const int cus = device_cu_count();
   if (k == 0) {
-    hipLaunchKernelGGL(k_ef_add, clamp_grid(cdiv(n, 4 * 256), cus * 16), 256, 0, s, grad, res, n);
+    hipLaunchKernelGGL(k_ef_add, (unsigned)cdiv(n, kTile), kBlock, 0, s, grad, res, n);
     return hipGetLastError();
   }
   prof_mark(s, 0);
   const bool quant = qsgd_levels > 0;
-  const Layout l = make_layout(ws, n, k, quant && out_val == nullptr);
+  // the workspace is laid out for the largest use (QSGD with staging); out_val given or
+  // not, the carve-outs stay where the size query put them
+  const Layout l = make_layout(ws, n, k, quant);
   TopkCtrl* ctrl = l.ctrl;
 
   // 1-2: sample and conservative bound L on the k-th largest key
-  const int64_t m = n < kSampleMax ? n : kSampleMax;
-  int64_t j;
-  if (m == n) {
-    j = k;
-  } else {
-    const double expect = (double)k * (double)m / (double)n;
-    j = (int64_t)(1.25 * expect + 8.0 * __builtin_sqrt(expect) + 16.0) + 1;
-    if (j > m) j = m;
-  }
+  const int64_t m = sample_size(n);
+  const int64_t j = sample_rank(n, k);
   hipLaunchKernelGGL(k_init, 1, 256, 0, s, ctrl, (unsigned long long)j);
   hipLaunchKernelGGL(k_sample, clamp_grid(cdiv(m, 256), cus * 8), 256, 0, s, grad, res, n, m, l.sample);
   const int shifts[3] = {20, 9, 0}, widths[3] = {11, 11, 9};
   const int sgrid = clamp_grid(cdiv(m, 256 * 8), cus * 2);
   for (int p = 0; p < 3; ++p) {
     hipLaunchKernelGGL((k_hist<0>), sgrid, kBlock, 0, s, ctrl, l.sample, m, (const float*)nullptr,
-                       (const float*)nullptr, n, shifts[p], widths[p]);
+                       (int64_t)0, (const float*)nullptr, n, shifts[p], widths[p]);
     hipLaunchKernelGGL(k_pick, 1, kBlock, 0, s, ctrl, shifts[p], p == 2 ? 1 : 0, (unsigned long long)k);
   }
 
   // 3: the streaming pass
-  const int grid1 = (int)(l.ntiles < kMaxGrid ? l.ntiles : kMaxGrid);
   prof_mark(s, 1);
-  hipLaunchKernelGGL(k_ef_cand, grid1, kBlock, 0, s, grad, res, n, l.ntiles, ctrl, l.tile_start,
-                     l.tile_count, l.page_fill, l.pool_val, l.pool_off, (uint32_t)l.cap_pages);
+  hipLaunchKernelGGL(k_ef_cand, (unsigned)l.ntiles, kBlock, 0, s, grad, res, n, ctrl, l.tile_start,
+                     l.tile_count, l.pool_val, l.pool_off, (uint32_t)l.region_cap);
   prof_mark(s, 2);
 
-  // 4: tile offsets, source decision
+  // 4: candidate total and offsets, source decision
   const int scan_grid = clamp_grid(cdiv(l.ntiles, kScanChunk), cus * 4);
   hipLaunchKernelGGL(k_scan_up, scan_grid, kBlock, 0, s, l.tile_count, (const uint32_t*)nullptr,
                      (const unsigned long long*)nullptr, l.ntiles, l.scan_up);
@@ -874,20 +910,21 @@ hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, i
   hipLaunchKernelGGL(k_scan_down, scan_grid, kBlock, 0, s, l.tile_count, (const uint32_t*)nullptr,
                      (const unsigned long long*)nullptr, l.ntiles, (const unsigned long long*)l.scan_up,
                      l.tile_excl, (unsigned long long*)nullptr);
-  hipLaunchKernelGGL(k_decide, 1, 64, 0, s, ctrl, (unsigned long long)k, n);
+  hipLaunchKernelGGL(k_decide, 1, 64, 0, s, ctrl, (const unsigned long long*)l.tile_excl,
+                     (const uint32_t*)l.tile_count, l.ntiles, (unsigned long long)k);
 
-  // 5: candidates in index order
-  hipLaunchKernelGGL(k_reorder, clamp_grid(grid1, cus * 8), kBlock, 0, s, ctrl, l.ntiles, grid1,
-                     l.tile_start, l.tile_count, l.tile_excl, l.pool_val, l.pool_off, l.cand_val,
-                     l.cand_idx);
-
-  // 6: exact k-th key over the selected source
+  // 5: exact k-th key over the selected source
   const int hgrid = cus * 4;
   for (int p = 0; p < 3; ++p) {
     hipLaunchKernelGGL((k_hist<1>), hgrid, kBlock, 0, s, ctrl, (const uint32_t*)nullptr, (int64_t)0,
-                       l.cand_val, res, n, shifts[p], widths[p]);
+                       (const float*)l.pool_val, l.region_cap, (const float*)res, n, shifts[p], widths[p]);
     hipLaunchKernelGGL(k_pick, 1, kBlock, 0, s, ctrl, shifts[p], p == 2 ? 2 : 0, (unsigned long long)k);
   }
+
+  // 6: candidates in index order
+  hipLaunchKernelGGL(k_reorder, clamp_grid(cdiv(l.ntiles, 128), cus * 8), kBlock, 0, s, ctrl, l.ntiles,
+                     l.tile_start, l.tile_count, l.tile_excl, l.pool_val, l.pool_off, l.cand_val,
+                     l.cand_idx);
 
   // 7: ordered compaction
   const int cgrid = clamp_grid(l.max_chunks, cus * 8);
@@ -897,18 +934,19 @@ hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, i
   hipLaunchKernelGGL(k_scan_up, cscan, kBlock, 0, s, l.chunk_gt, l.chunk_eq, nch_dev, (int64_t)0, l.scan_up);
   hipLaunchKernelGGL(k_scan_mid, 1, kBlock, 0, s, nch_dev, (int64_t)0, l.scan_up);
   hipLaunchKernelGGL(k_scan_down, cscan, kBlock, 0, s, l.chunk_gt, l.chunk_eq, nch_dev, (int64_t)0,
-                     (const unsigned long long*)l.scan_up, l.chunk_gt_excl, l.chunk_eq_excl);
+                     (const unsigned long long*)l.scan_up, l.gt_excl, l.eq_excl);
   float* vals = quant ? (out_val ? out_val : l.staging) : out_val;
-  hipLaunchKernelGGL(k_emit, cgrid, kBlock, 0, s, ctrl, l.cand_val, l.cand_idx, res, n, l.chunk_gt_excl,
-                     l.chunk_eq_excl, index_base, out_idx, vals, quant ? 0 : 1, k);
+  hipLaunchKernelGGL(k_emit, cgrid, kBlock, 0, s, ctrl, l.cand_val, l.cand_idx, res, n, l.gt_excl,
+                     l.eq_excl, index_base, out_idx, vals, quant ? 0 : 1, k);
 
-  // 8: QSGD on the kept values
+  // 8: QSGD on the kept values and the residual of the kept set
   if (quant) {
     int lpg_log2 = 0;
     while ((int64_t(4) << lpg_log2) < qsgd_group) ++lpg_log2;
     const int qgrid = clamp_grid(cdiv(cdiv(k, 4), kBlock), cus * 16);
-    hipLaunchKernelGGL(k_qsgd_kept, qgrid, kBlock, 0, s, vals, k, lpg_log2, (float)qsgd_levels, qsgd_seed,
-                       out_codes, out_norms, out_idx, index_base, res, n);
+    hipLaunchKernelGGL(k_qsgd_kept, qgrid, kBlock, 0, s, (const float*)vals, k, lpg_log2, (float)qsgd_levels,
+                       qsgd_seed, out_codes, out_norms, (const int64_t*)out_idx, index_base,
+                       res, n);
   }
   prof_mark(s, 3);
   return hipGetLastError();

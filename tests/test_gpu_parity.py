@@ -285,3 +285,12 @@ def test_decompress_all_kinds(gc):
                                   meta0=None if m0 is None else dev(m0), meta1=None if m1 is None else dev(m1),
                                   group=group, levels=levels, alpha=alpha, accumulate=bool(acc))
             assert_bits_equal(host(out), want, f"scatter kind {kind}")
+
+
+def test_topk_small_k_on_large_n(gc):
+    # k far below the sample's resolution: the candidate pool is sized from the bound
+    n = 9_000_001
+    g = workloads.bucket(n, seed=21)
+    r = np.zeros(n, F32)
+    for k in (1, 7, 1000):
+        check_topk(gc, g, r, k)
