@@ -37,12 +37,15 @@ def parse():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--layer-len", type=int, default=218_750_000)
     ap.add_argument("--ratio", type=float, default=0.01)
-    ap.add_argument("--cpu-sample-log2", type=int, default=25,
+    ap.add_argument("--cpu-sample-log2", type=int, default=27,
                     help="elements in the oracle's sample (2^N, split over the same 32 layers)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="run one device-to-device copy of this many GiB before the timed region "
                          "(a plain copy of known size for calibrating HBM byte counters)")
+    ap.add_argument("--rows", action="store_true",
+                    help="instead of the metric line, print one JSON line per compressor: each "
+                         "timed on the GPU against the HBM roofline, with the oracle timed beside it")
     return ap.parse_args()
 
 
@@ -69,6 +72,260 @@ def cpu_baseline(args, n_layers):
                    f"{dt:.2f} s on one core (numpy sort-based oracle); host has {os.cpu_count()} cpus"),
     }
 
+# ---------------------------------------------------------------------------
+# Per-compressor lines (--rows).  Each op runs on its own workload from the
+# seeded generators; the GPU side is timed with events on the launch stream
+# (single calls eagerly, back-to-back throughput as a replayed HIP graph of
+# several calls on distinct buffers, so that launch overhead does not hide the
+# kernels), and the oracle is timed beside it on the same (or a sampled) input.
+# ---------------------------------------------------------------------------
+
+def _median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2]
+
+
+def _eager_ms(torch, fn, reps=30, before=None):
+    """Median over reps of one call bracketed by events (before() runs outside them)."""
+    for _ in range(3):
+        if before:
+            before()
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        if before:
+            before()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    return _median(ts)
+
+
+def _graph_ms(torch, fn_list, reps=7):
+    """Capture the calls in one graph, replay it reps times; median ms per call."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for fn in fn_list:
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for fn in fn_list:
+                fn()
+        torch.cuda.synchronize()
+        run = g.replay
+    except RuntimeError as e:          # capture refused: time the same calls eagerly
+        print(f"[rows] graph capture failed ({e}); timing eager back-to-back calls", file=sys.stderr)
+        torch.cuda.synchronize()
+
+        def run():
+            for fn in fn_list:
+                fn()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run()
+        b.record()
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    return _median(ts) / len(fn_list), run
+
+
+def _oracle_s(fn):
+    t0 = time.perf_counter()
+    fn()
+    return time.perf_counter() - t0
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
+                   default=1)
+    except Exception:
+        return None
+
+
+def _row(name, workload, unit_bytes, unit, gpu_ms, eager_ms, oracle_s=None, oracle_units=1.0,
+         sample="", cores=1, extra=None):
+    achieved = unit_bytes / (gpu_ms / 1e3) / 1e9
+    line = {
+        "row": name, "workload": workload, "unit": unit,
+        "algorithmic_bytes_per_unit": unit_bytes,
+        "ms_per_unit": round(gpu_ms, 5), "eager_call_ms": round(eager_ms, 5),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)},
+    }
+    if oracle_s is not None:
+        per_unit = oracle_s / oracle_units
+        line["cpu_oracle"] = {"s_per_unit": round(per_unit, 4), "cores": cores, "kind": "oracle",
+                              "sample": sample, "gpu_speedup": round(per_unit * 1e3 / gpu_ms, 1)}
+    if extra:
+        line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+def rows_mode(args):
+    import numpy as np
+    import torch
+    import gradient_compression_ddp_amd as gc
+    import workloads
+    orc = None
+    if not args.no_cpu:
+        import oracle as orc
+    dev = torch.device("cuda:0")
+    say = lambda m: print(f"[rows] {m}", file=sys.stderr, flush=True)
+
+    # c1: EF Top-K on the 1e6 demo gradient, k = 1e4 (cache-resident; latency).
+    g1, _ = workloads.ef_demo_gradients()
+    n, k = g1.size, workloads.DEMO_K
+    say("EF Top-K demo")
+    gd = torch.from_numpy(g1).to(dev)
+    r0 = torch.zeros_like(gd)
+    rs = [torch.zeros_like(gd) for _ in range(8)]
+    ws = torch.empty(gc.workspace_size(gc.OP_EF_TOPK, n, k, 0), dtype=torch.uint8, device=dev)
+    oi = [torch.empty(k, dtype=torch.int64, device=dev) for _ in range(8)]
+    ov = [torch.empty(k, dtype=torch.float32, device=dev) for _ in range(8)]
+    r = torch.zeros_like(gd)
+    eager = _eager_ms(torch, lambda: gc.ef_topk(gd, r, k, out_idx=oi[0], out_val=ov[0], workspace=ws),
+                      before=lambda: r.copy_(r0))
+    gms, _ = _graph_ms(torch, [lambda i=i: gc.ef_topk(gd, rs[i], k, out_idx=oi[i], out_val=ov[i], workspace=ws)
+                               for i in range(8)])
+    osec = _oracle_s(lambda: orc.ef_topk(g1, np.zeros_like(g1), k)) if orc else None
+    _row("a1-a3 EF Top-K (pure)", f"n=1,000,000 N(0,1), k=10,000", 12.0 * n + 12.0 * k, "call", gms, eager,
+         osec, 1.0, "the same 1e6 input")
+
+    # c1: per-tensor int8 min-max on the demo gradient.
+    say("min-max per tensor")
+    ws_m = gc.workspace_size(gc.OP_QUANT_MINMAX, n, 0, 0)
+    wsm = torch.empty(max(ws_m, 1), dtype=torch.uint8, device=dev)
+    cm = torch.empty(n, dtype=torch.uint8, device=dev)
+    mn = torch.empty(1, dtype=torch.float32, device=dev)
+    sc = torch.empty(1, dtype=torch.float32, device=dev)
+    f = lambda: gc.quant_minmax(gd, 0, 8, codes=cm, mins=mn, scales=sc, workspace=wsm)
+    eager = _eager_ms(torch, f)
+    gms, _ = _graph_ms(torch, [f] * 8)
+    osec = _oracle_s(lambda: orc.quant_minmax(g1, 0, 8)) if orc else None
+    _row("a4 min-max int8, per tensor", "n=1,000,000 N(0,1)", 5.0 * n + 8, "call", gms, eager, osec, 1.0,
+         "the same 1e6 input")
+
+    # c2: one 25 MiB bucket; 40 distinct copies for back-to-back throughput.
+    NB = 40
+    xb = workloads.bucket()
+    n = xb.size
+    ng = n // 64
+    x40 = torch.from_numpy(xb).to(dev).repeat(NB)
+    xs = [x40[i * n:(i + 1) * n] for i in range(NB)]
+    for bits in (8, 4):
+        say(f"min-max int{bits} gs64")
+        nc = n if bits == 8 else (n + 1) // 2
+        codes = torch.empty(NB * nc, dtype=torch.uint8, device=dev)
+        mins = torch.empty(NB * ng, dtype=torch.float32, device=dev)
+        scales = torch.empty(NB * ng, dtype=torch.float32, device=dev)
+        wsz = gc.workspace_size(gc.OP_QUANT_MINMAX, n, 64, 0)
+        wsb = torch.empty(max(wsz, 1), dtype=torch.uint8, device=dev)
+        fns = [lambda i=i: gc.quant_minmax(xs[i], 64, bits, codes=codes[i * nc:(i + 1) * nc],
+                                           mins=mins[i * ng:(i + 1) * ng], scales=scales[i * ng:(i + 1) * ng],
+                                           workspace=wsb) for i in range(NB)]
+        eager = _eager_ms(torch, fns[0])
+        gms, _ = _graph_ms(torch, fns)
+        osec = _oracle_s(lambda: orc.quant_minmax(xb, 64, bits)) if orc else None
+        ub = (5.0 if bits == 8 else 4.5) * n + 8.0 * ng
+        _row(f"a4 min-max int{bits}, groups of 64", "25 MiB bucket: n=6,553,600 t(3)*1e-3, 40 buckets",
+             ub, "bucket", gms, eager, osec, 1.0, "one bucket")
+
+    say("QSGD s=15 gs64")
+    qc = torch.empty(NB * n, dtype=torch.int8, device=dev)
+    qn = torch.empty(NB * ng, dtype=torch.float32, device=dev)
+    fns = [lambda i=i: gc.qsgd(xs[i], 64, 15, 7, 0, codes=qc[i * n:(i + 1) * n], norms=qn[i * ng:(i + 1) * ng])
+           for i in range(NB)]
+    eager = _eager_ms(torch, fns[0])
+    gms, _ = _graph_ms(torch, fns)
+    osec = _oracle_s(lambda: orc.qsgd(xb, 64, 15, 7)) if orc else None
+    _row("a5+a6 QSGD s=15, groups of 64 (Philox4x32-10)", "25 MiB bucket, 40 buckets",
+         5.0 * n + 4.0 * ng, "bucket", gms, eager, osec, 1.0, "one bucket")
+
+    say("decompress QSGD / min-max int8 dense")
+    outb = torch.empty(NB * n, dtype=torch.float32, device=dev)
+    fns = [lambda i=i: gc.decompress_scatter(gc.KIND_QSGD, qc[i * n:(i + 1) * n], n, outb[i * n:(i + 1) * n],
+                                             meta0=qn[i * ng:(i + 1) * ng], group=64, levels=15)
+           for i in range(NB)]
+    eager = _eager_ms(torch, fns[0])
+    gms, _ = _graph_ms(torch, fns)
+    qc0, qn0 = qc[:n].cpu().numpy(), qn[:ng].cpu().numpy()
+    osec = _oracle_s(lambda: orc.decompress_scatter(orc.KIND_QSGD, None, n, 0, qc0, qn0, None, 64, 15, 1.0,
+                                                    False, np.empty(n, np.float32))) if orc else None
+    _row("a9 decompress QSGD, dense", "25 MiB bucket of codes, 40 buckets", 5.0 * n + 4.0 * ng, "bucket",
+         gms, eager, osec, 1.0, "one bucket")
+    del x40, xs, codes, mins, scales, qc, qn, outb
+
+    # a9 scatter: the pure Top-K payload of the demo gradient, accumulated into a dense buffer.
+    say("scatter f32 payload")
+    idx, val = gc.ef_topk(gd, torch.zeros_like(gd), k)
+    outs = torch.zeros_like(gd)
+    f = lambda: gc.decompress_scatter(gc.KIND_F32, val, k, outs, idx=idx, accumulate=True)
+    eager = _eager_ms(torch, f)
+    gms, _ = _graph_ms(torch, [f] * 8)
+    i0, v0 = idx.cpu().numpy(), val.cpu().numpy()
+    osec = _oracle_s(lambda: orc.decompress_scatter(orc.KIND_F32, i0, k, 0, v0, None, None, 0, 0, 1.0, True,
+                                                    np.zeros(g1.size, np.float32))) if orc else None
+    _row("a9 scatter-accumulate f32", "k=10,000 of n=1,000,000", 8.0 * k + 4.0 * k + 8.0 * k, "call",
+         gms, eager, osec, 1.0, "the same payload")
+    del gd, r0, rs, r, ws
+
+    # c3: TernGrad over 24 layers of 14,583,333 (~350M parameters), one segmented call.
+    say("TernGrad 24 layers")
+    L3, LL3 = workloads.TERN_LAYERS, workloads.TERN_LAYER_LEN
+    xt = workloads.layered_torch(L3, LL3, step=0, device=dev, seed=3)
+    off = np.arange(L3 + 1, dtype=np.int64) * LL3
+    n3 = L3 * LL3
+    nbytes = L3 * ((LL3 + 3) // 4)
+    pk = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    scl = torch.empty(L3, dtype=torch.float32, device=dev)
+    wst = torch.empty(max(gc.workspace_size(gc.OP_TERNGRAD, n3, L3, 0), 1), dtype=torch.uint8, device=dev)
+    f = lambda: gc.terngrad(xt, off, 3, 0, packed=pk, scales=scl, workspace=wst)
+    eager = _eager_ms(torch, f, reps=10)
+    gms, _ = _graph_ms(torch, [f] * 4, reps=5)
+    osec = None
+    if orc:
+        h = xt[:LL3].cpu().numpy()
+        osec = _oracle_s(lambda: orc.terngrad(h, [0, LL3], 3))
+    _row("a5+a7 TernGrad, per-layer scale", "24 layers x 14,583,333 (t(3) x lognormal(-7,1) scales)",
+         4.0 * n3 + nbytes + 4.0 * L3, "call (all 24 layers)", gms, eager, osec, 1.0 / L3,
+         "one layer of 14,583,333, scaled by 24")
+    del xt, pk, wst
+
+    # c4: PowerSGD rank 4 on the three matrix shapes, error feedback on.
+    qs = workloads.psgd_initial_q()
+    for j, (rows, cols) in enumerate(workloads.PSGD_SHAPES):
+        say(f"PowerSGD {rows}x{cols}")
+        G = torch.from_numpy(workloads.psgd_gradient(1, j, (rows, cols))).to(dev)
+        Es = [torch.zeros_like(G) for _ in range(2)]
+        Qs = [torch.from_numpy(qs[j]).to(dev) for _ in range(2)]
+        Ps = [torch.empty((rows, 4), dtype=torch.float32, device=dev) for _ in range(2)]
+        wsp = torch.empty(gc.workspace_size(gc.OP_POWERSGD, rows, cols, 4), dtype=torch.uint8, device=dev)
+        fns = [lambda i=i: gc.powersgd_step(G, Es[i], Qs[i], P=Ps[i], workspace=wsp) for i in range(2)]
+        eager = _eager_ms(torch, fns[0], reps=10)
+        gms, _ = _graph_ms(torch, fns * 2, reps=5)
+        osec, thr = None, None
+        if orc:
+            Gh = G.cpu().numpy()
+            osec = _oracle_s(lambda: orc.powersgd_step(Gh, np.zeros_like(Gh), qs[j]))
+            thr = _blas_threads()
+        flops = 2.0 * rows * cols * 4 * 3
+        _row(f"a8 PowerSGD rank 4", f"{rows}x{cols} N(0, 1e-4), E on", 24.0 * rows * cols, "step",
+             gms, eager, osec, 1.0, "the same matrix, float64 BLAS", cores=thr,
+             extra={"tflops_three_passes": round(flops / (gms / 1e3) / 1e12, 3)})
+        del G, Es, Qs, Ps, wsp
+
 
 def main():
     args = parse()
@@ -76,6 +333,9 @@ def main():
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the compression kernels run per GPU; no collectives are built)", file=sys.stderr)
         sys.exit(2)
+    if args.rows:
+        rows_mode(args)
+        return
 
     import torch
     import gradient_compression_ddp_amd as gc

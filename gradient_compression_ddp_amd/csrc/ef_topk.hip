@@ -21,11 +21,14 @@
 //              count >= k); otherwise the exact fallback selects over the full c;
 //  5. select   the exact k-th largest key T by three radix passes (11, 11, 9 bits) with
 //              LDS histograms, and `need`, the number of entries with key == T to keep;
-//  6. reorder  the candidates into one array in index order (entry-parallel over batches
-//              of 128 tiles, taken grid-stride so dense layers spread over all blocks);
-//  7. count + scan + emit: ordered compaction of {key > T} plus the first `need` entries
-//              with key == T (block-level ballot ranks over chunks of 4096 candidates);
-//              pure Top-K also sets the residual at kept positions to +0.0;
+//  6. count    per batch of 128 tiles, the candidates with key > T and key == T, and an
+//              exclusive scan of both over the batches;
+//  7. emit     ordered compaction straight from the pool: a batch's candidates are taken
+//              in (tile, offset) order, which is index order, and entry e goes to
+//              position gt_before(e) + min(eq_before(e), need) when key > T, or when
+//              key == T and eq_before(e) < need (so the lower index wins the ties); pure
+//              Top-K also sets the residual at kept positions to +0.0.  The fallback
+//              runs the same count / scan / emit over tiles of the full c;
 //  8. QSGD     (optional) on the kept values, groups in kept order, RNG index = kept
 //              position, and the new residual v - g_hat scattered to the kept positions.
 // HBM traffic is 12 B per element in K1 (read g and r, write c) plus O(candidates) plus
@@ -46,6 +49,8 @@ constexpr int kRegions = 32;                 // candidate-pool regions (tile % 3
 constexpr int kSampleMax = 1 << 20;
 constexpr int kScanChunk = 1024;             // items per block in the multi-block scan
 constexpr int kBins = 2048;
+constexpr int kBatch = 128;                  // tiles per batch of the candidate count / emit
+static_assert(kBatch == 2 * kWave, "the batch table scan assumes two waves");
 
 enum : uint32_t { MODE_CAND = 0, MODE_FULL = 1 };
 
@@ -62,6 +67,7 @@ struct TopkCtrl {
   unsigned long long nchunks; // tiles of the full fallback source
   unsigned long long hist[kBins];
   uint32_t region_fill[kRegions];
+  uint32_t batch_next[2];     // work queues of the batch count and the batch emit
 };
 
 struct Layout {
@@ -69,13 +75,11 @@ struct Layout {
   uint32_t* sample;        // [kSampleMax]
   uint32_t* tile_start;    // [ntiles] pool position of the tile's candidates
   uint32_t* tile_count;    // [ntiles] candidates of the tile
-  unsigned long long* tile_excl;  // [ntiles] exclusive prefix of the candidate counts
   unsigned long long* scan_up;    // [2 * scan blocks] block sums, then their exclusive scan
   float* pool_val;         // [pool] candidate values, region by region
   uint16_t* pool_off;      // [pool] offset of the candidate inside its tile
-  float* cand_val;         // [pool] candidates in index order
-  int64_t* cand_idx;       // [pool]
-  uint32_t* chunk_gt;      // [max_chunks] entries with key > T per chunk of the source
+  uint32_t* chunk_gt;      // [max_chunks] entries with key > T per batch (candidates) or
+                           //   per tile (fallback)
   uint32_t* chunk_eq;      // [max_chunks] entries with key == T
   unsigned long long* gt_excl;    // [max_chunks] exclusive prefixes
   unsigned long long* eq_excl;    // [max_chunks]
@@ -112,8 +116,7 @@ Layout make_layout(void* base, int64_t n, int64_t k, bool staging) {
   if (cap > cap_max) cap = cap_max;
   l.region_cap = cdiv(cdiv(cap, kRegions), 4) * 4;   // regions start 16-byte aligned
   l.pool = l.region_cap * kRegions;
-  const int64_t pool_chunks = cdiv(l.pool, kTile);
-  l.max_chunks = l.ntiles > pool_chunks ? l.ntiles : pool_chunks;
+  l.max_chunks = l.ntiles;   // >= the batches of kBatch tiles
   l.scan_blocks = cdiv(l.max_chunks, kScanChunk);
   size_t off = 0;
   char* b = reinterpret_cast<char*>(base);
@@ -126,12 +129,9 @@ Layout make_layout(void* base, int64_t n, int64_t k, bool staging) {
   l.sample = (uint32_t*)take(sizeof(uint32_t) * kSampleMax);
   l.tile_start = (uint32_t*)take(sizeof(uint32_t) * l.ntiles);
   l.tile_count = (uint32_t*)take(sizeof(uint32_t) * l.ntiles);
-  l.tile_excl = (unsigned long long*)take(sizeof(unsigned long long) * l.ntiles);
   l.scan_up = (unsigned long long*)take(sizeof(unsigned long long) * 4 * (l.scan_blocks + 1));
   l.pool_val = (float*)take(sizeof(float) * l.pool);
   l.pool_off = (uint16_t*)take(sizeof(uint16_t) * l.pool);
-  l.cand_val = (float*)take(sizeof(float) * l.pool);
-  l.cand_idx = (int64_t*)take(sizeof(int64_t) * l.pool);
   l.chunk_gt = (uint32_t*)take(sizeof(uint32_t) * l.max_chunks);
   l.chunk_eq = (uint32_t*)take(sizeof(uint32_t) * l.max_chunks);
   l.gt_excl = (unsigned long long*)take(sizeof(unsigned long long) * l.max_chunks);
@@ -180,6 +180,7 @@ __device__ __forceinline__ void block_scan32(const uint32_t* s_cnt, uint32_t* s_
 __global__ void k_init(TopkCtrl* __restrict__ ctrl, unsigned long long krem) {
   for (int i = threadIdx.x; i < kBins; i += blockDim.x) ctrl->hist[i] = 0ull;
   for (int i = threadIdx.x; i < kRegions; i += blockDim.x) ctrl->region_fill[i] = 0u;
+  if (threadIdx.x < 2) ctrl->batch_next[threadIdx.x] = 0u;
   if (threadIdx.x == 0) {
     ctrl->L = 0u;
     ctrl->overflow = 0u;
@@ -558,115 +559,246 @@ __global__ __launch_bounds__(kBlock) void k_scan_down(const uint32_t* __restrict
 
 
 // Choose the source of the exact selection.  Candidates hold the answer iff the pool did
-// not overflow and at least k entries reached the bound L (then T >= L).
-__global__ void k_decide(TopkCtrl* __restrict__ ctrl, const unsigned long long* __restrict__ tile_excl,
-                         const uint32_t* __restrict__ tile_count, int64_t ntiles,
-                         unsigned long long k) {
+// not overflow and at least k entries reached the bound L (then T >= L).  Without
+// overflow the region counters sum to the number of candidates.
+__global__ void k_decide(TopkCtrl* __restrict__ ctrl, int64_t ntiles, unsigned long long k) {
   if (threadIdx.x == 0) {
-    const unsigned long long ncand = tile_excl[ntiles - 1] + tile_count[ntiles - 1];
-    ctrl->ncand = ncand;
+    unsigned long long ncand = 0;
+    for (int i = 0; i < kRegions; ++i) ncand += ctrl->region_fill[i];
     const bool full = ctrl->overflow != 0u || ncand < k;
+    ctrl->ncand = full ? 0ull : ncand;
     ctrl->mode = full ? MODE_FULL : MODE_CAND;
-    ctrl->nchunks = full ? (unsigned long long)ntiles : (ncand + kTile - 1) / kTile;
+    ctrl->nchunks = (unsigned long long)(full ? ntiles : cdiv(ntiles, kBatch));
   }
 }
 
-// Copy each tile's candidates from the pool into one array in index order.  Work is
-// cut into batches of 128 consecutive tiles, taken grid-stride so that runs of dense
-// tiles (a layer with a large scale can hold ten times the average) spread over all
-// blocks.  A batch's entries are spread over the threads and mapped back to
-// (tile, offset) by binary search over the in-batch prefix of the tile counts.
-__global__ __launch_bounds__(kBlock) void k_reorder(const TopkCtrl* __restrict__ ctrl, int64_t ntiles,
-                                                    const uint32_t* __restrict__ tile_start,
-                                                    const uint32_t* __restrict__ tile_count,
-                                                    const unsigned long long* __restrict__ tile_excl,
-                                                    const float* __restrict__ pool_val,
-                                                    const uint16_t* __restrict__ pool_off,
-                                                    float* __restrict__ cand_val,
-                                                    int64_t* __restrict__ cand_idx) {
-  constexpr int kB = 128;
-  constexpr int kU = 8;      // independent entries per thread per iteration
-  __shared__ uint32_t s_pre[kB + 1];
-  __shared__ uint32_t s_start[kB];
-  __shared__ unsigned long long s_excl[kB];
-  __shared__ uint32_t s_w[2];
-  if (ctrl->mode != MODE_CAND) return;
-  const int64_t nbatch = cdiv(ntiles, kB);
-  for (int64_t bt = blockIdx.x; bt < nbatch; bt += gridDim.x) {
-    const int64_t t0 = bt * kB;
-    const int nt = (int)(ntiles - t0 < kB ? ntiles - t0 : kB);
-    if (threadIdx.x < kB) {
-      const int li = threadIdx.x;
-      uint32_t cn = 0;
-      if (li < nt) {
-        cn = tile_count[t0 + li];
-        s_start[li] = tile_start[t0 + li];
-        s_excl[li] = tile_excl[t0 + li];
-      }
-      uint32_t inc = cn;
-#pragma unroll
-      for (int d = 1; d < kWave; d <<= 1) {
-        const uint32_t o = (uint32_t)__shfl_up((int)inc, d, kWave);
-        if (lane_id() >= d) inc += o;
-      }
-      if (lane_id() == kWave - 1) s_w[li / kWave] = inc;
-      s_pre[li] = inc - cn;   // exclusive within the wave; the second wave adds s_w[0] below
+// ---- the candidates of a batch of kBatch consecutive tiles -----------------------------
+// pre[i] is the exclusive prefix of the tile counts inside the batch; past the last tile
+// (i >= nt, up to kBatch) it holds the total.  start[i] is the tile's pool position.
+// Entry j of the batch (0 <= j < total) lies in the tile lo with pre[lo] <= j <
+// pre[lo + 1], at pool position start[lo] + j - pre[lo]; taken in j order the entries
+// are in index order.  Batches are handed out by an atomic work queue, so a block that
+// drew a dense batch (a layer with a large scale holds ten times the average) does not
+// hold back a fixed share of the others.
+struct BatchTable {
+  uint32_t pre[kBatch + 1];
+  uint32_t start[kBatch];
+  uint32_t wsum[2];
+};
+
+// Fills the table for tiles [t0, t0 + nt); every thread calls it; returns the total.
+__device__ __forceinline__ uint32_t load_batch(BatchTable& bt, int64_t t0, int nt,
+                                               const uint32_t* __restrict__ tile_start,
+                                               const uint32_t* __restrict__ tile_count) {
+  if (threadIdx.x < kBatch) {
+    const int li = threadIdx.x;
+    uint32_t cn = 0;
+    if (li < nt) {
+      cn = tile_count[t0 + li];
+      bt.start[li] = tile_start[t0 + li];
     }
-    __syncthreads();
-    if (threadIdx.x >= kWave && threadIdx.x < kB) s_pre[threadIdx.x] += s_w[0];
-    const uint32_t total = s_w[0] + s_w[1];
-    // for nt < kB the padding entry s_pre[nt] (count 0) already holds the total
-    if (threadIdx.x == 0 && nt == kB) s_pre[kB] = total;
-    __syncthreads();
-    for (uint32_t j0 = 0; j0 < total; j0 += kBlock * kU) {
-      uint32_t src[kU];
-      unsigned long long dst[kU];
-      int64_t tbase[kU];
-      bool live[kU];
+    uint32_t inc = cn;
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
+    for (int d = 1; d < kWave; d <<= 1) {
+      const uint32_t o = (uint32_t)__shfl_up((int)inc, d, kWave);
+      if (lane_id() >= d) inc += o;
+    }
+    if (lane_id() == kWave - 1) bt.wsum[li / kWave] = inc;
+    bt.pre[li] = inc - cn;   // exclusive within the wave; the second wave adds wsum[0] below
+  }
+  __syncthreads();
+  if (threadIdx.x >= kWave && threadIdx.x < kBatch) bt.pre[threadIdx.x] += bt.wsum[0];
+  const uint32_t total = bt.wsum[0] + bt.wsum[1];
+  // padding entries pre[nt..kBatch-1] (count 0) already hold the total; so does pre[kBatch]
+  if (threadIdx.x == 0) bt.pre[kBatch] = total;
+  __syncthreads();
+  return total;
+}
+
+// Tile of entry j < total: the largest lo with pre[lo] <= j (that tile is non-empty).
+// A fixed 7-step search (the padding entries equal the total, so they are never taken),
+// which the compiler interleaves across a thread's independent entries.
+__device__ __forceinline__ int batch_tile(const BatchTable& bt, uint32_t j) {
+  int lo = 0;
+#pragma unroll
+  for (int step = kBatch / 2; step > 0; step >>= 1)
+    if (bt.pre[lo + step] <= j) lo += step;
+  return lo;
+}
+
+// Next batch from work queue q (every thread calls it; uniform result, or -1 when the
+// queue is empty, which every block reaches).
+__device__ __forceinline__ int64_t next_batch(TopkCtrl* ctrl, int q, int64_t nbatch, int64_t* s_b) {
+  __syncthreads();   // the previous batch is done with s_b and the batch table
+  if (threadIdx.x == 0) *s_b = (int64_t)atomicAdd(&ctrl->batch_next[q], 1u);
+  __syncthreads();
+  const int64_t b = *s_b;
+  return b < nbatch ? b : -1;
+}
+
+constexpr int kEmitU = 8;   // entries per thread per chunk of the batch walk
+
+// Candidates only: per-batch counts of key > T and key == T.
+__global__ __launch_bounds__(kBlock) void k_bcount(TopkCtrl* __restrict__ ctrl, int64_t ntiles,
+                                                   const uint32_t* __restrict__ tile_start,
+                                                   const uint32_t* __restrict__ tile_count,
+                                                   const float* __restrict__ pool_val,
+                                                   uint32_t* __restrict__ batch_gt,
+                                                   uint32_t* __restrict__ batch_eq) {
+  __shared__ BatchTable bt;
+  __shared__ uint32_t s[2][kWaves];
+  __shared__ int64_t s_b;
+  if (ctrl->mode != MODE_CAND) return;
+  const uint32_t T = ctrl->T;
+  const int64_t nbatch = cdiv(ntiles, kBatch);
+  for (int64_t b; (b = next_batch(ctrl, 0, nbatch, &s_b)) >= 0;) {
+    const int64_t t0 = b * kBatch;
+    const int nt = (int)(ntiles - t0 < kBatch ? ntiles - t0 : kBatch);
+    const uint32_t total = load_batch(bt, t0, nt, tile_start, tile_count);
+    uint32_t gt = 0, eq = 0;
+    for (uint32_t j0 = 0; j0 < total; j0 += kBlock * kEmitU) {
+      uint32_t src[kEmitU];
+      bool live[kEmitU];
+#pragma unroll
+      for (int u = 0; u < kEmitU; ++u) {
         const uint32_t j = j0 + u * kBlock + threadIdx.x;
         live[u] = j < total;
-        int lo = 0, hi = nt;   // invariant: s_pre[lo] <= j < s_pre[hi]
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (s_pre[mid] <= j) lo = mid; else hi = mid;
-        }
-        const uint32_t o = j - s_pre[lo];
-        src[u] = s_start[lo] + o;
-        dst[u] = s_excl[lo] + o;
-        tbase[u] = (t0 + lo) * kTile;
-      }
-      float v[kU];
-      uint32_t off[kU];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        v[u] = live[u] ? pool_val[src[u]] : 0.f;
-        off[u] = live[u] ? pool_off[src[u]] : 0u;
+        const int lo = live[u] ? batch_tile(bt, j) : 0;
+        src[u] = bt.start[lo] + (j - bt.pre[lo]);
       }
 #pragma unroll
-      for (int u = 0; u < kU; ++u)
+      for (int u = 0; u < kEmitU; ++u)
         if (live[u]) {
-          cand_val[dst[u]] = v[u];
-          cand_idx[dst[u]] = tbase[u] + off[u];
+          const uint32_t key = mag_key(pool_val[src[u]]);
+          gt += key > T;
+          eq += key == T;
         }
     }
+    gt = (uint32_t)wave_sum_u64(gt);
+    eq = (uint32_t)wave_sum_u64(eq);
+    if (lane_id() == 0) { s[0][threadIdx.x / kWave] = gt; s[1][threadIdx.x / kWave] = eq; }
     __syncthreads();
+    if (threadIdx.x == 0) {
+      batch_gt[b] = s[0][0] + s[0][1] + s[0][2] + s[0][3];
+      batch_eq[b] = s[1][0] + s[1][1] + s[1][2] + s[1][3];
+    }
   }
 }
 
-// Per-chunk counts of key > T and key == T over the selected source (the ordered
-// candidates, or the full c in the fallback).
+// Exclusive scan of kN <= 64 packed counts by the first wave (call between barriers).
+template <int kN>
+__device__ __forceinline__ void small_scan(const uint32_t* s_cnt, uint32_t* s_off, uint32_t* s_total) {
+  static_assert(kN <= kWave, "one wave scans the counts");
+  if (threadIdx.x < kWave) {
+    const int t = threadIdx.x;
+    const uint32_t v = t < kN ? s_cnt[t] : 0u;
+    uint32_t inc = v;
+#pragma unroll
+    for (int d = 1; d < kN; d <<= 1) {
+      const uint32_t o = (uint32_t)__shfl_up((int)inc, d, kWave);
+      if (t >= d) inc += o;
+    }
+    if (t < kN) s_off[t] = inc - v;
+    if (t == kN - 1) *s_total = inc;
+  }
+}
+
+// Candidates only: ordered compaction straight from the pool.  A chunk of a batch is
+// kBlock * kEmitU entries; entry j = j0 + u * kBlock + threadIdx.x, so (u, wave) order
+// is j order.  One packed scan counts both predicates: the low 16 bits count key > T and
+// the high 16 bits key == T (a chunk holds 2048 entries, so neither field carries).
+__global__ __launch_bounds__(kBlock) void k_bemit(TopkCtrl* __restrict__ ctrl, int64_t ntiles,
+                                                  const uint32_t* __restrict__ tile_start,
+                                                  const uint32_t* __restrict__ tile_count,
+                                                  const float* __restrict__ pool_val,
+                                                  const uint16_t* __restrict__ pool_off,
+                                                  const unsigned long long* __restrict__ gt_excl,
+                                                  const unsigned long long* __restrict__ eq_excl,
+                                                  float* __restrict__ r, int64_t index_base,
+                                                  int64_t* __restrict__ out_idx, float* __restrict__ out_val,
+                                                  int zero_residual, int64_t k) {
+  __shared__ BatchTable bt;
+  __shared__ uint32_t s_cnt[kEmitU * kWaves];
+  __shared__ uint32_t s_off[kEmitU * kWaves];
+  __shared__ uint32_t s_total;
+  __shared__ int64_t s_b;
+  if (ctrl->mode != MODE_CAND) return;
+  const uint32_t T = ctrl->T;
+  const unsigned long long need = ctrl->need;
+  const int w = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int64_t nbatch = cdiv(ntiles, kBatch);
+  for (int64_t b; (b = next_batch(ctrl, 1, nbatch, &s_b)) >= 0;) {
+    const int64_t t0 = b * kBatch;
+    const int nt = (int)(ntiles - t0 < kBatch ? ntiles - t0 : kBatch);
+    const uint32_t total = load_batch(bt, t0, nt, tile_start, tile_count);
+    unsigned long long gt_run = gt_excl[b], eq_run = eq_excl[b];
+    for (uint32_t j0 = 0; j0 < total; j0 += kBlock * kEmitU) {
+      uint32_t src[kEmitU];
+      int64_t tbase[kEmitU];
+      bool live[kEmitU];
+#pragma unroll
+      for (int u = 0; u < kEmitU; ++u) {
+        const uint32_t j = j0 + u * kBlock + threadIdx.x;
+        live[u] = j < total;
+        const int lo = live[u] ? batch_tile(bt, j) : 0;
+        src[u] = bt.start[lo] + (j - bt.pre[lo]);
+        tbase[u] = (t0 + lo) * kTile;
+      }
+      float v[kEmitU];
+      uint32_t off[kEmitU];
+#pragma unroll
+      for (int u = 0; u < kEmitU; ++u) {
+        v[u] = live[u] ? pool_val[src[u]] : 0.f;
+        off[u] = live[u] ? (uint32_t)pool_off[src[u]] : 0u;
+      }
+      uint32_t flag[kEmitU], gpre[kEmitU], epre[kEmitU];
+#pragma unroll
+      for (int u = 0; u < kEmitU; ++u) {
+        const uint32_t key = mag_key(v[u]);
+        const bool gtf = live[u] && key > T;
+        const bool eqf = live[u] && key == T;
+        const uint64_t bg = ballot(gtf), be = ballot(eqf);
+        gpre[u] = mbcnt(bg);
+        epre[u] = mbcnt(be);
+        flag[u] = (gtf ? 1u : 0u) | (eqf ? 2u : 0u);
+        if (lane == 0) s_cnt[u * kWaves + w] = ((uint32_t)__popcll(be) << 16) | (uint32_t)__popcll(bg);
+      }
+      __syncthreads();
+      small_scan<kEmitU * kWaves>(s_cnt, s_off, &s_total);
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kEmitU; ++u) {
+        if (!flag[u]) continue;
+        const uint32_t o = s_off[u * kWaves + w];
+        const unsigned long long gb = gt_run + (o & 0xFFFFu) + gpre[u];
+        const unsigned long long eb = eq_run + (o >> 16) + epre[u];
+        if ((flag[u] & 1u) || eb < need) {
+          const unsigned long long pos = gb + (eb < need ? eb : need);
+          const int64_t e = tbase[u] + off[u];
+          if (pos < (unsigned long long)k) {   // exactly k are kept; the guard only bounds stores
+            out_idx[pos] = e + index_base;
+            out_val[pos] = v[u];
+          }
+          if (zero_residual) r[e] = 0.f;
+        }
+      }
+      const uint32_t tot = s_total;
+      gt_run += tot & 0xFFFFu;
+      eq_run += tot >> 16;
+      __syncthreads();   // s_cnt / s_off / s_total are rewritten by the next chunk
+    }
+  }
+}
+
+// Fallback only: per-tile counts of key > T and key == T over the full c.
 __global__ __launch_bounds__(kBlock) void k_count(const TopkCtrl* __restrict__ ctrl,
-                                                  const float* __restrict__ cand,
                                                   const float* __restrict__ full, int64_t n,
                                                   uint32_t* __restrict__ chunk_gt,
                                                   uint32_t* __restrict__ chunk_eq) {
   __shared__ uint32_t s[2][kWaves];
-  const bool use_cand = ctrl->mode == MODE_CAND;
-  const float* __restrict__ src = use_cand ? cand : full;
-  const int64_t cnt = use_cand ? (int64_t)ctrl->ncand : n;
-  const int64_t nch = (int64_t)ctrl->nchunks;
+  if (ctrl->mode != MODE_FULL) return;
+  const int64_t nch = cdiv(n, kTile);
   const uint32_t T = ctrl->T;
   for (int64_t ch = blockIdx.x; ch < nch; ch += gridDim.x) {
     const int64_t base = ch * kTile;
@@ -674,8 +806,8 @@ __global__ __launch_bounds__(kBlock) void k_count(const TopkCtrl* __restrict__ c
 #pragma unroll
     for (int j = 0; j < kRounds; ++j) {
       const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4;
-      if (e + 4 <= cnt) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(src + e);
+      if (e + 4 <= n) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(full + e);
         const float v[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -686,8 +818,8 @@ __global__ __launch_bounds__(kBlock) void k_count(const TopkCtrl* __restrict__ c
       } else {
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-          if (e + m < cnt) {
-            const uint32_t key = mag_key(src[e + m]);
+          if (e + m < n) {
+            const uint32_t key = mag_key(full[e + m]);
             gt += key > T;
             eq += key == T;
           }
@@ -705,10 +837,9 @@ __global__ __launch_bounds__(kBlock) void k_count(const TopkCtrl* __restrict__ c
   }
 }
 
-// Ordered compaction: keep key > T, and the first `need` entries with key == T.
+// Fallback only: ordered compaction of the full c, tile by tile: keep key > T, and the
+// first `need` entries with key == T.
 __global__ __launch_bounds__(kBlock) void k_emit(const TopkCtrl* __restrict__ ctrl,
-                                                 const float* __restrict__ cand_val,
-                                                 const int64_t* __restrict__ cand_idx,
                                                  float* __restrict__ r, int64_t n,
                                                  const unsigned long long* __restrict__ gt_excl,
                                                  const unsigned long long* __restrict__ eq_excl,
@@ -718,10 +849,8 @@ __global__ __launch_bounds__(kBlock) void k_emit(const TopkCtrl* __restrict__ ct
   __shared__ uint32_t s_cnt[kRounds * kWaves];
   __shared__ uint32_t s_off[kRounds * kWaves];
   __shared__ uint32_t s_total;
-  const bool use_cand = ctrl->mode == MODE_CAND;
-  const float* __restrict__ src = use_cand ? cand_val : r;
-  const int64_t cnt = use_cand ? (int64_t)ctrl->ncand : n;
-  const int64_t nch = (int64_t)ctrl->nchunks;
+  if (ctrl->mode != MODE_FULL) return;
+  const int64_t nch = cdiv(n, kTile);
   const uint32_t T = ctrl->T;
   const unsigned long long need = ctrl->need;
   const int w = threadIdx.x / kWave;
@@ -733,18 +862,18 @@ __global__ __launch_bounds__(kBlock) void k_emit(const TopkCtrl* __restrict__ ct
 #pragma unroll
     for (int j = 0; j < kRounds; ++j) {
       const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4;
-      if (e + 4 <= cnt) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(src + e);
+      if (e + 4 <= n) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(r + e);
         v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
       } else {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) v[j][m] = e + m < cnt ? src[e + m] : 0.f;
+        for (int m = 0; m < 4; ++m) v[j][m] = e + m < n ? r[e + m] : 0.f;
       }
       uint32_t gb = 0, qb = 0;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const uint32_t key = mag_key(v[j][m]);
-        const bool in = e + m < cnt;
+        const bool in = e + m < n;
         gb |= (in && key > T) ? (1u << m) : 0u;
         qb |= (in && key == T) ? (1u << m) : 0u;
       }
@@ -791,12 +920,11 @@ __global__ __launch_bounds__(kBlock) void k_emit(const TopkCtrl* __restrict__ ct
         for (int m = 0; m < 4; ++m)
           if (keep[j] & (1u << m)) {
             const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4 + m;
-            const int64_t idx = use_cand ? cand_idx[e] : e;
             if (pos < (unsigned long long)k) {   // exactly k are kept; the guard only bounds stores
-              out_idx[pos] = idx + index_base;
+              out_idx[pos] = e + index_base;
               out_val[pos] = v[j][m];
             }
-            if (zero_residual) r[idx] = 0.f;
+            if (zero_residual) r[e] = 0.f;
             ++pos;
           }
       }
@@ -806,12 +934,15 @@ __global__ __launch_bounds__(kBlock) void k_emit(const TopkCtrl* __restrict__ ct
 }
 
 // QSGD over the kept values (groups in kept order, RNG index = kept position) and the
-// residual update r[idx] = v - g_hat.
+// residual update r[idx] = v - g_hat.  A block takes 1024 kept entries as 256 quads; the
+// residuals go through LDS so that the scattered stores are issued in kept order, 64
+// consecutive entries per wave store (neighbouring kept entries often share a sector).
 __global__ __launch_bounds__(kBlock) void k_qsgd_kept(const float* __restrict__ vals, int64_t k,
                                                       int lpg_log2, float s, uint64_t seed,
                                                       int8_t* __restrict__ codes, float* __restrict__ norms,
                                                       const int64_t* __restrict__ idx, int64_t index_base,
                                                       float* __restrict__ r, int64_t n) {
+  __shared__ float s_res[kBlock * 4];
   const int64_t nquads = (k + 3) >> 2;
   const int lpg = 1 << lpg_log2;
   const int lane = lane_id();
@@ -831,27 +962,35 @@ __global__ __launch_bounds__(kBlock) void k_qsgd_kept(const float* __restrict__ 
     }
     float ss = quad_sumsq(v);
     ss = seg_tree_sum(ss, lpg);
-    if (!live) continue;
-    const float nu = sqrtf(ss);
-    float u[4];
-    uniforms4(seed, (uint64_t)e0, u);
-    int lev[4];
-    float gh[4];
-    qsgd_quad(v, nu, s, u, lev, gh);
-    if (full) {
-      *reinterpret_cast<uint32_t*>(codes + e0) = pack_codes4(lev);
-    } else {
+    __syncthreads();   // s_res is still being read by the previous iteration's scatter
+    if (live) {
+      const float nu = sqrtf(ss);
+      float u[4];
+      uniforms4(seed, (uint64_t)e0, u);
+      int lev[4];
+      float gh[4];
+      qsgd_quad(v, nu, s, u, lev, gh);
+      if (full) {
+        *reinterpret_cast<uint32_t*>(codes + e0) = pack_codes4(lev);
+      } else {
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
-        if (e0 + m < k) codes[e0 + m] = (int8_t)lev[m];
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      if (e0 + m < k) {
-        const int64_t p = idx[e0 + m] - index_base;
-        if (p >= 0 && p < n) r[p] = v[m] - gh[m];
+        for (int m = 0; m < 4; ++m)
+          if (e0 + m < k) codes[e0 + m] = (int8_t)lev[m];
       }
-    if ((lane & (lpg - 1)) == 0) norms[e0 >> (lpg_log2 + 2)] = nu;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) s_res[threadIdx.x * 4 + m] = v[m] - gh[m];
+      if ((lane & (lpg - 1)) == 0) norms[e0 >> (lpg_log2 + 2)] = nu;
+    }
+    __syncthreads();
+    // entry base*4 + j sits at s_res[j]; entries at or beyond k were never kept
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int64_t j = base * 4 + m * kBlock + threadIdx.x;
+      if (j < k) {
+        const int64_t p = idx[j] - index_base;
+        if (p >= 0 && p < n) r[p] = s_res[m * kBlock + threadIdx.x];
+      }
+    }
   }
 }
 
@@ -902,16 +1041,8 @@ hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, i
                      l.tile_count, l.pool_val, l.pool_off, (uint32_t)l.region_cap);
   prof_mark(s, 2);
 
-  // 4: candidate total and offsets, source decision
-  const int scan_grid = clamp_grid(cdiv(l.ntiles, kScanChunk), cus * 4);
-  hipLaunchKernelGGL(k_scan_up, scan_grid, kBlock, 0, s, l.tile_count, (const uint32_t*)nullptr,
-                     (const unsigned long long*)nullptr, l.ntiles, l.scan_up);
-  hipLaunchKernelGGL(k_scan_mid, 1, kBlock, 0, s, (const unsigned long long*)nullptr, l.ntiles, l.scan_up);
-  hipLaunchKernelGGL(k_scan_down, scan_grid, kBlock, 0, s, l.tile_count, (const uint32_t*)nullptr,
-                     (const unsigned long long*)nullptr, l.ntiles, (const unsigned long long*)l.scan_up,
-                     l.tile_excl, (unsigned long long*)nullptr);
-  hipLaunchKernelGGL(k_decide, 1, 64, 0, s, ctrl, (const unsigned long long*)l.tile_excl,
-                     (const uint32_t*)l.tile_count, l.ntiles, (unsigned long long)k);
+  // 4: source decision
+  hipLaunchKernelGGL(k_decide, 1, 64, 0, s, ctrl, l.ntiles, (unsigned long long)k);
 
   // 5: exact k-th key over the selected source
   const int hgrid = cus * 4;
@@ -921,23 +1052,28 @@ hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, i
     hipLaunchKernelGGL(k_pick, 1, kBlock, 0, s, ctrl, shifts[p], p == 2 ? 2 : 0, (unsigned long long)k);
   }
 
-  // 6: candidates in index order
-  hipLaunchKernelGGL(k_reorder, clamp_grid(cdiv(l.ntiles, 128), cus * 8), kBlock, 0, s, ctrl, l.ntiles,
-                     l.tile_start, l.tile_count, l.tile_excl, l.pool_val, l.pool_off, l.cand_val,
-                     l.cand_idx);
-
-  // 7: ordered compaction
-  const int cgrid = clamp_grid(l.max_chunks, cus * 8);
-  hipLaunchKernelGGL(k_count, cgrid, kBlock, 0, s, ctrl, l.cand_val, res, n, l.chunk_gt, l.chunk_eq);
+  // 6: counts per batch (candidates) or per tile (fallback), and their scan; the kernel
+  // of the other mode returns at once
+  const int64_t nbatch = cdiv(l.ntiles, kBatch);
+  const int bgrid = clamp_grid(nbatch, cus * 8);
+  const int cgrid = clamp_grid(l.ntiles, cus * 8);
+  hipLaunchKernelGGL(k_bcount, bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
+                     l.pool_val, l.chunk_gt, l.chunk_eq);
+  hipLaunchKernelGGL(k_count, cgrid, kBlock, 0, s, ctrl, res, n, l.chunk_gt, l.chunk_eq);
   const unsigned long long* nch_dev = &ctrl->nchunks;
   const int cscan = clamp_grid(cdiv(l.max_chunks, kScanChunk), cus * 4);
   hipLaunchKernelGGL(k_scan_up, cscan, kBlock, 0, s, l.chunk_gt, l.chunk_eq, nch_dev, (int64_t)0, l.scan_up);
   hipLaunchKernelGGL(k_scan_mid, 1, kBlock, 0, s, nch_dev, (int64_t)0, l.scan_up);
   hipLaunchKernelGGL(k_scan_down, cscan, kBlock, 0, s, l.chunk_gt, l.chunk_eq, nch_dev, (int64_t)0,
                      (const unsigned long long*)l.scan_up, l.gt_excl, l.eq_excl);
+
+  // 7: ordered compaction
   float* vals = quant ? (out_val ? out_val : l.staging) : out_val;
-  hipLaunchKernelGGL(k_emit, cgrid, kBlock, 0, s, ctrl, l.cand_val, l.cand_idx, res, n, l.gt_excl,
-                     l.eq_excl, index_base, out_idx, vals, quant ? 0 : 1, k);
+  hipLaunchKernelGGL(k_bemit, bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
+                     (const float*)l.pool_val, (const uint16_t*)l.pool_off, (const unsigned long long*)l.gt_excl,
+                     (const unsigned long long*)l.eq_excl, res, index_base, out_idx, vals, quant ? 0 : 1, k);
+  hipLaunchKernelGGL(k_emit, cgrid, kBlock, 0, s, ctrl, res, n, (const unsigned long long*)l.gt_excl,
+                     (const unsigned long long*)l.eq_excl, index_base, out_idx, vals, quant ? 0 : 1, k);
 
   // 8: QSGD on the kept values and the residual of the kept set
   if (quant) {
