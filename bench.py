@@ -26,7 +26,27 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+
+# HBM bytes per launch of the streaming pass on this workload, from two rocprofv3 counter
+# runs (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, factors from a plain 4 GiB device copy; the
+# summary with its commands is profiles/k_ef_cand_7e9_hbm_traffic.md).  Valid only for the
+# kernel source it was measured on: the digest covers the tile constants, the block-rank
+# helpers and the kernel itself, and a mismatch reports the traffic as null.
+K1_TRAFFIC_BYTES = 8.4612e10
+K1_SOURCE_SHA256 = "cff8662bf0eab494eea940769a946440b82f3083f9bc81822df0a51543d98ae8"
 METRIC = "EF-Top-1%+int8 compress GB/s of fp32 grad input; % of HBM peak"
+
+
+def k1_source_digest():
+    src = open(os.path.join(ROOT, "gradient_compression_ddp_amd", "csrc", "ef_topk.hip")).read()
+    parts = []
+    for start, end in (("constexpr int kBlock = 256;", "enum : uint32_t"),
+                       ("__device__ __forceinline__ uint32_t rank_round", "// Kernels"),
+                       ("void k_ef_cand(", "\n}\n")):
+        a = src.index(start)
+        parts.append(src[a:src.index(end, a)])
+    import hashlib
+    return hashlib.sha256("\n".join(parts).encode()).hexdigest()
 
 
 def parse():
@@ -422,7 +442,10 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": (round(K1_TRAFFIC_BYTES / 1e9 / (pass_ms / 1e3), 1)
+                        if k1_source_digest() == K1_SOURCE_SHA256 else None),
+            "traffic_bytes_per_launch": (K1_TRAFFIC_BYTES if k1_source_digest() == K1_SOURCE_SHA256
+                                         else None),
             "bytes_per_launch": pass_bytes,
             "avg_launch_ms": round(pass_ms, 4),
         },
