@@ -5,7 +5,9 @@
 // gradient is dense with zeros off the kept set).  Each entry's value is the
 // dequantization formula of its compressor, in binary32, then multiplied by alpha and
 // stored to or added into out[pos].  Streaming: one pass over the payload, scattered
-// 4-byte stores (contiguous for a dense decode).
+// 4-byte stores.  A dense decode (no idx) with aligned buffers takes the tile kernel: one
+// 4096-entry tile per block, a lane owns an aligned quad (codes loaded as one word,
+// 16-byte non-temporal stores), all loads of the tile issued before any arithmetic.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -13,6 +15,105 @@ namespace gc {
 namespace {
 
 enum { KIND_F32 = 0, KIND_MINMAX8 = 1, KIND_MINMAX4 = 2, KIND_QSGD = 3, KIND_TERN = 4 };
+
+constexpr int kBlock = 256;
+constexpr int kRounds = 4;
+constexpr int64_t kTile = (int64_t)kBlock * 4 * kRounds;   // 4096 entries
+
+// The dequantized value of entry j from its code bits `q` (kind-specific meaning).
+template <int KIND>
+__device__ __forceinline__ float decode_one(uint32_t q, float m0, float m1, float s) {
+  if (KIND == KIND_MINMAX8 || KIND == KIND_MINMAX4) return (float)q * m1 + m0;
+  if (KIND == KIND_QSGD) {
+    const int c = (int)(int8_t)(uint8_t)q;
+    const float level = (float)(c < 0 ? -c : c);
+    const float mag = (m0 * level) / s;
+    return c < 0 ? -mag : mag;
+  }
+  // KIND_TERN: 01 -> +s, 11 -> -s, 00 -> 0
+  return q == 1u ? m0 : (q == 3u ? -m0 : 0.f);
+}
+
+// Dense decode, entries [0, count) to out[0, count).  Requires out 16-byte aligned and
+// codes aligned to one quad's code bytes (16 for F32, 4 for 8-bit codes, 2 for int4).
+template <int KIND>
+__global__ __launch_bounds__(kBlock) void k_decompress_dense(int64_t count, const void* __restrict__ codes,
+                                                             const float* __restrict__ meta0,
+                                                             const float* __restrict__ meta1, int64_t G,
+                                                             int lg, float s, float alpha, int accumulate,
+                                                             float* __restrict__ out) {
+  const int64_t base = (int64_t)blockIdx.x * kTile;
+  const uint8_t* c8 = reinterpret_cast<const uint8_t*>(codes);
+  uint32_t word[kRounds];
+  f32x4 fv[kRounds];
+#pragma unroll
+  for (int j = 0; j < kRounds; ++j) {
+    const int64_t e0 = base + j * (kBlock * 4) + threadIdx.x * 4;
+    word[j] = 0u;
+    fv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (e0 + 4 <= count) {
+      if (KIND == KIND_F32) fv[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(codes) + (e0 >> 2));
+      else if (KIND == KIND_MINMAX8 || KIND == KIND_QSGD)
+        word[j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(c8 + e0));
+      else if (KIND == KIND_MINMAX4)
+        word[j] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(c8 + (e0 >> 1)));
+      else
+        word[j] = c8[e0 >> 2];
+    } else if (e0 < count) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int64_t e = e0 + m;
+        if (e >= count) break;
+        if (KIND == KIND_F32) fv[j][m] = reinterpret_cast<const float*>(codes)[e];
+        else if (KIND == KIND_MINMAX8 || KIND == KIND_QSGD) word[j] |= (uint32_t)c8[e] << (8 * m);
+        else if (KIND == KIND_MINMAX4) word[j] |= (uint32_t)((c8[e >> 1] >> (4 * (e & 1))) & 15u) << (4 * m);
+        else word[j] |= (uint32_t)((c8[e >> 2] >> (2 * (e & 3))) & 3u) << (2 * m);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kRounds; ++j) {
+    const int64_t e0 = base + j * (kBlock * 4) + threadIdx.x * 4;
+    if (e0 >= count) continue;
+    float v[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      if (KIND == KIND_F32) {
+        v[m] = fv[j][m];
+      } else {
+        const int64_t e = e0 + m;
+        const int64_t g = lg >= 0 ? (e >> lg) : e / G;
+        const float m0 = (e < count) ? meta0[g] : 0.f;
+        const float m1 = (KIND == KIND_MINMAX8 || KIND == KIND_MINMAX4) && e < count ? meta1[g] : 0.f;
+        uint32_t q;
+        if (KIND == KIND_MINMAX8 || KIND == KIND_QSGD) q = (word[j] >> (8 * m)) & 0xFFu;
+        else if (KIND == KIND_MINMAX4) q = (word[j] >> (4 * m)) & 15u;
+        else q = (word[j] >> (2 * m)) & 3u;
+        v[m] = decode_one<KIND>(q, m0, m1, s);
+      }
+    }
+    if (e0 + 4 <= count) {
+      f32x4 o;
+      if (accumulate) {
+        const f32x4 prev = *reinterpret_cast<const f32x4*>(out + e0);
+        o.x = prev.x + alpha * v[0]; o.y = prev.y + alpha * v[1];
+        o.z = prev.z + alpha * v[2]; o.w = prev.w + alpha * v[3];
+      } else {
+        o.x = alpha * v[0]; o.y = alpha * v[1]; o.z = alpha * v[2]; o.w = alpha * v[3];
+      }
+      __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(out + e0));
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int64_t e = e0 + m;
+        if (e < count) {
+          const float a = alpha * v[m];
+          out[e] = accumulate ? out[e] + a : a;
+        }
+      }
+    }
+  }
+}
 
 template <int KIND>
 __global__ void k_decompress(const int64_t* __restrict__ idx, int64_t count, int64_t index_base,
@@ -63,6 +164,24 @@ hipError_t launch_decompress(int kind, const int64_t* idx, int64_t count, int64_
   if ((G & (G - 1)) == 0) {
     lg = 0;
     while ((int64_t(1) << lg) < G) ++lg;
+  }
+  const auto al = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; };
+  const uintptr_t code_align = kind == KIND_F32 ? 16 : (kind == KIND_MINMAX4 ? 2 : (kind == KIND_TERN ? 1 : 4));
+  if (!idx && al(out, 16) && al(codes, code_align)) {
+    const int64_t tiles = (count + kTile - 1) / kTile;
+    const float sd = (float)(levels > 0 ? levels : 1);
+#define GC_LAUNCH_DENSE(K)                                                                          \
+  hipLaunchKernelGGL((k_decompress_dense<K>), (unsigned)tiles, kBlock, 0, s, count, codes, meta0, meta1, \
+                     G, lg, sd, alpha, accumulate, out)
+    switch (kind) {
+      case KIND_F32: GC_LAUNCH_DENSE(KIND_F32); break;
+      case KIND_MINMAX8: GC_LAUNCH_DENSE(KIND_MINMAX8); break;
+      case KIND_MINMAX4: GC_LAUNCH_DENSE(KIND_MINMAX4); break;
+      case KIND_QSGD: GC_LAUNCH_DENSE(KIND_QSGD); break;
+      default: GC_LAUNCH_DENSE(KIND_TERN); break;
+    }
+#undef GC_LAUNCH_DENSE
+    return hipGetLastError();
   }
   int64_t blocks = (count + 255) / 256;
   const int64_t cap = (int64_t)device_cu_count() * 16;

@@ -196,11 +196,21 @@ __global__ __launch_bounds__(kBlock) void k_psum_gram(const float* __restrict__ 
 // Modified Gram-Schmidt in coefficient space: columns of T give P^ = P T.  A column in the
 // span of the previous ones becomes 0; numerically, one whose projected norm is at most
 // 1e-5 of its own norm (squared: 1e-10), below which its direction is rounding noise.
-__global__ void k_gs(const double* __restrict__ gram, int nblocks, int rank, double* __restrict__ T) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  double g[10] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-  for (int b = 0; b < nblocks; ++b)
+// One wave: lane l sums the block partials l, l + 64, ... in order, then a fixed xor
+// butterfly combines the lanes (deterministic); lane 0 runs the 4x4 Gram-Schmidt.
+__global__ __launch_bounds__(kWave) void k_gs(const double* __restrict__ gram, int nblocks, int rank,
+                                              double* __restrict__ T) {
+  if (blockIdx.x != 0) return;
+  double g[10];
+#pragma unroll
+  for (int t = 0; t < 10; ++t) g[t] = 0.0;
+  for (int b = threadIdx.x; b < nblocks; b += kWave)
+#pragma unroll
     for (int t = 0; t < 10; ++t) g[t] += gram[b * 10 + t];
+#pragma unroll
+  for (int t = 0; t < 10; ++t)
+    for (int m = 1; m < kWave; m <<= 1) g[t] += __shfl_xor(g[t], m, kWave);
+  if (threadIdx.x != 0) return;
   double G[4][4];
   int t = 0;
   for (int a = 0; a < 4; ++a)
@@ -303,18 +313,29 @@ __global__ __launch_bounds__(kBlock) void k_p2(const float* __restrict__ M, int6
 }
 
 // Q' = sum of the row-panel partials (in panel order); padded copy and the caller's Q.
-__global__ void k_qsum(const float* __restrict__ qpart, int64_t nrp, int64_t cols, int rank,
-                       float* __restrict__ qn, float* __restrict__ Q_out) {
-  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < cols;
-       c += (int64_t)gridDim.x * blockDim.x) {
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t r = 0; r < nrp; ++r) {
-      const f32x4 q = *reinterpret_cast<const f32x4*>(qpart + (r * cols + c) * 4);
-      v[0] += q.x; v[1] += q.y; v[2] += q.z; v[3] += q.w;
+// Thread t owns entry (column t/4, component t%4): neighbouring threads read neighbouring
+// floats, and 8 partials are loaded ahead of their (in-order) additions.
+__global__ __launch_bounds__(256) void k_qsum(const float* __restrict__ qpart, int64_t nrp, int64_t cols,
+                                              int rank, float* __restrict__ qn, float* __restrict__ Q_out) {
+  constexpr int kAhead = 8;
+  const int64_t total = cols * 4;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t c = t >> 2;
+    const int j = (int)(t & 3);
+    float v = 0.f;
+    int64_t r = 0;
+    for (; r + kAhead <= nrp; r += kAhead) {
+      float a[kAhead];
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) a[u] = qpart[(r + u) * total + t];
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) v += a[u];
     }
-    for (int j = rank; j < 4; ++j) v[j] = 0.f;
-    *reinterpret_cast<f32x4*>(qn + c * 4) = f32x4{v[0], v[1], v[2], v[3]};
-    for (int j = 0; j < rank; ++j) Q_out[c * rank + j] = v[j];
+    for (; r < nrp; ++r) v += qpart[r * total + t];
+    if (j >= rank) v = 0.f;
+    qn[t] = v;
+    if (j < rank) Q_out[c * rank + j] = v;
   }
 }
 
@@ -374,7 +395,7 @@ hipError_t launch_powersgd(const float* grad, float* res, int64_t rows, int64_t 
   const float* M = res ? res : grad;
   const dim3 g2((unsigned)cdiv(cols, 256), (unsigned)l.nrp);
   hipLaunchKernelGGL(k_p2, g2, kBlock, 0, s, M, rows, cols, l.phat, l.qpart);
-  hipLaunchKernelGGL(k_qsum, clamp_grid(cdiv(cols, 256), cus * 4), 256, 0, s, l.qpart, l.nrp, cols, rank, l.qn, Q);
+  hipLaunchKernelGGL(k_qsum, clamp_grid(cdiv(cols * 4, 256), cus * 8), 256, 0, s, l.qpart, l.nrp, cols, rank, l.qn, Q);
   if (res) {
     const dim3 g3((unsigned)cdiv(cols, kBlock * 4), (unsigned)cdiv(rows, kP3Rows));
     hipLaunchKernelGGL(k_p3, g3, kBlock, 0, s, M, res, rows, cols, l.phat, l.qn);

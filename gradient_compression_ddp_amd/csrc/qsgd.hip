@@ -10,7 +10,10 @@
 // a lane butterfly with offsets 1, 2, 4, ... (each step adds exactly one tree pair).
 // The random draw of element e is word (e&3) of the Philox block at counter e>>2, so an
 // aligned quad costs one Philox call.  One pass: 4 B read, 1 B code written per element
-// (+4 B read and written for the residual), 4 B per group for the norm.
+// (+4 B read and written for the residual), 4 B per group for the norm.  The pass is
+// bound by VALU work more than by HBM: a Philox4x32-10 block per quad (20 64-bit integer
+// multiply-adds) and two correctly rounded divisions per element; on a 25 MiB bucket two
+// quads per lane measured fastest (12.9 us against 14.8 with one and 14.4 with four).
 #include "common.hpp"
 #include "internal.hpp"
 #include "qsgd_core.hpp"
@@ -19,63 +22,71 @@ namespace gc {
 namespace {
 
 constexpr int kBlock = 256;
+constexpr int kRounds = 2;                                 // quads per thread per tile
+constexpr int64_t kTile = (int64_t)kBlock * 4 * kRounds;   // 2048 elements
 
+// One 2048-element tile per block: 2 rounds of 1024 elements, each starting at a multiple
+// of 1024 so that every group (G <= 256) lies inside one wave of one round.  All loads
+// of the tile are issued before any arithmetic (non-temporal 16-byte loads and stores).
 template <bool EF>
 __global__ __launch_bounds__(kBlock) void k_qsgd(const float* __restrict__ x, float* __restrict__ res,
                                                  int64_t n, int lpg_log2, float s, uint64_t seed,
                                                  int64_t index_base, int8_t* __restrict__ codes,
                                                  float* __restrict__ norms) {
-  const int64_t nquads = (n + 3) >> 2;
   const int lpg = 1 << lpg_log2;
   const int lane = lane_id();
-  const int64_t stride = (int64_t)gridDim.x * kBlock;
-  for (int64_t base = (int64_t)blockIdx.x * kBlock; base < nquads; base += stride) {
-    const int64_t q = base + threadIdx.x;
-    const int64_t e0 = q << 2;
-    const bool live = q < nquads;
-    const bool full = e0 + 4 <= n;
-    float v[4];
-    if (live && full) {
-      const float4 a = *reinterpret_cast<const float4*>(x + e0);
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  const int64_t base = (int64_t)blockIdx.x * kTile;
+  float v[kRounds][4];
+#pragma unroll
+  for (int j = 0; j < kRounds; ++j) {
+    const int64_t e0 = base + j * (kBlock * 4) + threadIdx.x * 4;
+    if (e0 + 4 <= n) {
+      const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x + e0));
+      v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
       if (EF) {
-        const float4 b = *reinterpret_cast<const float4*>(res + e0);
-        v[0] = v[0] + b.x; v[1] = v[1] + b.y; v[2] = v[2] + b.z; v[3] = v[3] + b.w;
+        const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(res + e0));
+        v[j][0] = v[j][0] + b.x; v[j][1] = v[j][1] + b.y; v[j][2] = v[j][2] + b.z; v[j][3] = v[j][3] + b.w;
       }
     } else {
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         float t = 0.f;
-        if (live && e0 + m < n) {
+        if (e0 + m < n) {
           t = x[e0 + m];
           if (EF) t = t + res[e0 + m];
         }
-        v[m] = t;
+        v[j][m] = t;
       }
     }
-    // pairwise tree: lane-local levels, then the lane butterfly
-    float ss = quad_sumsq(v);
+  }
+#pragma unroll
+  for (int j = 0; j < kRounds; ++j) {
+    const int64_t e0 = base + j * (kBlock * 4) + threadIdx.x * 4;
+    // pairwise tree: lane-local levels, then the lane butterfly (every lane takes part;
+    // lanes past the end hold +0.0)
+    float ss = quad_sumsq(v[j]);
     ss = seg_tree_sum(ss, lpg);
-    if (!live) continue;
+    if (e0 >= n) continue;
+    const bool full = e0 + 4 <= n;
     const float nu = sqrtf(ss);
     float u[4];
     uniforms4(seed, (uint64_t)(index_base + e0), u);
     int lev[4];
     float gh[4];
-    qsgd_quad(v, nu, s, u, lev, gh);
+    qsgd_quad(v[j], nu, s, u, lev, gh);
     if (full) {
-      *reinterpret_cast<uint32_t*>(codes + e0) = pack_codes4(lev);
+      __builtin_nontemporal_store(pack_codes4(lev), reinterpret_cast<uint32_t*>(codes + e0));
       if (EF) {
-        float4 r;
-        r.x = v[0] - gh[0]; r.y = v[1] - gh[1]; r.z = v[2] - gh[2]; r.w = v[3] - gh[3];
-        *reinterpret_cast<float4*>(res + e0) = r;
+        f32x4 r;
+        r.x = v[j][0] - gh[0]; r.y = v[j][1] - gh[1]; r.z = v[j][2] - gh[2]; r.w = v[j][3] - gh[3];
+        __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(res + e0));
       }
     } else {
 #pragma unroll
       for (int m = 0; m < 4; ++m)
         if (e0 + m < n) {
           codes[e0 + m] = (int8_t)lev[m];
-          if (EF) res[e0 + m] = v[m] - gh[m];
+          if (EF) res[e0 + m] = v[j][m] - gh[m];
         }
     }
     if ((lane & (lpg - 1)) == 0) norms[e0 >> (lpg_log2 + 2)] = nu;
@@ -90,10 +101,7 @@ hipError_t launch_qsgd(const float* x, float* res, int64_t n, int64_t group, int
   if (n == 0) return hipSuccess;
   int lpg_log2 = 0;
   while ((int64_t(4) << lpg_log2) < group) ++lpg_log2;
-  const int64_t nquads = (n + 3) / 4;
-  int64_t blocks = (nquads + kBlock - 1) / kBlock;
-  const int64_t cap = (int64_t)device_cu_count() * 16;
-  if (blocks > cap) blocks = cap;
+  const int64_t blocks = (n + kTile - 1) / kTile;
   const float sf = (float)levels;
   if (res)
     hipLaunchKernelGGL((k_qsgd<true>), (int)blocks, kBlock, 0, s, x, res, n, lpg_log2, sf, seed, index_base, codes, norms);

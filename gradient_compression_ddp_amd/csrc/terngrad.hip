@@ -12,6 +12,12 @@
 // codes of quad qs+b and the bottom d codes of quad qs+b+1, which the wave stitches with
 // one lane shuffle.  With d != 0 a run of 64 lanes emits 63 bytes and lane 63 only
 // supplies the neighbour codes.
+//
+// Both passes keep kUnroll independent 16-byte loads in flight per lane.  All segments
+// (up to 32 per launch) share one launch of each pass: grouping them so that pass B would
+// re-read from the 256 MB memory-side cache measured slower on MI355X (launches of
+// 60-170 MB each cost more than the cache saves).  Pass B is bound by its VALU work, a
+// Philox4x32-10 block per quad, rather than by HBM.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -20,6 +26,7 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kSegBatch = 32;
+constexpr int kUnroll = 4;
 
 struct SegBatch {
   int count;
@@ -70,15 +77,26 @@ __global__ __launch_bounds__(kBlock) void k_tern_max(const float* __restrict__ x
   const int si = blockIdx.y;
   const int64_t lo = sb.start[si], hi = sb.end[si];
   const int64_t q0 = lo >> 2, q1 = (hi + 3) >> 2;
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
   uint32_t mx = 0u;
-  for (int64_t Q = q0 + (int64_t)blockIdx.x * kBlock + threadIdx.x; Q < q1;
-       Q += (int64_t)gridDim.x * kBlock) {
-    float v[4];
-    bool ok[4];
-    load_quad_masked<EF>(x, res, Q, lo, hi, n, v, ok);
+  for (int64_t Q = q0 + (int64_t)blockIdx.x * kBlock + threadIdx.x; Q < q1; Q += kUnroll * stride) {
+    float v[kUnroll][4];
+    bool ok[kUnroll][4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-      if (ok[m]) mx = max(mx, fbits(fabsf(v[m])));
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t Qu = Q + u * stride;
+      if (Qu < q1) {
+        load_quad_masked<EF>(x, res, Qu, lo, hi, n, v[u], ok[u]);
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) { v[u][m] = 0.f; ok[u][m] = false; }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        if (ok[u][m]) mx = max(mx, fbits(fabsf(v[u][m])));
   }
   mx = seg_max_u32(mx, kWave);
   const int w = threadIdx.x / kWave;
@@ -111,39 +129,54 @@ __global__ __launch_bounds__(kBlock) void k_tern_codes(const float* __restrict__
   const int lane = lane_id();
   uint8_t* __restrict__ out = packed + sb.out_byte[si];
   const int64_t waves = ((int64_t)gridDim.x * kBlock) >> 6;
-  for (int64_t run = ((int64_t)blockIdx.x * kBlock + threadIdx.x) >> 6; run < runs; run += waves) {
-    const int64_t b0 = run * step;
-    const int64_t Q = qs + b0 + lane;
-    float v[4];
-    bool ok[4];
-    load_quad_masked<EF>(x, res, Q, lo, hi, n, v, ok);
-    float u[4];
-    uniforms4(seed, (uint64_t)(index_base + (Q << 2)), u);
-    uint32_t c8 = 0u;
-    float gh[4];
+  // The loop bound is uniform per wave, so every lane takes part in the shuffle.
+  for (int64_t run = ((int64_t)blockIdx.x * kBlock + threadIdx.x) >> 6; run < runs; run += kUnroll * waves) {
+    float v[kUnroll][4];
+    bool ok[kUnroll][4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      uint32_t bits = 0u;
-      float g = 0.f;
-      if (ok[m] && sc > 0.f) {
-        const float p = fabsf(v[m]) / sc;
-        if (u[m] < p) {
-          const bool neg = v[m] < 0.f;
-          bits = neg ? 3u : 1u;
-          g = neg ? -sc : sc;
-        }
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t ru = run + u * waves;
+      if (ru < runs) {
+        load_quad_masked<EF>(x, res, qs + ru * step + lane, lo, hi, n, v[u], ok[u]);
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) { v[u][m] = 0.f; ok[u][m] = false; }
       }
-      gh[m] = g;
-      c8 |= bits << (2 * m);
     }
-    const uint32_t nxt = (uint32_t)__shfl_down((int)c8, 1, kWave);
-    const uint32_t byte = d == 0 ? c8 : (((c8 >> (2 * d)) | (nxt << (8 - 2 * d))) & 0xFFu);
-    const bool owner = lane < step;
-    if (owner && b0 + lane < nb) out[b0 + lane] = (uint8_t)byte;
-    if (EF && owner) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
-        if (ok[m]) res[(Q << 2) + m] = v[m] - gh[m];
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t ru = run + u * waves;
+      if (ru >= runs) break;   // uniform across the wave
+      const int64_t b0 = ru * step;
+      const int64_t Q = qs + b0 + lane;
+      float uu[4];
+      uniforms4(seed, (uint64_t)(index_base + (Q << 2)), uu);
+      uint32_t c8 = 0u;
+      float gh[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        uint32_t bits = 0u;
+        float g = 0.f;
+        if (ok[u][m] && sc > 0.f) {
+          const float p = fabsf(v[u][m]) / sc;
+          if (uu[m] < p) {
+            const bool neg = v[u][m] < 0.f;
+            bits = neg ? 3u : 1u;
+            g = neg ? -sc : sc;
+          }
+        }
+        gh[m] = g;
+        c8 |= bits << (2 * m);
+      }
+      const uint32_t nxt = (uint32_t)__shfl_down((int)c8, 1, kWave);
+      const uint32_t byte = d == 0 ? c8 : (((c8 >> (2 * d)) | (nxt << (8 - 2 * d))) & 0xFFu);
+      const bool owner = lane < step;
+      if (owner && b0 + lane < nb) out[b0 + lane] = (uint8_t)byte;
+      if (EF && owner) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          if (ok[u][m]) res[(Q << 2) + m] = v[u][m] - gh[m];
+      }
     }
   }
 }
@@ -160,9 +193,10 @@ hipError_t launch_terngrad(const float* x, float* res, int nseg, const int64_t* 
   const int64_t n = off[nseg];
   const int cus = device_cu_count();
   int64_t out_byte = 0;
-  for (int b0 = 0; b0 < nseg; b0 += kSegBatch) {
+  for (int b0 = 0; b0 < nseg;) {
     SegBatch sb{};
-    sb.count = nseg - b0 < kSegBatch ? nseg - b0 : kSegBatch;
+    const int cnt = nseg - b0 < kSegBatch ? nseg - b0 : kSegBatch;
+    sb.count = cnt;
     int64_t maxlen = 0;
     for (int i = 0; i < sb.count; ++i) {
       sb.index[i] = b0 + i;
@@ -173,6 +207,7 @@ hipError_t launch_terngrad(const float* x, float* res, int nseg, const int64_t* 
       out_byte += (len + 3) / 4;
       if (len > maxlen) maxlen = len;
     }
+    b0 += cnt;
     if (maxlen == 0) continue;
     // spread roughly 8 blocks per CU over the batch
     int64_t per_seg = ((int64_t)cus * 8 + sb.count - 1) / sb.count;
