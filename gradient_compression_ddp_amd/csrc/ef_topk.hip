@@ -10,8 +10,11 @@
 //
 // Pipeline (all on the caller's stream, no host synchronization):
 //  1. sample   key(g+r) at m <= 2^20 jittered positions;
-//  2. select   a conservative lower bound L on the k-th largest key from the sample
-//              (exact when the sample is the whole input);
+//  2. select   a conservative lower bound L on the k-th largest key from the sample.
+//              When n <= 2^20 the sample is the whole input and this select is already
+//              exact (T and need); the pool then has room for all n elements and steps
+//              4-5 and the fallback are skipped, which halves the kernel count of a
+//              small call;
 //  3. K1       the one full streaming pass, one 4096-element tile per block: c = g + r
 //              written over r, and every element with key >= L appended to a candidate
 //              pool (a wave ballot and mbcnt give each candidate its slot; the tile claims
@@ -112,6 +115,10 @@ Layout make_layout(void* base, int64_t n, int64_t k, bool staging) {
   const double expect_cand = (double)sample_rank(n, k) * (double)n / (double)(m > 0 ? m : 1);
   const int64_t want = expect_cand > (double)k ? (int64_t)expect_cand : k;
   int64_t cap = 2 * want + (int64_t)kRegions * kTile;
+  // A whole-input sample gives the exact k-th key, and every element may tie with it:
+  // room for all n.  Region r then receives at most ceil(ntiles / 32) tiles of 4096,
+  // which is within its share cap / 32.
+  if (m == n) cap = n + (int64_t)kRegions * kTile;
   const int64_t cap_max = (int64_t)0xFFFFFFFFu - (int64_t)kRegions * (kTile + 4);
   if (cap > cap_max) cap = cap_max;
   l.region_cap = cdiv(cdiv(cap, kRegions), 4) * 4;   // regions start 16-byte aligned
@@ -177,7 +184,7 @@ __device__ __forceinline__ void block_scan32(const uint32_t* s_cnt, uint32_t* s_
 // ---------------------------------------------------------------------------------
 // Kernels
 // ---------------------------------------------------------------------------------
-__global__ void k_init(TopkCtrl* __restrict__ ctrl, unsigned long long krem) {
+__global__ void k_init(TopkCtrl* __restrict__ ctrl, unsigned long long krem, unsigned long long nchunks) {
   for (int i = threadIdx.x; i < kBins; i += blockDim.x) ctrl->hist[i] = 0ull;
   for (int i = threadIdx.x; i < kRegions; i += blockDim.x) ctrl->region_fill[i] = 0u;
   if (threadIdx.x < 2) ctrl->batch_next[threadIdx.x] = 0u;
@@ -190,7 +197,7 @@ __global__ void k_init(TopkCtrl* __restrict__ ctrl, unsigned long long krem) {
     ctrl->ncand = 0ull;
     ctrl->krem = krem;
     ctrl->need = 0ull;
-    ctrl->nchunks = 0ull;
+    ctrl->nchunks = nchunks;
   }
 }
 
@@ -274,7 +281,8 @@ __global__ __launch_bounds__(kBlock) void k_hist(TopkCtrl* __restrict__ ctrl,
 
 // Locate the bin holding rank `krem` (counted from the largest key) and fix its bits.
 // final_op: 0 = intermediate pass; 1 = last pass of the sample select (set L, reset for
-// the main select with rank k); 2 = last pass of the main select (set T and need).
+// the main select with rank k); 2 = last pass of the main select (set T and need);
+// 3 = last pass of a select over the whole input (L = T, and need).
 __global__ __launch_bounds__(kBlock) void k_pick(TopkCtrl* __restrict__ ctrl, int shift, int final_op,
                                                  unsigned long long k_main) {
   __shared__ unsigned long long s_sum[kBlock];
@@ -317,6 +325,7 @@ __global__ __launch_bounds__(kBlock) void k_pick(TopkCtrl* __restrict__ ctrl, in
       ctrl->prefix = 0u;
       ctrl->krem = k_main;
     } else {
+      if (final_op == 3) ctrl->L = T;
       ctrl->T = T;
       ctrl->need = ctrl->krem;
     }
@@ -557,6 +566,31 @@ __global__ __launch_bounds__(kBlock) void k_scan_down(const uint32_t* __restrict
   }
 }
 
+
+// One-block exclusive scan of two uint32 count arrays (small counts only).
+__global__ __launch_bounds__(kBlock) void k_scan_small(const uint32_t* __restrict__ a,
+                                                       const uint32_t* __restrict__ b, int64_t count,
+                                                       unsigned long long* __restrict__ oa,
+                                                       unsigned long long* __restrict__ ob) {
+  __shared__ unsigned long long s_w[2][kWaves];
+  unsigned long long ca = 0, cb = 0;
+  const int w = threadIdx.x / kWave;
+  for (int64_t r0 = 0; r0 < count; r0 += kBlock) {
+    const int64_t it = r0 + threadIdx.x;
+    const unsigned long long va = it < count ? a[it] : 0ull;
+    const unsigned long long vb = it < count ? b[it] : 0ull;
+    const unsigned long long ia = wave_incl_scan_u64(va);
+    const unsigned long long ib = wave_incl_scan_u64(vb);
+    if (lane_id() == kWave - 1) { s_w[0][w] = ia; s_w[1][w] = ib; }
+    __syncthreads();
+    unsigned long long pa = ca, pb = cb;
+    for (int i = 0; i < w; ++i) { pa += s_w[0][i]; pb += s_w[1][i]; }
+    if (it < count) { oa[it] = pa + ia - va; ob[it] = pb + ib - vb; }
+    ca += s_w[0][0] + s_w[0][1] + s_w[0][2] + s_w[0][3];
+    cb += s_w[1][0] + s_w[1][1] + s_w[1][2] + s_w[1][3];
+    __syncthreads();
+  }
+}
 
 // Choose the source of the exact selection.  Candidates hold the answer iff the pool did
 // not overflow and at least k entries reached the bound L (then T >= L).  Without
@@ -1025,14 +1059,17 @@ hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, i
   // 1-2: sample and conservative bound L on the k-th largest key
   const int64_t m = sample_size(n);
   const int64_t j = sample_rank(n, k);
-  hipLaunchKernelGGL(k_init, 1, 256, 0, s, ctrl, (unsigned long long)j);
+  const bool exact = m == n;   // the sample select is the exact select
+  const int64_t nbatch = cdiv(l.ntiles, kBatch);
+  hipLaunchKernelGGL(k_init, 1, 256, 0, s, ctrl, (unsigned long long)j, (unsigned long long)nbatch);
   hipLaunchKernelGGL(k_sample, clamp_grid(cdiv(m, 256), cus * 8), 256, 0, s, grad, res, n, m, l.sample);
   const int shifts[3] = {20, 9, 0}, widths[3] = {11, 11, 9};
   const int sgrid = clamp_grid(cdiv(m, 256 * 8), cus * 2);
   for (int p = 0; p < 3; ++p) {
     hipLaunchKernelGGL((k_hist<0>), sgrid, kBlock, 0, s, ctrl, l.sample, m, (const float*)nullptr,
                        (int64_t)0, (const float*)nullptr, n, shifts[p], widths[p]);
-    hipLaunchKernelGGL(k_pick, 1, kBlock, 0, s, ctrl, shifts[p], p == 2 ? 1 : 0, (unsigned long long)k);
+    hipLaunchKernelGGL(k_pick, 1, kBlock, 0, s, ctrl, shifts[p], p == 2 ? (exact ? 3 : 1) : 0,
+                       (unsigned long long)k);
   }
 
   // 3: the streaming pass
@@ -1041,39 +1078,47 @@ hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, i
                      l.tile_count, l.pool_val, l.pool_off, (uint32_t)l.region_cap);
   prof_mark(s, 2);
 
-  // 4: source decision
-  hipLaunchKernelGGL(k_decide, 1, 64, 0, s, ctrl, l.ntiles, (unsigned long long)k);
-
-  // 5: exact k-th key over the selected source
-  const int hgrid = cus * 4;
-  for (int p = 0; p < 3; ++p) {
-    hipLaunchKernelGGL((k_hist<1>), hgrid, kBlock, 0, s, ctrl, (const uint32_t*)nullptr, (int64_t)0,
-                       (const float*)l.pool_val, l.region_cap, (const float*)res, n, shifts[p], widths[p]);
-    hipLaunchKernelGGL(k_pick, 1, kBlock, 0, s, ctrl, shifts[p], p == 2 ? 2 : 0, (unsigned long long)k);
-  }
-
-  // 6: counts per batch (candidates) or per tile (fallback), and their scan; the kernel
-  // of the other mode returns at once
-  const int64_t nbatch = cdiv(l.ntiles, kBatch);
   const int bgrid = clamp_grid(nbatch, cus * 8);
   const int cgrid = clamp_grid(l.ntiles, cus * 8);
-  hipLaunchKernelGGL(k_bcount, bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
-                     l.pool_val, l.chunk_gt, l.chunk_eq);
-  hipLaunchKernelGGL(k_count, cgrid, kBlock, 0, s, ctrl, res, n, l.chunk_gt, l.chunk_eq);
-  const unsigned long long* nch_dev = &ctrl->nchunks;
-  const int cscan = clamp_grid(cdiv(l.max_chunks, kScanChunk), cus * 4);
-  hipLaunchKernelGGL(k_scan_up, cscan, kBlock, 0, s, l.chunk_gt, l.chunk_eq, nch_dev, (int64_t)0, l.scan_up);
-  hipLaunchKernelGGL(k_scan_mid, 1, kBlock, 0, s, nch_dev, (int64_t)0, l.scan_up);
-  hipLaunchKernelGGL(k_scan_down, cscan, kBlock, 0, s, l.chunk_gt, l.chunk_eq, nch_dev, (int64_t)0,
-                     (const unsigned long long*)l.scan_up, l.gt_excl, l.eq_excl);
+  if (exact) {
+    // T and need are known and the pool holds every candidate: count, one-block scan
+    hipLaunchKernelGGL(k_bcount, bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
+                       l.pool_val, l.chunk_gt, l.chunk_eq);
+    hipLaunchKernelGGL(k_scan_small, 1, kBlock, 0, s, (const uint32_t*)l.chunk_gt, (const uint32_t*)l.chunk_eq,
+                       nbatch, l.gt_excl, l.eq_excl);
+  } else {
+    // 4: source decision
+    hipLaunchKernelGGL(k_decide, 1, 64, 0, s, ctrl, l.ntiles, (unsigned long long)k);
+
+    // 5: exact k-th key over the selected source
+    const int hgrid = cus * 4;
+    for (int p = 0; p < 3; ++p) {
+      hipLaunchKernelGGL((k_hist<1>), hgrid, kBlock, 0, s, ctrl, (const uint32_t*)nullptr, (int64_t)0,
+                         (const float*)l.pool_val, l.region_cap, (const float*)res, n, shifts[p], widths[p]);
+      hipLaunchKernelGGL(k_pick, 1, kBlock, 0, s, ctrl, shifts[p], p == 2 ? 2 : 0, (unsigned long long)k);
+    }
+
+    // 6: counts per batch (candidates) or per tile (fallback), and their scan; the kernel
+    // of the other mode returns at once
+    hipLaunchKernelGGL(k_bcount, bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
+                       l.pool_val, l.chunk_gt, l.chunk_eq);
+    hipLaunchKernelGGL(k_count, cgrid, kBlock, 0, s, ctrl, res, n, l.chunk_gt, l.chunk_eq);
+    const unsigned long long* nch_dev = &ctrl->nchunks;
+    const int cscan = clamp_grid(cdiv(l.max_chunks, kScanChunk), cus * 4);
+    hipLaunchKernelGGL(k_scan_up, cscan, kBlock, 0, s, l.chunk_gt, l.chunk_eq, nch_dev, (int64_t)0, l.scan_up);
+    hipLaunchKernelGGL(k_scan_mid, 1, kBlock, 0, s, nch_dev, (int64_t)0, l.scan_up);
+    hipLaunchKernelGGL(k_scan_down, cscan, kBlock, 0, s, l.chunk_gt, l.chunk_eq, nch_dev, (int64_t)0,
+                       (const unsigned long long*)l.scan_up, l.gt_excl, l.eq_excl);
+  }
 
   // 7: ordered compaction
   float* vals = quant ? (out_val ? out_val : l.staging) : out_val;
   hipLaunchKernelGGL(k_bemit, bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
                      (const float*)l.pool_val, (const uint16_t*)l.pool_off, (const unsigned long long*)l.gt_excl,
                      (const unsigned long long*)l.eq_excl, res, index_base, out_idx, vals, quant ? 0 : 1, k);
-  hipLaunchKernelGGL(k_emit, cgrid, kBlock, 0, s, ctrl, res, n, (const unsigned long long*)l.gt_excl,
-                     (const unsigned long long*)l.eq_excl, index_base, out_idx, vals, quant ? 0 : 1, k);
+  if (!exact)
+    hipLaunchKernelGGL(k_emit, cgrid, kBlock, 0, s, ctrl, res, n, (const unsigned long long*)l.gt_excl,
+                       (const unsigned long long*)l.eq_excl, index_base, out_idx, vals, quant ? 0 : 1, k);
 
   // 8: QSGD on the kept values and the residual of the kept set
   if (quant) {

@@ -13,8 +13,10 @@
 // lane, non-temporal 16-byte loads and stores).  On a 25 MiB bucket, 1, 2 and 4 quads per
 // lane measured 10.9, 12.2 and 13.6 us on MI355X: at this size the launch ramp and load
 // latency dominate, and more resident waves hide them best.
-// Larger groups (and the whole-tensor case) take a reduce pass with ordered-integer
-// atomics, a per-group finalize and a quantize pass.
+// Larger groups take a reduce pass with ordered-integer atomics, a per-group finalize and
+// a quantize pass.  A single group (the whole tensor) takes two kernels and no atomics:
+// per-block partial min/max, then a quantize pass in which every block first combines the
+// partials (at most 2048, read from L2); min and max are order-free, so this is exact.
 //
 // Every float operation is one IEEE binary32 operation (the library is compiled with
 // -ffp-contract=off); min/max use the total order -0 < +0 through an order-preserving
@@ -281,6 +283,84 @@ __global__ __launch_bounds__(kBlock) void k_minmax_quant(const float* __restrict
   }
 }
 
+// ---- one group: the whole tensor ------------------------------------------------------
+
+constexpr int kTensorParts = 2048;   // most partial blocks of the whole-tensor reduce
+
+// Block-wide min and max of ordered encodings; every thread calls it, the result is
+// valid in every thread.
+__device__ __forceinline__ void block_minmax(uint32_t& lo, uint32_t& hi) {
+  __shared__ uint32_t s_lo[kBlock / kWave], s_hi[kBlock / kWave];
+  lo = seg_min_u32(lo, kWave);
+  hi = seg_max_u32(hi, kWave);
+  if (lane_id() == 0) { s_lo[threadIdx.x / kWave] = lo; s_hi[threadIdx.x / kWave] = hi; }
+  __syncthreads();
+  lo = s_lo[0]; hi = s_hi[0];
+#pragma unroll
+  for (int w = 1; w < kBlock / kWave; ++w) { lo = min(lo, s_lo[w]); hi = max(hi, s_hi[w]); }
+  __syncthreads();
+}
+
+template <bool EF>
+__global__ __launch_bounds__(kBlock) void k_minmax_tensor_partial(const float* __restrict__ x,
+                                                                  const float* __restrict__ res, int64_t n,
+                                                                  uint32_t* __restrict__ part) {
+  constexpr int kAhead = 4;
+  const int64_t nquads = (n + 3) >> 2;
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  for (int64_t q0 = (int64_t)blockIdx.x * kBlock + threadIdx.x; q0 < nquads; q0 += kAhead * stride) {
+    Quad qd[kAhead];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+      const int64_t q = q0 + u * stride;
+      if (q < nquads) {
+        qd[u] = load_quad<EF>(x, res, q << 2, n);
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) { qd[u].v[m] = 0.f; qd[u].ok[m] = false; }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        if (qd[u].ok[m]) {
+          const uint32_t e = ord_enc(qd[u].v[m]);
+          lo = min(lo, e);
+          hi = max(hi, e);
+        }
+  }
+  block_minmax(lo, hi);
+  if (threadIdx.x == 0) { part[2 * blockIdx.x] = lo; part[2 * blockIdx.x + 1] = hi; }
+}
+
+template <int BITS, bool EF>
+__global__ __launch_bounds__(kBlock) void k_minmax_tensor_quant(const float* __restrict__ x,
+                                                                float* __restrict__ res, int64_t n,
+                                                                const uint32_t* __restrict__ part, int nparts,
+                                                                uint8_t* __restrict__ codes,
+                                                                float* __restrict__ mins,
+                                                                float* __restrict__ scales) {
+  constexpr float L = (float)((1 << BITS) - 1);
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  for (int i = threadIdx.x; i < nparts; i += kBlock) {
+    lo = min(lo, part[2 * i]);
+    hi = max(hi, part[2 * i + 1]);
+  }
+  block_minmax(lo, hi);
+  const float mn = ord_dec(lo), mx = ord_dec(hi);
+  const float scale = (mx - mn) / L;
+  if (blockIdx.x == 0 && threadIdx.x == 0) { mins[0] = mn; scales[0] = scale; }
+  const float mna[4] = {mn, mn, mn, mn}, sca[4] = {scale, scale, scale, scale};
+  const int64_t nquads = (n + 3) >> 2;
+  for (int64_t q = (int64_t)blockIdx.x * kBlock + threadIdx.x; q < nquads; q += (int64_t)gridDim.x * kBlock) {
+    const int64_t e0 = q << 2;
+    const Quad qd = load_quad<EF>(x, res, e0, n);
+    emit_quad<BITS, EF>(qd, e0, n, mna, sca, codes, res);
+  }
+}
+
 int grid_for(int64_t work_items, int per_block, int max_blocks) {
   const int64_t b = (work_items + per_block - 1) / per_block;
   return (int)(b < 1 ? 1 : (b > max_blocks ? max_blocks : b));
@@ -309,6 +389,7 @@ hipError_t launch_minmax_small(const float* x, float* res, int64_t n, int64_t gr
 size_t minmax_large_workspace(int64_t n, int64_t group) {
   const int64_t G = group == 0 ? (n > 0 ? n : 1) : group;
   const int64_t ng = n == 0 ? 0 : (n + G - 1) / G;
+  if (ng == 1) return align256((size_t)2 * kTensorParts * sizeof(uint32_t));
   return 2 * align256((size_t)ng * sizeof(uint32_t));
 }
 
@@ -317,9 +398,23 @@ hipError_t launch_minmax_large(const float* x, float* res, int64_t n, int64_t gr
   if (n == 0) return hipSuccess;
   const int64_t G = group == 0 ? n : group;
   const int64_t ng = (n + G - 1) / G;
+  const int cus = device_cu_count();
+  if (ng == 1) {
+    uint32_t* part = reinterpret_cast<uint32_t*>(ws);
+    const int64_t nquads = (n + 3) / 4;
+    const int pgrid = grid_for(nquads, kBlock * 4, kTensorParts);
+    const int qgrid = grid_for(nquads, kBlock, cus * 16);
+    if (res) hipLaunchKernelGGL((k_minmax_tensor_partial<true>), pgrid, kBlock, 0, s, x, res, n, part);
+    else hipLaunchKernelGGL((k_minmax_tensor_partial<false>), pgrid, kBlock, 0, s, x, res, n, part);
+#define GC_TQ(B, E) hipLaunchKernelGGL((k_minmax_tensor_quant<B, E>), qgrid, kBlock, 0, s, x, res, n, \
+                                       (const uint32_t*)part, pgrid, codes, mins, scales)
+    if (bits == 8) { if (res) GC_TQ(8, true); else GC_TQ(8, false); }
+    else { if (res) GC_TQ(4, true); else GC_TQ(4, false); }
+#undef GC_TQ
+    return hipGetLastError();
+  }
   uint32_t* gmin = reinterpret_cast<uint32_t*>(ws);
   uint32_t* gmax = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) + align256((size_t)ng * 4));
-  const int cus = device_cu_count();
   const int fill_grid = grid_for(ng, 256, cus * 8);
   hipLaunchKernelGGL(k_fill_u32, fill_grid, 256, 0, s, gmin, ng, 0xFFFFFFFFu);
   hipLaunchKernelGGL(k_fill_u32, fill_grid, 256, 0, s, gmax, ng, 0u);

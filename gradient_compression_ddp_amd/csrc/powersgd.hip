@@ -36,7 +36,6 @@ constexpr int kGramBlocks = 256;
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct PLayout {
-  float* qp;      // [ceil(cols/64) * 64 * 4]   Q permuted for pass 1
   float* ppart;   // [ncp * rows * 4]          pass-1 partials per column panel
   float* p;       // [rows * 4]                P = M Q
   double* gram;   // [kGramBlocks * 10]        Gram partials
@@ -59,7 +58,6 @@ PLayout make_playout(void* base, int64_t rows, int64_t cols) {
     off += align256(bytes);
     return p;
   };
-  l.qp = (float*)take(sizeof(float) * cdiv(cols, 64) * 64 * 4);
   l.ppart = (float*)take(sizeof(float) * l.ncp * rows * 4);
   l.p = (float*)take(sizeof(float) * rows * 4);
   l.gram = (double*)take(sizeof(double) * kGramBlocks * 10);
@@ -81,25 +79,13 @@ __device__ __forceinline__ f32x4 load4_or_zero(const float* p, bool ok) {
   return z;
 }
 
-// Qp[kg][lane][s] = Q[kg*64 + 4*(lane/4) + s][lane%4], zero outside (cols, rank).
-__global__ void k_qperm(const float* __restrict__ Q, int64_t cols, int rank, float* __restrict__ qp) {
-  const int64_t total = cdiv(cols, 64) * 64 * 4;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
-       t += (int64_t)gridDim.x * blockDim.x) {
-    const int s = (int)(t & 3);
-    const int lane = (int)((t >> 2) & 63);
-    const int64_t kg = t >> 8;
-    const int64_t col = kg * 64 + 4 * (lane >> 2) + s;
-    const int j = lane & 3;
-    qp[t] = (col < cols && j < rank) ? Q[col * rank + j] : 0.f;
-  }
-}
-
 // Pass 1: M = G + E (written over E when E is given) and P partials per column panel.
+// Lane (b, i) takes Q[col + s][i] for the 4 columns col = kg*64 + 4b of its step (zero
+// outside cols x rank); Q is small enough to stay in cache.
 template <bool EF>
 __global__ __launch_bounds__(kBlock) void k_p1(const float* __restrict__ G, float* __restrict__ E,
-                                               int64_t rows, int64_t cols, const float* __restrict__ qp,
-                                               float* __restrict__ ppart) {
+                                               int64_t rows, int64_t cols, const float* __restrict__ Q,
+                                               int rank, float* __restrict__ ppart) {
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
   const int64_t cp = blockIdx.x;
@@ -113,7 +99,9 @@ __global__ __launch_bounds__(kBlock) void k_p1(const float* __restrict__ G, floa
     const int64_t kg = cp * (kP1Cols / 64) + ks;
     const int64_t col = kg * 64 + 4 * b;
     const bool col_ok = col < cols;
-    const f32x4 qv = *reinterpret_cast<const f32x4*>(qp + (kg * 64 + lane) * 4);
+    f32x4 qv;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qv[s] = (col + s < cols && i < rank) ? Q[(col + s) * rank + i] : 0.f;
     f32x4 m[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -385,10 +373,9 @@ hipError_t launch_powersgd(const float* grad, float* res, int64_t rows, int64_t 
                            float* P, void* ws, hipStream_t s) {
   const PLayout l = make_playout(ws, rows, cols);
   const int cus = device_cu_count();
-  hipLaunchKernelGGL(k_qperm, clamp_grid(cdiv(cdiv(cols, 64) * 256, 256), cus * 4), 256, 0, s, Q, cols, rank, l.qp);
   const dim3 g1((unsigned)l.ncp, (unsigned)l.nrp);
-  if (res) hipLaunchKernelGGL((k_p1<true>), g1, kBlock, 0, s, grad, res, rows, cols, l.qp, l.ppart);
-  else hipLaunchKernelGGL((k_p1<false>), g1, kBlock, 0, s, grad, res, rows, cols, l.qp, l.ppart);
+  if (res) hipLaunchKernelGGL((k_p1<true>), g1, kBlock, 0, s, grad, res, rows, cols, (const float*)Q, rank, l.ppart);
+  else hipLaunchKernelGGL((k_p1<false>), g1, kBlock, 0, s, grad, res, rows, cols, (const float*)Q, rank, l.ppart);
   hipLaunchKernelGGL(k_psum_gram, kGramBlocks, kBlock, 0, s, l.ppart, l.ncp, rows, l.p, l.gram);
   hipLaunchKernelGGL(k_gs, 1, 64, 0, s, l.gram, kGramBlocks, rank, l.t);
   hipLaunchKernelGGL(k_apply_t, clamp_grid(cdiv(rows, 256), cus * 4), 256, 0, s, l.p, l.t, rows, rank, l.phat, P);

@@ -179,7 +179,7 @@ def test_topk_demo_two_steps(gc):
 
 @pytest.mark.parametrize("n,k", [(8192 * 3 + 77, 1), (8192 * 3 + 77, 100), (8192 * 3 + 77, 8192 * 3 + 77),
                                  (1, 1), (7, 3), (8192, 8192), (100_000, 50_000), (2_500_001, 25_000),
-                                 (5_000_003, 4_000_000)])
+                                 (5_000_003, 4_000_000), (1 << 20, 10_000), ((1 << 20) + 1, 10_000)])
 def test_topk_sizes(gc, n, k):
     g = workloads.bucket(n, seed=11)
     r = (workloads.bucket(n, seed=12) * F32(0.1)).astype(F32)
@@ -196,6 +196,16 @@ def test_topk_ties_and_specials(gc):
     rng = np.random.default_rng(3)
     g = rng.choice(np.array([0.0, -0.0, 1.0, -1.0, 2.0, np.inf, -np.inf, np.nan, 1e-45], F32), n)
     check_topk(gc, g, np.zeros(n, F32), 10_000)
+
+
+def test_topk_whole_input_select_all_ties(gc):
+    # n = 2^20: the sample is the whole input, so the select is exact and the pool must
+    # hold every element when all of them tie with the k-th key
+    n = 1 << 20
+    check_topk(gc, np.full(n, 0.5, F32), np.zeros(n, F32), 3)
+    g = np.full(n, -0.25, F32)
+    g[n - 5:] = 0.25
+    check_topk(gc, g, np.zeros(n, F32), n - 2)
 
 
 def test_topk_forced_fallback(gc):
@@ -294,3 +304,38 @@ def test_topk_small_k_on_large_n(gc):
     r = np.zeros(n, F32)
     for k in (1, 7, 1000):
         check_topk(gc, g, r, k)
+
+
+@pytest.mark.parametrize("shift_out,shift_codes", [(0, 0), (1, 0), (0, 1)])
+def test_decompress_dense_tiles_groups_alignment(gc, shift_out, shift_codes):
+    """Dense decode over several 4096-entry tiles with a ragged tail, groups that are not
+    powers of two, and buffers offset so that the vector path cannot be used."""
+    n = 6 * 4100   # 24,600: six 4,096-entry tiles and a ragged tail; six TernGrad segments
+    x = workloads.bucket(n, seed=11)
+    cases = []
+    c8, m8, s8, _, _ = oracle.quant_minmax(x, 1000, 8)
+    cases.append((gc.KIND_MINMAX8, c8, m8, s8, 1000, 0))
+    c4, m4, s4, _, _ = oracle.quant_minmax(x, 64, 4)
+    cases.append((gc.KIND_MINMAX4, oracle.pack_int4(c4), m4, s4, 64, 0))
+    cq, nq, _, _ = oracle.qsgd(x, 64, 127, seed=9)
+    cases.append((gc.KIND_QSGD, cq, nq, None, 64, 127))
+    seg = np.arange(0, n + 1, 4100, dtype=np.int64)
+    pk, sc, _, _, _ = oracle.terngrad(x, seg, seed=5)
+    cases.append((gc.KIND_TERN, pk, sc, None, 4100, 0))
+    cases.append((gc.KIND_F32, x, None, None, 0, 0))
+    for kind, codes, m0, m1, group, levels in cases:
+        if shift_codes and kind != gc.KIND_MINMAX8:
+            continue   # a one-byte offset is only meaningful for byte codes
+        for alpha, acc in ((1.0, 0), (-0.5, 1)):
+            init = np.linspace(-2, 2, n + shift_out, dtype=F32)
+            want = oracle.decompress_scatter(kind, None, n, 0, codes, m0, m1, group, levels, alpha, acc,
+                                             init[shift_out:].copy())
+            out_full = dev(init)
+            out = out_full[shift_out:]
+            cbuf = dev(np.concatenate([np.zeros(shift_codes, codes.dtype), codes]))[shift_codes:]
+            gc.decompress_scatter(kind, cbuf, n, out, meta0=None if m0 is None else dev(m0),
+                                  meta1=None if m1 is None else dev(m1), group=group, levels=levels,
+                                  alpha=alpha, accumulate=bool(acc))
+            got = host(out_full)
+            assert_bits_equal(got[shift_out:], want, f"kind {kind} shift {shift_out}/{shift_codes}")
+            assert_bits_equal(got[:shift_out], init[:shift_out], "bytes before out untouched")
