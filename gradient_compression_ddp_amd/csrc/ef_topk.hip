@@ -24,9 +24,10 @@
 //              count >= k); otherwise the exact fallback selects over the full c;
 //  5. select   the exact k-th largest key T by three radix passes (11, 11, 9 bits) with
 //              LDS histograms, and `need`, the number of entries with key == T to keep;
-//  6. count    per batch of 128 tiles, the candidates with key > T and key == T, and an
-//              exclusive scan of both over the batches;
-//  7. emit     ordered compaction straight from the pool: a batch's candidates are taken
+//  6. count    per unit of 16 tiles, the candidates with key > T and key == T, and an
+//              exclusive scan of both over the units;
+//  7. emit     ordered compaction straight from the pool, by batches of 128 tiles (8
+//              units) from a device-side work queue: a batch's candidates are taken
 //              in (tile, offset) order, which is index order, and entry e goes to
 //              position gt_before(e) + min(eq_before(e), need) when key > T, or when
 //              key == T and eq_before(e) < need (so the lower index wins the ties); pure
@@ -47,13 +48,13 @@ constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / kWave;       // 4
 constexpr int kRounds = 4;                   // quads per thread per tile
 constexpr int64_t kTile = (int64_t)kBlock * 4 * kRounds;   // 4096 elements
-constexpr int kTileShift = 12;
 constexpr int kRegions = 32;                 // candidate-pool regions (tile % 32)
 constexpr int kSampleMax = 1 << 20;
 constexpr int kScanChunk = 1024;             // items per block in the multi-block scan
 constexpr int kBins = 2048;
-constexpr int kBatch = 128;                  // tiles per batch of the candidate count / emit
-static_assert(kBatch == 2 * kWave, "the batch table scan assumes two waves");
+constexpr int kUnit = 16;                    // tiles per unit of the candidate count and scan
+constexpr int kBatch = 128;                  // tiles per batch of the emit (8 units)
+static_assert(kBatch % kUnit == 0 && kBatch <= 2 * kWave && kUnit <= kWave, "batch tables");
 
 enum : uint32_t { MODE_CAND = 0, MODE_FULL = 1 };
 
@@ -70,7 +71,7 @@ struct TopkCtrl {
   unsigned long long nchunks; // tiles of the full fallback source
   unsigned long long hist[kBins];
   uint32_t region_fill[kRegions];
-  uint32_t batch_next[2];     // work queues of the batch count and the batch emit
+  uint32_t emit_next;         // work queue of the batch emit
 };
 
 struct Layout {
@@ -187,7 +188,7 @@ __device__ __forceinline__ void block_scan32(const uint32_t* s_cnt, uint32_t* s_
 __global__ void k_init(TopkCtrl* __restrict__ ctrl, unsigned long long krem, unsigned long long nchunks) {
   for (int i = threadIdx.x; i < kBins; i += blockDim.x) ctrl->hist[i] = 0ull;
   for (int i = threadIdx.x; i < kRegions; i += blockDim.x) ctrl->region_fill[i] = 0u;
-  if (threadIdx.x < 2) ctrl->batch_next[threadIdx.x] = 0u;
+  if (threadIdx.x == 0) ctrl->emit_next = 0u;
   if (threadIdx.x == 0) {
     ctrl->L = 0u;
     ctrl->overflow = 0u;
@@ -602,29 +603,31 @@ __global__ void k_decide(TopkCtrl* __restrict__ ctrl, int64_t ntiles, unsigned l
     const bool full = ctrl->overflow != 0u || ncand < k;
     ctrl->ncand = full ? 0ull : ncand;
     ctrl->mode = full ? MODE_FULL : MODE_CAND;
-    ctrl->nchunks = (unsigned long long)(full ? ntiles : cdiv(ntiles, kBatch));
+    ctrl->nchunks = (unsigned long long)(full ? ntiles : cdiv(ntiles, kUnit));
   }
 }
 
-// ---- the candidates of a batch of kBatch consecutive tiles -----------------------------
-// pre[i] is the exclusive prefix of the tile counts inside the batch; past the last tile
-// (i >= nt, up to kBatch) it holds the total.  start[i] is the tile's pool position.
-// Entry j of the batch (0 <= j < total) lies in the tile lo with pre[lo] <= j <
-// pre[lo + 1], at pool position start[lo] + j - pre[lo]; taken in j order the entries
-// are in index order.  Batches are handed out by an atomic work queue, so a block that
-// drew a dense batch (a layer with a large scale holds ten times the average) does not
-// hold back a fixed share of the others.
+// ---- the candidates of KB consecutive tiles (a unit or a batch) ------------------------
+// pre[i] is the exclusive prefix of the tile counts inside the group; past the last tile
+// (i >= nt, up to KB) it holds the total.  start[i] is the tile's pool position.  Entry j
+// of the group (0 <= j < total) lies in the tile lo with pre[lo] <= j < pre[lo + 1], at
+// pool position start[lo] + j - pre[lo]; taken in j order the entries are in index order.
+template <int KB>
 struct BatchTable {
-  uint32_t pre[kBatch + 1];
-  uint32_t start[kBatch];
+  uint32_t pre[KB + 1];
+  uint32_t start[KB];
   uint32_t wsum[2];
+  uint32_t total;
 };
 
-// Fills the table for tiles [t0, t0 + nt); every thread calls it; returns the total.
-__device__ __forceinline__ uint32_t load_batch(BatchTable& bt, int64_t t0, int nt,
+// Fills the table for tiles [t0, t0 + nt); every thread calls it (it ends with a
+// barrier) and gets the total.  KB <= 64 uses one wave, KB = 128 two.
+template <int KB>
+__device__ __forceinline__ uint32_t load_batch(BatchTable<KB>& bt, int64_t t0, int nt,
                                                const uint32_t* __restrict__ tile_start,
                                                const uint32_t* __restrict__ tile_count) {
-  if (threadIdx.x < kBatch) {
+  constexpr int kScanWidth = KB < kWave ? KB : kWave;
+  if (threadIdx.x < (KB < kWave ? kWave : KB)) {
     const int li = threadIdx.x;
     uint32_t cn = 0;
     if (li < nt) {
@@ -633,75 +636,85 @@ __device__ __forceinline__ uint32_t load_batch(BatchTable& bt, int64_t t0, int n
     }
     uint32_t inc = cn;
 #pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
+    for (int d = 1; d < kScanWidth; d <<= 1) {
       const uint32_t o = (uint32_t)__shfl_up((int)inc, d, kWave);
       if (lane_id() >= d) inc += o;
     }
-    if (lane_id() == kWave - 1) bt.wsum[li / kWave] = inc;
-    bt.pre[li] = inc - cn;   // exclusive within the wave; the second wave adds wsum[0] below
+    if (li < KB) bt.pre[li] = inc - cn;   // exclusive within the wave
+    if (KB <= kWave) {
+      if (li == KB - 1) { bt.pre[KB] = inc; bt.total = inc; }
+    } else if (lane_id() == kWave - 1) {
+      bt.wsum[li / kWave] = inc;
+    }
   }
   __syncthreads();
-  if (threadIdx.x >= kWave && threadIdx.x < kBatch) bt.pre[threadIdx.x] += bt.wsum[0];
-  const uint32_t total = bt.wsum[0] + bt.wsum[1];
-  // padding entries pre[nt..kBatch-1] (count 0) already hold the total; so does pre[kBatch]
-  if (threadIdx.x == 0) bt.pre[kBatch] = total;
-  __syncthreads();
-  return total;
+  if (KB > kWave) {
+    // the second wave adds the first wave's sum; padding entries (count 0) then hold the
+    // total, and so does pre[KB]
+    if (threadIdx.x >= kWave && threadIdx.x < KB) bt.pre[threadIdx.x] += bt.wsum[0];
+    if (threadIdx.x == 0) { bt.total = bt.wsum[0] + bt.wsum[1]; bt.pre[KB] = bt.total; }
+    __syncthreads();
+  }
+  return bt.total;
 }
 
 // Tile of entry j < total: the largest lo with pre[lo] <= j (that tile is non-empty).
-// A fixed 7-step search (the padding entries equal the total, so they are never taken),
+// A fixed-step search (the padding entries equal the total, so they are never taken),
 // which the compiler interleaves across a thread's independent entries.
-__device__ __forceinline__ int batch_tile(const BatchTable& bt, uint32_t j) {
+template <int KB>
+__device__ __forceinline__ int batch_tile(const BatchTable<KB>& bt, uint32_t j) {
   int lo = 0;
 #pragma unroll
-  for (int step = kBatch / 2; step > 0; step >>= 1)
+  for (int step = KB / 2; step > 0; step >>= 1)
     if (bt.pre[lo + step] <= j) lo += step;
   return lo;
 }
 
-// Next batch from work queue q (every thread calls it; uniform result, or -1 when the
-// queue is empty, which every block reaches).
-__device__ __forceinline__ int64_t next_batch(TopkCtrl* ctrl, int q, int64_t nbatch, int64_t* s_b) {
+// Next batch from the emit's work queue (every thread calls it; uniform result, or -1
+// when the queue is empty, which every block reaches).  Dense batches hold ten times the
+// average, so a queue keeps blocks from waiting on a fixed share of them.
+__device__ __forceinline__ int64_t next_batch(TopkCtrl* ctrl, int64_t nbatch, int64_t* s_b) {
   __syncthreads();   // the previous batch is done with s_b and the batch table
-  if (threadIdx.x == 0) *s_b = (int64_t)atomicAdd(&ctrl->batch_next[q], 1u);
+  if (threadIdx.x == 0) *s_b = (int64_t)atomicAdd(&ctrl->emit_next, 1u);
   __syncthreads();
   const int64_t b = *s_b;
   return b < nbatch ? b : -1;
 }
 
-constexpr int kEmitU = 8;   // entries per thread per chunk of the batch walk
+constexpr int kEmitU = 8;   // entries per thread per chunk of the batch emit
+constexpr int kCountU = 4;  // entries per thread per chunk of the unit count
 
-// Candidates only: per-batch counts of key > T and key == T.
-__global__ __launch_bounds__(kBlock) void k_bcount(TopkCtrl* __restrict__ ctrl, int64_t ntiles,
+// Candidates only: per-unit counts of key > T and key == T (units of kUnit tiles, taken
+// grid-stride: small enough that a dense layer spreads over many blocks).
+__global__ __launch_bounds__(kBlock) void k_bcount(const TopkCtrl* __restrict__ ctrl, int64_t ntiles,
                                                    const uint32_t* __restrict__ tile_start,
                                                    const uint32_t* __restrict__ tile_count,
                                                    const float* __restrict__ pool_val,
-                                                   uint32_t* __restrict__ batch_gt,
-                                                   uint32_t* __restrict__ batch_eq) {
-  __shared__ BatchTable bt;
+                                                   uint32_t* __restrict__ unit_gt,
+                                                   uint32_t* __restrict__ unit_eq) {
+  __shared__ BatchTable<kUnit> bt;
   __shared__ uint32_t s[2][kWaves];
-  __shared__ int64_t s_b;
   if (ctrl->mode != MODE_CAND) return;
   const uint32_t T = ctrl->T;
-  const int64_t nbatch = cdiv(ntiles, kBatch);
-  for (int64_t b; (b = next_batch(ctrl, 0, nbatch, &s_b)) >= 0;) {
-    const int64_t t0 = b * kBatch;
-    const int nt = (int)(ntiles - t0 < kBatch ? ntiles - t0 : kBatch);
+  const int64_t nunit = cdiv(ntiles, kUnit);
+  for (int64_t b = blockIdx.x; b < nunit; b += gridDim.x) {
+    __syncthreads();   // the previous unit is done with the table and s
+    const int64_t t0 = b * kUnit;
+    const int nt = (int)(ntiles - t0 < kUnit ? ntiles - t0 : kUnit);
     const uint32_t total = load_batch(bt, t0, nt, tile_start, tile_count);
     uint32_t gt = 0, eq = 0;
-    for (uint32_t j0 = 0; j0 < total; j0 += kBlock * kEmitU) {
-      uint32_t src[kEmitU];
-      bool live[kEmitU];
+    for (uint32_t j0 = 0; j0 < total; j0 += kBlock * kCountU) {
+      uint32_t src[kCountU];
+      bool live[kCountU];
 #pragma unroll
-      for (int u = 0; u < kEmitU; ++u) {
+      for (int u = 0; u < kCountU; ++u) {
         const uint32_t j = j0 + u * kBlock + threadIdx.x;
         live[u] = j < total;
-        const int lo = live[u] ? batch_tile(bt, j) : 0;
+        const int lo = live[u] ? batch_tile<kUnit>(bt, j) : 0;
         src[u] = bt.start[lo] + (j - bt.pre[lo]);
       }
 #pragma unroll
-      for (int u = 0; u < kEmitU; ++u)
+      for (int u = 0; u < kCountU; ++u)
         if (live[u]) {
           const uint32_t key = mag_key(pool_val[src[u]]);
           gt += key > T;
@@ -713,8 +726,8 @@ __global__ __launch_bounds__(kBlock) void k_bcount(TopkCtrl* __restrict__ ctrl, 
     if (lane_id() == 0) { s[0][threadIdx.x / kWave] = gt; s[1][threadIdx.x / kWave] = eq; }
     __syncthreads();
     if (threadIdx.x == 0) {
-      batch_gt[b] = s[0][0] + s[0][1] + s[0][2] + s[0][3];
-      batch_eq[b] = s[1][0] + s[1][1] + s[1][2] + s[1][3];
+      unit_gt[b] = s[0][0] + s[0][1] + s[0][2] + s[0][3];
+      unit_eq[b] = s[1][0] + s[1][1] + s[1][2] + s[1][3];
     }
   }
 }
@@ -751,7 +764,7 @@ __global__ __launch_bounds__(kBlock) void k_bemit(TopkCtrl* __restrict__ ctrl, i
                                                   float* __restrict__ r, int64_t index_base,
                                                   int64_t* __restrict__ out_idx, float* __restrict__ out_val,
                                                   int zero_residual, int64_t k) {
-  __shared__ BatchTable bt;
+  __shared__ BatchTable<kBatch> bt;
   __shared__ uint32_t s_cnt[kEmitU * kWaves];
   __shared__ uint32_t s_off[kEmitU * kWaves];
   __shared__ uint32_t s_total;
@@ -762,11 +775,12 @@ __global__ __launch_bounds__(kBlock) void k_bemit(TopkCtrl* __restrict__ ctrl, i
   const int w = threadIdx.x / kWave;
   const int lane = lane_id();
   const int64_t nbatch = cdiv(ntiles, kBatch);
-  for (int64_t b; (b = next_batch(ctrl, 1, nbatch, &s_b)) >= 0;) {
+  for (int64_t b; (b = next_batch(ctrl, nbatch, &s_b)) >= 0;) {
     const int64_t t0 = b * kBatch;
     const int nt = (int)(ntiles - t0 < kBatch ? ntiles - t0 : kBatch);
     const uint32_t total = load_batch(bt, t0, nt, tile_start, tile_count);
-    unsigned long long gt_run = gt_excl[b], eq_run = eq_excl[b];
+    // the exclusive prefixes of the batch's first unit
+    unsigned long long gt_run = gt_excl[b * (kBatch / kUnit)], eq_run = eq_excl[b * (kBatch / kUnit)];
     for (uint32_t j0 = 0; j0 < total; j0 += kBlock * kEmitU) {
       uint32_t src[kEmitU];
       int64_t tbase[kEmitU];
@@ -775,7 +789,7 @@ __global__ __launch_bounds__(kBlock) void k_bemit(TopkCtrl* __restrict__ ctrl, i
       for (int u = 0; u < kEmitU; ++u) {
         const uint32_t j = j0 + u * kBlock + threadIdx.x;
         live[u] = j < total;
-        const int lo = live[u] ? batch_tile(bt, j) : 0;
+        const int lo = live[u] ? batch_tile<kBatch>(bt, j) : 0;
         src[u] = bt.start[lo] + (j - bt.pre[lo]);
         tbase[u] = (t0 + lo) * kTile;
       }
@@ -1060,8 +1074,9 @@ hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, i
   const int64_t m = sample_size(n);
   const int64_t j = sample_rank(n, k);
   const bool exact = m == n;   // the sample select is the exact select
+  const int64_t nunit = cdiv(l.ntiles, kUnit);
   const int64_t nbatch = cdiv(l.ntiles, kBatch);
-  hipLaunchKernelGGL(k_init, 1, 256, 0, s, ctrl, (unsigned long long)j, (unsigned long long)nbatch);
+  hipLaunchKernelGGL(k_init, 1, 256, 0, s, ctrl, (unsigned long long)j, (unsigned long long)nunit);
   hipLaunchKernelGGL(k_sample, clamp_grid(cdiv(m, 256), cus * 8), 256, 0, s, grad, res, n, m, l.sample);
   const int shifts[3] = {20, 9, 0}, widths[3] = {11, 11, 9};
   const int sgrid = clamp_grid(cdiv(m, 256 * 8), cus * 2);
@@ -1078,14 +1093,15 @@ hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, i
                      l.tile_count, l.pool_val, l.pool_off, (uint32_t)l.region_cap);
   prof_mark(s, 2);
 
+  const int ugrid = clamp_grid(nunit, cus * 8);
   const int bgrid = clamp_grid(nbatch, cus * 8);
   const int cgrid = clamp_grid(l.ntiles, cus * 8);
   if (exact) {
     // T and need are known and the pool holds every candidate: count, one-block scan
-    hipLaunchKernelGGL(k_bcount, bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
+    hipLaunchKernelGGL(k_bcount, ugrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
                        l.pool_val, l.chunk_gt, l.chunk_eq);
     hipLaunchKernelGGL(k_scan_small, 1, kBlock, 0, s, (const uint32_t*)l.chunk_gt, (const uint32_t*)l.chunk_eq,
-                       nbatch, l.gt_excl, l.eq_excl);
+                       nunit, l.gt_excl, l.eq_excl);
   } else {
     // 4: source decision
     hipLaunchKernelGGL(k_decide, 1, 64, 0, s, ctrl, l.ntiles, (unsigned long long)k);
@@ -1100,7 +1116,7 @@ hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, i
 
     // 6: counts per batch (candidates) or per tile (fallback), and their scan; the kernel
     // of the other mode returns at once
-    hipLaunchKernelGGL(k_bcount, bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
+    hipLaunchKernelGGL(k_bcount, ugrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
                        l.pool_val, l.chunk_gt, l.chunk_eq);
     hipLaunchKernelGGL(k_count, cgrid, kBlock, 0, s, ctrl, res, n, l.chunk_gt, l.chunk_eq);
     const unsigned long long* nch_dev = &ctrl->nchunks;
