@@ -33,19 +33,22 @@ HBM_PEAK_GBS = 8000.0
 # kernel source it was measured on: the digest covers the tile constants, the block-rank
 # helpers and the kernel itself, and a mismatch reports the traffic as null.
 K1_TRAFFIC_BYTES = 8.4612e10
-K1_SOURCE_SHA256 = "cff8662bf0eab494eea940769a946440b82f3083f9bc81822df0a51543d98ae8"
+K1_SOURCE_SHA256 = "a5e899df42a9a417828aea2e7ffb0f6dc52c03f72c678f1e692c3b455ae2856a"
 METRIC = "EF-Top-1%+int8 compress GB/s of fp32 grad input; % of HBM peak"
 
 
 def k1_source_digest():
+    """SHA-256 of the text the streaming pass is built from: the tile constants it uses,
+    the block-rank helpers and the kernel itself."""
+    import hashlib
+    import re
     src = open(os.path.join(ROOT, "gradient_compression_ddp_amd", "csrc", "ef_topk.hip")).read()
-    parts = []
-    for start, end in (("constexpr int kBlock = 256;", "enum : uint32_t"),
-                       ("__device__ __forceinline__ uint32_t rank_round", "// Kernels"),
+    parts = [m.group(0) for m in re.finditer(r"^constexpr \w+ (kBlock|kWaves|kRounds|kTile|kRegions) = .*$",
+                                             src, re.M)]
+    for start, end in (("__device__ __forceinline__ uint32_t rank_round", "// Kernels"),
                        ("void k_ef_cand(", "\n}\n")):
         a = src.index(start)
         parts.append(src[a:src.index(end, a)])
-    import hashlib
     return hashlib.sha256("\n".join(parts).encode()).hexdigest()
 
 
