@@ -225,25 +225,55 @@ __global__ void k_sample(const float* __restrict__ g, const float* __restrict__ 
 }
 
 
-__device__ __forceinline__ void hist_add(uint32_t* my, uint32_t key, uint32_t hshift, uint32_t want,
-                                         int shift, uint32_t mask) {
-  if ((key >> hshift) == want) atomicAdd(&my[(key >> shift) & mask], 1u);
+// Histogram counts go to LDS per run: a thread keeps the bin it last added to and a
+// count, and adds to LDS only when the bin changes.  The keys of the candidate pool
+// crowd into a few bins, so this removes most of the same-address LDS atomics.
+struct BinRun {
+  uint32_t bin, cnt;
+};
+
+__device__ __forceinline__ void run_flush(uint32_t* my, BinRun& r) {
+  if (r.cnt) atomicAdd(&my[r.bin], r.cnt);
+  r.cnt = 0u;
 }
 
-// Histogram of nq quads plus a scalar tail of `count` floats starting at src (16-byte aligned).
+__device__ __forceinline__ void hist_add(uint32_t* my, BinRun& r, uint32_t key, uint32_t hshift, uint32_t want,
+                                         int shift, uint32_t mask) {
+  if ((key >> hshift) == want) {
+    const uint32_t b = (key >> shift) & mask;
+    if (b != r.bin) {
+      run_flush(my, r);
+      r.bin = b;
+    }
+    ++r.cnt;
+  }
+}
+
+// Histogram of nq quads plus a scalar tail of `count` floats starting at src (16-byte
+// aligned); four quads per thread are loaded before any is counted.
 __device__ __forceinline__ void hist_span(const float* __restrict__ src, int64_t count, int64_t first,
-                                          int64_t stride, bool tail_owner, uint32_t* my,
+                                          int64_t stride, bool tail_owner, uint32_t* my, BinRun& r,
                                           uint32_t hshift, uint32_t want, int shift, uint32_t mask) {
+  constexpr int kAhead = 4;
   const int64_t nq = count >> 2;
-  for (int64_t q = first; q < nq; q += stride) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(src + (q << 2));
-    hist_add(my, mag_key(v.x), hshift, want, shift, mask);
-    hist_add(my, mag_key(v.y), hshift, want, shift, mask);
-    hist_add(my, mag_key(v.z), hshift, want, shift, mask);
-    hist_add(my, mag_key(v.w), hshift, want, shift, mask);
+  for (int64_t q = first; q < nq; q += kAhead * stride) {
+    f32x4 v[kAhead];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+      const int64_t qq = q + u * stride;
+      v[u] = qq < nq ? *reinterpret_cast<const f32x4*>(src + (qq << 2)) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+      if (q + u * stride >= nq) break;
+      hist_add(my, r, mag_key(v[u].x), hshift, want, shift, mask);
+      hist_add(my, r, mag_key(v[u].y), hshift, want, shift, mask);
+      hist_add(my, r, mag_key(v[u].z), hshift, want, shift, mask);
+      hist_add(my, r, mag_key(v[u].w), hshift, want, shift, mask);
+    }
   }
   if (tail_owner && threadIdx.x < (count & 3))
-    hist_add(my, mag_key(src[(nq << 2) + threadIdx.x]), hshift, want, shift, mask);
+    hist_add(my, r, mag_key(src[(nq << 2) + threadIdx.x]), hshift, want, shift, mask);
 }
 
 // Radix histogram pass over the key bits [shift, shift+bits) of the entries whose higher
@@ -264,15 +294,17 @@ __global__ __launch_bounds__(kBlock) void k_hist(TopkCtrl* __restrict__ ctrl,
   uint32_t* my = lh[threadIdx.x / kWave];
   const int64_t stride = (int64_t)gridDim.x * kBlock;
   const int64_t first = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  BinRun run{0u, 0u};
   if (SRC == 0) {
-    for (int64_t i = first; i < sample_n; i += stride) hist_add(my, sample_keys[i], hshift, want, shift, mask);
+    for (int64_t i = first; i < sample_n; i += stride) hist_add(my, run, sample_keys[i], hshift, want, shift, mask);
   } else if (ctrl->mode == MODE_CAND) {
     for (int rg = 0; rg < kRegions; ++rg)
       hist_span(pool + rg * region_cap, (int64_t)ctrl->region_fill[rg], first, stride,
-                blockIdx.x == (unsigned)(rg % gridDim.x), my, hshift, want, shift, mask);
+                blockIdx.x == (unsigned)(rg % gridDim.x), my, run, hshift, want, shift, mask);
   } else {
-    hist_span(full, n, first, stride, blockIdx.x == 0, my, hshift, want, shift, mask);
+    hist_span(full, n, first, stride, blockIdx.x == 0, my, run, hshift, want, shift, mask);
   }
+  run_flush(my, run);
   __syncthreads();
   for (int b = threadIdx.x; b < kBins; b += kBlock) {
     const uint32_t c = lh[0][b] + lh[1][b] + lh[2][b] + lh[3][b];
