@@ -276,6 +276,33 @@ def rows_mode(args):
     _row("a5+a6 QSGD s=15, groups of 64 (Philox4x32-10)", "25 MiB bucket, 40 buckets",
          5.0 * n + 4.0 * ng, "bucket", gms, eager, osec, 1.0, "one bucket")
 
+    say("receive: 8 QSGD payloads of one bucket, averaged")
+    W = 8
+    hq = gc.payload_layout(gc.KIND_QSGD, n, n, 64, 15)
+    pays = [torch.zeros(hq.bytes, dtype=torch.uint8, device=dev) for _ in range(W)]
+    for w in range(W):
+        gc.write_payload_header(pays[w], hq)
+        sec = gc.payload_sections(pays[w], hq)
+        gc.qsgd(xs[w], 64, 15, 7 + w, codes=sec["codes"], norms=sec["meta0"])
+    outs = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(4)]
+    fns = [lambda i=i: gc.decompress_payloads(pays, [hq] * W, outs[i]) for i in range(4)]
+    eager = _eager_ms(torch, fns[0])
+    gms, _ = _graph_ms(torch, fns)
+    osec = None
+    if orc:
+        hcodes = [gc.payload_sections(pays[w], hq)["codes"].cpu().numpy() for w in range(W)]
+        hnorms = [gc.payload_sections(pays[w], hq)["meta0"].cpu().numpy() for w in range(W)]
+
+        def o_recv():
+            acc = np.zeros(n, np.float32)
+            for w in range(W):
+                orc.decompress_scatter(orc.KIND_QSGD, None, n, 0, hcodes[w], hnorms[w], None, 64, 15,
+                                       np.float32(1.0 / W), True, acc)
+        osec = _oracle_s(o_recv)
+    _row("a9 receive: average of W=8 dense QSGD payloads (one pass)", "8 x 25 MiB-bucket payloads, s = 15",
+         W * (1.0 * n + 4.0 * ng) + 4.0 * n, "call", gms, eager, osec, 1.0, "the same 8 payloads")
+    del pays, outs
+
     say("decompress QSGD / min-max int8 dense")
     outb = torch.empty(NB * n, dtype=torch.float32, device=dev)
     fns = [lambda i=i: gc.decompress_scatter(gc.KIND_QSGD, qc[i * n:(i + 1) * n], n, outb[i * n:(i + 1) * n],
@@ -303,6 +330,40 @@ def rows_mode(args):
     _row("a9 scatter-accumulate f32", "k=10,000 of n=1,000,000", 8.0 * k + 4.0 * k + 8.0 * k, "call",
          gms, eager, osec, 1.0, "the same payload")
     del gd, r0, rs, r, ws
+
+    # a9 receive, sparse: 8 workers' EF-Top-1% + QSGD-127 payloads into one 1e8 vector.
+    say("receive: 8 sparse Top-1% + QSGD-127 payloads")
+    W, ns, ks = 8, 100_000_000, 1_000_000
+    hs = gc.payload_layout(gc.KIND_QSGD, ns, ks, 64, 127, sparse=True)
+    pays = [torch.zeros(hs.bytes, dtype=torch.uint8, device=dev) for _ in range(W)]
+    wsk = torch.empty(gc.workspace_size(gc.OP_EF_TOPK, ns, ks, 127), dtype=torch.uint8, device=dev)
+    for w in range(W):
+        gw = workloads.layered_torch(4, ns // 4, step=w, device=dev, seed=9)
+        rw = torch.zeros_like(gw)
+        gc.write_payload_header(pays[w], hs)
+        sec = gc.payload_sections(pays[w], hs)
+        gc.ef_topk(gw, rw, ks, qsgd_levels=127, qsgd_group=64, qsgd_seed=900 + w, out_idx=sec["idx"],
+                   out_codes=sec["codes"], out_norms=sec["meta0"], want_values=False, workspace=wsk)
+        del gw, rw
+    del wsk
+    outb = torch.empty(ns, dtype=torch.float32, device=dev)
+    f = lambda: gc.decompress_payloads(pays, [hs] * W, outb)
+    eager = _eager_ms(torch, f, reps=10)
+    gms, _ = _graph_ms(torch, [f] * 2, reps=5)
+    osec = None
+    if orc:
+        hp = [{k: v.cpu().numpy() for k, v in gc.payload_sections(pays[w], hs).items()} for w in range(W)]
+
+        def o_recv_sparse():
+            acc = np.zeros(ns, np.float32)
+            for w in range(W):
+                orc.decompress_scatter(orc.KIND_QSGD, hp[w]["idx"], ks, 0, hp[w]["codes"], hp[w]["meta0"], None,
+                                       64, 127, np.float32(1.0 / W), True, acc)
+        osec = _oracle_s(o_recv_sparse)
+    _row("a9 receive: average of W=8 sparse Top-1% + QSGD-127 payloads", "8 payloads of k = 1e6 into n = 1e8",
+         4.0 * ns + W * (ks * (8.0 + 1.0 + 8.0) + 4.0 * ks / 64), "call", gms, eager, osec, 1.0,
+         "the same 8 payloads")
+    del pays, outb
 
     # c3: TernGrad over 24 layers of 14,583,333 (~350M parameters), one segmented call.
     say("TernGrad 24 layers")

@@ -17,7 +17,9 @@ __all__ = [
     "lib_path", "GCError", "workspace_size", "ef_topk", "quant_minmax", "qsgd", "terngrad",
     "powersgd_step", "decompress_scatter", "KIND_F32", "KIND_MINMAX8", "KIND_MINMAX4",
     "KIND_QSGD", "KIND_TERN", "OP_EF_TOPK", "OP_QUANT_MINMAX", "OP_QSGD", "OP_TERNGRAD",
-    "OP_POWERSGD", "OP_DECOMPRESS", "profile_enable", "profile_collect",
+    "OP_POWERSGD", "OP_DECOMPRESS", "profile_enable", "profile_collect", "PayloadHeader",
+    "PAYLOAD_MAGIC", "PAYLOAD_SPARSE", "payload_layout", "payload_sections", "write_payload_header",
+    "read_payload_header", "decompress_payloads",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -34,6 +36,20 @@ if not os.path.exists(lib_path):
 
 _lib = ctypes.CDLL(lib_path)
 
+PAYLOAD_MAGIC, PAYLOAD_VERSION, PAYLOAD_SPARSE = 0x31504347, 1, 1
+
+
+class PayloadHeader(ctypes.Structure):
+    """The 128-byte wire header of one payload (include/gc.h, gc_payload_header)."""
+    _fields_ = [("magic", ctypes.c_uint32), ("version", ctypes.c_uint16), ("kind", ctypes.c_uint16),
+                ("flags", ctypes.c_uint32), ("levels", ctypes.c_int32), ("n", ctypes.c_int64),
+                ("count", ctypes.c_int64), ("index_base", ctypes.c_int64), ("group", ctypes.c_int64),
+                ("off_idx", ctypes.c_uint64), ("off_codes", ctypes.c_uint64), ("off_meta0", ctypes.c_uint64),
+                ("off_meta1", ctypes.c_uint64), ("bytes", ctypes.c_uint64), ("reserved", ctypes.c_uint8 * 40)]
+
+
+assert ctypes.sizeof(PayloadHeader) == 128
+
 _p, _i64, _u64, _i32, _f32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_int,
                                    ctypes.c_float, ctypes.c_size_t)
 _SIGS = {
@@ -48,6 +64,9 @@ _SIGS = {
     "gc_powersgd_step": ([_p, _p, _i64, _i64, _i32, _p, _p, _p, _sz, _p], _i32),
     "gc_decompress_scatter": ([_i32, _p, _i64, _i64, _p, _p, _p, _i64, _i32, _f32, _i32, _p, _i64, _p],
                               _i32),
+    "gc_payload_layout": ([_i32, _i64, _i64, _i64, _i32, _i32, _i64, ctypes.POINTER(PayloadHeader)], _i32),
+    "gc_decompress_payloads": ([_i32, ctypes.POINTER(_p), ctypes.POINTER(PayloadHeader), _f32, _i32, _p, _i64,
+                                _p], _i32),
     "gc_profile_enable": ([_i32], _i32),
     "gc_profile_collect": ([ctypes.POINTER(_i64), ctypes.POINTER(ctypes.c_double),
                             ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)], _i32),
@@ -240,3 +259,76 @@ def profile_collect():
     _check(_lib.gc_profile_collect(ctypes.byref(calls), ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)),
            "gc_profile_collect")
     return int(calls.value), a.value, b.value, c.value
+
+
+# ---------------------------------------------------------------------------
+# Wire format and the receive side
+# ---------------------------------------------------------------------------
+
+_CODE_DTYPE = {KIND_F32: torch.float32, KIND_MINMAX8: torch.uint8, KIND_MINMAX4: torch.uint8,
+               KIND_QSGD: torch.int8, KIND_TERN: torch.uint8}
+
+
+def payload_layout(kind, n, count, group=0, levels=0, sparse=False, index_base=0) -> PayloadHeader:
+    """Header (section offsets and total size) of a payload of this shape."""
+    h = PayloadHeader()
+    _check(_lib.gc_payload_layout(kind, n, count, group, levels, 1 if sparse else 0, index_base,
+                                  ctypes.byref(h)), "gc_payload_layout")
+    return h
+
+
+def _code_len(kind, count):
+    return {KIND_F32: count, KIND_MINMAX8: count, KIND_MINMAX4: (count + 1) // 2,
+            KIND_QSGD: count, KIND_TERN: (count + 3) // 4}[kind]
+
+
+def payload_sections(buf, h: PayloadHeader) -> dict:
+    """Typed views of the sections of payload `buf` (uint8 device tensor of h.bytes bytes)."""
+    _dev(buf, torch.uint8, "payload")
+    if buf.numel() < h.bytes:
+        raise ValueError("payload buffer is smaller than the header says")
+    g = h.group if h.group > 0 else max(h.count, 1)
+    ng = 0 if h.count == 0 else (h.count + g - 1) // g
+    out = {}
+    if h.off_idx:
+        out["idx"] = buf[h.off_idx:h.off_idx + 8 * h.count].view(torch.int64)
+    dt = _CODE_DTYPE[h.kind]
+    nbytes = _code_len(h.kind, h.count) * (4 if h.kind == KIND_F32 else 1)
+    out["codes"] = buf[h.off_codes:h.off_codes + nbytes].view(dt)
+    if h.off_meta0:
+        out["meta0"] = buf[h.off_meta0:h.off_meta0 + 4 * ng].view(torch.float32)
+    if h.off_meta1:
+        out["meta1"] = buf[h.off_meta1:h.off_meta1 + 4 * ng].view(torch.float32)
+    return out
+
+
+def write_payload_header(buf, h: PayloadHeader) -> None:
+    """Store the header in the first 128 bytes of the payload (a host-to-device copy)."""
+    _dev(buf, torch.uint8, "payload")
+    raw = torch.frombuffer(bytearray(bytes(h)), dtype=torch.uint8)
+    buf[:128].copy_(raw)
+
+
+def read_payload_header(buf) -> PayloadHeader:
+    """Copy the first 128 bytes of a payload back to the host as a header."""
+    return PayloadHeader.from_buffer_copy(bytes(buf[:128].cpu().numpy().tobytes()))
+
+
+def decompress_payloads(payloads, headers, out, *, alpha=None, accumulate=False, stream=None):
+    """out = (out if accumulate else 0) + sum_w alpha * decode(payload w), in payload order.
+
+    payloads: list of uint8 device tensors (each 256-byte aligned); headers: their
+    PayloadHeader objects.  alpha defaults to 1/W (the average)."""
+    _dev(out, torch.float32, "out")
+    W = len(payloads)
+    if W != len(headers):
+        raise ValueError("one header per payload")
+    for b in payloads:
+        _dev(b, torch.uint8, "payload")
+    ptrs = (ctypes.c_void_p * W)(*[b.data_ptr() for b in payloads])
+    hdrs = (PayloadHeader * W)(*headers)
+    a = 1.0 / W if alpha is None else alpha
+    _check(_lib.gc_decompress_payloads(W, ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p)), hdrs, a,
+                                       1 if accumulate else 0, _ptr(out), out.numel(), _stream(stream)),
+           "gc_decompress_payloads")
+    return out

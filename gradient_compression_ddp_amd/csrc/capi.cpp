@@ -115,7 +115,120 @@ void prof_mark(hipStream_t s, int stage) {
 
 }  // namespace gc
 
+static_assert(sizeof(gc_payload_header) == 128, "the wire header is 128 bytes");
+
+namespace {
+
+uint64_t round256(uint64_t b) { return (b + 255u) & ~uint64_t(255); }
+
+int64_t code_bytes(int kind, int64_t count) {
+  switch (kind) {
+    case GC_KIND_F32: return 4 * count;
+    case GC_KIND_MINMAX8: return count;
+    case GC_KIND_MINMAX4: return (count + 1) / 2;
+    case GC_KIND_QSGD: return count;
+    default: return (count + 3) / 4;   // GC_KIND_TERN
+  }
+}
+
+int layout(int kind, int64_t n, int64_t count, int64_t group, int levels, int sparse, int64_t index_base,
+           gc_payload_header* h) {
+  GC_REQUIRE(kind >= GC_KIND_F32 && kind <= GC_KIND_TERN, "unknown payload kind %d", kind);
+  GC_REQUIRE(n >= 0 && n <= kMaxN && count >= 0 && count <= n, "need 0 <= count <= n <= 2^40");
+  GC_REQUIRE(group >= 0, "group must be >= 0");
+  GC_REQUIRE(kind != GC_KIND_QSGD || (levels >= 1 && levels <= 127), "QSGD levels must lie in [1, 127]");
+  GC_REQUIRE(index_base >= 0, "index_base must be >= 0");
+  std::memset(h, 0, sizeof(*h));
+  h->magic = GC_PAYLOAD_MAGIC;
+  h->version = GC_PAYLOAD_VERSION;
+  h->kind = (uint16_t)kind;
+  h->flags = sparse ? GC_PAYLOAD_SPARSE : 0u;
+  h->levels = kind == GC_KIND_QSGD ? levels : 0;
+  h->n = n;
+  h->count = count;
+  h->index_base = index_base;
+  h->group = group;
+  const int64_t G = group == 0 ? (count > 0 ? count : 1) : group;
+  const int64_t ng = count == 0 ? 0 : (count + G - 1) / G;
+  uint64_t off = 256;   // the header, padded
+  if (sparse) { h->off_idx = off; off = round256(off + 8u * (uint64_t)count); }
+  h->off_codes = off;
+  off = round256(off + (uint64_t)code_bytes(kind, count));
+  if (kind != GC_KIND_F32) { h->off_meta0 = off; off = round256(off + 4u * (uint64_t)ng); }
+  if (kind == GC_KIND_MINMAX8 || kind == GC_KIND_MINMAX4) { h->off_meta1 = off; off = round256(off + 4u * (uint64_t)ng); }
+  h->bytes = off;
+  return GC_OK;
+}
+
+}  // namespace
+
 extern "C" {
+
+int gc_payload_layout(int kind, int64_t n, int64_t count, int64_t group, int levels, int sparse,
+                      int64_t index_base, gc_payload_header* hdr) {
+  GC_REQUIRE(hdr != nullptr, "hdr must be non-NULL");
+  const int st = layout(kind, n, count, group, levels, sparse, index_base, hdr);
+  return st == GC_OK ? ok() : st;
+}
+
+int gc_decompress_payloads(int W, const void* const* payloads, const gc_payload_header* headers,
+                           float alpha, int accumulate, float* out, int64_t n_out, void* stream) {
+  GC_REQUIRE(W >= 1 && W <= 1024, "W must lie in [1, 1024]");
+  GC_REQUIRE(payloads && headers, "payloads and headers (host arrays) must be non-NULL");
+  GC_REQUIRE(n_out >= 0 && n_out <= kMaxN, "n_out out of range");
+  GC_REQUIRE(out != nullptr && aligned(out, 4), "out must be non-NULL and 4-byte aligned");
+  // every header must be exactly what gc_payload_layout gives for its own fields
+  for (int w = 0; w < W; ++w) {
+    const gc_payload_header& h = headers[w];
+    GC_REQUIRE(h.magic == GC_PAYLOAD_MAGIC && h.version == GC_PAYLOAD_VERSION, "payload %d: bad magic or version", w);
+    GC_REQUIRE((h.flags & ~GC_PAYLOAD_SPARSE) == 0u, "payload %d: unknown flags", w);
+    gc_payload_header want;
+    const int st = layout(h.kind, h.n, h.count, h.group, h.levels, (h.flags & GC_PAYLOAD_SPARSE) != 0u,
+                          h.index_base, &want);
+    if (st != GC_OK) return st;
+    GC_REQUIRE(want.off_idx == h.off_idx && want.off_codes == h.off_codes && want.off_meta0 == h.off_meta0 &&
+                   want.off_meta1 == h.off_meta1 && want.bytes == h.bytes,
+               "payload %d: section offsets do not match the layout", w);
+    GC_REQUIRE(h.n <= n_out, "payload %d encodes %lld elements, out has %lld", w, (long long)h.n, (long long)n_out);
+    GC_REQUIRE(payloads[w] != nullptr && aligned(payloads[w], 256), "payload %d must be non-NULL and 256-byte aligned", w);
+  }
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const auto at = [&](int w, uint64_t off) -> const char* {
+    return off ? reinterpret_cast<const char*>(payloads[w]) + off : nullptr;
+  };
+  bool fused = aligned(out, 16);
+  for (int w = 0; w < W && fused; ++w) {
+    const gc_payload_header& h = headers[w];
+    fused = !(h.flags & GC_PAYLOAD_SPARSE) && h.kind == headers[0].kind && h.count == headers[0].count &&
+            h.group == headers[0].group && h.levels == headers[0].levels;
+  }
+  if (fused) {
+    std::vector<const void*> codes(W);
+    std::vector<const float*> m0(W), m1(W);
+    for (int w = 0; w < W; ++w) {
+      codes[w] = at(w, headers[w].off_codes);
+      m0[w] = reinterpret_cast<const float*>(at(w, headers[w].off_meta0));
+      m1[w] = reinterpret_cast<const float*>(at(w, headers[w].off_meta1));
+    }
+    return hip_status(gc::launch_decode_sum(headers[0].kind, W, codes.data(), m0.data(), m1.data(),
+                                            headers[0].count, headers[0].group, headers[0].levels, alpha,
+                                            accumulate, out, s),
+                      "gc_decompress_payloads launch");
+  }
+  if (!accumulate) {
+    const hipError_t e = gc::launch_fill_zero(out, n_out, s);
+    if (e != hipSuccess) return hip_status(e, "gc_decompress_payloads launch");
+  }
+  for (int w = 0; w < W; ++w) {
+    const gc_payload_header& h = headers[w];
+    const hipError_t e = gc::launch_decompress(
+        h.kind, reinterpret_cast<const int64_t*>(at(w, h.off_idx)), h.count, h.index_base, at(w, h.off_codes),
+        reinterpret_cast<const float*>(at(w, h.off_meta0)), reinterpret_cast<const float*>(at(w, h.off_meta1)),
+        h.group, h.levels, alpha, 1, out, n_out, s);
+    if (e != hipSuccess) return hip_status(e, "gc_decompress_payloads launch");
+  }
+  return ok();
+}
 
 int gc_profile_enable(int on) {
   gc::ProfState& p = gc::prof();

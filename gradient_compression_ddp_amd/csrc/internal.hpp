@@ -49,6 +49,12 @@ hipError_t launch_decompress(int kind, const int64_t* idx, int64_t count, int64_
                              const void* codes, const float* meta0, const float* meta1,
                              int64_t group, int levels, float alpha, int accumulate, float* out,
                              int64_t n_out, hipStream_t s);
+// out[0..count) = (accumulate ? out : 0) + sum_w alpha * decode(payload w), W dense payloads
+// of one kind and shape, summed in payload order (16 payloads per launch).
+hipError_t launch_decode_sum(int kind, int W, const void* const* codes, const float* const* meta0,
+                             const float* const* meta1, int64_t count, int64_t group, int levels,
+                             float alpha, int accumulate, float* out, hipStream_t s);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

@@ -219,6 +219,74 @@ int gc_decompress_scatter(int kind, const int64_t* idx, int64_t count, int64_t i
                           float* out, int64_t n_out, void* stream);
 
 /*
+ * Wire format of one payload, and the receive side of a data-parallel step.
+ *
+ * Operation ([P2] section 四: each worker sends its compressed gradient, the gradients
+ * are aggregated and every worker decompresses before the update; [P4] "梯度压缩原理":
+ * aggregation sums the workers' gradients and averages them).  Codes of different
+ * workers cannot be summed as they are (each has its own scales or index set), so a
+ * receiver gathers W payloads and computes out = sum_w alpha * g_hat_w, with alpha = 1/W
+ * for the average.
+ *
+ * A payload is one contiguous byte buffer: this 128-byte header, then the sections it
+ * lists, each starting at a multiple of 256 bytes from the payload start:
+ *   idx    int64[count], ascending  (sparse payloads only; flags & GC_PAYLOAD_SPARSE)
+ *   codes  as for gc_decompress_scatter: float[count] (F32), uint8[count] (MINMAX8),
+ *          uint8[ceil(count/2)] (MINMAX4), int8[count] (QSGD), uint8[ceil(count/4)] (TERN)
+ *   meta0  float[ng]: mins (MINMAX*), norms (QSGD), scales (TERN); absent for F32
+ *   meta1  float[ng]: scales (MINMAX*); absent otherwise
+ * with ng = ceil(count / group) (group 0: one group).  Multi-byte fields are
+ * little-endian.  An absent section has offset 0.  The producer fills the sections by
+ * pointing the compressors at them.
+ */
+#define GC_PAYLOAD_MAGIC 0x31504347u   /* "GCP1" */
+#define GC_PAYLOAD_VERSION 1u
+#define GC_PAYLOAD_SPARSE 1u
+
+typedef struct gc_payload_header {
+  uint32_t magic;        /* GC_PAYLOAD_MAGIC */
+  uint16_t version;      /* GC_PAYLOAD_VERSION */
+  uint16_t kind;         /* enum gc_kind */
+  uint32_t flags;        /* GC_PAYLOAD_SPARSE */
+  int32_t levels;        /* QSGD levels (0 for other kinds) */
+  int64_t n;             /* length of the dense gradient the payload encodes */
+  int64_t count;         /* entries */
+  int64_t index_base;    /* subtracted from idx (sparse payloads) */
+  int64_t group;         /* entries per metadata group, 0 = one group */
+  uint64_t off_idx;      /* byte offsets of the sections from the payload start */
+  uint64_t off_codes;
+  uint64_t off_meta0;
+  uint64_t off_meta1;
+  uint64_t bytes;        /* total payload size */
+  uint8_t reserved[40];  /* zero */
+} gc_payload_header;
+
+/*
+ * gc_payload_layout -- fill *hdr (host) for a payload of the given shape: the offsets of
+ * its sections and its total size.  Host only; no device call.  sparse != 0 adds the
+ * idx section.  Errors: GC_EINVAL for an unknown kind, count < 0, count > n for a dense
+ * payload, a group that is negative, or levels outside [1, 127] for QSGD.
+ */
+int gc_payload_layout(int kind, int64_t n, int64_t count, int64_t group, int levels, int sparse,
+                      int64_t index_base, gc_payload_header* hdr);
+
+/*
+ * gc_decompress_payloads -- out = (accumulate ? out : 0) + sum over w = 0..W-1, in this
+ * order, of alpha * g_hat_w, where g_hat_w is payload w decoded as gc_decompress_scatter
+ * decodes it (scattered through its idx when sparse).  Every element receives its terms
+ * one at a time in payload order: out_e = fl(out_e + fl(alpha * g_hat_{w,e})).
+ * payloads: HOST array of W device pointers, each 256-byte aligned; headers: HOST array of
+ * their W headers (the caller holds them: it built them, or read them after the gather).
+ * Each payload must encode n <= n_out elements.  W in [1, 1024].
+ * When every payload is dense with the same kind, count, group and levels, one pass
+ * reads all W code streams and writes out once (up to 16 payloads per launch);
+ * otherwise out is cleared (if accumulate == 0) and the payloads are added one launch
+ * each.  Needs no workspace.
+ */
+int gc_decompress_payloads(int W, const void* const* payloads, const gc_payload_header* headers,
+                           float alpha, int accumulate, float* out, int64_t n_out, void* stream);
+
+/*
  * Stage timing (profiling aid, not part of any operation).  While enabled, every
  * gc_ef_topk call records four HIP events on its stream: call start, start and end of the
  * full streaming pass (the fused add + candidate kernel), and call end.

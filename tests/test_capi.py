@@ -112,3 +112,79 @@ def test_other_calls_reject_bad_arguments(lib):
     assert d(0, None, 11, 0, FAKE, None, None, 0, 0, 1.0, 0, FAKE, 10, None) == 1  # dense overrun
     assert d(3, None, 10, 0, FAKE, FAKE, None, 64, 0, 1.0, 0, FAKE, 10, None) == 1  # QSGD levels
     assert d(1, None, 10, 0, FAKE, FAKE, None, 64, 0, 1.0, 0, FAKE, 10, None) == 1  # min-max meta1
+
+
+# ---- wire format and the receive side (host checks only) ---------------------------
+
+def _hdr_mod():
+    import gradient_compression_ddp_amd as gcm
+    return gcm
+
+
+def test_payload_layout_sections(lib):
+    gcm = _hdr_mod()
+    code_len = {gcm.KIND_F32: lambda c: 4 * c, gcm.KIND_MINMAX8: lambda c: c, gcm.KIND_MINMAX4: lambda c: (c + 1) // 2,
+                gcm.KIND_QSGD: lambda c: c, gcm.KIND_TERN: lambda c: (c + 3) // 4}
+    for kind in code_len:
+        for count, group, sparse in ((0, 0, False), (1, 0, False), (1001, 64, False), (70_001, 1000, True),
+                                     (12_345, 0, True)):
+            h = gcm.payload_layout(kind, 10 ** 6, count, group, 15 if kind == gcm.KIND_QSGD else 0, sparse, 7)
+            assert (h.magic, h.version, h.kind, h.count, h.group) == (gcm.PAYLOAD_MAGIC, 1, kind, count, group)
+            g = group if group else max(count, 1)
+            ng = 0 if count == 0 else -(-count // g)
+            sections = []
+            if sparse:
+                sections.append((h.off_idx, 8 * count))
+            else:
+                assert h.off_idx == 0
+            sections.append((h.off_codes, code_len[kind](count)))
+            if kind == gcm.KIND_F32:
+                assert h.off_meta0 == 0 and h.off_meta1 == 0
+            else:
+                sections.append((h.off_meta0, 4 * ng))
+            if kind in (gcm.KIND_MINMAX8, gcm.KIND_MINMAX4):
+                sections.append((h.off_meta1, 4 * ng))
+            else:
+                assert h.off_meta1 == 0
+            end = 128
+            for off, size in sections:          # aligned, in order, not overlapping
+                assert off % 256 == 0 and off >= end
+                end = off + size
+            assert h.bytes >= end and h.bytes % 256 == 0 and h.bytes - end < 256
+            assert bytes(h.reserved) == bytes(40)
+
+
+def test_payload_layout_rejects(lib):
+    gcm = _hdr_mod()
+    h = gcm.PayloadHeader()
+    f = gcm._lib.gc_payload_layout
+    assert f(9, 10, 5, 0, 0, 0, 0, ctypes.byref(h)) == 1           # kind
+    assert f(gcm.KIND_F32, 10, 11, 0, 0, 0, 0, ctypes.byref(h)) == 1   # count > n
+    assert f(gcm.KIND_QSGD, 10, 5, 0, 0, 0, 0, ctypes.byref(h)) == 1   # QSGD levels
+    assert f(gcm.KIND_F32, 10, 5, -1, 0, 0, 0, ctypes.byref(h)) == 1   # group
+    assert f(gcm.KIND_F32, 10, 5, 0, 0, 0, 0, None) == 1               # no header
+
+
+def test_decompress_payloads_rejects_before_any_launch(lib):
+    gcm = _hdr_mod()
+    good = gcm.payload_layout(gcm.KIND_QSGD, 1000, 1000, 64, 15)
+    fake = 1 << 20                                    # never dereferenced: every call below is invalid
+    out = ctypes.c_void_p(fake)
+
+    def call(W, headers, ptrs, n_out=1000, out_ptr=out):
+        P = (ctypes.c_void_p * max(W, 1))(*ptrs)
+        H = (gcm.PayloadHeader * max(W, 1))(*headers)
+        return gcm._lib.gc_decompress_payloads(W, ctypes.cast(P, ctypes.POINTER(ctypes.c_void_p)), H, 1.0, 0,
+                                               out_ptr, n_out, None)
+    assert call(0, [good], [fake]) == 1                              # W
+    bad = gcm.PayloadHeader.from_buffer_copy(bytes(good)); bad.magic = 0
+    assert call(1, [bad], [fake]) == 1                               # magic
+    bad = gcm.PayloadHeader.from_buffer_copy(bytes(good)); bad.off_meta0 += 256
+    assert call(1, [bad], [fake]) == 1                               # offsets differ from the layout
+    bad = gcm.PayloadHeader.from_buffer_copy(bytes(good)); bad.flags = 2
+    assert call(1, [bad], [fake]) == 1                               # unknown flag
+    assert call(1, [good], [fake + 16]) == 1                         # payload not 256-byte aligned
+    assert call(1, [good], [None]) == 1                              # payload NULL
+    assert call(1, [good], [fake], n_out=999) == 1                   # n > n_out
+    assert call(2, [good, bad], [fake, fake]) == 1                   # any bad header rejects the call
+    assert call(1, [good], [fake], out_ptr=ctypes.c_void_p(fake + 2)) == 1   # out misaligned

@@ -1,0 +1,173 @@
+"""GPU parity of the receive side (gc_decompress_payloads) and the wire format.
+
+Each payload is produced on the GPU by the library's compressors writing straight into
+the sections of one wire buffer; the expected result comes from the oracle alone: it
+compresses the same inputs itself and adds the decoded payloads in order
+(out = 0 or out, then out += alpha * g_hat_w for w = 0..W-1).  Bit-exact."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gc_testlib import assert_bits_equal
+
+pytestmark = pytest.mark.gpu
+
+F32 = np.float32
+
+
+@pytest.fixture(scope="module")
+def gc():
+    import torch  # noqa: F401
+    import gradient_compression_ddp_amd as lib
+    return lib
+
+
+def dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def new_payload(gc, kind, n, count, group=0, levels=0, sparse=False, index_base=0):
+    import torch
+    h = gc.payload_layout(kind, n, count, group, levels, sparse, index_base)
+    buf = torch.zeros(h.bytes, dtype=torch.uint8, device="cuda")
+    gc.write_payload_header(buf, h)
+    return buf, h
+
+
+def dense_payload(gc, kind, x, group, levels, seed):
+    """GPU payload of x, and the oracle's (codes, meta0, meta1) of the same x."""
+    n = x.size
+    buf, h = new_payload(gc, kind, n, n, group, levels)
+    sec = gc.payload_sections(buf, h)
+    xd = dev(x)
+    if kind == gc.KIND_QSGD:
+        gc.qsgd(xd, group, levels, seed, codes=sec["codes"], norms=sec["meta0"])
+        c, nu, _, _ = oracle.qsgd(x, group, levels, seed)
+        want = (c, nu, None)
+    elif kind in (gc.KIND_MINMAX8, gc.KIND_MINMAX4):
+        bits = 8 if kind == gc.KIND_MINMAX8 else 4
+        gc.quant_minmax(xd, group, bits, codes=sec["codes"], mins=sec["meta0"], scales=sec["meta1"],
+                        workspace=None)
+        c, mn, sc, _, _ = oracle.quant_minmax(x, group, bits)
+        want = (c if bits == 8 else oracle.pack_int4(c), mn, sc)
+    elif kind == gc.KIND_TERN:
+        gc.terngrad(xd, [0, n], seed, packed=sec["codes"], scales=sec["meta0"])
+        pk, s, _, _, _ = oracle.terngrad(x, [0, n], seed)
+        want = (pk, s, None)
+    else:
+        sec["codes"].copy_(xd)
+        want = (x, None, None)
+    return buf, h, want
+
+
+def expected(kind, wants, count, group, levels, alpha, init, idx=None, index_base=0):
+    out = init.copy()
+    for w, (codes, m0, m1) in enumerate(wants):
+        ix = None if idx is None else idx[w]
+        oracle.decompress_scatter(kind, ix, count, index_base, codes, m0, m1, group, levels, alpha, True, out)
+    return out
+
+
+@pytest.mark.parametrize("kind,group,levels", [(3, 64, 15), (1, 1000, 0), (2, 64, 0), (4, 0, 0), (0, 0, 0)])
+@pytest.mark.parametrize("W,accumulate", [(8, False), (3, True), (20, False)])
+def test_dense_payloads_fused(gc, kind, group, levels, W, accumulate):
+    n = 3 * 4096 + 1003
+    bufs, hdrs, wants = [], [], []
+    for w in range(W):
+        x = workloads.bucket(n, seed=100 + w)
+        b, h, want = dense_payload(gc, kind, x, group, levels, seed=7 + w)
+        bufs.append(b); hdrs.append(h); wants.append(want)
+    init = np.linspace(-1, 1, n, dtype=F32) if accumulate else np.zeros(n, F32)
+    out = dev(init)
+    alpha = F32(1.0) / F32(W)
+    gc.decompress_payloads(bufs, hdrs, out, alpha=float(alpha), accumulate=accumulate)
+    want = expected(kind, wants, n, group, levels, alpha, init)
+    assert_bits_equal(host(out), want, f"kind {kind} W {W}")
+
+
+def test_dense_payloads_unaligned_out_takes_the_sequential_path(gc):
+    import torch
+    n, W = 5000, 4
+    bufs, hdrs, wants = [], [], []
+    for w in range(W):
+        b, h, want = dense_payload(gc, gc.KIND_QSGD, workloads.bucket(n, seed=w), 64, 127, seed=w)
+        bufs.append(b); hdrs.append(h); wants.append(want)
+    full = torch.full((n + 1,), 3.0, dtype=torch.float32, device="cuda")
+    gc.decompress_payloads(bufs, hdrs, full[1:])           # out offset by 4 bytes, not accumulating
+    got = host(full)
+    want = expected(gc.KIND_QSGD, wants, n, 64, 127, F32(1.0) / F32(W), np.zeros(n, F32))
+    assert got[0] == F32(3.0)
+    assert_bits_equal(got[1:], want, "unaligned out")
+
+
+def test_sparse_topk_payloads(gc):
+    """W Top-K payloads (values, and QSGD-coded kept values) from different gradients."""
+    import torch
+    n, k, W, base = 300_007, 3_000, 4, 1000
+    for quant in (False, True):
+        bufs, hdrs, idxs, wants = [], [], [], []
+        for w in range(W):
+            g = workloads.bucket(n, seed=40 + w)
+            r = (workloads.bucket(n, seed=50 + w) * F32(0.1)).astype(F32)
+            kind = gc.KIND_QSGD if quant else gc.KIND_F32
+            b, h = new_payload(gc, kind, n, k, 64 if quant else 0, 127 if quant else 0, True, base)
+            sec = gc.payload_sections(b, h)
+            rd = dev(r)
+            if quant:
+                gc.ef_topk(dev(g), rd, k, index_base=base, qsgd_levels=127, qsgd_group=64, qsgd_seed=500 + w,
+                           out_idx=sec["idx"], out_codes=sec["codes"], out_norms=sec["meta0"], want_values=False)
+                oi, oc, onu, _, _ = oracle.ef_topk_qsgd(g, r, k, levels=127, group=64, seed=500 + w,
+                                                        index_base=base)
+                wants.append((oc, onu, None))
+            else:
+                gc.ef_topk(dev(g), rd, k, index_base=base, out_idx=sec["idx"], out_val=sec["codes"])
+                oi, ov, _ = oracle.ef_topk(g, r, k, index_base=base)
+                wants.append((ov, None, None))
+            idxs.append(oi)
+            bufs.append(b); hdrs.append(h)
+        out = torch.zeros(n, dtype=torch.float32, device="cuda")
+        gc.decompress_payloads(bufs, hdrs, out)
+        kind = gc.KIND_QSGD if quant else gc.KIND_F32
+        want = expected(kind, wants, k, 64 if quant else 0, 127 if quant else 0, F32(1.0) / F32(W),
+                        np.zeros(n, F32), idx=idxs, index_base=base)
+        assert_bits_equal(host(out), want, f"sparse quant={quant}")
+
+
+def test_mixed_kinds_and_header_round_trip(gc):
+    import torch
+    n = 20_000
+    specs = [(gc.KIND_MINMAX8, 64, 0), (gc.KIND_QSGD, 128, 15), (gc.KIND_TERN, 0, 0), (gc.KIND_F32, 0, 0)]
+    bufs, hdrs, expect_out = [], [], np.zeros(n, F32)
+    alpha = F32(0.25)
+    for w, (kind, group, levels) in enumerate(specs):
+        x = workloads.bucket(n, seed=200 + w)
+        b, h, (c, m0, m1) = dense_payload(gc, kind, x, group, levels, seed=60 + w)
+        h2 = gc.read_payload_header(b)                    # what a receiver would parse after a gather
+        assert bytes(h2) == bytes(h)
+        bufs.append(b); hdrs.append(h2)
+        oracle.decompress_scatter(kind, None, n, 0, c, m0, m1, group, levels, alpha, True, expect_out)
+    out = torch.full((n,), 9.0, dtype=torch.float32, device="cuda")
+    gc.decompress_payloads(bufs, hdrs, out, alpha=float(alpha))
+    assert_bits_equal(host(out), expect_out, "mixed kinds")
+
+
+def test_bucket_full_size_eight_workers(gc):
+    """Eight QSGD payloads of the 25 MiB bucket (s = 15, groups of 64), averaged."""
+    import torch
+    n, W = workloads.BUCKET_N, 8
+    bufs, hdrs, wants = [], [], []
+    for w in range(W):
+        b, h, want = dense_payload(gc, gc.KIND_QSGD, workloads.bucket(n, seed=300 + w), 64, 15, seed=7 + w)
+        bufs.append(b); hdrs.append(h); wants.append(want)
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    gc.decompress_payloads(bufs, hdrs, out)
+    want = expected(gc.KIND_QSGD, wants, n, 64, 15, F32(1.0) / F32(W), np.zeros(n, F32))
+    assert_bits_equal(host(out), want, "bucket W=8")
