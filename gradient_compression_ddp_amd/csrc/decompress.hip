@@ -4,7 +4,10 @@
 // decompresses what it receives before the update) and section 二.2 (a sparsified
 // gradient is dense with zeros off the kept set).  Each entry's value is the
 // dequantization formula of its compressor, in binary32, then multiplied by alpha and
-// stored to or added into out[pos].  Streaming: one pass over the payload, scattered
+// stored to or added into out[pos].  The receive side of a data-parallel step (aiqz.cc
+// "梯度聚合通信优化实战方案", section "通信瓶颈分析": the workers' gradients are summed and
+// averaged) adds W payloads into one vector in payload order; k_decode_sum does it for W
+// dense payloads of one shape in a single pass.  Streaming: one pass over the payload, scattered
 // 4-byte stores.  A dense decode (no idx) with aligned buffers takes the tile kernel: one
 // 4096-entry tile per block, a lane owns an aligned quad (codes loaded as one word,
 // 16-byte non-temporal stores), all loads of the tile issued before any arithmetic.

@@ -222,7 +222,7 @@ int gc_decompress_scatter(int kind, const int64_t* idx, int64_t count, int64_t i
  * Wire format of one payload, and the receive side of a data-parallel step.
  *
  * Operation ([P2] section 四: each worker sends its compressed gradient, the gradients
- * are aggregated and every worker decompresses before the update; [P4] "梯度压缩原理":
+ * are aggregated and every worker decompresses before the update; [P4] "通信瓶颈分析":
  * aggregation sums the workers' gradients and averages them).  Codes of different
  * workers cannot be summed as they are (each has its own scales or index set), so a
  * receiver gathers W payloads and computes out = sum_w alpha * g_hat_w, with alpha = 1/W
