@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0
 # kernel source it was measured on: the digest covers the tile constants, the block-rank
 # helpers and the kernel itself, and a mismatch reports the traffic as null.
 K1_TRAFFIC_BYTES = 8.4612e10
-K1_SOURCE_SHA256 = "a5e899df42a9a417828aea2e7ffb0f6dc52c03f72c678f1e692c3b455ae2856a"
+K1_SOURCE_SHA256 = "d65c59ac29b1adc9e6b1b0a1e720226d0e5bf703649a0720d538b01233f986cd"
 METRIC = "EF-Top-1%+int8 compress GB/s of fp32 grad input; % of HBM peak"
 
 
@@ -364,6 +364,31 @@ def rows_mode(args):
          4.0 * ns + W * (ks * (8.0 + 1.0 + 8.0) + 4.0 * ks / 64), "call", gms, eager, osec, 1.0,
          "the same 8 payloads")
     del pays, outb
+
+    # EF Random-1% + QSGD-127 over 1e9 elements of the layered workload (32 layers).
+    say("EF Random-K 1% + QSGD-127, 1e9")
+    LR, LLR = 32, 31_250_000
+    nr, kr = LR * LLR, LR * LLR // 100
+    gr = workloads.layered_torch(LR, LLR, step=1, device=dev, seed=5)
+    rr = torch.zeros_like(gr)
+    oir = torch.empty(kr, dtype=torch.int64, device=dev)
+    ocr = torch.empty(kr, dtype=torch.int8, device=dev)
+    onr = torch.empty((kr + 63) // 64, dtype=torch.float32, device=dev)
+    wsr = torch.empty(gc.workspace_size(gc.OP_EF_RANDK, nr, kr, 127), dtype=torch.uint8, device=dev)
+    f = lambda: gc.ef_randk(gr, rr, kr, 77, qsgd_levels=127, qsgd_group=64, qsgd_seed=501, out_idx=oir,
+                            out_codes=ocr, out_norms=onr, want_values=False, workspace=wsr)
+    eager = _eager_ms(torch, f, reps=10)
+    gms, _ = _graph_ms(torch, [f] * 2, reps=5)
+    osec = None
+    ns_o = 1 << 24
+    if orc:
+        h = gr[:ns_o].cpu().numpy()
+        osec = _oracle_s(lambda: orc.ef_randk_qsgd(h, np.zeros_like(h), ns_o // 100, 77, levels=127, group=64,
+                                                   qsgd_seed=501))
+    _row("next-3 EF Random-K 1% + QSGD-127", "n=1e9 (32 layers x 31,250,000, t(3) x lognormal scales), k=1e7",
+         12.0 * nr + kr * (8.0 + 1.0 + 4.0 / 64 + 4.0 + 4.0), "call", gms, eager, osec, ns_o / nr,
+         "the first 2^24 elements, k = 1% of them")
+    del gr, rr, oir, ocr, onr, wsr
 
     # c3: TernGrad over 24 layers of 14,583,333 (~350M parameters), one segmented call.
     say("TernGrad 24 layers")

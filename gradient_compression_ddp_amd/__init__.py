@@ -14,10 +14,10 @@ import os
 import torch
 
 __all__ = [
-    "lib_path", "GCError", "workspace_size", "ef_topk", "quant_minmax", "qsgd", "terngrad",
+    "lib_path", "GCError", "workspace_size", "ef_topk", "ef_randk", "quant_minmax", "qsgd", "terngrad",
     "powersgd_step", "decompress_scatter", "KIND_F32", "KIND_MINMAX8", "KIND_MINMAX4",
     "KIND_QSGD", "KIND_TERN", "OP_EF_TOPK", "OP_QUANT_MINMAX", "OP_QSGD", "OP_TERNGRAD",
-    "OP_POWERSGD", "OP_DECOMPRESS", "profile_enable", "profile_collect", "PayloadHeader",
+    "OP_POWERSGD", "OP_DECOMPRESS", "OP_EF_RANDK", "profile_enable", "profile_collect", "PayloadHeader",
     "PAYLOAD_MAGIC", "PAYLOAD_SPARSE", "payload_layout", "payload_sections", "write_payload_header",
     "read_payload_header", "decompress_payloads",
 ]
@@ -27,6 +27,7 @@ lib_path = os.path.join(_HERE, "libgc.so")
 
 GC_OK, GC_EINVAL, GC_EWORKSPACE, GC_EUNSUPPORTED, GC_EHIP = 0, 1, 2, 3, 4
 OP_EF_TOPK, OP_QUANT_MINMAX, OP_QSGD, OP_TERNGRAD, OP_POWERSGD, OP_DECOMPRESS = 1, 2, 3, 4, 5, 6
+OP_EF_RANDK = 7
 KIND_F32, KIND_MINMAX8, KIND_MINMAX4, KIND_QSGD, KIND_TERN = 0, 1, 2, 3, 4
 
 if not os.path.exists(lib_path):
@@ -58,6 +59,7 @@ _SIGS = {
     "gc_version": ([], _i32),
     "gc_workspace_size": ([_i32, _i64, _i64, _i64, ctypes.POINTER(_sz)], _i32),
     "gc_ef_topk": ([_p, _p, _i64, _i64, _i64, _p, _p, _i32, _i64, _u64, _p, _p, _p, _sz, _p], _i32),
+    "gc_ef_randk": ([_p, _p, _i64, _i64, _i64, _u64, _p, _p, _i32, _i64, _u64, _p, _p, _p, _sz, _p], _i32),
     "gc_quant_minmax": ([_p, _p, _i64, _i64, _i32, _p, _p, _p, _p, _sz, _p], _i32),
     "gc_qsgd": ([_p, _p, _i64, _i64, _i32, _u64, _i64, _p, _p, _p], _i32),
     "gc_terngrad": ([_p, _p, _i32, _p, _u64, _i64, _p, _p, _p, _sz, _p], _i32),
@@ -125,14 +127,8 @@ def _workspace(op, n, k, aux, device, workspace):
     return workspace, workspace.numel()
 
 
-def ef_topk(grad, residual, k, index_base=0, *, qsgd_levels=0, qsgd_group=64, qsgd_seed=0,
-            out_idx=None, out_val=None, out_codes=None, out_norms=None, want_values=True,
-            workspace=None, stream=None):
-    """Error-feedback Top-K; with qsgd_levels > 0 also QSGD on the kept values.
-
-    Updates ``residual`` in place.  Returns ``(idx, val)`` for pure Top-K, or
-    ``(idx, codes, norms, val)`` with QSGD (``val`` is None when ``want_values`` is False).
-    """
+def _sparsify(name, op, grad, residual, k, index_base, extra, qsgd_levels, qsgd_group, qsgd_seed,
+              out_idx, out_val, out_codes, out_norms, want_values, workspace, stream):
     _dev(grad, torch.float32, "grad")
     _dev(residual, torch.float32, "residual")
     n = grad.numel()
@@ -149,13 +145,36 @@ def ef_topk(grad, residual, k, index_base=0, *, qsgd_levels=0, qsgd_group=64, qs
             out_codes = torch.empty(k, dtype=torch.int8, device=dev)
         if out_norms is None:
             out_norms = torch.empty((k + qsgd_group - 1) // qsgd_group, dtype=torch.float32, device=dev)
-    ws, ws_bytes = _workspace(OP_EF_TOPK, n, k, qsgd_levels, dev, workspace)
-    _check(_lib.gc_ef_topk(_ptr(grad), _ptr(residual), n, k, index_base, _ptr(out_idx), _ptr(out_val),
-                           qsgd_levels, qsgd_group, qsgd_seed, _ptr(out_codes), _ptr(out_norms),
-                           _ptr(ws), ws_bytes, _stream(stream)), "gc_ef_topk")
+    ws, ws_bytes = _workspace(op, n, k, qsgd_levels, dev, workspace)
+    _check(getattr(_lib, name)(_ptr(grad), _ptr(residual), n, k, index_base, *extra, _ptr(out_idx),
+                               _ptr(out_val), qsgd_levels, qsgd_group, qsgd_seed, _ptr(out_codes),
+                               _ptr(out_norms), _ptr(ws), ws_bytes, _stream(stream)), name)
     if quant:
         return out_idx, out_codes, out_norms, out_val
     return out_idx, out_val
+
+
+def ef_topk(grad, residual, k, index_base=0, *, qsgd_levels=0, qsgd_group=64, qsgd_seed=0,
+            out_idx=None, out_val=None, out_codes=None, out_norms=None, want_values=True,
+            workspace=None, stream=None):
+    """Error-feedback Top-K; with qsgd_levels > 0 also QSGD on the kept values.
+
+    Updates ``residual`` in place.  Returns ``(idx, val)`` for pure Top-K, or
+    ``(idx, codes, norms, val)`` with QSGD (``val`` is None when ``want_values`` is False).
+    """
+    return _sparsify("gc_ef_topk", OP_EF_TOPK, grad, residual, k, index_base, (), qsgd_levels, qsgd_group,
+                     qsgd_seed, out_idx, out_val, out_codes, out_norms, want_values, workspace, stream)
+
+
+def ef_randk(grad, residual, k, select_seed, index_base=0, *, qsgd_levels=0, qsgd_group=64, qsgd_seed=0,
+             out_idx=None, out_val=None, out_codes=None, out_norms=None, want_values=True,
+             workspace=None, stream=None):
+    """Error-feedback Random-K (the k indices with the largest Philox keys under
+    ``select_seed``); with qsgd_levels > 0 also QSGD on the kept values.  Outputs as
+    :func:`ef_topk`."""
+    return _sparsify("gc_ef_randk", OP_EF_RANDK, grad, residual, k, index_base, (select_seed,), qsgd_levels,
+                     qsgd_group, qsgd_seed, out_idx, out_val, out_codes, out_norms, want_values, workspace,
+                     stream)
 
 
 def quant_minmax(x, group, bits, residual=None, *, codes=None, mins=None, scales=None,

@@ -287,6 +287,11 @@ int gc_workspace_size(int op, int64_t n, int64_t k, int64_t aux, size_t* bytes) 
       GC_REQUIRE(aux >= 0 && aux <= 127, "qsgd levels must lie in [0, 127]");
       *bytes = (n == 0 || k == 0) ? 0 : gc::ef_topk_workspace(n, k, (int)aux);
       return ok();
+    case GC_OP_EF_RANDK:
+      GC_REQUIRE(k >= 0 && k <= n, "k must lie in [0, n]");
+      GC_REQUIRE(aux >= 0 && aux <= 127, "qsgd levels must lie in [0, 127]");
+      *bytes = (n == 0 || k == 0) ? 0 : gc::ef_randk_workspace(n, k, (int)aux);
+      return ok();
     case GC_OP_QUANT_MINMAX:
       GC_REQUIRE(k == 0 || k >= 4, "group must be 0 or >= 4");
       *bytes = (k == 0 || k > 256) ? gc::minmax_large_workspace(n, k) : 0;
@@ -307,10 +312,10 @@ int gc_workspace_size(int op, int64_t n, int64_t k, int64_t aux, size_t* bytes) 
   }
 }
 
-int gc_ef_topk(const float* grad, float* residual, int64_t n, int64_t k, int64_t index_base,
-               int64_t* out_idx, float* out_val, int qsgd_levels, int64_t qsgd_group,
-               uint64_t qsgd_seed, int8_t* out_codes, float* out_norms, void* workspace,
-               size_t workspace_bytes, void* stream) {
+// Argument checks shared by the two sparsifiers (everything but the workspace).
+static int check_sparsify(const float* grad, float* residual, int64_t n, int64_t k,
+                          int64_t index_base, int64_t* out_idx, float* out_val, int qsgd_levels,
+                          int64_t qsgd_group, int8_t* out_codes, float* out_norms) {
   GC_REQUIRE(n >= 0 && n <= kMaxN, "n must lie in [0, 2^40]");
   GC_REQUIRE(k >= 0 && k <= n, "k must lie in [0, n]");
   GC_REQUIRE(index_base >= 0 && index_base <= (int64_t(1) << 62) - n, "index_base out of range");
@@ -329,14 +334,42 @@ int gc_ef_topk(const float* grad, float* residual, int64_t n, int64_t k, int64_t
       GC_REQUIRE(out_norms && aligned(out_norms, 4), "out_norms must be non-NULL");
       GC_REQUIRE(!out_val || aligned(out_val, 16), "out_val must be 16-byte aligned when given");
     }
-    const size_t need = gc::ef_topk_workspace(n, k, qsgd_levels);
-    const int w = check_workspace(workspace, workspace_bytes, need);
+  }
+  return ok();
+}
+
+int gc_ef_topk(const float* grad, float* residual, int64_t n, int64_t k, int64_t index_base,
+               int64_t* out_idx, float* out_val, int qsgd_levels, int64_t qsgd_group,
+               uint64_t qsgd_seed, int8_t* out_codes, float* out_norms, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  const int c = check_sparsify(grad, residual, n, k, index_base, out_idx, out_val, qsgd_levels,
+                               qsgd_group, out_codes, out_norms);
+  if (c != GC_OK || n == 0) return c;
+  if (k > 0) {
+    const int w = check_workspace(workspace, workspace_bytes, gc::ef_topk_workspace(n, k, qsgd_levels));
     if (w != GC_OK) return w;
   }
   return hip_status(gc::launch_ef_topk(grad, residual, n, k, index_base, out_idx, out_val, qsgd_levels,
                                        qsgd_group, qsgd_seed, out_codes, out_norms, workspace,
                                        workspace_bytes, reinterpret_cast<hipStream_t>(stream)),
                     "gc_ef_topk launch");
+}
+
+int gc_ef_randk(const float* grad, float* residual, int64_t n, int64_t k, int64_t index_base,
+                uint64_t select_seed, int64_t* out_idx, float* out_val, int qsgd_levels,
+                int64_t qsgd_group, uint64_t qsgd_seed, int8_t* out_codes, float* out_norms,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  const int c = check_sparsify(grad, residual, n, k, index_base, out_idx, out_val, qsgd_levels,
+                               qsgd_group, out_codes, out_norms);
+  if (c != GC_OK || n == 0) return c;
+  if (k > 0) {
+    const int w = check_workspace(workspace, workspace_bytes, gc::ef_randk_workspace(n, k, qsgd_levels));
+    if (w != GC_OK) return w;
+  }
+  return hip_status(gc::launch_ef_randk(grad, residual, n, k, index_base, select_seed, out_idx, out_val,
+                                        qsgd_levels, qsgd_group, qsgd_seed, out_codes, out_norms, workspace,
+                                        workspace_bytes, reinterpret_cast<hipStream_t>(stream)),
+                    "gc_ef_randk launch");
 }
 
 int gc_quant_minmax(const float* x, float* residual, int64_t n, int64_t group, int bits,

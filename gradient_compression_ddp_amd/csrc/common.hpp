@@ -56,15 +56,15 @@ __device__ __forceinline__ float u24(uint32_t w) {
   return (float)(w >> 8) * 5.9604644775390625e-08f;
 }
 
-// Uniforms of the four consecutive element indices e0..e0+3 (any alignment).  When
+// Raw words of the four consecutive element indices e0..e0+3 (any alignment).  When
 // e0 % 4 == 0 this is one Philox block; otherwise two blocks are stitched.
-__device__ __forceinline__ void uniforms4(uint64_t seed, uint64_t e0, float u[4]) {
+__device__ __forceinline__ void words4(uint64_t seed, uint64_t e0, uint32_t out[4]) {
   const uint64_t c = e0 >> 2;
   const uint32_t sh = (uint32_t)(e0 & 3u);
   const Words4 a = philox_block(seed, c);
   if (sh == 0) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) u[m] = u24(a.w[m]);
+    for (int m = 0; m < 4; ++m) out[m] = a.w[m];
   } else {
     const Words4 b = philox_block(seed, c + 1);
     uint32_t w[8];
@@ -76,9 +76,28 @@ __device__ __forceinline__ void uniforms4(uint64_t seed, uint64_t e0, float u[4]
       uint32_t v = w[m + 1];
       v = (sh == 2) ? w[m + 2] : v;
       v = (sh == 3) ? w[m + 3] : v;
-      u[m] = u24(v);
+      out[m] = v;
     }
   }
+}
+
+// Uniforms of the four consecutive element indices e0..e0+3 (any alignment).
+__device__ __forceinline__ void uniforms4(uint64_t seed, uint64_t e0, float u[4]) {
+  uint32_t w[4];
+  words4(seed, e0, w);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) u[m] = u24(w[m]);
+}
+
+// The word of one element index.
+__device__ __forceinline__ uint32_t philox_word(uint64_t seed, uint64_t e) {
+  const Words4 a = philox_block(seed, e >> 2);
+  const uint32_t sh = (uint32_t)(e & 3u);
+  uint32_t v = a.w[0];
+  v = (sh == 1) ? a.w[1] : v;
+  v = (sh == 2) ? a.w[2] : v;
+  v = (sh == 3) ? a.w[3] : v;
+  return v;
 }
 
 // ---------------------------------------------------------------------------------

@@ -37,6 +37,14 @@
 //              position, and the new residual v - g_hat scattered to the kept positions.
 // HBM traffic is 12 B per element in K1 (read g and r, write c) plus O(candidates) plus
 // the scattered residual update of the kept set (one 64-byte sector per isolated entry).
+//
+// Error-feedback Random-K (hotdry.top, section 2.2; zyxy.net/archives/25733, section
+// 二.2) runs the same pipeline with another key: the Philox word of the element's global
+// index under the selection seed, shifted right by one (31 bits, like the magnitude key).
+// Its instantiations (RAND = true) draw the sample from the generator, store each
+// candidate's key bits in pool_val and its value in pool_c, and compute keys from the
+// index in the fallback; the k largest keys, lower index first among equal keys, are a
+// uniform choice of k entries without replacement.
 #include "common.hpp"
 #include "internal.hpp"
 #include "qsgd_core.hpp"
@@ -80,7 +88,9 @@ struct Layout {
   uint32_t* tile_start;    // [ntiles] pool position of the tile's candidates
   uint32_t* tile_count;    // [ntiles] candidates of the tile
   unsigned long long* scan_up;    // [2 * scan blocks] block sums, then their exclusive scan
-  float* pool_val;         // [pool] candidate values, region by region
+  float* pool_val;         // [pool] candidate values, region by region (Random-K: the
+                           //   selection key bits, whose magnitude key is the key itself)
+  float* pool_c;           // [pool] Random-K only: the candidate values
   uint16_t* pool_off;      // [pool] offset of the candidate inside its tile
   uint32_t* chunk_gt;      // [max_chunks] entries with key > T per batch (candidates) or
                            //   per tile (fallback)
@@ -107,7 +117,7 @@ int64_t sample_rank(int64_t n, int64_t k) {
   return j > m ? m : j;
 }
 
-Layout make_layout(void* base, int64_t n, int64_t k, bool staging) {
+Layout make_layout(void* base, int64_t n, int64_t k, bool staging, bool rand) {
   Layout l{};
   l.ntiles = cdiv(n, kTile);
   // Room for twice the expected candidates (at least 2k) plus one full tile per region;
@@ -140,6 +150,7 @@ Layout make_layout(void* base, int64_t n, int64_t k, bool staging) {
   l.scan_up = (unsigned long long*)take(sizeof(unsigned long long) * 4 * (l.scan_blocks + 1));
   l.pool_val = (float*)take(sizeof(float) * l.pool);
   l.pool_off = (uint16_t*)take(sizeof(uint16_t) * l.pool);
+  l.pool_c = rand ? (float*)take(sizeof(float) * l.pool) : nullptr;
   l.chunk_gt = (uint32_t*)take(sizeof(uint32_t) * l.max_chunks);
   l.chunk_eq = (uint32_t*)take(sizeof(uint32_t) * l.max_chunks);
   l.gt_excl = (unsigned long long*)take(sizeof(unsigned long long) * l.max_chunks);
@@ -211,8 +222,14 @@ __device__ __forceinline__ uint64_t mix64(uint64_t z) {
   return z ^ (z >> 31);
 }
 
+// Selection key of element e.  Top-K: the magnitude key of c = g + r.  Random-K: the
+// Philox word of the global index index_base + e under the selection seed, shifted right
+// by one (a 31-bit key, like the magnitude key, so the radix passes are shared).
+__device__ __forceinline__ uint32_t rand_key(uint32_t word) { return word >> 1; }
+
+template <bool RAND>
 __global__ void k_sample(const float* __restrict__ g, const float* __restrict__ r, int64_t n, int64_t m,
-                         uint32_t* __restrict__ keys) {
+                         uint32_t* __restrict__ keys, uint64_t seed, int64_t index_base) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < m;
        i += (int64_t)gridDim.x * blockDim.x) {
     // i < 2^20 and n <= 2^40, so the products stay below 2^61, and hi - lo <= 2^20
@@ -220,7 +237,7 @@ __global__ void k_sample(const float* __restrict__ g, const float* __restrict__ 
     const int64_t hi = (int64_t)(((uint64_t)(i + 1) * (uint64_t)n) / (uint64_t)m);
     const uint64_t h = mix64((uint64_t)i) >> 32;
     const int64_t p = lo + (int64_t)((h * (uint64_t)(hi - lo)) >> 32);
-    keys[i] = mag_key(g[p] + r[p]);
+    keys[i] = RAND ? rand_key(philox_word(seed, (uint64_t)(index_base + p))) : mag_key(g[p] + r[p]);
   }
 }
 
@@ -276,15 +293,33 @@ __device__ __forceinline__ void hist_span(const float* __restrict__ src, int64_t
     hist_add(my, r, mag_key(src[(nq << 2) + threadIdx.x]), hshift, want, shift, mask);
 }
 
+// Random-K keys of the n elements, quad by quad (the fallback's full source).
+__device__ __forceinline__ void hist_rand(int64_t n, uint64_t seed, int64_t index_base, int64_t first,
+                                          int64_t stride, bool tail_owner, uint32_t* my, BinRun& r,
+                                          uint32_t hshift, uint32_t want, int shift, uint32_t mask) {
+  const int64_t nq = n >> 2;
+  for (int64_t q = first; q < nq; q += stride) {
+    uint32_t w[4];
+    words4(seed, (uint64_t)(index_base + (q << 2)), w);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) hist_add(my, r, rand_key(w[m]), hshift, want, shift, mask);
+  }
+  if (tail_owner && threadIdx.x < (n & 3))
+    hist_add(my, r, rand_key(philox_word(seed, (uint64_t)(index_base + (nq << 2) + threadIdx.x))), hshift,
+             want, shift, mask);
+}
+
 // Radix histogram pass over the key bits [shift, shift+bits) of the entries whose higher
 // bits equal the prefix fixed so far.  SRC 0: sample keys; SRC 1: the candidate pool
-// (region by region) or, in the fallback, the full c.
+// (region by region) or, in the fallback, the magnitude keys of the full c; SRC 2: the
+// pool or, in the fallback, the Random-K keys of all n indices.
 template <int SRC>
 __global__ __launch_bounds__(kBlock) void k_hist(TopkCtrl* __restrict__ ctrl,
                                                  const uint32_t* __restrict__ sample_keys,
                                                  int64_t sample_n, const float* __restrict__ pool,
                                                  int64_t region_cap, const float* __restrict__ full,
-                                                 int64_t n, int shift, int bits) {
+                                                 int64_t n, int shift, int bits, uint64_t seed,
+                                                 int64_t index_base) {
   __shared__ uint32_t lh[kWaves][kBins];
   for (int i = threadIdx.x; i < kWaves * kBins; i += kBlock) (&lh[0][0])[i] = 0u;
   __syncthreads();
@@ -301,8 +336,10 @@ __global__ __launch_bounds__(kBlock) void k_hist(TopkCtrl* __restrict__ ctrl,
     for (int rg = 0; rg < kRegions; ++rg)
       hist_span(pool + rg * region_cap, (int64_t)ctrl->region_fill[rg], first, stride,
                 blockIdx.x == (unsigned)(rg % gridDim.x), my, run, hshift, want, shift, mask);
-  } else {
+  } else if (SRC == 1) {
     hist_span(full, n, first, stride, blockIdx.x == 0, my, run, hshift, want, shift, mask);
+  } else {
+    hist_rand(n, seed, index_base, first, stride, blockIdx.x == 0, my, run, hshift, want, shift, mask);
   }
   run_flush(my, run);
   __syncthreads();
@@ -371,13 +408,18 @@ __global__ __launch_bounds__(kBlock) void k_pick(TopkCtrl* __restrict__ ctrl, in
 // streaming shape measured on MI355X.  A tile with candidates claims its pool segment
 // with one atomic on the counter of region (tile % 32): few enough regions that a run of
 // consecutive tiles keeps its segments close together, enough to keep each counter cold.
+// RAND: the key is the Random-K key of the index (its Philox block does not depend on
+// the loads, so it is computed under their latency); the pool then holds the key bits
+// in pool_val and the value in pool_c.
+template <bool RAND>
 __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g, float* __restrict__ r,
                                                     int64_t n, TopkCtrl* __restrict__ ctrl,
                                                     uint32_t* __restrict__ tile_start,
                                                     uint32_t* __restrict__ tile_count,
                                                     float* __restrict__ pool_val,
                                                     uint16_t* __restrict__ pool_off,
-                                                    uint32_t region_cap) {
+                                                    uint32_t region_cap, float* __restrict__ pool_c,
+                                                    uint64_t seed, int64_t index_base) {
   __shared__ uint32_t s_cnt[kRounds * kWaves];
   __shared__ uint32_t s_off[kRounds * kWaves];
   __shared__ uint32_t s_total;
@@ -421,6 +463,18 @@ __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g,
       }
     }
   }
+  uint32_t key[kRounds][4];
+#pragma unroll
+  for (int j = 0; j < kRounds; ++j) {
+    if (RAND) {
+      words4(seed, (uint64_t)(index_base + base + j * (kBlock * 4) + threadIdx.x * 4), key[j]);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) key[j][m] = rand_key(key[j][m]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) key[j][m] = mag_key(c[j][m]);
+    }
+  }
   uint32_t nib[kRounds], pre[kRounds];
 #pragma unroll
   for (int j = 0; j < kRounds; ++j) {
@@ -428,7 +482,7 @@ __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g,
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4 + m;
-      b |= ((mag_key(c[j][m]) >= L) && e < n) ? (1u << m) : 0u;
+      b |= ((key[j][m] >= L) && e < n) ? (1u << m) : 0u;
     }
     nib[j] = b;
     uint32_t wc;
@@ -465,7 +519,12 @@ __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g,
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           if (nib[j] & (1u << m)) {
-            pool_val[pos] = c[j][m];
+            if (RAND) {
+              pool_val[pos] = bitsf(key[j][m]);
+              pool_c[pos] = c[j][m];
+            } else {
+              pool_val[pos] = c[j][m];
+            }
             pool_off[pos] = (uint16_t)(j * (kBlock * 4) + threadIdx.x * 4 + m);
             ++pos;
           }
@@ -786,6 +845,8 @@ __device__ __forceinline__ void small_scan(const uint32_t* s_cnt, uint32_t* s_of
 // kBlock * kEmitU entries; entry j = j0 + u * kBlock + threadIdx.x, so (u, wave) order
 // is j order.  One packed scan counts both predicates: the low 16 bits count key > T and
 // the high 16 bits key == T (a chunk holds 2048 entries, so neither field carries).
+// RAND: the pool holds key bits, and the kept value is read from pool_c.
+template <bool RAND>
 __global__ __launch_bounds__(kBlock) void k_bemit(TopkCtrl* __restrict__ ctrl, int64_t ntiles,
                                                   const uint32_t* __restrict__ tile_start,
                                                   const uint32_t* __restrict__ tile_count,
@@ -795,7 +856,8 @@ __global__ __launch_bounds__(kBlock) void k_bemit(TopkCtrl* __restrict__ ctrl, i
                                                   const unsigned long long* __restrict__ eq_excl,
                                                   float* __restrict__ r, int64_t index_base,
                                                   int64_t* __restrict__ out_idx, float* __restrict__ out_val,
-                                                  int zero_residual, int64_t k) {
+                                                  int zero_residual, int64_t k,
+                                                  const float* __restrict__ pool_c) {
   __shared__ BatchTable<kBatch> bt;
   __shared__ uint32_t s_cnt[kEmitU * kWaves];
   __shared__ uint32_t s_off[kEmitU * kWaves];
@@ -858,7 +920,7 @@ __global__ __launch_bounds__(kBlock) void k_bemit(TopkCtrl* __restrict__ ctrl, i
           const int64_t e = tbase[u] + off[u];
           if (pos < (unsigned long long)k) {   // exactly k are kept; the guard only bounds stores
             out_idx[pos] = e + index_base;
-            out_val[pos] = v[u];
+            out_val[pos] = RAND ? pool_c[src[u]] : v[u];
           }
           if (zero_residual) r[e] = 0.f;
         }
@@ -871,11 +933,40 @@ __global__ __launch_bounds__(kBlock) void k_bemit(TopkCtrl* __restrict__ ctrl, i
   }
 }
 
-// Fallback only: per-tile counts of key > T and key == T over the full c.
+// Keys of the four entries at e..e+3 of the full source (e % 4 == 0; entries at or past n
+// are not read and must be masked by the caller).  v receives the values of c.
+template <bool RAND>
+__device__ __forceinline__ void full_keys4(const float* __restrict__ full, int64_t n, int64_t e,
+                                           uint64_t seed, int64_t index_base, bool need_val,
+                                           float v[4], uint32_t key[4]) {
+  if (RAND) {
+    words4(seed, (uint64_t)(index_base + e), key);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) key[m] = rand_key(key[m]);
+  }
+  if (!RAND || need_val) {
+    if (e + 4 <= n) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(full + e);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) v[m] = e + m < n ? full[e + m] : 0.f;
+    }
+  }
+  if (!RAND) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) key[m] = mag_key(v[m]);
+  }
+}
+
+// Fallback only: per-tile counts of key > T and key == T over the full c (RAND: over the
+// keys of all n indices, which need no load).
+template <bool RAND>
 __global__ __launch_bounds__(kBlock) void k_count(const TopkCtrl* __restrict__ ctrl,
                                                   const float* __restrict__ full, int64_t n,
                                                   uint32_t* __restrict__ chunk_gt,
-                                                  uint32_t* __restrict__ chunk_eq) {
+                                                  uint32_t* __restrict__ chunk_eq, uint64_t seed,
+                                                  int64_t index_base) {
   __shared__ uint32_t s[2][kWaves];
   if (ctrl->mode != MODE_FULL) return;
   const int64_t nch = cdiv(n, kTile);
@@ -886,24 +977,16 @@ __global__ __launch_bounds__(kBlock) void k_count(const TopkCtrl* __restrict__ c
 #pragma unroll
     for (int j = 0; j < kRounds; ++j) {
       const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4;
-      if (e + 4 <= n) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(full + e);
-        const float v[4] = {a.x, a.y, a.z, a.w};
+      if (e >= n) continue;
+      float v[4];
+      uint32_t key[4];
+      full_keys4<RAND>(full, n, e, seed, index_base, false, v, key);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint32_t key = mag_key(v[m]);
-          gt += key > T;
-          eq += key == T;
+      for (int m = 0; m < 4; ++m)
+        if (e + m < n) {
+          gt += key[m] > T;
+          eq += key[m] == T;
         }
-      } else {
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-          if (e + m < n) {
-            const uint32_t key = mag_key(full[e + m]);
-            gt += key > T;
-            eq += key == T;
-          }
-      }
     }
     gt = (uint32_t)wave_sum_u64(gt);
     eq = (uint32_t)wave_sum_u64(eq);
@@ -919,13 +1002,14 @@ __global__ __launch_bounds__(kBlock) void k_count(const TopkCtrl* __restrict__ c
 
 // Fallback only: ordered compaction of the full c, tile by tile: keep key > T, and the
 // first `need` entries with key == T.
+template <bool RAND>
 __global__ __launch_bounds__(kBlock) void k_emit(const TopkCtrl* __restrict__ ctrl,
                                                  float* __restrict__ r, int64_t n,
                                                  const unsigned long long* __restrict__ gt_excl,
                                                  const unsigned long long* __restrict__ eq_excl,
                                                  int64_t index_base, int64_t* __restrict__ out_idx,
                                                  float* __restrict__ out_val, int zero_residual,
-                                                 int64_t k) {
+                                                 int64_t k, uint64_t seed) {
   __shared__ uint32_t s_cnt[kRounds * kWaves];
   __shared__ uint32_t s_off[kRounds * kWaves];
   __shared__ uint32_t s_total;
@@ -942,20 +1026,16 @@ __global__ __launch_bounds__(kBlock) void k_emit(const TopkCtrl* __restrict__ ct
 #pragma unroll
     for (int j = 0; j < kRounds; ++j) {
       const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4;
-      if (e + 4 <= n) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(r + e);
-        v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
-      } else {
+      uint32_t key[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int m = 0; m < 4; ++m) v[j][m] = e + m < n ? r[e + m] : 0.f;
-      }
+      for (int m = 0; m < 4; ++m) v[j][m] = 0.f;
+      if (e < n) full_keys4<RAND>(r, n, e, seed, index_base, true, v[j], key);
       uint32_t gb = 0, qb = 0;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const uint32_t key = mag_key(v[j][m]);
         const bool in = e + m < n;
-        gb |= (in && key > T) ? (1u << m) : 0u;
-        qb |= (in && key == T) ? (1u << m) : 0u;
+        gb |= (in && key[m] > T) ? (1u << m) : 0u;
+        qb |= (in && key[m] == T) ? (1u << m) : 0u;
       }
       gtn[j] = gb;
       eqn[j] = qb;
@@ -1079,16 +1159,12 @@ int clamp_grid(int64_t want, int64_t cap) {
   return (int)(want > cap ? cap : want);
 }
 
-}  // namespace
-
-size_t ef_topk_workspace(int64_t n, int64_t k, int qsgd_levels) {
-  return make_layout(nullptr, n, k, qsgd_levels > 0).bytes;
-}
-
-hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, int64_t index_base,
-                          int64_t* out_idx, float* out_val, int qsgd_levels, int64_t qsgd_group,
-                          uint64_t qsgd_seed, int8_t* out_codes, float* out_norms, void* ws,
-                          size_t, hipStream_t s) {
+// The whole pipeline for one key source (Top-K magnitudes, or Random-K index keys).
+template <bool RAND>
+hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, int64_t index_base,
+                         uint64_t select_seed, int64_t* out_idx, float* out_val, int qsgd_levels,
+                         int64_t qsgd_group, uint64_t qsgd_seed, int8_t* out_codes, float* out_norms,
+                         void* ws, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const int cus = device_cu_count();
   if (k == 0) {
@@ -1099,7 +1175,7 @@ hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, i
   const bool quant = qsgd_levels > 0;
   // the workspace is laid out for the largest use (QSGD with staging); out_val given or
   // not, the carve-outs stay where the size query put them
-  const Layout l = make_layout(ws, n, k, quant);
+  const Layout l = make_layout(ws, n, k, quant, RAND);
   TopkCtrl* ctrl = l.ctrl;
 
   // 1-2: sample and conservative bound L on the k-th largest key
@@ -1109,20 +1185,22 @@ hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, i
   const int64_t nunit = cdiv(l.ntiles, kUnit);
   const int64_t nbatch = cdiv(l.ntiles, kBatch);
   hipLaunchKernelGGL(k_init, 1, 256, 0, s, ctrl, (unsigned long long)j, (unsigned long long)nunit);
-  hipLaunchKernelGGL(k_sample, clamp_grid(cdiv(m, 256), cus * 8), 256, 0, s, grad, res, n, m, l.sample);
+  hipLaunchKernelGGL(k_sample<RAND>, clamp_grid(cdiv(m, 256), cus * 8), 256, 0, s, grad, res, n, m, l.sample,
+                     select_seed, index_base);
   const int shifts[3] = {20, 9, 0}, widths[3] = {11, 11, 9};
   const int sgrid = clamp_grid(cdiv(m, 256 * 8), cus * 2);
   for (int p = 0; p < 3; ++p) {
     hipLaunchKernelGGL((k_hist<0>), sgrid, kBlock, 0, s, ctrl, l.sample, m, (const float*)nullptr,
-                       (int64_t)0, (const float*)nullptr, n, shifts[p], widths[p]);
+                       (int64_t)0, (const float*)nullptr, n, shifts[p], widths[p], (uint64_t)0, (int64_t)0);
     hipLaunchKernelGGL(k_pick, 1, kBlock, 0, s, ctrl, shifts[p], p == 2 ? (exact ? 3 : 1) : 0,
                        (unsigned long long)k);
   }
 
   // 3: the streaming pass
   prof_mark(s, 1);
-  hipLaunchKernelGGL(k_ef_cand, (unsigned)l.ntiles, kBlock, 0, s, grad, res, n, ctrl, l.tile_start,
-                     l.tile_count, l.pool_val, l.pool_off, (uint32_t)l.region_cap);
+  hipLaunchKernelGGL(k_ef_cand<RAND>, (unsigned)l.ntiles, kBlock, 0, s, grad, res, n, ctrl, l.tile_start,
+                     l.tile_count, l.pool_val, l.pool_off, (uint32_t)l.region_cap, l.pool_c, select_seed,
+                     index_base);
   prof_mark(s, 2);
 
   const int ugrid = clamp_grid(nunit, cus * 8);
@@ -1141,8 +1219,9 @@ hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, i
     // 5: exact k-th key over the selected source
     const int hgrid = cus * 4;
     for (int p = 0; p < 3; ++p) {
-      hipLaunchKernelGGL((k_hist<1>), hgrid, kBlock, 0, s, ctrl, (const uint32_t*)nullptr, (int64_t)0,
-                         (const float*)l.pool_val, l.region_cap, (const float*)res, n, shifts[p], widths[p]);
+      hipLaunchKernelGGL((k_hist<RAND ? 2 : 1>), hgrid, kBlock, 0, s, ctrl, (const uint32_t*)nullptr, (int64_t)0,
+                         (const float*)l.pool_val, l.region_cap, (const float*)res, n, shifts[p], widths[p],
+                         select_seed, index_base);
       hipLaunchKernelGGL(k_pick, 1, kBlock, 0, s, ctrl, shifts[p], p == 2 ? 2 : 0, (unsigned long long)k);
     }
 
@@ -1150,7 +1229,8 @@ hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, i
     // of the other mode returns at once
     hipLaunchKernelGGL(k_bcount, ugrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
                        l.pool_val, l.chunk_gt, l.chunk_eq);
-    hipLaunchKernelGGL(k_count, cgrid, kBlock, 0, s, ctrl, res, n, l.chunk_gt, l.chunk_eq);
+    hipLaunchKernelGGL(k_count<RAND>, cgrid, kBlock, 0, s, ctrl, res, n, l.chunk_gt, l.chunk_eq, select_seed,
+                       index_base);
     const unsigned long long* nch_dev = &ctrl->nchunks;
     const int cscan = clamp_grid(cdiv(l.max_chunks, kScanChunk), cus * 4);
     hipLaunchKernelGGL(k_scan_up, cscan, kBlock, 0, s, l.chunk_gt, l.chunk_eq, nch_dev, (int64_t)0, l.scan_up);
@@ -1161,12 +1241,14 @@ hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, i
 
   // 7: ordered compaction
   float* vals = quant ? (out_val ? out_val : l.staging) : out_val;
-  hipLaunchKernelGGL(k_bemit, bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
+  hipLaunchKernelGGL(k_bemit<RAND>, bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
                      (const float*)l.pool_val, (const uint16_t*)l.pool_off, (const unsigned long long*)l.gt_excl,
-                     (const unsigned long long*)l.eq_excl, res, index_base, out_idx, vals, quant ? 0 : 1, k);
+                     (const unsigned long long*)l.eq_excl, res, index_base, out_idx, vals, quant ? 0 : 1, k,
+                     (const float*)l.pool_c);
   if (!exact)
-    hipLaunchKernelGGL(k_emit, cgrid, kBlock, 0, s, ctrl, res, n, (const unsigned long long*)l.gt_excl,
-                       (const unsigned long long*)l.eq_excl, index_base, out_idx, vals, quant ? 0 : 1, k);
+    hipLaunchKernelGGL(k_emit<RAND>, cgrid, kBlock, 0, s, ctrl, res, n, (const unsigned long long*)l.gt_excl,
+                       (const unsigned long long*)l.eq_excl, index_base, out_idx, vals, quant ? 0 : 1, k,
+                       select_seed);
 
   // 8: QSGD on the kept values and the residual of the kept set
   if (quant) {
@@ -1179,6 +1261,32 @@ hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, i
   }
   prof_mark(s, 3);
   return hipGetLastError();
+}
+
+}  // namespace
+
+size_t ef_topk_workspace(int64_t n, int64_t k, int qsgd_levels) {
+  return make_layout(nullptr, n, k, qsgd_levels > 0, false).bytes;
+}
+
+size_t ef_randk_workspace(int64_t n, int64_t k, int qsgd_levels) {
+  return make_layout(nullptr, n, k, qsgd_levels > 0, true).bytes;
+}
+
+hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, int64_t index_base,
+                          int64_t* out_idx, float* out_val, int qsgd_levels, int64_t qsgd_group,
+                          uint64_t qsgd_seed, int8_t* out_codes, float* out_norms, void* ws,
+                          size_t, hipStream_t s) {
+  return launch_select<false>(grad, res, n, k, index_base, 0, out_idx, out_val, qsgd_levels, qsgd_group,
+                              qsgd_seed, out_codes, out_norms, ws, s);
+}
+
+hipError_t launch_ef_randk(const float* grad, float* res, int64_t n, int64_t k, int64_t index_base,
+                           uint64_t select_seed, int64_t* out_idx, float* out_val, int qsgd_levels,
+                           int64_t qsgd_group, uint64_t qsgd_seed, int8_t* out_codes, float* out_norms,
+                           void* ws, size_t, hipStream_t s) {
+  return launch_select<true>(grad, res, n, k, index_base, select_seed, out_idx, out_val, qsgd_levels,
+                             qsgd_group, qsgd_seed, out_codes, out_norms, ws, s);
 }
 
 }  // namespace gc

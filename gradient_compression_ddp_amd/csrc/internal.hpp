@@ -39,6 +39,13 @@ hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, i
                           uint64_t qsgd_seed, int8_t* out_codes, float* out_norms, void* ws,
                           size_t ws_bytes, hipStream_t s);
 
+// ---- EF Random-K (the EF Top-K pipeline with index keys) ---------------------------
+size_t ef_randk_workspace(int64_t n, int64_t k, int qsgd_levels);
+hipError_t launch_ef_randk(const float* grad, float* res, int64_t n, int64_t k, int64_t index_base,
+                           uint64_t select_seed, int64_t* out_idx, float* out_val, int qsgd_levels,
+                           int64_t qsgd_group, uint64_t qsgd_seed, int8_t* out_codes, float* out_norms,
+                           void* ws, size_t ws_bytes, hipStream_t s);
+
 // ---- PowerSGD ------------------------------------------------------------------
 size_t powersgd_workspace(int64_t rows, int64_t cols, int rank);
 hipError_t launch_powersgd(const float* grad, float* res, int64_t rows, int64_t cols, int rank,

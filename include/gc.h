@@ -2,8 +2,8 @@
  * gc.h -- C ABI of the MI355X (gfx950) gradient-compression library (libgc.so).
  *
  * The library compresses one GPU's flat fp32 gradient bucket in HBM before it is sent
- * anywhere: error-feedback Top-K, min-max int8/int4, QSGD, TernGrad, PowerSGD, and the
- * matching decompression.
+ * anywhere: error-feedback Top-K and Random-K, min-max int8/int4, QSGD, TernGrad, PowerSGD,
+ * and the matching decompression.
  *
  * Conventions for every call
  *   - Data pointers are DEVICE pointers (HBM) unless a comment says "host".
@@ -27,7 +27,7 @@
  *     inputs produce unspecified (but finite-time, in-bounds) results, except in Top-K,
  *     where NaN and Inf are ordered by their bit pattern.
  *
- * Random draws (QSGD, TernGrad) use Philox4x32-10 (Salmon et al., "Parallel Random
+ * Random draws (QSGD, TernGrad, Random-K) use Philox4x32-10 (Salmon et al., "Parallel Random
  * Numbers: As Easy as 1, 2, 3", SC'11): element e takes word (e & 3) of the block at
  * counter (e >> 2, 0) under key (seed_lo, seed_hi), and U = (word >> 8) * 2^-24.
  * Rounding goes up when U < p.  The draw depends only on (seed, e), never on the
@@ -64,7 +64,8 @@ enum gc_op {
   GC_OP_QSGD = 3,          /* needs no workspace                                         */
   GC_OP_TERNGRAD = 4,      /* n = total elements, k = number of segments                 */
   GC_OP_POWERSGD = 5,      /* n = rows, k = cols, aux = rank                             */
-  GC_OP_DECOMPRESS = 6     /* needs no workspace                                         */
+  GC_OP_DECOMPRESS = 6,    /* needs no workspace                                         */
+  GC_OP_EF_RANDK = 7       /* n = elements, k = kept, aux = QSGD levels (0: none)       */
 };
 
 /* Payload kinds for gc_decompress_scatter(). */
@@ -124,6 +125,32 @@ int gc_ef_topk(const float* grad, float* residual, int64_t n, int64_t k, int64_t
                int qsgd_levels, int64_t qsgd_group, uint64_t qsgd_seed,
                int8_t* out_codes, float* out_norms,
                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gc_ef_randk -- error-feedback Random-K sparsification, optionally followed by QSGD on
+ * the kept values.
+ *
+ * Operation ([P1] section 2.2 Random-K, with the error feedback of section 2.1; [P2]
+ * section 二.2 random sparsification).  The pages fix only that a random subset of the
+ * gradient is kept; this call keeps exactly k entries, drawn without replacement from a
+ * counter-based generator, so that the payload has a fixed size and the choice is
+ * reproducible on any rank and independent of the values:
+ *   key_i  = (Philox word of global index index_base + i under select_seed) >> 1
+ *            (the same word the quantizers draw, see the top of this file; 31 bits)
+ *   S      = the k elements with the largest key; among equal keys the lower index wins
+ * and then everything as gc_ef_topk with this S: c = fl(grad + residual), out_idx
+ * ascending (plus index_base), out_val = c[idx] or QSGD of those values, and the residual
+ * at kept positions +0.0 (pure) or fl(v - g_hat) (with QSGD).  The choice depends only on
+ * (select_seed, index_base, n, k); callers pass a new seed each step.
+ *
+ * Arguments, layout, ownership and errors as gc_ef_topk.
+ * Workspace: gc_workspace_size(GC_OP_EF_RANDK, n, k, qsgd_levels).
+ */
+int gc_ef_randk(const float* grad, float* residual, int64_t n, int64_t k, int64_t index_base,
+                uint64_t select_seed, int64_t* out_idx, float* out_val,
+                int qsgd_levels, int64_t qsgd_group, uint64_t qsgd_seed,
+                int8_t* out_codes, float* out_norms,
+                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * gc_quant_minmax -- per-group min-max (linear) quantization with deterministic

@@ -1,6 +1,5 @@
 """Shared helpers for the tests: building/loading the library and moving arrays."""
 import os
-import sys
 
 import numpy as np
 
@@ -11,9 +10,13 @@ LIB = os.path.join(ROOT, "gradient_compression_ddp_amd", "libgc.so")
 def ensure_built():
     """Build libgc.so only if it is not there yet."""
     if not os.path.exists(LIB):
-        sys.path.insert(0, ROOT)
-        from gradient_compression_ddp_amd.build import build
-        build()
+        # by path: importing the package would load the library that is missing
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_gc_build", os.path.join(ROOT, "gradient_compression_ddp_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
     return LIB
 
 

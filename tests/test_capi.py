@@ -85,6 +85,27 @@ def test_ef_topk_rejects_bad_arguments(lib):
     assert f(None, None, 0, 0, 0, None, None, 0, 64, 0, None, None, None, 0, None) == 0
 
 
+def test_ef_randk_rejects_bad_arguments(lib):
+    lib.gc_last_error.restype = ctypes.c_char_p
+    f = lib.gc_ef_randk
+    f.argtypes = [VP, VP, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_uint64, VP, VP, ctypes.c_int,
+                  ctypes.c_int64, ctypes.c_uint64, VP, VP, VP, ctypes.c_size_t, VP]
+    assert f(FAKE, FAKE, 10, 11, 0, 3, FAKE, FAKE, 0, 64, 0, None, None, FAKE, 1 << 20, None) == 1
+    assert b"k must" in lib.gc_last_error()
+    assert f(FAKE, MISALIGNED, 10, 1, 0, 3, FAKE, FAKE, 0, 64, 0, None, None, FAKE, 1 << 20, None) == 1
+    assert f(FAKE, FAKE, 10, 1, 0, 3, None, FAKE, 0, 64, 0, None, None, FAKE, 1 << 20, None) == 1
+    assert f(FAKE, FAKE, 10, 1, 0, 3, FAKE, FAKE, 127, 64, 0, None, FAKE, FAKE, 1 << 20, None) == 1
+    assert f(FAKE, FAKE, 10, 1, 1 << 62, 3, FAKE, FAKE, 0, 64, 0, None, None, FAKE, 1 << 20, None) == 1
+    assert f(FAKE, FAKE, 10, 1, 0, 3, FAKE, FAKE, 0, 64, 0, None, None, None, 0, None) == 2
+    assert f(None, None, 0, 0, 0, 3, None, None, 0, 64, 0, None, None, None, 0, None) == 0
+    # the pool also keeps each candidate's value: more workspace than Top-K of the same size
+    st_t, b_t = _ws(lib, 1, 5_000_000, 50_000, 0)
+    st_r, b_r = _ws(lib, 7, 5_000_000, 50_000, 0)
+    assert st_t == 0 and st_r == 0 and b_r > b_t
+    assert _ws(lib, 7, 100, 0, 0) == (0, 0)
+    assert _ws(lib, 7, 100, 101, 0)[0] == 1
+
+
 def test_other_calls_reject_bad_arguments(lib):
     q = lib.gc_quant_minmax
     q.argtypes = [VP, VP, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, VP, VP, VP, VP, ctypes.c_size_t, VP]
