@@ -1,8 +1,13 @@
 """Benchmark: fused error-feedback Top-1% + 8-bit QSGD on a 7e9-element fp32 gradient.
 
-One step = one gc_ef_topk call with QSGD (s = 127, groups of 64) over the whole flat
-gradient: c = g + r, exact Top-k (k = 1% = 7e7), ordered compaction, QSGD of the kept
-values and the residual update.  Inputs live in HBM before the timed region starts.
+One step = one gc_ef_topk_deferred call with QSGD (s = 127, groups of 64) over the whole
+flat gradient: c = g + r with the previous step's kept-set residuals applied in the same
+pass, exact Top-k (k = 1% = 7e7), ordered compaction, QSGD of the kept values, and the
+kept set's new residuals recorded for the next step.  The timed region ends with one
+gc_ef_flush, so the K timed steps apply exactly K sets of kept-set residuals (the first
+step applies the warm-up's) and the residual is exact when the clock stops.  --direct
+times gc_ef_topk instead, which scatters the kept set's residuals inside each call.
+Inputs live in HBM before the timed region starts.
 
 Workload (synthetic, generated on the GPU): 32 layers of 218,750,000 elements, each
 t(3) times a per-layer lognormal(-7, 1) scale; three step gradients g_1..g_3 (step t
@@ -28,12 +33,13 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 
 # HBM bytes per launch of the streaming pass on this workload, from two rocprofv3 counter
-# runs (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, factors from a plain 4 GiB device copy; the
-# summary with its commands is profiles/k_ef_cand_7e9_hbm_traffic.md).  Valid only for the
-# kernel source it was measured on: the digest covers the tile constants, the block-rank
-# helpers and the kernel itself, and a mismatch reports the traffic as null.
-K1_TRAFFIC_BYTES = 8.4612e10
-K1_SOURCE_SHA256 = "d65c59ac29b1adc9e6b1b0a1e720226d0e5bf703649a0720d538b01233f986cd"
+# runs per mode (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, factors from a plain 4 GiB device
+# copy; the summary with its commands is profiles/k_ef_cand_7e9_hbm_traffic.md).  Valid
+# only for the kernel source it was measured on: the digest covers the tile constants,
+# the pending-record helpers, the block-rank helpers and the kernel itself, and a
+# mismatch reports the traffic as null.
+K1_TRAFFIC_BYTES = {"deferred": 8.5718e10, "direct": 8.4612e10}
+K1_SOURCE_SHA256 = "886a4efdca6423eece807e306b0a768c77a32aa161877b041607a83d1c624648"
 METRIC = "EF-Top-1%+int8 compress GB/s of fp32 grad input; % of HBM peak"
 
 
@@ -45,7 +51,8 @@ def k1_source_digest():
     src = open(os.path.join(ROOT, "gradient_compression_ddp_amd", "csrc", "ef_topk.hip")).read()
     parts = [m.group(0) for m in re.finditer(r"^constexpr \w+ (kBlock|kWaves|kRounds|kTile|kRegions) = .*$",
                                              src, re.M)]
-    for start, end in (("__device__ __forceinline__ uint32_t rank_round", "// Kernels"),
+    for start, end in (("struct PendHdr {", "// Block-level ordered ranking"),
+                       ("__device__ __forceinline__ uint32_t rank_round", "// Kernels"),
                        ("void k_ef_cand(", "\n}\n")):
         a = src.index(start)
         parts.append(src[a:src.index(end, a)])
@@ -66,6 +73,9 @@ def parse():
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="run one device-to-device copy of this many GiB before the timed region "
                          "(a plain copy of known size for calibrating HBM byte counters)")
+    ap.add_argument("--direct", action="store_true",
+                    help="time gc_ef_topk (kept-set residuals scattered inside each call) instead of "
+                         "gc_ef_topk_deferred + a final gc_ef_flush")
     ap.add_argument("--rows", action="store_true",
                     help="instead of the metric line, print one JSON line per compressor: each "
                          "timed on the GPU against the HBM roofline, with the oracle timed beside it")
@@ -461,13 +471,18 @@ def main():
     out_codes = torch.empty(k, dtype=torch.int8, device=dev)
     out_norms = torch.empty((k + 63) // 64, dtype=torch.float32, device=dev)
     ws = torch.empty(gc.workspace_size(gc.OP_EF_TOPK, n, k, 127), dtype=torch.uint8, device=dev)
+    mode = "direct" if args.direct else "deferred"
+    pend = None if args.direct else gc.pending_record(n, k, dev)
     torch.cuda.synchronize()
 
     def step(i):
         t = i % 3
-        gc.ef_topk(grads[t], res, k, qsgd_levels=127, qsgd_group=64, qsgd_seed=501 + t,
-                   out_idx=out_idx, out_codes=out_codes, out_norms=out_norms, want_values=False,
-                   workspace=ws)
+        kw = dict(qsgd_levels=127, qsgd_group=64, qsgd_seed=501 + t, out_idx=out_idx, out_codes=out_codes,
+                  out_norms=out_norms, want_values=False, workspace=ws)
+        if pend is None:
+            gc.ef_topk(grads[t], res, k, **kw)
+        else:
+            gc.ef_topk_deferred(grads[t], res, k, pend, **kw)
 
     if args.copy_calibration_gib > 0:
         nb = int(args.copy_calibration_gib * (1 << 30)) // 4
@@ -487,6 +502,8 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.warmup, args.warmup + args.steps):
         step(i)
+    if pend is not None:
+        gc.ef_flush(res, pend)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     gc.profile_enable(False)
@@ -498,8 +515,11 @@ def main():
     alg_step = 12.0 * n + 8.0 * k + 1.0 * k + 4.0 * ((k + 63) // 64)
     value = in_bytes / (ms_step / 1e3) / 1e9
     pass_ms = ms_pass / max(calls, 1)
-    pass_bytes = 12.0 * n
+    # read g and r, write c; deferred: also the record of the previous step (a 4-byte
+    # offset and a 4-byte value per kept entry, 12 bytes of tile table per tile)
+    pass_bytes = 12.0 * n + (0.0 if args.direct else 8.0 * k + 12.0 * ((n + 4095) // 4096))
     achieved = pass_bytes / (pass_ms / 1e3) / 1e9
+    traffic = K1_TRAFFIC_BYTES[mode] if k1_source_digest() == K1_SOURCE_SHA256 else None
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -515,7 +535,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "ef_topk_1pct_qsgd8_7e9",
-            "elements": n, "layers": L, "layer_len": LL, "k": k,
+            "elements": n, "layers": L, "layer_len": LL, "k": k, "residual_update": mode,
             "qsgd_levels": 127, "qsgd_group": 64, "step_gradients": 3,
             "parallelism": "single GPU",
         },
@@ -526,21 +546,21 @@ def main():
                               "after_pass": round(ms_after / max(calls, 1), 4)},
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_ef_cand (fused c = g + r, write c, candidate extraction)",
+            "kernel": ("k_ef_cand (fused c = g + r, write c, candidate extraction)" if args.direct else
+                       "k_ef_cand (fused c = g + r with the previous step's kept-set residuals applied, "
+                       "write c, candidate extraction)"),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": (round(K1_TRAFFIC_BYTES / 1e9 / (pass_ms / 1e3), 1)
-                        if k1_source_digest() == K1_SOURCE_SHA256 else None),
-            "traffic_bytes_per_launch": (K1_TRAFFIC_BYTES if k1_source_digest() == K1_SOURCE_SHA256
-                                         else None),
+            "traffic": round(traffic / 1e9 / (pass_ms / 1e3), 1) if traffic else None,
+            "traffic_bytes_per_launch": traffic,
             "bytes_per_launch": pass_bytes,
             "avg_launch_ms": round(pass_ms, 4),
         },
     }
     if not args.no_cpu:
-        del grads, res, ws
+        del grads, res, ws, pend
         torch.cuda.empty_cache()
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args, L)

@@ -14,10 +14,11 @@ import os
 import torch
 
 __all__ = [
-    "lib_path", "GCError", "workspace_size", "ef_topk", "ef_randk", "quant_minmax", "qsgd", "terngrad",
+    "lib_path", "GCError", "workspace_size", "ef_topk", "ef_topk_deferred", "ef_flush", "pending_record",
+    "ef_randk", "quant_minmax", "qsgd", "terngrad",
     "powersgd_step", "decompress_scatter", "KIND_F32", "KIND_MINMAX8", "KIND_MINMAX4",
     "KIND_QSGD", "KIND_TERN", "OP_EF_TOPK", "OP_QUANT_MINMAX", "OP_QSGD", "OP_TERNGRAD",
-    "OP_POWERSGD", "OP_DECOMPRESS", "OP_EF_RANDK", "profile_enable", "profile_collect", "PayloadHeader",
+    "OP_POWERSGD", "OP_DECOMPRESS", "OP_EF_RANDK", "OP_EF_PENDING", "profile_enable", "profile_collect", "PayloadHeader",
     "PAYLOAD_MAGIC", "PAYLOAD_SPARSE", "payload_layout", "payload_sections", "write_payload_header",
     "read_payload_header", "decompress_payloads",
 ]
@@ -27,7 +28,7 @@ lib_path = os.path.join(_HERE, "libgc.so")
 
 GC_OK, GC_EINVAL, GC_EWORKSPACE, GC_EUNSUPPORTED, GC_EHIP = 0, 1, 2, 3, 4
 OP_EF_TOPK, OP_QUANT_MINMAX, OP_QSGD, OP_TERNGRAD, OP_POWERSGD, OP_DECOMPRESS = 1, 2, 3, 4, 5, 6
-OP_EF_RANDK = 7
+OP_EF_RANDK, OP_EF_PENDING = 7, 8
 KIND_F32, KIND_MINMAX8, KIND_MINMAX4, KIND_QSGD, KIND_TERN = 0, 1, 2, 3, 4
 
 if not os.path.exists(lib_path):
@@ -59,6 +60,9 @@ _SIGS = {
     "gc_version": ([], _i32),
     "gc_workspace_size": ([_i32, _i64, _i64, _i64, ctypes.POINTER(_sz)], _i32),
     "gc_ef_topk": ([_p, _p, _i64, _i64, _i64, _p, _p, _i32, _i64, _u64, _p, _p, _p, _sz, _p], _i32),
+    "gc_ef_topk_deferred": ([_p, _p, _i64, _i64, _i64, _p, _p, _i32, _i64, _u64, _p, _p, _p, _sz, _p, _sz, _p],
+                            _i32),
+    "gc_ef_flush": ([_p, _i64, _p, _sz, _p], _i32),
     "gc_ef_randk": ([_p, _p, _i64, _i64, _i64, _u64, _p, _p, _i32, _i64, _u64, _p, _p, _p, _sz, _p], _i32),
     "gc_quant_minmax": ([_p, _p, _i64, _i64, _i32, _p, _p, _p, _p, _sz, _p], _i32),
     "gc_qsgd": ([_p, _p, _i64, _i64, _i32, _u64, _i64, _p, _p, _p], _i32),
@@ -128,7 +132,7 @@ def _workspace(op, n, k, aux, device, workspace):
 
 
 def _sparsify(name, op, grad, residual, k, index_base, extra, qsgd_levels, qsgd_group, qsgd_seed,
-              out_idx, out_val, out_codes, out_norms, want_values, workspace, stream):
+              out_idx, out_val, out_codes, out_norms, want_values, workspace, stream, tail=()):
     _dev(grad, torch.float32, "grad")
     _dev(residual, torch.float32, "residual")
     n = grad.numel()
@@ -148,7 +152,7 @@ def _sparsify(name, op, grad, residual, k, index_base, extra, qsgd_levels, qsgd_
     ws, ws_bytes = _workspace(op, n, k, qsgd_levels, dev, workspace)
     _check(getattr(_lib, name)(_ptr(grad), _ptr(residual), n, k, index_base, *extra, _ptr(out_idx),
                                _ptr(out_val), qsgd_levels, qsgd_group, qsgd_seed, _ptr(out_codes),
-                               _ptr(out_norms), _ptr(ws), ws_bytes, _stream(stream)), name)
+                               _ptr(out_norms), *tail, _ptr(ws), ws_bytes, _stream(stream)), name)
     if quant:
         return out_idx, out_codes, out_norms, out_val
     return out_idx, out_val
@@ -164,6 +168,32 @@ def ef_topk(grad, residual, k, index_base=0, *, qsgd_levels=0, qsgd_group=64, qs
     """
     return _sparsify("gc_ef_topk", OP_EF_TOPK, grad, residual, k, index_base, (), qsgd_levels, qsgd_group,
                      qsgd_seed, out_idx, out_val, out_codes, out_norms, want_values, workspace, stream)
+
+
+def pending_record(n, k_max, device):
+    """A zero-filled (empty) pending record for :func:`ef_topk_deferred` on n elements."""
+    return torch.zeros(max(workspace_size(OP_EF_PENDING, n, k_max), 1), dtype=torch.uint8, device=device)
+
+
+def ef_topk_deferred(grad, residual, k, pending, index_base=0, *, qsgd_levels=0, qsgd_group=64, qsgd_seed=0,
+                     out_idx=None, out_val=None, out_codes=None, out_norms=None, want_values=True,
+                     workspace=None, stream=None):
+    """:func:`ef_topk` whose kept-set residual update is recorded in ``pending`` (a
+    uint8 tensor from :func:`pending_record`) and applied by the next call or by
+    :func:`ef_flush`.  Outputs as :func:`ef_topk`."""
+    _dev(pending, torch.uint8, "pending")
+    return _sparsify("gc_ef_topk_deferred", OP_EF_TOPK, grad, residual, k, index_base, (), qsgd_levels,
+                     qsgd_group, qsgd_seed, out_idx, out_val, out_codes, out_norms, want_values, workspace,
+                     stream, tail=(_ptr(pending), pending.numel()))
+
+
+def ef_flush(residual, pending, stream=None):
+    """Apply ``pending`` to ``residual`` (which then equals what :func:`ef_topk` would
+    have left) and empty the record."""
+    _dev(residual, torch.float32, "residual")
+    _dev(pending, torch.uint8, "pending")
+    _check(_lib.gc_ef_flush(_ptr(residual), residual.numel(), _ptr(pending), pending.numel(), _stream(stream)),
+           "gc_ef_flush")
 
 
 def ef_randk(grad, residual, k, select_seed, index_base=0, *, qsgd_levels=0, qsgd_group=64, qsgd_seed=0,

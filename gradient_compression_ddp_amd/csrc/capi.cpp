@@ -292,6 +292,10 @@ int gc_workspace_size(int op, int64_t n, int64_t k, int64_t aux, size_t* bytes) 
       GC_REQUIRE(aux >= 0 && aux <= 127, "qsgd levels must lie in [0, 127]");
       *bytes = (n == 0 || k == 0) ? 0 : gc::ef_randk_workspace(n, k, (int)aux);
       return ok();
+    case GC_OP_EF_PENDING:
+      GC_REQUIRE(k >= 0 && k <= n, "k must lie in [0, n]");
+      *bytes = n == 0 ? 0 : gc::ef_pending_bytes(n, k);
+      return ok();
     case GC_OP_QUANT_MINMAX:
       GC_REQUIRE(k == 0 || k >= 4, "group must be 0 or >= 4");
       *bytes = (k == 0 || k > 256) ? gc::minmax_large_workspace(n, k) : 0;
@@ -353,6 +357,39 @@ int gc_ef_topk(const float* grad, float* residual, int64_t n, int64_t k, int64_t
                                        qsgd_group, qsgd_seed, out_codes, out_norms, workspace,
                                        workspace_bytes, reinterpret_cast<hipStream_t>(stream)),
                     "gc_ef_topk launch");
+}
+
+int gc_ef_topk_deferred(const float* grad, float* residual, int64_t n, int64_t k, int64_t index_base,
+                        int64_t* out_idx, float* out_val, int qsgd_levels, int64_t qsgd_group,
+                        uint64_t qsgd_seed, int8_t* out_codes, float* out_norms, void* pending,
+                        size_t pending_bytes, void* workspace, size_t workspace_bytes, void* stream) {
+  const int c = check_sparsify(grad, residual, n, k, index_base, out_idx, out_val, qsgd_levels,
+                               qsgd_group, out_codes, out_norms);
+  if (c != GC_OK || n == 0) return c;
+  GC_REQUIRE(pending && aligned(pending, 256), "pending must be non-NULL and 256-byte aligned");
+  if (pending_bytes < gc::ef_pending_bytes(n, k))
+    return fail(GC_EWORKSPACE, "pending record of %zu bytes is smaller than the %zu this n and k need",
+                pending_bytes, gc::ef_pending_bytes(n, k));
+  if (k > 0) {
+    const int w = check_workspace(workspace, workspace_bytes, gc::ef_topk_workspace(n, k, qsgd_levels));
+    if (w != GC_OK) return w;
+  }
+  return hip_status(gc::launch_ef_topk_deferred(grad, residual, n, k, index_base, out_idx, out_val,
+                                                qsgd_levels, qsgd_group, qsgd_seed, out_codes, out_norms,
+                                                pending, pending_bytes, workspace, workspace_bytes,
+                                                reinterpret_cast<hipStream_t>(stream)),
+                    "gc_ef_topk_deferred launch");
+}
+
+int gc_ef_flush(float* residual, int64_t n, void* pending, size_t pending_bytes, void* stream) {
+  GC_REQUIRE(n >= 0 && n <= kMaxN, "n must lie in [0, 2^40]");
+  if (n == 0) return ok();
+  GC_REQUIRE(residual && aligned(residual, 16), "residual must be non-NULL and 16-byte aligned");
+  GC_REQUIRE(pending && aligned(pending, 256), "pending must be non-NULL and 256-byte aligned");
+  if (pending_bytes < gc::ef_pending_bytes(n, 0))
+    return fail(GC_EWORKSPACE, "pending record of %zu bytes is too small for n", pending_bytes);
+  return hip_status(gc::launch_ef_flush(residual, n, pending, pending_bytes, reinterpret_cast<hipStream_t>(stream)),
+                    "gc_ef_flush launch");
 }
 
 int gc_ef_randk(const float* grad, float* residual, int64_t n, int64_t k, int64_t index_base,

@@ -161,6 +161,101 @@ Layout make_layout(void* base, int64_t n, int64_t k, bool staging, bool rand) {
 }
 
 // ---------------------------------------------------------------------------------
+// Pending kept-set corrections (the deferred residual update).  A deferred call leaves
+// c = g + r in the residual everywhere and records, for each kept entry, its offset in
+// its 4096-element tile and the residual value it should hold (+0.0 for pure Top-K,
+// v - g_hat with QSGD).  The next call's streaming pass applies them to r as it reads
+// it, so the kept set's residual is written by a coalesced pass instead of a scatter.
+// Record layout (caller-owned, zero-filled before first use = empty):
+//   PendHdr | tile_first u64[ntiles] | tile_cnt u32[ntiles] | chunks of 64 entries
+// Entry j lives in chunk j / 64: 64 uint32 offsets, then 64 float values, so 64
+// consecutive entries fill two whole 256-byte runs.  The layout depends only on n.
+// ---------------------------------------------------------------------------------
+struct PendHdr {
+  unsigned long long n;       // elements of the residual the corrections belong to (0: none)
+  unsigned long long count;   // corrections recorded
+  uint32_t has_vals;          // values recorded (QSGD); otherwise every correction is +0.0
+  uint32_t pad[59];
+};
+static_assert(sizeof(PendHdr) == 256, "pending header is 256 bytes");
+
+struct Pending {
+  PendHdr* hdr;
+  unsigned long long* tile_first;   // kept-order index of the tile's first correction
+  uint32_t* tile_cnt;               // corrections in the tile
+  uint32_t* chunks;                 // entry storage
+  int64_t ntiles;
+  size_t bytes;
+};
+
+Pending pending_layout(void* base, int64_t n, int64_t kmax) {
+  Pending p{};
+  p.ntiles = cdiv(n, kTile);
+  char* b = reinterpret_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void* {
+    void* q = b ? b + off : nullptr;
+    off += align256(bytes);
+    return q;
+  };
+  p.hdr = (PendHdr*)take(sizeof(PendHdr));
+  p.tile_first = (unsigned long long*)take(sizeof(unsigned long long) * p.ntiles);
+  p.tile_cnt = (uint32_t*)take(sizeof(uint32_t) * p.ntiles);
+  p.chunks = (uint32_t*)take((size_t)cdiv(kmax > 0 ? kmax : 1, 64) * 512);
+  p.bytes = off;
+  return p;
+}
+
+__device__ __forceinline__ uint32_t* pend_off(uint32_t* chunks, unsigned long long j) {
+  return chunks + (j >> 6) * 128 + (j & 63);
+}
+__device__ __forceinline__ float* pend_val(uint32_t* chunks, unsigned long long j) {
+  return reinterpret_cast<float*>(chunks + (j >> 6) * 128 + 64 + (j & 63));
+}
+
+// The recorded corrections of tile t, clamped to the record's capacity (so that even a
+// record that was never zero-filled is read in bounds).
+__device__ __forceinline__ void pend_range(const Pending& pd, unsigned long long cap, int64_t t,
+                                           unsigned long long* first, uint32_t* cnt) {
+  unsigned long long f = pd.tile_first[t];
+  unsigned long long c = pd.tile_cnt[t];
+  if (f > cap) f = cap;
+  if (c > cap - f) c = cap - f;
+  *first = f;
+  *cnt = (uint32_t)c;
+}
+
+// The residual of element p: its recorded correction if it has one, else rv.
+__device__ __forceinline__ float pend_lookup(const Pending& pd, unsigned long long cap, int64_t p,
+                                             uint32_t has_vals, float rv) {
+  unsigned long long f;
+  uint32_t cnt;
+  pend_range(pd, cap, p / kTile, &f, &cnt);
+  const uint32_t o = (uint32_t)(p % kTile);
+  uint32_t a = 0, b = cnt;   // first entry with offset >= o (offsets ascend in a tile)
+  while (a < b) {
+    const uint32_t mid = (a + b) >> 1;
+    if (*pend_off(pd.chunks, f + mid) < o) a = mid + 1; else b = mid;
+  }
+  if (a < cnt && *pend_off(pd.chunks, f + a) == o) return has_vals ? *pend_val(pd.chunks, f + a) : 0.f;
+  return rv;
+}
+
+// Spreads a tile's corrections into LDS: s_cv[o] = value, bit o of s_cf set.  Called by
+// every thread of the block (it holds two barriers).
+__device__ __forceinline__ void pend_overlay(const Pending& pd, unsigned long long f, uint32_t cnt,
+                                             uint32_t has_vals, float* s_cv, uint32_t* s_cf) {
+  for (int i = threadIdx.x; i < kTile / 32; i += kBlock) s_cf[i] = 0u;
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < cnt; i += kBlock) {
+    const uint32_t o = *pend_off(pd.chunks, f + i) & (uint32_t)(kTile - 1);
+    s_cv[o] = has_vals ? *pend_val(pd.chunks, f + i) : 0.f;
+    atomicOr(&s_cf[o >> 5], 1u << (o & 31));
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------------
 // Block-level ordered ranking.  A block handles 4096 entries as 4 rounds x 4 waves x
 // 64 lanes x 4 entries; entry (j, w, lane, m) has index j*1024 + w*256 + lane*4 + m.
 // For a predicate held as one 4-bit mask per lane and round, rank_round() returns the
@@ -227,9 +322,17 @@ __device__ __forceinline__ uint64_t mix64(uint64_t z) {
 // by one (a 31-bit key, like the magnitude key, so the radix passes are shared).
 __device__ __forceinline__ uint32_t rand_key(uint32_t word) { return word >> 1; }
 
-template <bool RAND>
+// DEFER: r is corrected by the recorded corrections of the previous call first.
+template <bool RAND, bool DEFER>
 __global__ void k_sample(const float* __restrict__ g, const float* __restrict__ r, int64_t n, int64_t m,
-                         uint32_t* __restrict__ keys, uint64_t seed, int64_t index_base) {
+                         uint32_t* __restrict__ keys, uint64_t seed, int64_t index_base, Pending pd,
+                         unsigned long long cap) {
+  bool apply = false;
+  uint32_t has_vals = 0u;
+  if (DEFER && !RAND) {
+    apply = pd.hdr->n == (unsigned long long)n;
+    has_vals = pd.hdr->has_vals;
+  }
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < m;
        i += (int64_t)gridDim.x * blockDim.x) {
     // i < 2^20 and n <= 2^40, so the products stay below 2^61, and hi - lo <= 2^20
@@ -237,7 +340,13 @@ __global__ void k_sample(const float* __restrict__ g, const float* __restrict__ 
     const int64_t hi = (int64_t)(((uint64_t)(i + 1) * (uint64_t)n) / (uint64_t)m);
     const uint64_t h = mix64((uint64_t)i) >> 32;
     const int64_t p = lo + (int64_t)((h * (uint64_t)(hi - lo)) >> 32);
-    keys[i] = RAND ? rand_key(philox_word(seed, (uint64_t)(index_base + p))) : mag_key(g[p] + r[p]);
+    if (RAND) {
+      keys[i] = rand_key(philox_word(seed, (uint64_t)(index_base + p)));
+    } else {
+      float rv = r[p];
+      if (DEFER && apply) rv = pend_lookup(pd, cap, p, has_vals, rv);
+      keys[i] = mag_key(g[p] + rv);
+    }
   }
 }
 
@@ -411,7 +520,9 @@ __global__ __launch_bounds__(kBlock) void k_pick(TopkCtrl* __restrict__ ctrl, in
 // RAND: the key is the Random-K key of the index (its Philox block does not depend on
 // the loads, so it is computed under their latency); the pool then holds the key bits
 // in pool_val and the value in pool_c.
-template <bool RAND>
+// DEFER: the previous call's recorded corrections of this tile are spread into LDS
+// while the loads are in flight and replace r at their positions before the add.
+template <bool RAND, bool DEFER>
 __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g, float* __restrict__ r,
                                                     int64_t n, TopkCtrl* __restrict__ ctrl,
                                                     uint32_t* __restrict__ tile_start,
@@ -419,17 +530,26 @@ __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g,
                                                     float* __restrict__ pool_val,
                                                     uint16_t* __restrict__ pool_off,
                                                     uint32_t region_cap, float* __restrict__ pool_c,
-                                                    uint64_t seed, int64_t index_base) {
+                                                    uint64_t seed, int64_t index_base, Pending pd,
+                                                    unsigned long long cap) {
   __shared__ uint32_t s_cnt[kRounds * kWaves];
   __shared__ uint32_t s_off[kRounds * kWaves];
   __shared__ uint32_t s_total;
   __shared__ uint32_t s_base;
   __shared__ uint32_t s_ok;
+  __shared__ float s_cv[DEFER ? kTile : 1];
+  __shared__ uint32_t s_cf[DEFER ? kTile / 32 : 1];
   const uint32_t L = ctrl->L;
   const int w = threadIdx.x / kWave;
   const int lane = lane_id();
   const int64_t tile = blockIdx.x;
   const int64_t base = tile * kTile;
+  unsigned long long pf = 0;
+  uint32_t pc = 0u, has_vals = 0u;
+  if (DEFER && pd.hdr->n == (unsigned long long)n) {
+    pend_range(pd, cap, tile, &pf, &pc);
+    has_vals = pd.hdr->has_vals;
+  }
   float c[kRounds][4];
   if (base + kTile <= n) {
     f32x4 gv[kRounds], rv[kRounds];
@@ -438,6 +558,20 @@ __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g,
       const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4;
       gv[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + e));
       rv[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(r + e));
+    }
+    if (DEFER && pc) {
+      pend_overlay(pd, pf, pc, has_vals, s_cv, s_cf);
+#pragma unroll
+      for (int j = 0; j < kRounds; ++j) {
+        const int q = j * (kBlock * 4) + threadIdx.x * 4;
+        const uint32_t bits = (s_cf[q >> 5] >> (q & 31)) & 0xFu;
+        if (bits) {
+          if (bits & 1u) rv[j].x = s_cv[q];
+          if (bits & 2u) rv[j].y = s_cv[q + 1];
+          if (bits & 4u) rv[j].z = s_cv[q + 2];
+          if (bits & 8u) rv[j].w = s_cv[q + 3];
+        }
+      }
     }
 #pragma unroll
     for (int j = 0; j < kRounds; ++j) {
@@ -449,6 +583,7 @@ __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g,
       c[j][0] = cv.x; c[j][1] = cv.y; c[j][2] = cv.z; c[j][3] = cv.w;
     }
   } else {
+    if (DEFER && pc) pend_overlay(pd, pf, pc, has_vals, s_cv, s_cf);
 #pragma unroll
     for (int j = 0; j < kRounds; ++j) {
 #pragma unroll
@@ -456,7 +591,12 @@ __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g,
         const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4 + m;
         float v = 0.f;
         if (e < n) {
-          v = g[e] + r[e];
+          float rr = r[e];
+          if (DEFER && pc) {
+            const int q = j * (kBlock * 4) + threadIdx.x * 4 + m;
+            if ((s_cf[q >> 5] >> (q & 31)) & 1u) rr = s_cv[q];
+          }
+          v = g[e] + rr;
           r[e] = v;
         }
         c[j][m] = v;
@@ -659,7 +799,8 @@ __global__ __launch_bounds__(kBlock) void k_scan_down(const uint32_t* __restrict
 }
 
 
-// One-block exclusive scan of two uint32 count arrays (small counts only).
+// One-block exclusive scan of one or two uint32 count arrays (small counts only; b and
+// ob may be null).
 __global__ __launch_bounds__(kBlock) void k_scan_small(const uint32_t* __restrict__ a,
                                                        const uint32_t* __restrict__ b, int64_t count,
                                                        unsigned long long* __restrict__ oa,
@@ -670,14 +811,17 @@ __global__ __launch_bounds__(kBlock) void k_scan_small(const uint32_t* __restric
   for (int64_t r0 = 0; r0 < count; r0 += kBlock) {
     const int64_t it = r0 + threadIdx.x;
     const unsigned long long va = it < count ? a[it] : 0ull;
-    const unsigned long long vb = it < count ? b[it] : 0ull;
+    const unsigned long long vb = (b && it < count) ? b[it] : 0ull;
     const unsigned long long ia = wave_incl_scan_u64(va);
     const unsigned long long ib = wave_incl_scan_u64(vb);
     if (lane_id() == kWave - 1) { s_w[0][w] = ia; s_w[1][w] = ib; }
     __syncthreads();
     unsigned long long pa = ca, pb = cb;
     for (int i = 0; i < w; ++i) { pa += s_w[0][i]; pb += s_w[1][i]; }
-    if (it < count) { oa[it] = pa + ia - va; ob[it] = pb + ib - vb; }
+    if (it < count) {
+      oa[it] = pa + ia - va;
+      if (ob) ob[it] = pb + ib - vb;
+    }
     ca += s_w[0][0] + s_w[0][1] + s_w[0][2] + s_w[0][3];
     cb += s_w[1][0] + s_w[1][1] + s_w[1][2] + s_w[1][3];
     __syncthreads();
@@ -846,7 +990,9 @@ __device__ __forceinline__ void small_scan(const uint32_t* s_cnt, uint32_t* s_of
 // is j order.  One packed scan counts both predicates: the low 16 bits count key > T and
 // the high 16 bits key == T (a chunk holds 2048 entries, so neither field carries).
 // RAND: the pool holds key bits, and the kept value is read from pool_c.
-template <bool RAND>
+// DEFER: instead of writing the kept residual, record each kept entry's tile offset at
+// its kept position and count the kept entries of every tile.
+template <bool RAND, bool DEFER>
 __global__ __launch_bounds__(kBlock) void k_bemit(TopkCtrl* __restrict__ ctrl, int64_t ntiles,
                                                   const uint32_t* __restrict__ tile_start,
                                                   const uint32_t* __restrict__ tile_count,
@@ -857,12 +1003,13 @@ __global__ __launch_bounds__(kBlock) void k_bemit(TopkCtrl* __restrict__ ctrl, i
                                                   float* __restrict__ r, int64_t index_base,
                                                   int64_t* __restrict__ out_idx, float* __restrict__ out_val,
                                                   int zero_residual, int64_t k,
-                                                  const float* __restrict__ pool_c) {
+                                                  const float* __restrict__ pool_c, Pending pd) {
   __shared__ BatchTable<kBatch> bt;
   __shared__ uint32_t s_cnt[kEmitU * kWaves];
   __shared__ uint32_t s_off[kEmitU * kWaves];
   __shared__ uint32_t s_total;
   __shared__ int64_t s_b;
+  __shared__ uint32_t s_kc[DEFER ? kBatch : 1];
   if (ctrl->mode != MODE_CAND) return;
   const uint32_t T = ctrl->T;
   const unsigned long long need = ctrl->need;
@@ -872,12 +1019,14 @@ __global__ __launch_bounds__(kBlock) void k_bemit(TopkCtrl* __restrict__ ctrl, i
   for (int64_t b; (b = next_batch(ctrl, nbatch, &s_b)) >= 0;) {
     const int64_t t0 = b * kBatch;
     const int nt = (int)(ntiles - t0 < kBatch ? ntiles - t0 : kBatch);
+    if (DEFER && threadIdx.x < kBatch) s_kc[threadIdx.x] = 0u;   // visible after load_batch's barrier
     const uint32_t total = load_batch(bt, t0, nt, tile_start, tile_count);
     // the exclusive prefixes of the batch's first unit
     unsigned long long gt_run = gt_excl[b * (kBatch / kUnit)], eq_run = eq_excl[b * (kBatch / kUnit)];
     for (uint32_t j0 = 0; j0 < total; j0 += kBlock * kEmitU) {
       uint32_t src[kEmitU];
       int64_t tbase[kEmitU];
+      int tlo[kEmitU];
       bool live[kEmitU];
 #pragma unroll
       for (int u = 0; u < kEmitU; ++u) {
@@ -886,6 +1035,7 @@ __global__ __launch_bounds__(kBlock) void k_bemit(TopkCtrl* __restrict__ ctrl, i
         const int lo = live[u] ? batch_tile<kBatch>(bt, j) : 0;
         src[u] = bt.start[lo] + (j - bt.pre[lo]);
         tbase[u] = (t0 + lo) * kTile;
+        tlo[u] = lo;
       }
       float v[kEmitU];
       uint32_t off[kEmitU];
@@ -921,8 +1071,12 @@ __global__ __launch_bounds__(kBlock) void k_bemit(TopkCtrl* __restrict__ ctrl, i
           if (pos < (unsigned long long)k) {   // exactly k are kept; the guard only bounds stores
             out_idx[pos] = e + index_base;
             out_val[pos] = RAND ? pool_c[src[u]] : v[u];
+            if (DEFER) {
+              *pend_off(pd.chunks, pos) = off[u];
+              atomicAdd(&s_kc[tlo[u]], 1u);
+            }
           }
-          if (zero_residual) r[e] = 0.f;
+          if (!DEFER && zero_residual) r[e] = 0.f;
         }
       }
       const uint32_t tot = s_total;
@@ -930,6 +1084,7 @@ __global__ __launch_bounds__(kBlock) void k_bemit(TopkCtrl* __restrict__ ctrl, i
       eq_run += tot >> 16;
       __syncthreads();   // s_cnt / s_off / s_total are rewritten by the next chunk
     }
+    if (DEFER && threadIdx.x < nt) pd.tile_cnt[t0 + threadIdx.x] = s_kc[threadIdx.x];
   }
 }
 
@@ -1001,15 +1156,16 @@ __global__ __launch_bounds__(kBlock) void k_count(const TopkCtrl* __restrict__ c
 }
 
 // Fallback only: ordered compaction of the full c, tile by tile: keep key > T, and the
-// first `need` entries with key == T.
-template <bool RAND>
+// first `need` entries with key == T.  DEFER: record offsets and per-tile counts as the
+// batch emit does.
+template <bool RAND, bool DEFER>
 __global__ __launch_bounds__(kBlock) void k_emit(const TopkCtrl* __restrict__ ctrl,
                                                  float* __restrict__ r, int64_t n,
                                                  const unsigned long long* __restrict__ gt_excl,
                                                  const unsigned long long* __restrict__ eq_excl,
                                                  int64_t index_base, int64_t* __restrict__ out_idx,
                                                  float* __restrict__ out_val, int zero_residual,
-                                                 int64_t k, uint64_t seed) {
+                                                 int64_t k, uint64_t seed, Pending pd) {
   __shared__ uint32_t s_cnt[kRounds * kWaves];
   __shared__ uint32_t s_off[kRounds * kWaves];
   __shared__ uint32_t s_total;
@@ -1072,6 +1228,7 @@ __global__ __launch_bounds__(kBlock) void k_emit(const TopkCtrl* __restrict__ ct
     block_scan32(s_cnt, s_off, &s_total);
     __syncthreads();
     const unsigned long long kept0 = gt_excl[ch] + (eq0 < need ? eq0 : need);
+    if (DEFER && threadIdx.x == 0) pd.tile_cnt[ch] = s_total;
 #pragma unroll
     for (int j = 0; j < kRounds; ++j) {
       if (keep[j]) {
@@ -1083,8 +1240,9 @@ __global__ __launch_bounds__(kBlock) void k_emit(const TopkCtrl* __restrict__ ct
             if (pos < (unsigned long long)k) {   // exactly k are kept; the guard only bounds stores
               out_idx[pos] = e + index_base;
               out_val[pos] = v[j][m];
+              if (DEFER) *pend_off(pd.chunks, pos) = (uint32_t)(j * (kBlock * 4) + threadIdx.x * 4 + m);
             }
-            if (zero_residual) r[e] = 0.f;
+            if (!DEFER && zero_residual) r[e] = 0.f;
             ++pos;
           }
       }
@@ -1097,11 +1255,13 @@ __global__ __launch_bounds__(kBlock) void k_emit(const TopkCtrl* __restrict__ ct
 // residual update r[idx] = v - g_hat.  A block takes 1024 kept entries as 256 quads; the
 // residuals go through LDS so that the scattered stores are issued in kept order, 64
 // consecutive entries per wave store (neighbouring kept entries often share a sector).
+// DEFER: the residuals go to the record's values, in kept order, instead of r.
+template <bool DEFER>
 __global__ __launch_bounds__(kBlock) void k_qsgd_kept(const float* __restrict__ vals, int64_t k,
                                                       int lpg_log2, float s, uint64_t seed,
                                                       int8_t* __restrict__ codes, float* __restrict__ norms,
                                                       const int64_t* __restrict__ idx, int64_t index_base,
-                                                      float* __restrict__ r, int64_t n) {
+                                                      float* __restrict__ r, int64_t n, Pending pd) {
   __shared__ float s_res[kBlock * 4];
   const int64_t nquads = (k + 3) >> 2;
   const int lpg = 1 << lpg_log2;
@@ -1147,11 +1307,48 @@ __global__ __launch_bounds__(kBlock) void k_qsgd_kept(const float* __restrict__ 
     for (int m = 0; m < 4; ++m) {
       const int64_t j = base * 4 + m * kBlock + threadIdx.x;
       if (j < k) {
-        const int64_t p = idx[j] - index_base;
-        if (p >= 0 && p < n) r[p] = s_res[m * kBlock + threadIdx.x];
+        if (DEFER) {
+          *pend_val(pd.chunks, (unsigned long long)j) = s_res[m * kBlock + threadIdx.x];
+        } else {
+          const int64_t p = idx[j] - index_base;
+          if (p >= 0 && p < n) r[p] = s_res[m * kBlock + threadIdx.x];
+        }
       }
     }
   }
+}
+
+// Writes every recorded correction into r, one wave per tile, so that r becomes the
+// exact residual; k_pend_set then marks the record empty.
+__global__ __launch_bounds__(kBlock) void k_pend_flush(float* __restrict__ r, int64_t n, Pending pd,
+                                                       unsigned long long cap) {
+  if (pd.hdr->n != (unsigned long long)n) return;
+  const int64_t t = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
+  if (t >= pd.ntiles) return;
+  const uint32_t has_vals = pd.hdr->has_vals;
+  unsigned long long f;
+  uint32_t cnt;
+  pend_range(pd, cap, t, &f, &cnt);
+  for (uint32_t i = (uint32_t)lane_id(); i < cnt; i += kWave) {
+    const int64_t e = t * kTile + (*pend_off(pd.chunks, f + i) & (uint32_t)(kTile - 1));
+    if (e < n) r[e] = has_vals ? *pend_val(pd.chunks, f + i) : 0.f;
+  }
+}
+
+__global__ void k_pend_set(PendHdr* __restrict__ hdr, unsigned long long n, unsigned long long count,
+                           uint32_t has_vals) {
+  if (threadIdx.x == 0) {
+    hdr->n = n;
+    hdr->count = count;
+    hdr->has_vals = has_vals;
+  }
+}
+
+// Entries a record of `bytes` bytes holds for n elements (0 if it is too small for the
+// fixed part).
+unsigned long long pending_capacity(int64_t n, size_t bytes) {
+  const size_t fixed = pending_layout(nullptr, n, 0).bytes - 512;
+  return bytes < fixed ? 0ull : (unsigned long long)((bytes - fixed) / 512) * 64ull;
 }
 
 int clamp_grid(int64_t want, int64_t cap) {
@@ -1159,15 +1356,25 @@ int clamp_grid(int64_t want, int64_t cap) {
   return (int)(want > cap ? cap : want);
 }
 
-// The whole pipeline for one key source (Top-K magnitudes, or Random-K index keys).
-template <bool RAND>
+void launch_flush(float* res, int64_t n, const Pending& pd, unsigned long long cap, hipStream_t s) {
+  hipLaunchKernelGGL(k_pend_flush, (unsigned)cdiv(pd.ntiles, kWaves), kBlock, 0, s, res, n, pd, cap);
+  hipLaunchKernelGGL(k_pend_set, 1, 64, 0, s, pd.hdr, 0ull, 0ull, 0u);
+}
+
+// The whole pipeline for one key source (Top-K magnitudes, or Random-K index keys), with
+// the kept set's residual written directly or recorded for the next call (DEFER).
+template <bool RAND, bool DEFER>
 hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, int64_t index_base,
                          uint64_t select_seed, int64_t* out_idx, float* out_val, int qsgd_levels,
                          int64_t qsgd_group, uint64_t qsgd_seed, int8_t* out_codes, float* out_norms,
-                         void* ws, hipStream_t s) {
+                         void* ws, void* pend, size_t pend_bytes, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const int cus = device_cu_count();
+  const unsigned long long cap = DEFER ? pending_capacity(n, pend_bytes) : 0ull;
+  const Pending pd = DEFER ? pending_layout(pend, n, (int64_t)cap) : Pending{};
   if (k == 0) {
+    // nothing is kept: apply what the previous call recorded, then the plain add
+    if (DEFER) launch_flush(res, n, pd, cap, s);
     hipLaunchKernelGGL(k_ef_add, (unsigned)cdiv(n, kTile), kBlock, 0, s, grad, res, n);
     return hipGetLastError();
   }
@@ -1185,8 +1392,8 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
   const int64_t nunit = cdiv(l.ntiles, kUnit);
   const int64_t nbatch = cdiv(l.ntiles, kBatch);
   hipLaunchKernelGGL(k_init, 1, 256, 0, s, ctrl, (unsigned long long)j, (unsigned long long)nunit);
-  hipLaunchKernelGGL(k_sample<RAND>, clamp_grid(cdiv(m, 256), cus * 8), 256, 0, s, grad, res, n, m, l.sample,
-                     select_seed, index_base);
+  hipLaunchKernelGGL((k_sample<RAND, DEFER>), clamp_grid(cdiv(m, 256), cus * 8), 256, 0, s, grad, res, n, m,
+                     l.sample, select_seed, index_base, pd, cap);
   const int shifts[3] = {20, 9, 0}, widths[3] = {11, 11, 9};
   const int sgrid = clamp_grid(cdiv(m, 256 * 8), cus * 2);
   for (int p = 0; p < 3; ++p) {
@@ -1198,9 +1405,9 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
 
   // 3: the streaming pass
   prof_mark(s, 1);
-  hipLaunchKernelGGL(k_ef_cand<RAND>, (unsigned)l.ntiles, kBlock, 0, s, grad, res, n, ctrl, l.tile_start,
-                     l.tile_count, l.pool_val, l.pool_off, (uint32_t)l.region_cap, l.pool_c, select_seed,
-                     index_base);
+  hipLaunchKernelGGL((k_ef_cand<RAND, DEFER>), (unsigned)l.ntiles, kBlock, 0, s, grad, res, n, ctrl,
+                     l.tile_start, l.tile_count, l.pool_val, l.pool_off, (uint32_t)l.region_cap, l.pool_c,
+                     select_seed, index_base, pd, cap);
   prof_mark(s, 2);
 
   const int ugrid = clamp_grid(nunit, cus * 8);
@@ -1241,23 +1448,41 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
 
   // 7: ordered compaction
   float* vals = quant ? (out_val ? out_val : l.staging) : out_val;
-  hipLaunchKernelGGL(k_bemit<RAND>, bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
+  const int zero_res = (quant || DEFER) ? 0 : 1;
+  hipLaunchKernelGGL((k_bemit<RAND, DEFER>), bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
                      (const float*)l.pool_val, (const uint16_t*)l.pool_off, (const unsigned long long*)l.gt_excl,
-                     (const unsigned long long*)l.eq_excl, res, index_base, out_idx, vals, quant ? 0 : 1, k,
-                     (const float*)l.pool_c);
+                     (const unsigned long long*)l.eq_excl, res, index_base, out_idx, vals, zero_res, k,
+                     (const float*)l.pool_c, pd);
   if (!exact)
-    hipLaunchKernelGGL(k_emit<RAND>, cgrid, kBlock, 0, s, ctrl, res, n, (const unsigned long long*)l.gt_excl,
-                       (const unsigned long long*)l.eq_excl, index_base, out_idx, vals, quant ? 0 : 1, k,
-                       select_seed);
+    hipLaunchKernelGGL((k_emit<RAND, DEFER>), cgrid, kBlock, 0, s, ctrl, res, n,
+                       (const unsigned long long*)l.gt_excl, (const unsigned long long*)l.eq_excl, index_base,
+                       out_idx, vals, zero_res, k, select_seed, pd);
 
   // 8: QSGD on the kept values and the residual of the kept set
   if (quant) {
     int lpg_log2 = 0;
     while ((int64_t(4) << lpg_log2) < qsgd_group) ++lpg_log2;
     const int qgrid = clamp_grid(cdiv(cdiv(k, 4), kBlock), cus * 16);
-    hipLaunchKernelGGL(k_qsgd_kept, qgrid, kBlock, 0, s, (const float*)vals, k, lpg_log2, (float)qsgd_levels,
-                       qsgd_seed, out_codes, out_norms, (const int64_t*)out_idx, index_base,
-                       res, n);
+    hipLaunchKernelGGL(k_qsgd_kept<DEFER>, qgrid, kBlock, 0, s, (const float*)vals, k, lpg_log2,
+                       (float)qsgd_levels, qsgd_seed, out_codes, out_norms, (const int64_t*)out_idx, index_base,
+                       res, n, pd);
+  }
+  if (DEFER) {
+    // tile_first = exclusive scan of the per-tile kept counts; then the record is live
+    if (l.ntiles <= 16 * kScanChunk) {
+      hipLaunchKernelGGL(k_scan_small, 1, kBlock, 0, s, (const uint32_t*)pd.tile_cnt, (const uint32_t*)nullptr,
+                         l.ntiles, pd.tile_first, (unsigned long long*)nullptr);
+    } else {
+      const int tscan = clamp_grid(cdiv(l.ntiles, kScanChunk), cus * 4);
+      hipLaunchKernelGGL(k_scan_up, tscan, kBlock, 0, s, (const uint32_t*)pd.tile_cnt, (const uint32_t*)nullptr,
+                         (const unsigned long long*)nullptr, l.ntiles, l.scan_up);
+      hipLaunchKernelGGL(k_scan_mid, 1, kBlock, 0, s, (const unsigned long long*)nullptr, l.ntiles, l.scan_up);
+      hipLaunchKernelGGL(k_scan_down, tscan, kBlock, 0, s, (const uint32_t*)pd.tile_cnt, (const uint32_t*)nullptr,
+                         (const unsigned long long*)nullptr, l.ntiles, (const unsigned long long*)l.scan_up,
+                         pd.tile_first, (unsigned long long*)nullptr);
+    }
+    hipLaunchKernelGGL(k_pend_set, 1, 64, 0, s, pd.hdr, (unsigned long long)n, (unsigned long long)k,
+                       quant ? 1u : 0u);
   }
   prof_mark(s, 3);
   return hipGetLastError();
@@ -1277,16 +1502,35 @@ hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, i
                           int64_t* out_idx, float* out_val, int qsgd_levels, int64_t qsgd_group,
                           uint64_t qsgd_seed, int8_t* out_codes, float* out_norms, void* ws,
                           size_t, hipStream_t s) {
-  return launch_select<false>(grad, res, n, k, index_base, 0, out_idx, out_val, qsgd_levels, qsgd_group,
-                              qsgd_seed, out_codes, out_norms, ws, s);
+  return launch_select<false, false>(grad, res, n, k, index_base, 0, out_idx, out_val, qsgd_levels,
+                                     qsgd_group, qsgd_seed, out_codes, out_norms, ws, nullptr, 0, s);
+}
+
+size_t ef_pending_bytes(int64_t n, int64_t kmax) { return pending_layout(nullptr, n, kmax).bytes; }
+
+unsigned long long ef_pending_capacity(int64_t n, size_t bytes) { return pending_capacity(n, bytes); }
+
+hipError_t launch_ef_topk_deferred(const float* grad, float* res, int64_t n, int64_t k, int64_t index_base,
+                                   int64_t* out_idx, float* out_val, int qsgd_levels, int64_t qsgd_group,
+                                   uint64_t qsgd_seed, int8_t* out_codes, float* out_norms, void* pend,
+                                   size_t pend_bytes, void* ws, size_t, hipStream_t s) {
+  return launch_select<false, true>(grad, res, n, k, index_base, 0, out_idx, out_val, qsgd_levels,
+                                    qsgd_group, qsgd_seed, out_codes, out_norms, ws, pend, pend_bytes, s);
+}
+
+hipError_t launch_ef_flush(float* res, int64_t n, void* pend, size_t pend_bytes, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const unsigned long long cap = pending_capacity(n, pend_bytes);
+  launch_flush(res, n, pending_layout(pend, n, (int64_t)cap), cap, s);
+  return hipGetLastError();
 }
 
 hipError_t launch_ef_randk(const float* grad, float* res, int64_t n, int64_t k, int64_t index_base,
                            uint64_t select_seed, int64_t* out_idx, float* out_val, int qsgd_levels,
                            int64_t qsgd_group, uint64_t qsgd_seed, int8_t* out_codes, float* out_norms,
                            void* ws, size_t, hipStream_t s) {
-  return launch_select<true>(grad, res, n, k, index_base, select_seed, out_idx, out_val, qsgd_levels,
-                             qsgd_group, qsgd_seed, out_codes, out_norms, ws, s);
+  return launch_select<true, false>(grad, res, n, k, index_base, select_seed, out_idx, out_val, qsgd_levels,
+                                    qsgd_group, qsgd_seed, out_codes, out_norms, ws, nullptr, 0, s);
 }
 
 }  // namespace gc

@@ -65,7 +65,8 @@ enum gc_op {
   GC_OP_TERNGRAD = 4,      /* n = total elements, k = number of segments                 */
   GC_OP_POWERSGD = 5,      /* n = rows, k = cols, aux = rank                             */
   GC_OP_DECOMPRESS = 6,    /* needs no workspace                                         */
-  GC_OP_EF_RANDK = 7       /* n = elements, k = kept, aux = QSGD levels (0: none)       */
+  GC_OP_EF_RANDK = 7,      /* n = elements, k = kept, aux = QSGD levels (0: none)       */
+  GC_OP_EF_PENDING = 8     /* size of a pending record: n = elements, k = largest k     */
 };
 
 /* Payload kinds for gc_decompress_scatter(). */
@@ -125,6 +126,46 @@ int gc_ef_topk(const float* grad, float* residual, int64_t n, int64_t k, int64_t
                int qsgd_levels, int64_t qsgd_group, uint64_t qsgd_seed,
                int8_t* out_codes, float* out_norms,
                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gc_ef_topk_deferred -- gc_ef_topk with the residual update of the kept set deferred to
+ * the next call on the same residual.
+ *
+ * Same operation and outputs as gc_ef_topk ([P1] section 2.1: what is not sent is kept
+ * and added to the next step's gradient).  The difference is only where the new
+ * residual of the kept entries lives between calls: this call leaves c in `residual` at
+ * every position and records, in the caller-owned `pending` record, each kept entry's
+ * residual value (+0.0, or fl(v - g_hat) with QSGD).  The next gc_ef_topk_deferred or
+ * gc_ef_flush on the same residual applies them: the next call does so inside its one
+ * coalesced pass over the residual, which saves the scattered writes of the kept set.
+ * Indices, values, codes and norms are bit-identical to gc_ef_topk's, and so is the
+ * residual once flushed.
+ *
+ * pending: device memory, 256-byte aligned, of pending_bytes >=
+ *   gc_workspace_size(GC_OP_EF_PENDING, n, k_max, 0) for the largest k it will see.  It
+ *   must be zero-filled before its first use (empty) and belongs to one residual of n
+ *   elements until it is flushed: calls with another residual or another n must not use
+ *   it.  Between calls, the exact residual is `residual` patched by the record; call
+ *   gc_ef_flush before reading the residual or using it with any other call.
+ * k == 0 applies the record, performs residual = c and leaves the record empty.
+ * Other arguments, the workspace and errors as gc_ef_topk; a too small record returns
+ * GC_EWORKSPACE.
+ */
+int gc_ef_topk_deferred(const float* grad, float* residual, int64_t n, int64_t k, int64_t index_base,
+                        int64_t* out_idx, float* out_val,
+                        int qsgd_levels, int64_t qsgd_group, uint64_t qsgd_seed,
+                        int8_t* out_codes, float* out_norms,
+                        void* pending, size_t pending_bytes,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gc_ef_flush -- apply a pending record to its residual and empty the record.
+ *
+ * residual: float[n] of the gc_ef_topk_deferred calls that filled `pending`; afterwards
+ * it equals the residual gc_ef_topk would have left.  An empty record (or one filled for
+ * another n) changes nothing.  n == 0 is a no-op.
+ */
+int gc_ef_flush(float* residual, int64_t n, void* pending, size_t pending_bytes, void* stream);
 
 /*
  * gc_ef_randk -- error-feedback Random-K sparsification, optionally followed by QSGD on

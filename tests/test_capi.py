@@ -106,6 +106,30 @@ def test_ef_randk_rejects_bad_arguments(lib):
     assert _ws(lib, 7, 100, 101, 0)[0] == 1
 
 
+def test_deferred_calls_reject_bad_arguments(lib):
+    f = lib.gc_ef_topk_deferred
+    f.argtypes = [VP, VP, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, VP, VP, ctypes.c_int, ctypes.c_int64,
+                  ctypes.c_uint64, VP, VP, VP, ctypes.c_size_t, VP, ctypes.c_size_t, VP]
+    st, need = _ws(lib, 8, 100_000, 1000, 0)
+    assert st == 0 and need > 0
+    # the record grows by one 512-byte chunk per 64 entries of k
+    assert _ws(lib, 8, 100_000, 1000 + 64 * 10, 0)[1] - need == 10 * 512
+    assert _ws(lib, 8, 100, 101, 0)[0] == 1
+    args = (FAKE, FAKE, 100_000, 1000, 0, FAKE, FAKE, 0, 64, 0, None, None)
+    assert f(*args, None, need, FAKE, 1 << 30, None) == 1                       # no record
+    assert f(*args, MISALIGNED, need, FAKE, 1 << 30, None) == 1                 # misaligned record
+    assert f(*args, VP(0x200000), need - 1, FAKE, 1 << 30, None) == 2           # record too small
+    assert f(*args, VP(0x200000), need, None, 0, None) == 2                     # no workspace
+    assert f(FAKE, FAKE, 100_000, 100_001, 0, FAKE, FAKE, 0, 64, 0, None, None, FAKE, need, FAKE, 1 << 30,
+             None) == 1                                                          # k > n
+    fl = lib.gc_ef_flush
+    fl.argtypes = [VP, ctypes.c_int64, VP, ctypes.c_size_t, VP]
+    assert fl(MISALIGNED, 100_000, VP(0x200000), need, None) == 1
+    assert fl(FAKE, 100_000, None, need, None) == 1
+    assert fl(FAKE, 100_000, VP(0x200000), 16, None) == 2
+    assert fl(None, 0, None, 0, None) == 0
+
+
 def test_other_calls_reject_bad_arguments(lib):
     q = lib.gc_quant_minmax
     q.argtypes = [VP, VP, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, VP, VP, VP, VP, ctypes.c_size_t, VP]
