@@ -30,6 +30,7 @@ from .powersgd import powersgd_step, modified_gram_schmidt
 from .decompress import decompress_scatter, KIND_F32, KIND_MINMAX8, KIND_MINMAX4, KIND_QSGD, KIND_TERN
 from .pipeline import ef_topk_qsgd
 from .randk import randk_keys, ef_randk, ef_randk_qsgd
+from .monitor import norm_stats, monitored_step
 
 __all__ = [
     "philox4x32_10", "uniform24", "magnitude_key", "ef_topk", "topk_invariant_holds",
@@ -37,5 +38,5 @@ __all__ = [
     "pairwise_sum_of_squares", "terngrad", "dequant_terngrad", "pack_ternary",
     "unpack_ternary", "powersgd_step", "modified_gram_schmidt", "decompress_scatter",
     "KIND_F32", "KIND_MINMAX8", "KIND_MINMAX4", "KIND_QSGD", "KIND_TERN", "ef_topk_qsgd",
-    "randk_keys", "ef_randk", "ef_randk_qsgd",
+    "randk_keys", "ef_randk", "ef_randk_qsgd", "norm_stats", "monitored_step",
 ]
