@@ -1,12 +1,13 @@
 """Benchmark: fused error-feedback Top-1% + 8-bit QSGD on a 7e9-element fp32 gradient.
 
-One step = one gc_ef_topk_deferred call with QSGD (s = 127, groups of 64) over the whole
-flat gradient: c = g + r with the previous step's kept-set residuals applied in the same
+One step = one deferred EF Top-K call (gc_ef_compress with a pending record, which is
+gc_ef_topk_deferred) with QSGD (s = 127, groups of 64) over the whole flat gradient: c = g + r with the previous step's kept-set residuals applied in the same
 pass, exact Top-k (k = 1% = 7e7), ordered compaction, QSGD of the kept values, and the
 kept set's new residuals recorded for the next step.  The timed region ends with one
 gc_ef_flush, so the K timed steps apply exactly K sets of kept-set residuals (the first
 step applies the warm-up's) and the residual is exact when the clock stops.  --direct
-times gc_ef_topk instead, which scatters the kept set's residuals inside each call.
+times gc_ef_topk instead, which scatters the kept set's residuals inside each call;
+--monitor adds the gradient-norm-ratio monitor to every step.
 Inputs live in HBM before the timed region starts.
 
 Workload (synthetic, generated on the GPU): 32 layers of 218,750,000 elements, each
@@ -39,7 +40,7 @@ HBM_PEAK_GBS = 8000.0
 # the pending-record helpers, the block-rank helpers and the kernel itself, and a
 # mismatch reports the traffic as null.
 K1_TRAFFIC_BYTES = {"deferred": 8.5718e10, "direct": 8.4612e10}
-K1_SOURCE_SHA256 = "886a4efdca6423eece807e306b0a768c77a32aa161877b041607a83d1c624648"
+K1_SOURCE_SHA256 = "ebddc6a2a4d31de1dbf741e7a83f8d2d470564d67a5efd71841c34eb0ecdca0d"
 METRIC = "EF-Top-1%+int8 compress GB/s of fp32 grad input; % of HBM peak"
 
 
@@ -76,6 +77,8 @@ def parse():
     ap.add_argument("--direct", action="store_true",
                     help="time gc_ef_topk (kept-set residuals scattered inside each call) instead of "
                          "gc_ef_topk_deferred + a final gc_ef_flush")
+    ap.add_argument("--monitor", action="store_true",
+                    help="also run the gradient-norm-ratio monitor in every step (gc_ef_compress stats)")
     ap.add_argument("--rows", action="store_true",
                     help="instead of the metric line, print one JSON line per compressor: each "
                          "timed on the GPU against the HBM roofline, with the oracle timed beside it")
@@ -375,8 +378,9 @@ def rows_mode(args):
          "the same 8 payloads")
     del pays, outb
 
-    # EF Random-1% + QSGD-127 over 1e9 elements of the layered workload (32 layers).
-    say("EF Random-K 1% + QSGD-127, 1e9")
+    # EF sparsification variants over 1e9 elements of the layered workload (32 layers),
+    # k = 1%, QSGD-127 on the kept values: Random-K (direct and deferred residual) and the
+    # norm monitor's cost on the deferred Top-K step.
     LR, LLR = 32, 31_250_000
     nr, kr = LR * LLR, LR * LLR // 100
     gr = workloads.layered_torch(LR, LLR, step=1, device=dev, seed=5)
@@ -385,20 +389,34 @@ def rows_mode(args):
     ocr = torch.empty(kr, dtype=torch.int8, device=dev)
     onr = torch.empty((kr + 63) // 64, dtype=torch.float32, device=dev)
     wsr = torch.empty(gc.workspace_size(gc.OP_EF_RANDK, nr, kr, 127), dtype=torch.uint8, device=dev)
-    f = lambda: gc.ef_randk(gr, rr, kr, 77, qsgd_levels=127, qsgd_group=64, qsgd_seed=501, out_idx=oir,
-                            out_codes=ocr, out_norms=onr, want_values=False, workspace=wsr)
-    eager = _eager_ms(torch, f, reps=10)
-    gms, _ = _graph_ms(torch, [f] * 2, reps=5)
-    osec = None
+    pend = gc.pending_record(nr, kr, dev)
+    st = torch.zeros(3, dtype=torch.float64, device=dev)
     ns_o = 1 << 24
-    if orc:
-        h = gr[:ns_o].cpu().numpy()
-        osec = _oracle_s(lambda: orc.ef_randk_qsgd(h, np.zeros_like(h), ns_o // 100, 77, levels=127, group=64,
-                                                   qsgd_seed=501))
-    _row("next-3 EF Random-K 1% + QSGD-127", "n=1e9 (32 layers x 31,250,000, t(3) x lognormal scales), k=1e7",
-         12.0 * nr + kr * (8.0 + 1.0 + 4.0 / 64 + 4.0 + 4.0), "call", gms, eager, osec, ns_o / nr,
-         "the first 2^24 elements, k = 1% of them")
-    del gr, rr, oir, ocr, onr, wsr
+    h = gr[:ns_o].cpu().numpy() if orc else None
+    kept_bytes = kr * (8.0 + 1.0 + 4.0 / 64 + 4.0 + 4.0)
+    variants = [
+        ("next-3 EF Random-K 1% + QSGD-127", dict(select="randk", select_seed=77), 12.0 * nr + kept_bytes,
+         lambda: orc.ef_randk_qsgd(h, np.zeros_like(h), ns_o // 100, 77, levels=127, group=64, qsgd_seed=501)),
+        ("next-3 EF Random-K 1% + QSGD-127, deferred residual", dict(select="randk", select_seed=77, pending=pend),
+         12.0 * nr + kept_bytes + 16.0 * kr, None),
+        ("a10 EF Top-K 1% + QSGD-127, deferred residual", dict(pending=pend), 12.0 * nr + kept_bytes + 16.0 * kr,
+         lambda: orc.ef_topk_qsgd(h, np.zeros_like(h), ns_o // 100, levels=127, group=64, seed=501)),
+        ("next-2 the same with the norm monitor", dict(pending=pend, stats=st), 12.0 * nr + kept_bytes + 16.0 * kr,
+         lambda: orc.monitored_step(h, np.zeros_like(h), ns_o // 100, levels=127, group=64, qsgd_seed=501)),
+    ]
+    for name, opt, ub, ofn in variants:
+        say(name)
+        if "pending" in opt:
+            gc.ef_flush(rr, pend)                  # each variant starts from an exact residual
+        f = lambda opt=opt: gc.ef_compress(gr, rr, kr, qsgd_levels=127, qsgd_group=64, qsgd_seed=501, out_idx=oir,
+                                           out_codes=ocr, out_norms=onr, want_values=False, workspace=wsr, **opt)
+        eager = _eager_ms(torch, f, reps=10)
+        gms, _ = _graph_ms(torch, [f] * 2, reps=5)
+        osec = _oracle_s(ofn) if (orc and ofn) else None
+        extra = {"norm_ratio": round(float(st[2]), 6)} if "stats" in opt else None
+        _row(name, "n=1e9 (32 layers x 31,250,000, t(3) x lognormal scales), k=1e7", ub, "call", gms, eager, osec,
+             ns_o / nr, "the first 2^24 elements, k = 1% of them", extra=extra)
+    del gr, rr, oir, ocr, onr, wsr, pend, st
 
     # c3: TernGrad over 24 layers of 14,583,333 (~350M parameters), one segmented call.
     say("TernGrad 24 layers")
@@ -473,16 +491,14 @@ def main():
     ws = torch.empty(gc.workspace_size(gc.OP_EF_TOPK, n, k, 127), dtype=torch.uint8, device=dev)
     mode = "direct" if args.direct else "deferred"
     pend = None if args.direct else gc.pending_record(n, k, dev)
+    stats = torch.zeros(3, dtype=torch.float64, device=dev) if args.monitor else None
     torch.cuda.synchronize()
 
     def step(i):
         t = i % 3
-        kw = dict(qsgd_levels=127, qsgd_group=64, qsgd_seed=501 + t, out_idx=out_idx, out_codes=out_codes,
-                  out_norms=out_norms, want_values=False, workspace=ws)
-        if pend is None:
-            gc.ef_topk(grads[t], res, k, **kw)
-        else:
-            gc.ef_topk_deferred(grads[t], res, k, pend, **kw)
+        gc.ef_compress(grads[t], res, k, pending=pend, stats=stats, qsgd_levels=127, qsgd_group=64,
+                       qsgd_seed=501 + t, out_idx=out_idx, out_codes=out_codes, out_norms=out_norms,
+                       want_values=False, workspace=ws)
 
     if args.copy_calibration_gib > 0:
         nb = int(args.copy_calibration_gib * (1 << 30)) // 4
@@ -536,6 +552,7 @@ def main():
         "config": {
             "workload": "ef_topk_1pct_qsgd8_7e9",
             "elements": n, "layers": L, "layer_len": LL, "k": k, "residual_update": mode,
+            "norm_monitor": bool(args.monitor),
             "qsgd_levels": 127, "qsgd_group": 64, "step_gradients": 3,
             "parallelism": "single GPU",
         },
@@ -559,6 +576,8 @@ def main():
             "avg_launch_ms": round(pass_ms, 4),
         },
     }
+    if stats is not None:
+        line["norm_ratio_last_step"] = round(float(stats[2]), 6)
     if not args.no_cpu:
         del grads, res, ws, pend
         torch.cuda.empty_cache()

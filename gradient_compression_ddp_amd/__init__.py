@@ -14,7 +14,8 @@ import os
 import torch
 
 __all__ = [
-    "lib_path", "GCError", "workspace_size", "ef_topk", "ef_topk_deferred", "ef_flush", "pending_record",
+    "lib_path", "GCError", "workspace_size", "ef_compress", "EfOptions", "ef_topk", "ef_topk_deferred",
+    "ef_flush", "pending_record",
     "ef_randk", "quant_minmax", "qsgd", "terngrad",
     "powersgd_step", "decompress_scatter", "KIND_F32", "KIND_MINMAX8", "KIND_MINMAX4",
     "KIND_QSGD", "KIND_TERN", "OP_EF_TOPK", "OP_QUANT_MINMAX", "OP_QSGD", "OP_TERNGRAD",
@@ -52,6 +53,14 @@ class PayloadHeader(ctypes.Structure):
 
 assert ctypes.sizeof(PayloadHeader) == 128
 
+SELECT_TOPK, SELECT_RANDK = 0, 1
+
+
+class EfOptions(ctypes.Structure):
+    """gc_ef_options (include/gc.h): selector, pending record, norm-monitor output."""
+    _fields_ = [("size", ctypes.c_uint32), ("select", ctypes.c_uint32), ("select_seed", ctypes.c_uint64),
+                ("pending", ctypes.c_void_p), ("pending_bytes", ctypes.c_size_t), ("stats", ctypes.c_void_p)]
+
 _p, _i64, _u64, _i32, _f32, _sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint64, ctypes.c_int,
                                    ctypes.c_float, ctypes.c_size_t)
 _SIGS = {
@@ -60,6 +69,8 @@ _SIGS = {
     "gc_version": ([], _i32),
     "gc_workspace_size": ([_i32, _i64, _i64, _i64, ctypes.POINTER(_sz)], _i32),
     "gc_ef_topk": ([_p, _p, _i64, _i64, _i64, _p, _p, _i32, _i64, _u64, _p, _p, _p, _sz, _p], _i32),
+    "gc_ef_compress": ([_p, _p, _i64, _i64, _i64, _p, _p, _i32, _i64, _u64, _p, _p, ctypes.POINTER(EfOptions),
+                        _p, _sz, _p], _i32),
     "gc_ef_topk_deferred": ([_p, _p, _i64, _i64, _i64, _p, _p, _i32, _i64, _u64, _p, _p, _p, _sz, _p, _sz, _p],
                             _i32),
     "gc_ef_flush": ([_p, _i64, _p, _sz, _p], _i32),
@@ -168,6 +179,34 @@ def ef_topk(grad, residual, k, index_base=0, *, qsgd_levels=0, qsgd_group=64, qs
     """
     return _sparsify("gc_ef_topk", OP_EF_TOPK, grad, residual, k, index_base, (), qsgd_levels, qsgd_group,
                      qsgd_seed, out_idx, out_val, out_codes, out_norms, want_values, workspace, stream)
+
+
+def ef_compress(grad, residual, k, index_base=0, *, select="topk", select_seed=0, pending=None, stats=None,
+                qsgd_levels=0, qsgd_group=64, qsgd_seed=0, out_idx=None, out_val=None, out_codes=None,
+                out_norms=None, want_values=True, workspace=None, stream=None):
+    """One EF sparsification step with every option (gc_ef_compress).
+
+    select: "topk" or "randk" (keys under ``select_seed``); pending: a record from
+    :func:`pending_record` to defer the kept set's residual (apply with the next call or
+    :func:`ef_flush`); stats: a float64 GPU tensor of 3 that receives the norm monitor
+    (sum c^2, sum g_hat^2, ratio).  Outputs as :func:`ef_topk`.
+    """
+    if select not in ("topk", "randk"):
+        raise ValueError("select must be 'topk' or 'randk'")
+    opts = EfOptions(size=ctypes.sizeof(EfOptions), select=SELECT_RANDK if select == "randk" else SELECT_TOPK,
+                     select_seed=select_seed)
+    if pending is not None:
+        _dev(pending, torch.uint8, "pending")
+        opts.pending, opts.pending_bytes = pending.data_ptr(), pending.numel()
+    if stats is not None:
+        _dev(stats, torch.float64, "stats")
+        if stats.numel() < 3:
+            raise ValueError("stats must hold 3 doubles")
+        opts.stats = stats.data_ptr()
+    op = OP_EF_RANDK if select == "randk" else OP_EF_TOPK
+    return _sparsify("gc_ef_compress", op, grad, residual, k, index_base, (), qsgd_levels, qsgd_group, qsgd_seed,
+                     out_idx, out_val, out_codes, out_norms, want_values, workspace, stream,
+                     tail=(ctypes.byref(opts),))
 
 
 def pending_record(n, k_max, device):

@@ -342,43 +342,77 @@ static int check_sparsify(const float* grad, float* residual, int64_t n, int64_t
   return ok();
 }
 
+static_assert(sizeof(gc_ef_options) == 40, "gc_ef_options layout");
+
+int gc_ef_compress(const float* grad, float* residual, int64_t n, int64_t k, int64_t index_base,
+                   int64_t* out_idx, float* out_val, int qsgd_levels, int64_t qsgd_group, uint64_t qsgd_seed,
+                   int8_t* out_codes, float* out_norms, const gc_ef_options* opts, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  gc_ef_options o{};
+  if (opts) {
+    GC_REQUIRE(opts->size >= sizeof(gc_ef_options), "opts->size must be sizeof(gc_ef_options)");
+    o = *opts;
+  }
+  GC_REQUIRE(o.select == GC_SELECT_TOPK || o.select == GC_SELECT_RANDK, "opts->select must be TOPK or RANDK");
+  const int c = check_sparsify(grad, residual, n, k, index_base, out_idx, out_val, qsgd_levels,
+                               qsgd_group, out_codes, out_norms);
+  if (c != GC_OK) return c;
+  GC_REQUIRE(!o.stats || k > 0, "the norm monitor needs k > 0");
+  GC_REQUIRE(!o.stats || aligned(o.stats, 8), "opts->stats must be 8-byte aligned");
+  if (n == 0) return ok();
+  if (o.pending) {
+    GC_REQUIRE(aligned(o.pending, 256), "opts->pending must be 256-byte aligned");
+    if (o.pending_bytes < gc::ef_pending_bytes(n, k))
+      return fail(GC_EWORKSPACE, "pending record of %zu bytes is smaller than the %zu this n and k need",
+                  o.pending_bytes, gc::ef_pending_bytes(n, k));
+  }
+  const bool randk = o.select == GC_SELECT_RANDK;
+  if (k > 0) {
+    const size_t need = randk ? gc::ef_randk_workspace(n, k, qsgd_levels) : gc::ef_topk_workspace(n, k, qsgd_levels);
+    const int w = check_workspace(workspace, workspace_bytes, need);
+    if (w != GC_OK) return w;
+  }
+  gc::EfArgs a{};
+  a.grad = grad; a.res = residual; a.n = n; a.k = k; a.index_base = index_base;
+  a.randk = randk; a.select_seed = o.select_seed;
+  a.out_idx = out_idx; a.out_val = out_val;
+  a.qsgd_levels = qsgd_levels; a.qsgd_group = qsgd_group; a.qsgd_seed = qsgd_seed;
+  a.out_codes = out_codes; a.out_norms = out_norms;
+  a.ws = workspace; a.pending = o.pending; a.pending_bytes = o.pending_bytes; a.stats = o.stats;
+  return hip_status(gc::launch_ef(a, reinterpret_cast<hipStream_t>(stream)), "gc_ef_compress launch");
+}
+
 int gc_ef_topk(const float* grad, float* residual, int64_t n, int64_t k, int64_t index_base,
                int64_t* out_idx, float* out_val, int qsgd_levels, int64_t qsgd_group,
                uint64_t qsgd_seed, int8_t* out_codes, float* out_norms, void* workspace,
                size_t workspace_bytes, void* stream) {
-  const int c = check_sparsify(grad, residual, n, k, index_base, out_idx, out_val, qsgd_levels,
-                               qsgd_group, out_codes, out_norms);
-  if (c != GC_OK || n == 0) return c;
-  if (k > 0) {
-    const int w = check_workspace(workspace, workspace_bytes, gc::ef_topk_workspace(n, k, qsgd_levels));
-    if (w != GC_OK) return w;
-  }
-  return hip_status(gc::launch_ef_topk(grad, residual, n, k, index_base, out_idx, out_val, qsgd_levels,
-                                       qsgd_group, qsgd_seed, out_codes, out_norms, workspace,
-                                       workspace_bytes, reinterpret_cast<hipStream_t>(stream)),
-                    "gc_ef_topk launch");
+  return gc_ef_compress(grad, residual, n, k, index_base, out_idx, out_val, qsgd_levels, qsgd_group, qsgd_seed,
+                        out_codes, out_norms, nullptr, workspace, workspace_bytes, stream);
 }
 
 int gc_ef_topk_deferred(const float* grad, float* residual, int64_t n, int64_t k, int64_t index_base,
                         int64_t* out_idx, float* out_val, int qsgd_levels, int64_t qsgd_group,
                         uint64_t qsgd_seed, int8_t* out_codes, float* out_norms, void* pending,
                         size_t pending_bytes, void* workspace, size_t workspace_bytes, void* stream) {
-  const int c = check_sparsify(grad, residual, n, k, index_base, out_idx, out_val, qsgd_levels,
-                               qsgd_group, out_codes, out_norms);
-  if (c != GC_OK || n == 0) return c;
-  GC_REQUIRE(pending && aligned(pending, 256), "pending must be non-NULL and 256-byte aligned");
-  if (pending_bytes < gc::ef_pending_bytes(n, k))
-    return fail(GC_EWORKSPACE, "pending record of %zu bytes is smaller than the %zu this n and k need",
-                pending_bytes, gc::ef_pending_bytes(n, k));
-  if (k > 0) {
-    const int w = check_workspace(workspace, workspace_bytes, gc::ef_topk_workspace(n, k, qsgd_levels));
-    if (w != GC_OK) return w;
-  }
-  return hip_status(gc::launch_ef_topk_deferred(grad, residual, n, k, index_base, out_idx, out_val,
-                                                qsgd_levels, qsgd_group, qsgd_seed, out_codes, out_norms,
-                                                pending, pending_bytes, workspace, workspace_bytes,
-                                                reinterpret_cast<hipStream_t>(stream)),
-                    "gc_ef_topk_deferred launch");
+  GC_REQUIRE(n == 0 || pending, "pending must be non-NULL");
+  gc_ef_options o{};
+  o.size = sizeof(o);
+  o.pending = pending;
+  o.pending_bytes = pending_bytes;
+  return gc_ef_compress(grad, residual, n, k, index_base, out_idx, out_val, qsgd_levels, qsgd_group, qsgd_seed,
+                        out_codes, out_norms, &o, workspace, workspace_bytes, stream);
+}
+
+int gc_ef_randk(const float* grad, float* residual, int64_t n, int64_t k, int64_t index_base,
+                uint64_t select_seed, int64_t* out_idx, float* out_val, int qsgd_levels,
+                int64_t qsgd_group, uint64_t qsgd_seed, int8_t* out_codes, float* out_norms,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  gc_ef_options o{};
+  o.size = sizeof(o);
+  o.select = GC_SELECT_RANDK;
+  o.select_seed = select_seed;
+  return gc_ef_compress(grad, residual, n, k, index_base, out_idx, out_val, qsgd_levels, qsgd_group, qsgd_seed,
+                        out_codes, out_norms, &o, workspace, workspace_bytes, stream);
 }
 
 int gc_ef_flush(float* residual, int64_t n, void* pending, size_t pending_bytes, void* stream) {
@@ -390,23 +424,6 @@ int gc_ef_flush(float* residual, int64_t n, void* pending, size_t pending_bytes,
     return fail(GC_EWORKSPACE, "pending record of %zu bytes is too small for n", pending_bytes);
   return hip_status(gc::launch_ef_flush(residual, n, pending, pending_bytes, reinterpret_cast<hipStream_t>(stream)),
                     "gc_ef_flush launch");
-}
-
-int gc_ef_randk(const float* grad, float* residual, int64_t n, int64_t k, int64_t index_base,
-                uint64_t select_seed, int64_t* out_idx, float* out_val, int qsgd_levels,
-                int64_t qsgd_group, uint64_t qsgd_seed, int8_t* out_codes, float* out_norms,
-                void* workspace, size_t workspace_bytes, void* stream) {
-  const int c = check_sparsify(grad, residual, n, k, index_base, out_idx, out_val, qsgd_levels,
-                               qsgd_group, out_codes, out_norms);
-  if (c != GC_OK || n == 0) return c;
-  if (k > 0) {
-    const int w = check_workspace(workspace, workspace_bytes, gc::ef_randk_workspace(n, k, qsgd_levels));
-    if (w != GC_OK) return w;
-  }
-  return hip_status(gc::launch_ef_randk(grad, residual, n, k, index_base, select_seed, out_idx, out_val,
-                                        qsgd_levels, qsgd_group, qsgd_seed, out_codes, out_norms, workspace,
-                                        workspace_bytes, reinterpret_cast<hipStream_t>(stream)),
-                    "gc_ef_randk launch");
 }
 
 int gc_quant_minmax(const float* x, float* residual, int64_t n, int64_t group, int bits,

@@ -163,6 +163,14 @@ __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
   return v;
 }
 
+// float64 sum across the wave by the xor butterfly (a fixed order; every lane ends with
+// the sum).
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
 #pragma unroll
   for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);

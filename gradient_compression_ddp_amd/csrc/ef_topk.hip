@@ -62,6 +62,8 @@ constexpr int kScanChunk = 1024;             // items per block in the multi-blo
 constexpr int kBins = 2048;
 constexpr int kUnit = 16;                    // tiles per unit of the candidate count and scan
 constexpr int kBatch = 128;                  // tiles per batch of the emit (8 units)
+constexpr int kKeptChunk = kBlock * 4;       // kept entries per norm-monitor partial
+constexpr int kSumChunk = 4096;              // partials per block of the monitor's second level
 static_assert(kBatch % kUnit == 0 && kBatch <= 2 * kWave && kUnit <= kWave, "batch tables");
 
 enum : uint32_t { MODE_CAND = 0, MODE_FULL = 1 };
@@ -98,7 +100,11 @@ struct Layout {
   unsigned long long* gt_excl;    // [max_chunks] exclusive prefixes
   unsigned long long* eq_excl;    // [max_chunks]
   float* staging;          // [k] kept values (QSGD mode without out_val)
-  int64_t ntiles, region_cap, pool, max_chunks, scan_blocks;
+  double* mon_c;           // [ntiles] norm monitor: sum of c^2 per tile
+  double* mon_g;           // [kchunks] sum of g_hat^2 per 1024 kept entries
+  double* mon_c2;          // [cdiv(ntiles, kSumChunk)] second level
+  double* mon_g2;          // [cdiv(kchunks, kSumChunk)]
+  int64_t ntiles, region_cap, pool, max_chunks, scan_blocks, kchunks;
   size_t bytes;
 };
 
@@ -156,6 +162,11 @@ Layout make_layout(void* base, int64_t n, int64_t k, bool staging, bool rand) {
   l.gt_excl = (unsigned long long*)take(sizeof(unsigned long long) * l.max_chunks);
   l.eq_excl = (unsigned long long*)take(sizeof(unsigned long long) * l.max_chunks);
   l.staging = staging ? (float*)take(sizeof(float) * (k > 0 ? k : 1)) : nullptr;
+  l.kchunks = cdiv(k > 0 ? k : 1, kKeptChunk);
+  l.mon_c = (double*)take(sizeof(double) * l.ntiles);
+  l.mon_g = (double*)take(sizeof(double) * l.kchunks);
+  l.mon_c2 = (double*)take(sizeof(double) * cdiv(l.ntiles, kSumChunk));
+  l.mon_g2 = (double*)take(sizeof(double) * cdiv(l.kchunks, kSumChunk));
   l.bytes = off;
   return l;
 }
@@ -522,7 +533,8 @@ __global__ __launch_bounds__(kBlock) void k_pick(TopkCtrl* __restrict__ ctrl, in
 // in pool_val and the value in pool_c.
 // DEFER: the previous call's recorded corrections of this tile are spread into LDS
 // while the loads are in flight and replace r at their positions before the add.
-template <bool RAND, bool DEFER>
+// MON: the tile's sum of c^2 in float64 (exact squares, fixed order) goes to mon_c.
+template <bool RAND, bool DEFER, bool MON>
 __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g, float* __restrict__ r,
                                                     int64_t n, TopkCtrl* __restrict__ ctrl,
                                                     uint32_t* __restrict__ tile_start,
@@ -531,8 +543,9 @@ __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g,
                                                     uint16_t* __restrict__ pool_off,
                                                     uint32_t region_cap, float* __restrict__ pool_c,
                                                     uint64_t seed, int64_t index_base, Pending pd,
-                                                    unsigned long long cap) {
+                                                    unsigned long long cap, double* __restrict__ mon_c) {
   __shared__ uint32_t s_cnt[kRounds * kWaves];
+  __shared__ double s_mon[MON ? kWaves : 1];
   __shared__ uint32_t s_off[kRounds * kWaves];
   __shared__ uint32_t s_total;
   __shared__ uint32_t s_base;
@@ -603,6 +616,15 @@ __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g,
       }
     }
   }
+  if (MON) {
+    double ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) ss += (double)c[j][m] * (double)c[j][m];
+    ss = wave_sum_f64(ss);
+    if (lane == 0) s_mon[w] = ss;
+  }
   uint32_t key[kRounds][4];
 #pragma unroll
   for (int j = 0; j < kRounds; ++j) {
@@ -649,6 +671,7 @@ __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g,
     tile_count[tile] = total;
     s_base = start;
     s_ok = ok;
+    if (MON) mon_c[tile] = ((s_mon[0] + s_mon[1]) + s_mon[2]) + s_mon[3];
   }
   __syncthreads();
   if (s_ok) {
@@ -1256,13 +1279,16 @@ __global__ __launch_bounds__(kBlock) void k_emit(const TopkCtrl* __restrict__ ct
 // residuals go through LDS so that the scattered stores are issued in kept order, 64
 // consecutive entries per wave store (neighbouring kept entries often share a sector).
 // DEFER: the residuals go to the record's values, in kept order, instead of r.
-template <bool DEFER>
+// MON: the sum of g_hat^2 of each 1024 kept entries (float64, fixed order) goes to mon_g.
+template <bool DEFER, bool MON>
 __global__ __launch_bounds__(kBlock) void k_qsgd_kept(const float* __restrict__ vals, int64_t k,
                                                       int lpg_log2, float s, uint64_t seed,
                                                       int8_t* __restrict__ codes, float* __restrict__ norms,
                                                       const int64_t* __restrict__ idx, int64_t index_base,
-                                                      float* __restrict__ r, int64_t n, Pending pd) {
+                                                      float* __restrict__ r, int64_t n, Pending pd,
+                                                      double* __restrict__ mon_g) {
   __shared__ float s_res[kBlock * 4];
+  __shared__ double s_mon[MON ? kWaves : 1];
   const int64_t nquads = (k + 3) >> 2;
   const int lpg = 1 << lpg_log2;
   const int lane = lane_id();
@@ -1283,6 +1309,7 @@ __global__ __launch_bounds__(kBlock) void k_qsgd_kept(const float* __restrict__ 
     float ss = quad_sumsq(v);
     ss = seg_tree_sum(ss, lpg);
     __syncthreads();   // s_res is still being read by the previous iteration's scatter
+    double gg = 0.0;
     if (live) {
       const float nu = sqrtf(ss);
       float u[4];
@@ -1300,8 +1327,17 @@ __global__ __launch_bounds__(kBlock) void k_qsgd_kept(const float* __restrict__ 
 #pragma unroll
       for (int m = 0; m < 4; ++m) s_res[threadIdx.x * 4 + m] = v[m] - gh[m];
       if ((lane & (lpg - 1)) == 0) norms[e0 >> (lpg_log2 + 2)] = nu;
+      if (MON) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) gg += (double)gh[m] * (double)gh[m];
+      }
+    }
+    if (MON) {
+      gg = wave_sum_f64(gg);
+      if (lane == 0) s_mon[threadIdx.x / kWave] = gg;
     }
     __syncthreads();
+    if (MON && threadIdx.x == 0) mon_g[base / kBlock] = ((s_mon[0] + s_mon[1]) + s_mon[2]) + s_mon[3];
     // entry base*4 + j sits at s_res[j]; entries at or beyond k were never kept
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -1315,6 +1351,58 @@ __global__ __launch_bounds__(kBlock) void k_qsgd_kept(const float* __restrict__ 
         }
       }
     }
+  }
+}
+
+// ---- norm monitor: float64 sums of squares in a fixed order --------------------------
+// Sum of v^2 over each kKeptChunk entries of v (the kept values of pure selection).
+__global__ __launch_bounds__(kBlock) void k_sq_chunks(const float* __restrict__ v, int64_t len,
+                                                      double* __restrict__ part) {
+  __shared__ double s[kWaves];
+  const int64_t e0 = (int64_t)blockIdx.x * kKeptChunk + threadIdx.x * 4;
+  double a = 0.0;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    if (e0 + m < len) a += (double)v[e0 + m] * (double)v[e0 + m];
+  a = wave_sum_f64(a);
+  if (lane_id() == 0) s[threadIdx.x / kWave] = a;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = ((s[0] + s[1]) + s[2]) + s[3];
+}
+
+// Block-level sum of up to kBlock * per consecutive doubles, each thread taking every
+// kBlock-th one in order; every thread gets the result.
+__device__ __forceinline__ double block_sum_f64(const double* __restrict__ in, int64_t count, double* s) {
+  double a = 0.0;
+  for (int64_t i = threadIdx.x; i < count; i += kBlock) a += in[i];
+  a = wave_sum_f64(a);
+  __syncthreads();
+  if (lane_id() == 0) s[threadIdx.x / kWave] = a;
+  __syncthreads();
+  return ((s[0] + s[1]) + s[2]) + s[3];
+}
+
+// Second level: out[b] = sum of in[b * kSumChunk, (b + 1) * kSumChunk).
+__global__ __launch_bounds__(kBlock) void k_sum_f64(const double* __restrict__ in, int64_t count,
+                                                    double* __restrict__ out) {
+  __shared__ double s[kWaves];
+  const int64_t b0 = (int64_t)blockIdx.x * kSumChunk;
+  const int64_t len = count - b0 < kSumChunk ? count - b0 : kSumChunk;
+  const double t = block_sum_f64(in + b0, len, s);
+  if (threadIdx.x == 0) out[blockIdx.x] = t;
+}
+
+// stats = {sum c^2, sum g_hat^2, sqrt(sum g_hat^2 / sum c^2)} (ratio 1 when c is zero).
+__global__ __launch_bounds__(kBlock) void k_mon_final(const double* __restrict__ c2, int64_t nc,
+                                                      const double* __restrict__ g2, int64_t ng,
+                                                      double* __restrict__ stats) {
+  __shared__ double s[kWaves];
+  const double sc = block_sum_f64(c2, nc, s);
+  const double sg = block_sum_f64(g2, ng, s);
+  if (threadIdx.x == 0) {
+    stats[0] = sc;
+    stats[1] = sg;
+    stats[2] = sc > 0.0 ? sqrt(sg / sc) : 1.0;
   }
 }
 
@@ -1367,8 +1455,9 @@ template <bool RAND, bool DEFER>
 hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, int64_t index_base,
                          uint64_t select_seed, int64_t* out_idx, float* out_val, int qsgd_levels,
                          int64_t qsgd_group, uint64_t qsgd_seed, int8_t* out_codes, float* out_norms,
-                         void* ws, void* pend, size_t pend_bytes, hipStream_t s) {
+                         void* ws, void* pend, size_t pend_bytes, double* stats, hipStream_t s) {
   if (n == 0) return hipSuccess;
+  const bool mon = stats != nullptr;
   const int cus = device_cu_count();
   const unsigned long long cap = DEFER ? pending_capacity(n, pend_bytes) : 0ull;
   const Pending pd = DEFER ? pending_layout(pend, n, (int64_t)cap) : Pending{};
@@ -1405,9 +1494,14 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
 
   // 3: the streaming pass
   prof_mark(s, 1);
-  hipLaunchKernelGGL((k_ef_cand<RAND, DEFER>), (unsigned)l.ntiles, kBlock, 0, s, grad, res, n, ctrl,
-                     l.tile_start, l.tile_count, l.pool_val, l.pool_off, (uint32_t)l.region_cap, l.pool_c,
-                     select_seed, index_base, pd, cap);
+  if (mon)
+    hipLaunchKernelGGL((k_ef_cand<RAND, DEFER, true>), (unsigned)l.ntiles, kBlock, 0, s, grad, res, n, ctrl,
+                       l.tile_start, l.tile_count, l.pool_val, l.pool_off, (uint32_t)l.region_cap, l.pool_c,
+                       select_seed, index_base, pd, cap, l.mon_c);
+  else
+    hipLaunchKernelGGL((k_ef_cand<RAND, DEFER, false>), (unsigned)l.ntiles, kBlock, 0, s, grad, res, n, ctrl,
+                       l.tile_start, l.tile_count, l.pool_val, l.pool_off, (uint32_t)l.region_cap, l.pool_c,
+                       select_seed, index_base, pd, cap, (double*)nullptr);
   prof_mark(s, 2);
 
   const int ugrid = clamp_grid(nunit, cus * 8);
@@ -1463,9 +1557,24 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
     int lpg_log2 = 0;
     while ((int64_t(4) << lpg_log2) < qsgd_group) ++lpg_log2;
     const int qgrid = clamp_grid(cdiv(cdiv(k, 4), kBlock), cus * 16);
-    hipLaunchKernelGGL(k_qsgd_kept<DEFER>, qgrid, kBlock, 0, s, (const float*)vals, k, lpg_log2,
-                       (float)qsgd_levels, qsgd_seed, out_codes, out_norms, (const int64_t*)out_idx, index_base,
-                       res, n, pd);
+    if (mon)
+      hipLaunchKernelGGL((k_qsgd_kept<DEFER, true>), qgrid, kBlock, 0, s, (const float*)vals, k, lpg_log2,
+                         (float)qsgd_levels, qsgd_seed, out_codes, out_norms, (const int64_t*)out_idx,
+                         index_base, res, n, pd, l.mon_g);
+    else
+      hipLaunchKernelGGL((k_qsgd_kept<DEFER, false>), qgrid, kBlock, 0, s, (const float*)vals, k, lpg_log2,
+                         (float)qsgd_levels, qsgd_seed, out_codes, out_norms, (const int64_t*)out_idx,
+                         index_base, res, n, pd, (double*)nullptr);
+  } else if (mon) {
+    // pure selection sends the kept values themselves
+    hipLaunchKernelGGL(k_sq_chunks, (unsigned)l.kchunks, kBlock, 0, s, (const float*)vals, k, l.mon_g);
+  }
+  if (mon) {
+    const int64_t nc2 = cdiv(l.ntiles, kSumChunk), ng2 = cdiv(l.kchunks, kSumChunk);
+    hipLaunchKernelGGL(k_sum_f64, (unsigned)nc2, kBlock, 0, s, (const double*)l.mon_c, l.ntiles, l.mon_c2);
+    hipLaunchKernelGGL(k_sum_f64, (unsigned)ng2, kBlock, 0, s, (const double*)l.mon_g, l.kchunks, l.mon_g2);
+    hipLaunchKernelGGL(k_mon_final, 1, kBlock, 0, s, (const double*)l.mon_c2, nc2, (const double*)l.mon_g2, ng2,
+                       stats);
   }
   if (DEFER) {
     // tile_first = exclusive scan of the per-tile kept counts; then the record is live
@@ -1498,24 +1607,19 @@ size_t ef_randk_workspace(int64_t n, int64_t k, int qsgd_levels) {
   return make_layout(nullptr, n, k, qsgd_levels > 0, true).bytes;
 }
 
-hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, int64_t index_base,
-                          int64_t* out_idx, float* out_val, int qsgd_levels, int64_t qsgd_group,
-                          uint64_t qsgd_seed, int8_t* out_codes, float* out_norms, void* ws,
-                          size_t, hipStream_t s) {
-  return launch_select<false, false>(grad, res, n, k, index_base, 0, out_idx, out_val, qsgd_levels,
-                                     qsgd_group, qsgd_seed, out_codes, out_norms, ws, nullptr, 0, s);
-}
-
 size_t ef_pending_bytes(int64_t n, int64_t kmax) { return pending_layout(nullptr, n, kmax).bytes; }
 
 unsigned long long ef_pending_capacity(int64_t n, size_t bytes) { return pending_capacity(n, bytes); }
 
-hipError_t launch_ef_topk_deferred(const float* grad, float* res, int64_t n, int64_t k, int64_t index_base,
-                                   int64_t* out_idx, float* out_val, int qsgd_levels, int64_t qsgd_group,
-                                   uint64_t qsgd_seed, int8_t* out_codes, float* out_norms, void* pend,
-                                   size_t pend_bytes, void* ws, size_t, hipStream_t s) {
-  return launch_select<false, true>(grad, res, n, k, index_base, 0, out_idx, out_val, qsgd_levels,
-                                    qsgd_group, qsgd_seed, out_codes, out_norms, ws, pend, pend_bytes, s);
+hipError_t launch_ef(const EfArgs& a, hipStream_t s) {
+  const bool defer = a.pending != nullptr;
+#define GC_EF_LAUNCH(R, D)                                                                         \
+  launch_select<R, D>(a.grad, a.res, a.n, a.k, a.index_base, a.select_seed, a.out_idx, a.out_val,  \
+                      a.qsgd_levels, a.qsgd_group, a.qsgd_seed, a.out_codes, a.out_norms, a.ws,     \
+                      a.pending, a.pending_bytes, a.stats, s)
+  if (a.randk) return defer ? GC_EF_LAUNCH(true, true) : GC_EF_LAUNCH(true, false);
+  return defer ? GC_EF_LAUNCH(false, true) : GC_EF_LAUNCH(false, false);
+#undef GC_EF_LAUNCH
 }
 
 hipError_t launch_ef_flush(float* res, int64_t n, void* pend, size_t pend_bytes, hipStream_t s) {
@@ -1523,14 +1627,6 @@ hipError_t launch_ef_flush(float* res, int64_t n, void* pend, size_t pend_bytes,
   const unsigned long long cap = pending_capacity(n, pend_bytes);
   launch_flush(res, n, pending_layout(pend, n, (int64_t)cap), cap, s);
   return hipGetLastError();
-}
-
-hipError_t launch_ef_randk(const float* grad, float* res, int64_t n, int64_t k, int64_t index_base,
-                           uint64_t select_seed, int64_t* out_idx, float* out_val, int qsgd_levels,
-                           int64_t qsgd_group, uint64_t qsgd_seed, int8_t* out_codes, float* out_norms,
-                           void* ws, size_t, hipStream_t s) {
-  return launch_select<true, false>(grad, res, n, k, index_base, select_seed, out_idx, out_val, qsgd_levels,
-                                    qsgd_group, qsgd_seed, out_codes, out_norms, ws, nullptr, 0, s);
 }
 
 }  // namespace gc

@@ -32,28 +32,31 @@ hipError_t launch_terngrad(const float* x, float* res, int nseg, const int64_t* 
                            uint64_t seed, int64_t index_base, uint8_t* packed, float* scales,
                            void* ws, hipStream_t s);
 
-// ---- EF Top-K ------------------------------------------------------------------
+// ---- EF Top-K / Random-K, direct or deferred residual, optional norm monitor -------
+struct EfArgs {
+  const float* grad;
+  float* res;
+  int64_t n, k, index_base;
+  bool randk;
+  uint64_t select_seed;
+  int64_t* out_idx;
+  float* out_val;
+  int qsgd_levels;
+  int64_t qsgd_group;
+  uint64_t qsgd_seed;
+  int8_t* out_codes;
+  float* out_norms;
+  void* ws;
+  void* pending;          // null: the kept set's residual is written by the call
+  size_t pending_bytes;
+  double* stats;          // null: no norm monitor
+};
 size_t ef_topk_workspace(int64_t n, int64_t k, int qsgd_levels);
-hipError_t launch_ef_topk(const float* grad, float* res, int64_t n, int64_t k, int64_t index_base,
-                          int64_t* out_idx, float* out_val, int qsgd_levels, int64_t qsgd_group,
-                          uint64_t qsgd_seed, int8_t* out_codes, float* out_norms, void* ws,
-                          size_t ws_bytes, hipStream_t s);
-
-// ---- EF Top-K with the kept set's residual deferred to the next call ---------------
+size_t ef_randk_workspace(int64_t n, int64_t k, int qsgd_levels);
 size_t ef_pending_bytes(int64_t n, int64_t kmax);
 unsigned long long ef_pending_capacity(int64_t n, size_t bytes);
-hipError_t launch_ef_topk_deferred(const float* grad, float* res, int64_t n, int64_t k, int64_t index_base,
-                                   int64_t* out_idx, float* out_val, int qsgd_levels, int64_t qsgd_group,
-                                   uint64_t qsgd_seed, int8_t* out_codes, float* out_norms, void* pend,
-                                   size_t pend_bytes, void* ws, size_t ws_bytes, hipStream_t s);
+hipError_t launch_ef(const EfArgs& a, hipStream_t s);
 hipError_t launch_ef_flush(float* res, int64_t n, void* pend, size_t pend_bytes, hipStream_t s);
-
-// ---- EF Random-K (the EF Top-K pipeline with index keys) ---------------------------
-size_t ef_randk_workspace(int64_t n, int64_t k, int qsgd_levels);
-hipError_t launch_ef_randk(const float* grad, float* res, int64_t n, int64_t k, int64_t index_base,
-                           uint64_t select_seed, int64_t* out_idx, float* out_val, int qsgd_levels,
-                           int64_t qsgd_group, uint64_t qsgd_seed, int8_t* out_codes, float* out_norms,
-                           void* ws, size_t ws_bytes, hipStream_t s);
 
 // ---- PowerSGD ------------------------------------------------------------------
 size_t powersgd_workspace(int64_t rows, int64_t cols, int rank);

@@ -127,6 +127,51 @@ int gc_ef_topk(const float* grad, float* residual, int64_t n, int64_t k, int64_t
                int8_t* out_codes, float* out_norms,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Selectors of gc_ef_options.select. */
+enum gc_select {
+  GC_SELECT_TOPK = 0,   /* the k largest magnitudes (gc_ef_topk)        */
+  GC_SELECT_RANDK = 1   /* the k largest Philox index keys (gc_ef_randk) */
+};
+
+/* Options of gc_ef_compress (a HOST struct; zero-fill it, then set `size`). */
+typedef struct gc_ef_options {
+  uint32_t size;          /* sizeof(gc_ef_options)                                       */
+  uint32_t select;        /* GC_SELECT_TOPK or GC_SELECT_RANDK                           */
+  uint64_t select_seed;   /* Random-K key seed (see gc_ef_randk)                         */
+  void* pending;          /* NULL: the kept set's residual is written by the call; else a
+                             pending record as in gc_ef_topk_deferred                      */
+  size_t pending_bytes;
+  double* stats;          /* NULL, or DEVICE double[3] receiving the norm monitor        */
+} gc_ef_options;
+
+/*
+ * gc_ef_compress -- one error-feedback sparsification step with every option: Top-K or
+ * Random-K selection, the kept set's residual written by the call or deferred to the
+ * next one, and the gradient-norm-ratio monitor.  gc_ef_topk, gc_ef_topk_deferred and
+ * gc_ef_randk are this call with the matching options.  opts == NULL selects Top-K,
+ * direct residual, no monitor.
+ *
+ * Norm monitor ([P1] section 3.2 item 2: watch the ratio of the gradient norm after
+ * compression to the norm before it; a ratio that stays below 0.9 means the compression
+ * is too strong).  With opts->stats set (k > 0 required), the call writes
+ *   stats[0] = sum over all n of c^2           (c = fl(grad + residual), what is compressed)
+ *   stats[1] = sum over the kept set of g_hat^2 (the decoded payload: the kept values, or
+ *              their QSGD reconstruction fl(nu*level)/s with QSGD)
+ *   stats[2] = sqrt(stats[1] / stats[0])        (1 when stats[0] == 0)
+ * The squares are exact float64 products of the float32 values; the sums are float64 in
+ * a fixed order (per 4096-element tile inside the streaming pass, per 1024 kept entries,
+ * then two fixed-shape reduction levels), so the result is deterministic and within the
+ * float64 rounding of the exact sums.  The monitor adds no pass over the gradient.
+ *
+ * Workspace: gc_workspace_size(GC_OP_EF_TOPK or GC_OP_EF_RANDK, n, k, qsgd_levels).
+ * Everything else as gc_ef_topk.
+ */
+int gc_ef_compress(const float* grad, float* residual, int64_t n, int64_t k, int64_t index_base,
+                   int64_t* out_idx, float* out_val,
+                   int qsgd_levels, int64_t qsgd_group, uint64_t qsgd_seed,
+                   int8_t* out_codes, float* out_norms, const gc_ef_options* opts,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * gc_ef_topk_deferred -- gc_ef_topk with the residual update of the kept set deferred to
  * the next call on the same residual.

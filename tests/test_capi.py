@@ -130,6 +130,29 @@ def test_deferred_calls_reject_bad_arguments(lib):
     assert fl(None, 0, None, 0, None) == 0
 
 
+def test_ef_compress_rejects_bad_options(lib):
+    import gradient_compression_ddp_amd as gcm
+    f = lib.gc_ef_compress
+    f.argtypes = [VP, VP, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, VP, VP, ctypes.c_int, ctypes.c_int64,
+                  ctypes.c_uint64, VP, VP, ctypes.POINTER(gcm.EfOptions), VP, ctypes.c_size_t, VP]
+    assert ctypes.sizeof(gcm.EfOptions) == 40
+    args = (FAKE, FAKE, 100_000, 1000, 0, FAKE, FAKE, 0, 64, 0, None, None)
+    o = gcm.EfOptions(size=ctypes.sizeof(gcm.EfOptions), select=2)
+    assert f(*args, ctypes.byref(o), FAKE, 1 << 30, None) == 1                     # unknown selector
+    o = gcm.EfOptions(size=8)
+    assert f(*args, ctypes.byref(o), FAKE, 1 << 30, None) == 1                     # struct too small
+    o = gcm.EfOptions(size=ctypes.sizeof(gcm.EfOptions), stats=0x100004)
+    assert f(*args, ctypes.byref(o), FAKE, 1 << 30, None) == 1                     # misaligned stats
+    o = gcm.EfOptions(size=ctypes.sizeof(gcm.EfOptions), stats=0x100000)
+    assert f(FAKE, FAKE, 100_000, 0, 0, FAKE, FAKE, 0, 64, 0, None, None, ctypes.byref(o), None, 0, None) == 1
+    assert b"k > 0" in lib.gc_last_error()
+    o = gcm.EfOptions(size=ctypes.sizeof(gcm.EfOptions), select=1)
+    need_t = _ws(lib, 1, 100_000, 1000, 0)[1]
+    assert f(*args, ctypes.byref(o), FAKE, need_t, None) == 2                      # Random-K needs more
+    o = gcm.EfOptions(size=ctypes.sizeof(gcm.EfOptions), pending=0x200000, pending_bytes=64)
+    assert f(*args, ctypes.byref(o), FAKE, 1 << 30, None) == 2                     # record too small
+
+
 def test_other_calls_reject_bad_arguments(lib):
     q = lib.gc_quant_minmax
     q.argtypes = [VP, VP, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, VP, VP, VP, VP, ctypes.c_size_t, VP]
