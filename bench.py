@@ -209,6 +209,58 @@ def _row(name, workload, unit_bytes, unit, gpu_ms, eager_ms, oracle_s=None, orac
     print(json.dumps(line), flush=True)
 
 
+def ddp_hook_row(torch, gc, dev, say):
+    import socket
+    import torch.distributed as dist
+    from torch.nn.parallel import DistributedDataParallel as DDP
+    from gradient_compression_ddp_amd.ddp_hook import CompressionHookState, ef_compress_hook
+    say("DDP hook, world size 1")
+    with socket.socket() as sk:
+        sk.bind(("127.0.0.1", 0))
+        port = sk.getsockname()[1]
+    dist.init_process_group("nccl", init_method=f"tcp://127.0.0.1:{port}", rank=0, world_size=1)
+    try:
+        def build(hook):
+            torch.manual_seed(0)
+            layers = []
+            for _ in range(6):
+                layers += [torch.nn.Linear(4096, 4096), torch.nn.ReLU()]
+            m = DDP(torch.nn.Sequential(*layers).to(dev), device_ids=[0], bucket_cap_mb=25,
+                    gradient_as_bucket_view=True)
+            state = None
+            if hook:
+                state = CompressionHookState(ratio=0.01, qsgd_levels=127, deferred=True)
+                m.register_comm_hook(state, ef_compress_hook)
+            return m, state
+
+        x = torch.randn(64, 4096, device=dev)
+
+        def it_ms(m):
+            def f():
+                m.zero_grad(set_to_none=False)
+                m(x).square().mean().backward()
+            return _eager_ms(torch, f, reps=20)
+        m0, _ = build(False)
+        base = it_ms(m0)
+        del m0
+        m1, state = build(True)
+        hooked = it_ms(m1)
+        n = sum(p.numel() for p in m1.parameters())
+        nb = len(state.buckets)
+        k = sum(b.k for b in state.buckets.values())
+        del m1, state
+    finally:
+        dist.destroy_process_group()
+    # per iteration: the EF pass (12 B per element, + the record), the kept set's outputs,
+    # and the receive (payload read, 4 B per element written)
+    ub = 12.0 * n + k * (8.0 + 1.0 + 4.0 / 64 + 4.0 + 4.0 + 16.0) + 4.0 * n + k * (8.0 + 1.0 + 4.0 / 64)
+    extra = max(hooked - base, 1e-6)
+    _row("next-4 DDP comm hook, world size 1 (EF Top-1% + QSGD-127, deferred)",
+         f"6 x Linear(4096, 4096), {n:,} parameters in {nb} buckets of <= 25 MiB, batch 64", ub,
+         "iteration (time over DDP's own hook)", extra, extra,
+         extra={"iteration_ms_allreduce_hook": round(base, 4), "iteration_ms_compression_hook": round(hooked, 4)})
+
+
 def rows_mode(args):
     import numpy as np
     import torch
@@ -417,6 +469,12 @@ def rows_mode(args):
         _row(name, "n=1e9 (32 layers x 31,250,000, t(3) x lognormal scales), k=1e7", ub, "call", gms, eager, osec,
              ns_o / nr, "the first 2^24 elements, k = 1% of them", extra=extra)
     del gr, rr, oir, ocr, onr, wsr, pend, st
+
+    # next-4: the DDP communication hook at world size 1 (NCCL on this GPU): forward and
+    # backward of a 6 x Linear(4096, 4096) model (100.7M parameters, 16 buckets of 25 MiB)
+    # with DDP's own all-reduce hook and with the compression hook (deferred EF Top-1% +
+    # QSGD-127, all_gather of the payloads, receive).
+    ddp_hook_row(torch, gc, dev, say)
 
     # c3: TernGrad over 24 layers of 14,583,333 (~350M parameters), one segmented call.
     say("TernGrad 24 layers")

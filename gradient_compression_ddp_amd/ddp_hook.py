@@ -1,0 +1,137 @@
+"""DDP communication hook: error-feedback Top-K (or Random-K) + QSGD on every gradient bucket.
+
+Sources: hotdry.top "gradient-compression-quantization-sparsification", section 3.2
+(compress inside the framework's communication step, before the gradient leaves GPU
+memory, overlapped with the backward pass); aiqz.cc "梯度聚合通信优化实战方案", section
+"通信计算重叠" (gradient buckets: each bucket is sent as soon as the backward pass has
+filled it) and "通信瓶颈分析" (the aggregate is the average over workers);
+zyxy.net/archives/25733, section 四 (compress, exchange, decompress before the update).
+
+Per bucket and step, on the stream DDP runs the hook on:
+  1. gc_ef_compress: c = bucket + residual, exact Top-k (or Random-k) of c, QSGD of the
+     kept values, written straight into this rank's payload (the 128-byte header and the
+     idx / codes / norms sections of the wire format), the kept set's residual deferred
+     to the bucket's next step by default;
+  2. all_gather of the fixed-size payloads (every rank's k and layout are equal);
+  3. gc_decompress_payloads: the bucket becomes the average of the W decoded payloads.
+The library's calls are asynchronous on the current stream, and step 3 runs as the
+continuation of the all_gather future, so the whole hook overlaps the rest of the
+backward pass the way DDP's own all-reduce does.
+
+State per bucket (keyed by DDP's bucket index and size; DDP may regroup buckets after its
+first iteration, and a bucket whose size changes starts from a zero residual): residual,
+pending record, workspace, this rank's payload and the gathered payloads.
+"""
+# No postponed annotations here: DDP checks the hook's annotations at run time.
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Tuple
+
+import torch
+import torch.distributed as dist
+
+from . import (KIND_F32, KIND_QSGD, OP_EF_RANDK, OP_EF_TOPK, decompress_payloads, ef_compress, ef_flush,
+               payload_layout, payload_sections, pending_record, workspace_size, write_payload_header)
+
+
+def _align256(b: int) -> int:
+    return (b + 255) & ~255
+
+
+@dataclass
+class _Bucket:
+    n: int
+    k: int
+    header: object
+    residual: torch.Tensor
+    pending: Optional[torch.Tensor]
+    workspace: torch.Tensor
+    payload: torch.Tensor
+    gathered: torch.Tensor
+    stride: int
+    stats: Optional[torch.Tensor]
+    calls: int = 0
+
+
+@dataclass
+class CompressionHookState:
+    """Options and per-bucket state of :func:`ef_compress_hook`."""
+    process_group: Optional[dist.ProcessGroup] = None
+    ratio: float = 0.01               # kept fraction k / n of every bucket
+    qsgd_levels: int = 127            # 8-bit codes (sign + 7-bit level); 0 sends fp32 values
+    qsgd_group: int = 64
+    select: str = "topk"              # or "randk"
+    deferred: bool = True             # kept-set residual applied by the bucket's next step
+    monitor: bool = False             # keep the norm-ratio stats of every bucket
+    seed: int = 0
+    buckets: Dict[int, _Bucket] = field(default_factory=dict)
+    # tests: when a list, (bucket index, step, bucket before, bucket after) is appended
+    capture: Optional[List[Tuple[int, int, torch.Tensor, torch.Tensor]]] = None
+
+    def seeds(self, index: int, step: int) -> Tuple[int, int]:
+        """(selection seed, QSGD seed) of a bucket's step; equal on every rank."""
+        base = (self.seed * 1_000_003 + index) * 1_000_033 + step
+        return base * 2 + 1, base * 2
+
+    def k_for(self, n: int) -> int:
+        return max(1, min(n, int(n * self.ratio)))
+
+    def bucket(self, index: int, n: int, device) -> _Bucket:
+        b = self.buckets.get(index)
+        if b is not None and b.n == n:
+            return b
+        W = dist.get_world_size(self.process_group)
+        k = self.k_for(n)
+        if self.qsgd_levels > 0:
+            h = payload_layout(KIND_QSGD, n, k, self.qsgd_group, self.qsgd_levels, sparse=True)
+        else:
+            h = payload_layout(KIND_F32, n, k, sparse=True)
+        stride = _align256(h.bytes)
+        payload = torch.zeros(stride, dtype=torch.uint8, device=device)
+        write_payload_header(payload, h)
+        op = OP_EF_RANDK if self.select == "randk" else OP_EF_TOPK
+        ws = torch.empty(max(workspace_size(op, n, k, self.qsgd_levels), 1), dtype=torch.uint8, device=device)
+        b = _Bucket(n=n, k=k, header=h, residual=torch.zeros(n, dtype=torch.float32, device=device),
+                    pending=pending_record(n, k, device) if self.deferred else None, workspace=ws,
+                    payload=payload, gathered=torch.empty(W * stride, dtype=torch.uint8, device=device),
+                    stride=stride,
+                    stats=torch.zeros(3, dtype=torch.float64, device=device) if self.monitor else None)
+        self.buckets[index] = b
+        return b
+
+    def flush(self) -> None:
+        """Apply every bucket's pending record, so each residual is exact (e.g. before a
+        checkpoint of the residuals)."""
+        for b in self.buckets.values():
+            if b.pending is not None:
+                ef_flush(b.residual, b.pending)
+
+
+def ef_compress_hook(state: CompressionHookState, bucket: dist.GradBucket) -> torch.futures.Future[torch.Tensor]:
+    buf = bucket.buffer()
+    if buf.dtype != torch.float32:
+        raise TypeError("the compression hook handles float32 gradient buckets")
+    index = bucket.index()
+    b = state.bucket(index, buf.numel(), buf.device)
+    step = b.calls
+    b.calls += 1
+    before = buf.clone() if state.capture is not None else None
+    sel_seed, q_seed = state.seeds(index, step)
+    sec = payload_sections(b.payload, b.header)
+    if state.qsgd_levels > 0:
+        outs = dict(out_codes=sec["codes"], out_norms=sec["meta0"], want_values=False)
+    else:
+        outs = dict(out_val=sec["codes"])
+    ef_compress(buf, b.residual, b.k, select=state.select, select_seed=sel_seed, pending=b.pending, stats=b.stats,
+                qsgd_levels=state.qsgd_levels, qsgd_group=state.qsgd_group, qsgd_seed=q_seed,
+                out_idx=sec["idx"], workspace=b.workspace, **outs)
+    W = dist.get_world_size(state.process_group)
+    work = dist.all_gather_into_tensor(b.gathered, b.payload, group=state.process_group, async_op=True)
+
+    def decode(fut):
+        views = [b.gathered[w * b.stride:(w + 1) * b.stride] for w in range(W)]
+        decompress_payloads(views, [b.header] * W, buf)
+        if state.capture is not None:
+            state.capture.append((index, step, before, buf.clone()))
+        return buf
+
+    return work.get_future().then(decode)
