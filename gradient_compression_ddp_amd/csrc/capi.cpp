@@ -356,10 +356,9 @@ int gc_ef_compress(const float* grad, float* residual, int64_t n, int64_t k, int
   GC_REQUIRE(o.select == GC_SELECT_TOPK || o.select == GC_SELECT_RANDK, "opts->select must be TOPK or RANDK");
   const int c = check_sparsify(grad, residual, n, k, index_base, out_idx, out_val, qsgd_levels,
                                qsgd_group, out_codes, out_norms);
-  if (c != GC_OK) return c;
+  if (c != GC_OK || n == 0) return c;
   GC_REQUIRE(!o.stats || k > 0, "the norm monitor needs k > 0");
   GC_REQUIRE(!o.stats || aligned(o.stats, 8), "opts->stats must be 8-byte aligned");
-  if (n == 0) return ok();
   if (o.pending) {
     GC_REQUIRE(aligned(o.pending, 256), "opts->pending must be 256-byte aligned");
     if (o.pending_bytes < gc::ef_pending_bytes(n, k))

@@ -62,9 +62,11 @@ constexpr int kScanChunk = 1024;             // items per block in the multi-blo
 constexpr int kBins = 2048;
 constexpr int kUnit = 16;                    // tiles per unit of the candidate count and scan
 constexpr int kBatch = 128;                  // tiles per batch of the emit (8 units)
+constexpr int kBatchSmall = kUnit;           // the emit's batch when 128-tile batches are too few
 constexpr int kKeptChunk = kBlock * 4;       // kept entries per norm-monitor partial
 constexpr int kSumChunk = 4096;              // partials per block of the monitor's second level
 static_assert(kBatch % kUnit == 0 && kBatch <= 2 * kWave && kUnit <= kWave, "batch tables");
+static_assert(kBatchSmall % kUnit == 0 && kBatchSmall <= kWave, "small batch tables");
 
 enum : uint32_t { MODE_CAND = 0, MODE_FULL = 1 };
 
@@ -113,8 +115,14 @@ __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 
 // Sample size and the sample rank whose key is taken as the candidate bound L.
 // The rank sits 2% above the expected sample rank plus 8 standard deviations, so the
 // candidates hold the k largest unless the sample is off by far more than sampling error.
-// A sample of the whole input gives the exact k-th key.
-int64_t sample_size(int64_t n) { return n < kSampleMax ? n : kSampleMax; }
+// Up to 2^20 elements the sample is the whole input, which gives the exact k-th key.
+// Above, one element in 64 is drawn, between 2^18 and 2^20: the draw costs two random
+// sectors per point, which a call on a 25 MB bucket would otherwise spend mostly here.
+int64_t sample_size(int64_t n) {
+  if (n <= kSampleMax) return n;
+  const int64_t m = n >> 6;
+  return m < (kSampleMax >> 2) ? (kSampleMax >> 2) : (m > kSampleMax ? kSampleMax : m);
+}
 int64_t sample_rank(int64_t n, int64_t k) {
   const int64_t m = sample_size(n);
   if (m == n) return k;
@@ -413,6 +421,47 @@ __device__ __forceinline__ void hist_span(const float* __restrict__ src, int64_t
     hist_add(my, r, mag_key(src[(nq << 2) + threadIdx.x]), hshift, want, shift, mask);
 }
 
+// Histogram of the candidate pool with its 32 regions taken as one sequence of quads:
+// s_rq[r] is the number of whole quads in regions below r, so every thread issues all of
+// its loads at once however the candidates are spread over the regions.  The 0-3
+// trailing candidates of region r are counted by block r % gridDim.x.
+__device__ __forceinline__ void hist_pool(const float* __restrict__ pool, int64_t region_cap,
+                                          const uint32_t* __restrict__ region_fill, const uint32_t* s_rq,
+                                          int64_t first, int64_t stride, uint32_t* my, BinRun& r,
+                                          uint32_t hshift, uint32_t want, int shift, uint32_t mask) {
+  constexpr int kAhead = 4;
+  const int64_t total = s_rq[kRegions];
+  for (int64_t q = first; q < total; q += kAhead * stride) {
+    f32x4 v[kAhead];
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+      const int64_t qq = q + u * stride;
+      if (qq < total) {
+        int rg = 0;   // the region holding quad qq: the largest rg with s_rq[rg] <= qq
+#pragma unroll
+        for (int st = kRegions / 2; st > 0; st >>= 1)
+          if ((int64_t)s_rq[rg + st] <= qq) rg += st;
+        v[u] = *reinterpret_cast<const f32x4*>(pool + rg * region_cap + ((qq - s_rq[rg]) << 2));
+      } else {
+        v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kAhead; ++u) {
+      if (q + u * stride >= total) break;
+      hist_add(my, r, mag_key(v[u].x), hshift, want, shift, mask);
+      hist_add(my, r, mag_key(v[u].y), hshift, want, shift, mask);
+      hist_add(my, r, mag_key(v[u].z), hshift, want, shift, mask);
+      hist_add(my, r, mag_key(v[u].w), hshift, want, shift, mask);
+    }
+  }
+  for (int rg = blockIdx.x; rg < kRegions; rg += gridDim.x) {
+    const uint32_t fill = region_fill[rg];
+    if (threadIdx.x < (fill & 3u))
+      hist_add(my, r, mag_key(pool[rg * region_cap + (fill & ~3u) + threadIdx.x]), hshift, want, shift, mask);
+  }
+}
+
 // Random-K keys of the n elements, quad by quad (the fallback's full source).
 __device__ __forceinline__ void hist_rand(int64_t n, uint64_t seed, int64_t index_base, int64_t first,
                                           int64_t stride, bool tail_owner, uint32_t* my, BinRun& r,
@@ -441,7 +490,20 @@ __global__ __launch_bounds__(kBlock) void k_hist(TopkCtrl* __restrict__ ctrl,
                                                  int64_t n, int shift, int bits, uint64_t seed,
                                                  int64_t index_base) {
   __shared__ uint32_t lh[kWaves][kBins];
+  __shared__ uint32_t s_rq[kRegions + 1];
   for (int i = threadIdx.x; i < kWaves * kBins; i += kBlock) (&lh[0][0])[i] = 0u;
+  if (SRC != 0 && threadIdx.x < kWave) {
+    // exclusive prefix of the regions' whole-quad counts (candidate mode only reads it)
+    const uint32_t c = threadIdx.x < kRegions ? ctrl->region_fill[threadIdx.x] >> 2 : 0u;
+    uint32_t inc = c;
+#pragma unroll
+    for (int d = 1; d < kRegions; d <<= 1) {
+      const uint32_t o = (uint32_t)__shfl_up((int)inc, d, kWave);
+      if (threadIdx.x >= d) inc += o;
+    }
+    if (threadIdx.x < kRegions) s_rq[threadIdx.x] = inc - c;
+    if (threadIdx.x == kRegions - 1) s_rq[kRegions] = inc;
+  }
   __syncthreads();
   const uint32_t hshift = (uint32_t)(shift + bits);
   const uint32_t want = ctrl->prefix >> hshift;
@@ -453,9 +515,7 @@ __global__ __launch_bounds__(kBlock) void k_hist(TopkCtrl* __restrict__ ctrl,
   if (SRC == 0) {
     for (int64_t i = first; i < sample_n; i += stride) hist_add(my, run, sample_keys[i], hshift, want, shift, mask);
   } else if (ctrl->mode == MODE_CAND) {
-    for (int rg = 0; rg < kRegions; ++rg)
-      hist_span(pool + rg * region_cap, (int64_t)ctrl->region_fill[rg], first, stride,
-                blockIdx.x == (unsigned)(rg % gridDim.x), my, run, hshift, want, shift, mask);
+    hist_pool(pool, region_cap, ctrl->region_fill, s_rq, first, stride, my, run, hshift, want, shift, mask);
   } else if (SRC == 1) {
     hist_span(full, n, first, stride, blockIdx.x == 0, my, run, hshift, want, shift, mask);
   } else {
@@ -823,27 +883,39 @@ __global__ __launch_bounds__(kBlock) void k_scan_down(const uint32_t* __restrict
 
 
 // One-block exclusive scan of one or two uint32 count arrays (small counts only; b and
-// ob may be null).
+// ob may be null).  A thread takes four consecutive items per round of 1024.
 __global__ __launch_bounds__(kBlock) void k_scan_small(const uint32_t* __restrict__ a,
                                                        const uint32_t* __restrict__ b, int64_t count,
                                                        unsigned long long* __restrict__ oa,
                                                        unsigned long long* __restrict__ ob) {
+  constexpr int kPer = 4;
   __shared__ unsigned long long s_w[2][kWaves];
   unsigned long long ca = 0, cb = 0;
   const int w = threadIdx.x / kWave;
-  for (int64_t r0 = 0; r0 < count; r0 += kBlock) {
-    const int64_t it = r0 + threadIdx.x;
-    const unsigned long long va = it < count ? a[it] : 0ull;
-    const unsigned long long vb = (b && it < count) ? b[it] : 0ull;
-    const unsigned long long ia = wave_incl_scan_u64(va);
-    const unsigned long long ib = wave_incl_scan_u64(vb);
+  for (int64_t r0 = 0; r0 < count; r0 += (int64_t)kBlock * kPer) {
+    const int64_t i0 = r0 + (int64_t)threadIdx.x * kPer;
+    unsigned long long va[kPer], vb[kPer], ta = 0, tb = 0;
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      va[m] = i0 + m < count ? a[i0 + m] : 0ull;
+      vb[m] = (b && i0 + m < count) ? b[i0 + m] : 0ull;
+      ta += va[m];
+      tb += vb[m];
+    }
+    const unsigned long long ia = wave_incl_scan_u64(ta);
+    const unsigned long long ib = wave_incl_scan_u64(tb);
     if (lane_id() == kWave - 1) { s_w[0][w] = ia; s_w[1][w] = ib; }
     __syncthreads();
-    unsigned long long pa = ca, pb = cb;
+    unsigned long long pa = ca + ia - ta, pb = cb + ib - tb;
     for (int i = 0; i < w; ++i) { pa += s_w[0][i]; pb += s_w[1][i]; }
-    if (it < count) {
-      oa[it] = pa + ia - va;
-      if (ob) ob[it] = pb + ib - vb;
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      if (i0 + m < count) {
+        oa[i0 + m] = pa;
+        if (ob) ob[i0 + m] = pb;
+      }
+      pa += va[m];
+      pb += vb[m];
     }
     ca += s_w[0][0] + s_w[0][1] + s_w[0][2] + s_w[0][3];
     cb += s_w[1][0] + s_w[1][1] + s_w[1][2] + s_w[1][3];
@@ -1015,7 +1087,8 @@ __device__ __forceinline__ void small_scan(const uint32_t* s_cnt, uint32_t* s_of
 // RAND: the pool holds key bits, and the kept value is read from pool_c.
 // DEFER: instead of writing the kept residual, record each kept entry's tile offset at
 // its kept position and count the kept entries of every tile.
-template <bool RAND, bool DEFER>
+// KB: tiles per batch (kBatch, or kBatchSmall when there are fewer batches than CUs).
+template <bool RAND, bool DEFER, int KB>
 __global__ __launch_bounds__(kBlock) void k_bemit(TopkCtrl* __restrict__ ctrl, int64_t ntiles,
                                                   const uint32_t* __restrict__ tile_start,
                                                   const uint32_t* __restrict__ tile_count,
@@ -1027,25 +1100,25 @@ __global__ __launch_bounds__(kBlock) void k_bemit(TopkCtrl* __restrict__ ctrl, i
                                                   int64_t* __restrict__ out_idx, float* __restrict__ out_val,
                                                   int zero_residual, int64_t k,
                                                   const float* __restrict__ pool_c, Pending pd) {
-  __shared__ BatchTable<kBatch> bt;
+  __shared__ BatchTable<KB> bt;
   __shared__ uint32_t s_cnt[kEmitU * kWaves];
   __shared__ uint32_t s_off[kEmitU * kWaves];
   __shared__ uint32_t s_total;
   __shared__ int64_t s_b;
-  __shared__ uint32_t s_kc[DEFER ? kBatch : 1];
+  __shared__ uint32_t s_kc[DEFER ? KB : 1];
   if (ctrl->mode != MODE_CAND) return;
   const uint32_t T = ctrl->T;
   const unsigned long long need = ctrl->need;
   const int w = threadIdx.x / kWave;
   const int lane = lane_id();
-  const int64_t nbatch = cdiv(ntiles, kBatch);
+  const int64_t nbatch = cdiv(ntiles, KB);
   for (int64_t b; (b = next_batch(ctrl, nbatch, &s_b)) >= 0;) {
-    const int64_t t0 = b * kBatch;
-    const int nt = (int)(ntiles - t0 < kBatch ? ntiles - t0 : kBatch);
-    if (DEFER && threadIdx.x < kBatch) s_kc[threadIdx.x] = 0u;   // visible after load_batch's barrier
+    const int64_t t0 = b * KB;
+    const int nt = (int)(ntiles - t0 < KB ? ntiles - t0 : KB);
+    if (DEFER && threadIdx.x < KB) s_kc[threadIdx.x] = 0u;   // visible after load_batch's barrier
     const uint32_t total = load_batch(bt, t0, nt, tile_start, tile_count);
     // the exclusive prefixes of the batch's first unit
-    unsigned long long gt_run = gt_excl[b * (kBatch / kUnit)], eq_run = eq_excl[b * (kBatch / kUnit)];
+    unsigned long long gt_run = gt_excl[b * (KB / kUnit)], eq_run = eq_excl[b * (KB / kUnit)];
     for (uint32_t j0 = 0; j0 < total; j0 += kBlock * kEmitU) {
       uint32_t src[kEmitU];
       int64_t tbase[kEmitU];
@@ -1055,7 +1128,7 @@ __global__ __launch_bounds__(kBlock) void k_bemit(TopkCtrl* __restrict__ ctrl, i
       for (int u = 0; u < kEmitU; ++u) {
         const uint32_t j = j0 + u * kBlock + threadIdx.x;
         live[u] = j < total;
-        const int lo = live[u] ? batch_tile<kBatch>(bt, j) : 0;
+        const int lo = live[u] ? batch_tile<KB>(bt, j) : 0;
         src[u] = bt.start[lo] + (j - bt.pre[lo]);
         tbase[u] = (t0 + lo) * kTile;
         tlo[u] = lo;
@@ -1481,10 +1554,15 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
   const int64_t nunit = cdiv(l.ntiles, kUnit);
   const int64_t nbatch = cdiv(l.ntiles, kBatch);
   hipLaunchKernelGGL(k_init, 1, 256, 0, s, ctrl, (unsigned long long)j, (unsigned long long)nunit);
-  hipLaunchKernelGGL((k_sample<RAND, DEFER>), clamp_grid(cdiv(m, 256), cus * 8), 256, 0, s, grad, res, n, m,
+  hipLaunchKernelGGL((k_sample<RAND, DEFER>), clamp_grid(cdiv(m, 256), cus * 16), 256, 0, s, grad, res, n, m,
                      l.sample, select_seed, index_base, pd, cap);
   const int shifts[3] = {20, 9, 0}, widths[3] = {11, 11, 9};
-  const int sgrid = clamp_grid(cdiv(m, 256 * 8), cus * 2);
+  // pool histogram grid: each block clears and flushes a 2048-bin LDS histogram, so a
+  // block takes at least 16384 of the candidates the pool is expected to hold
+  const int sgrid = clamp_grid(cdiv(m, 2048), cus * 2);
+  const int64_t expect_cand = (int64_t)((double)j * (double)n / (double)m);
+  int hgrid = clamp_grid(cdiv(expect_cand, 16384), cus * 4);
+  if (hgrid < 32) hgrid = 32;
   for (int p = 0; p < 3; ++p) {
     hipLaunchKernelGGL((k_hist<0>), sgrid, kBlock, 0, s, ctrl, l.sample, m, (const float*)nullptr,
                        (int64_t)0, (const float*)nullptr, n, shifts[p], widths[p], (uint64_t)0, (int64_t)0);
@@ -1505,7 +1583,9 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
   prof_mark(s, 2);
 
   const int ugrid = clamp_grid(nunit, cus * 8);
-  const int bgrid = clamp_grid(nbatch, cus * 8);
+  // fewer 128-tile batches than CUs: batches of one unit keep the emit spread out
+  const bool small_batches = nbatch < cus;
+  const int bgrid = clamp_grid(small_batches ? nunit : nbatch, cus * 8);
   const int cgrid = clamp_grid(l.ntiles, cus * 8);
   if (exact) {
     // T and need are known and the pool holds every candidate: count, one-block scan
@@ -1518,7 +1598,6 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
     hipLaunchKernelGGL(k_decide, 1, 64, 0, s, ctrl, l.ntiles, (unsigned long long)k);
 
     // 5: exact k-th key over the selected source
-    const int hgrid = cus * 4;
     for (int p = 0; p < 3; ++p) {
       hipLaunchKernelGGL((k_hist<RAND ? 2 : 1>), hgrid, kBlock, 0, s, ctrl, (const uint32_t*)nullptr, (int64_t)0,
                          (const float*)l.pool_val, l.region_cap, (const float*)res, n, shifts[p], widths[p],
@@ -1543,10 +1622,16 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
   // 7: ordered compaction
   float* vals = quant ? (out_val ? out_val : l.staging) : out_val;
   const int zero_res = (quant || DEFER) ? 0 : 1;
-  hipLaunchKernelGGL((k_bemit<RAND, DEFER>), bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
-                     (const float*)l.pool_val, (const uint16_t*)l.pool_off, (const unsigned long long*)l.gt_excl,
-                     (const unsigned long long*)l.eq_excl, res, index_base, out_idx, vals, zero_res, k,
-                     (const float*)l.pool_c, pd);
+  if (small_batches)
+    hipLaunchKernelGGL((k_bemit<RAND, DEFER, kBatchSmall>), bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start,
+                       l.tile_count, (const float*)l.pool_val, (const uint16_t*)l.pool_off,
+                       (const unsigned long long*)l.gt_excl, (const unsigned long long*)l.eq_excl, res, index_base,
+                       out_idx, vals, zero_res, k, (const float*)l.pool_c, pd);
+  else
+    hipLaunchKernelGGL((k_bemit<RAND, DEFER, kBatch>), bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start,
+                       l.tile_count, (const float*)l.pool_val, (const uint16_t*)l.pool_off,
+                       (const unsigned long long*)l.gt_excl, (const unsigned long long*)l.eq_excl, res, index_base,
+                       out_idx, vals, zero_res, k, (const float*)l.pool_c, pd);
   if (!exact)
     hipLaunchKernelGGL((k_emit<RAND, DEFER>), cgrid, kBlock, 0, s, ctrl, res, n,
                        (const unsigned long long*)l.gt_excl, (const unsigned long long*)l.eq_excl, index_base,
