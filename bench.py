@@ -218,6 +218,11 @@ def ddp_hook_row(torch, gc, dev, say):
     with socket.socket() as sk:
         sk.bind(("127.0.0.1", 0))
         port = sk.getsockname()[1]
+    # the collective library prints a banner to stdout when its communicator starts: keep
+    # stdout for the JSON lines by pointing fd 1 at stderr while the row runs
+    sys.stdout.flush()
+    saved_fd = os.dup(1)
+    os.dup2(2, 1)
     dist.init_process_group("nccl", init_method=f"tcp://127.0.0.1:{port}", rank=0, world_size=1)
     try:
         def build(hook):
@@ -251,6 +256,9 @@ def ddp_hook_row(torch, gc, dev, say):
         del m1, state
     finally:
         dist.destroy_process_group()
+        sys.stdout.flush()
+        os.dup2(saved_fd, 1)
+        os.close(saved_fd)
     # per iteration: the EF pass (12 B per element, + the record), the kept set's outputs,
     # and the receive (payload read, 4 B per element written)
     ub = 12.0 * n + k * (8.0 + 1.0 + 4.0 / 64 + 4.0 + 4.0 + 16.0) + 4.0 * n + k * (8.0 + 1.0 + 4.0 / 64)
