@@ -31,7 +31,10 @@ def keys(t):
     return t.view(torch.int32) & 0x7FFFFFFF
 
 
-def test_metric_path_7e9_two_steps(gc):
+@pytest.mark.parametrize("mode", ["direct", "deferred"])
+def test_metric_path_7e9_two_steps(gc, mode):
+    # deferred: the call bench.py times (gc_ef_compress with a pending record); the true
+    # residual before a step is rebuilt by flushing copies of the residual and the record
     import torch
     dev = torch.device("cuda:0")
     L, LL = workloads.BIG_LAYERS, workloads.BIG_LAYER_LEN
@@ -43,11 +46,14 @@ def test_metric_path_7e9_two_steps(gc):
     out_codes = torch.empty(k, dtype=torch.int8, device=dev)
     out_norms = torch.empty((k + 63) // 64, dtype=torch.float32, device=dev)
     ws = torch.empty(gc.workspace_size(gc.OP_EF_TOPK, n, k, 127), dtype=torch.uint8, device=dev)
+    pend = gc.pending_record(n, k, dev) if mode == "deferred" else None
     for t in (1, 2):
         workloads.layered_torch(L, LL, step=t, device=dev, out=g)
         r_prev.copy_(r)
-        gc.ef_topk(g, r, k, qsgd_levels=127, qsgd_group=64, qsgd_seed=500 + t, out_idx=out_idx,
-                   out_codes=out_codes, out_norms=out_norms, want_values=False, workspace=ws)
+        if pend is not None:
+            gc.ef_flush(r_prev, pend.clone())
+        gc.ef_compress(g, r, k, pending=pend, qsgd_levels=127, qsgd_group=64, qsgd_seed=500 + t,
+                       out_idx=out_idx, out_codes=out_codes, out_norms=out_norms, want_values=False, workspace=ws)
         torch.cuda.synchronize()
         idx = out_idx
         assert int(idx[0]) >= 0 and int(idx[-1]) < n
@@ -70,9 +76,11 @@ def test_metric_path_7e9_two_steps(gc):
             del c, kc, pos
         assert gt == kept_gt, f"step {t}: {gt - kept_gt} dropped entries exceed the threshold"
         assert eq_before == kept_eq, f"step {t}: a dropped tie precedes a kept one"
-        # the residual equals c everywhere off the kept set
+        # the residual equals c everywhere off the kept set (deferred: everywhere, the kept
+        # set's residual waiting in the record)
         mask = torch.ones(n, dtype=torch.bool, device=dev)
-        mask[idx] = False
+        if pend is None:
+            mask[idx] = False
         for l in range(L):
             sl = slice(l * LL, (l + 1) * LL)
             c = g[sl] + r_prev[sl]
@@ -85,7 +93,14 @@ def test_metric_path_7e9_two_steps(gc):
         codes, norms, ghat, _ = oracle.qsgd(v_h, 64, 127, seed=500 + t)
         assert_bits_equal(out_codes.cpu().numpy(), codes, f"step {t} codes")
         assert_bits_equal(out_norms.cpu().numpy(), norms, f"step {t} norms")
-        assert_bits_equal(r[idx].cpu().numpy(), (v_h - ghat).astype(F32), f"step {t} kept residual")
+        if pend is None:
+            kept_res = r[idx]
+        else:
+            r_chk = r.clone()
+            gc.ef_flush(r_chk, pend.clone())
+            kept_res = r_chk[idx]
+            del r_chk
+        assert_bits_equal(kept_res.cpu().numpy(), (v_h - ghat).astype(F32), f"step {t} kept residual")
         del v, kv
 
 
