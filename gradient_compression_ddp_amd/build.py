@@ -29,7 +29,7 @@ COMMON_FLAGS = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 HIP_FLAGS = [
-    "-x", "hip", f"--offload-arch={ARCH}", "-fno-gpu-rdc",
+    f"--offload-arch={ARCH}", "-fno-gpu-rdc",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
@@ -43,8 +43,10 @@ def hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + COMMON_FLAGS
-    if src.endswith(".hip"):
+    hip = src.endswith(".hip")
+    # the language flag must come before the source it applies to
+    cmd = [hipcc()] + (["-x", "hip"] if hip else []) + ["-c", os.path.join(CSRC, src), "-o", obj] + COMMON_FLAGS
+    if hip:
         cmd += HIP_FLAGS
     if verbose:
         print(" ".join(cmd), flush=True)
