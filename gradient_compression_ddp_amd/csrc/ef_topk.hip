@@ -310,7 +310,9 @@ __device__ __forceinline__ void block_scan32(const uint32_t* s_cnt, uint32_t* s_
 // ---------------------------------------------------------------------------------
 // Kernels
 // ---------------------------------------------------------------------------------
-__global__ void k_init(TopkCtrl* __restrict__ ctrl, unsigned long long krem, unsigned long long nchunks) {
+// Resets the control block for a call (block 0 of the sample kernel runs it).
+__device__ __forceinline__ void init_ctrl(TopkCtrl* __restrict__ ctrl, unsigned long long krem,
+                                          unsigned long long nchunks) {
   for (int i = threadIdx.x; i < kBins; i += blockDim.x) ctrl->hist[i] = 0ull;
   for (int i = threadIdx.x; i < kRegions; i += blockDim.x) ctrl->region_fill[i] = 0u;
   if (threadIdx.x == 0) ctrl->emit_next = 0u;
@@ -342,10 +344,13 @@ __device__ __forceinline__ uint64_t mix64(uint64_t z) {
 __device__ __forceinline__ uint32_t rand_key(uint32_t word) { return word >> 1; }
 
 // DEFER: r is corrected by the recorded corrections of the previous call first.
+// Block 0 also resets the control block (no kernel before this one reads it).
 template <bool RAND, bool DEFER>
 __global__ void k_sample(const float* __restrict__ g, const float* __restrict__ r, int64_t n, int64_t m,
                          uint32_t* __restrict__ keys, uint64_t seed, int64_t index_base, Pending pd,
-                         unsigned long long cap) {
+                         unsigned long long cap, TopkCtrl* __restrict__ ctrl, unsigned long long krem,
+                         unsigned long long nchunks) {
+  if (blockIdx.x == 0) init_ctrl(ctrl, krem, nchunks);
   bool apply = false;
   uint32_t has_vals = 0u;
   if (DEFER && !RAND) {
@@ -478,20 +483,42 @@ __device__ __forceinline__ void hist_rand(int64_t n, uint64_t seed, int64_t inde
              want, shift, mask);
 }
 
+// Choose the source of the exact selection (one thread).  Candidates hold the answer iff
+// the pool did not overflow and at least k entries reached the bound L (then T >= L).
+// Without overflow the region counters sum to the number of candidates.  `publish`
+// stores the decision in the control block for the kernels that follow.
+__device__ __forceinline__ uint32_t decide_mode(TopkCtrl* __restrict__ ctrl, int64_t ntiles,
+                                                unsigned long long k, bool publish) {
+  unsigned long long ncand = 0;
+  for (int i = 0; i < kRegions; ++i) ncand += ctrl->region_fill[i];
+  const bool full = ctrl->overflow != 0u || ncand < k;
+  if (publish) {
+    ctrl->ncand = full ? 0ull : ncand;
+    ctrl->mode = full ? MODE_FULL : MODE_CAND;
+    ctrl->nchunks = (unsigned long long)(full ? ntiles : cdiv(ntiles, kUnit));
+  }
+  return full ? MODE_FULL : MODE_CAND;
+}
+
 // Radix histogram pass over the key bits [shift, shift+bits) of the entries whose higher
 // bits equal the prefix fixed so far.  SRC 0: sample keys; SRC 1: the candidate pool
 // (region by region) or, in the fallback, the magnitude keys of the full c; SRC 2: the
-// pool or, in the fallback, the Random-K keys of all n indices.
+// pool or, in the fallback, the Random-K keys of all n indices.  decide_k > 0 (the first
+// pass over the pool): every block takes the source decision itself, and block 0 also
+// publishes it.
 template <int SRC>
 __global__ __launch_bounds__(kBlock) void k_hist(TopkCtrl* __restrict__ ctrl,
                                                  const uint32_t* __restrict__ sample_keys,
                                                  int64_t sample_n, const float* __restrict__ pool,
                                                  int64_t region_cap, const float* __restrict__ full,
                                                  int64_t n, int shift, int bits, uint64_t seed,
-                                                 int64_t index_base) {
+                                                 int64_t index_base, int64_t ntiles, unsigned long long decide_k) {
   __shared__ uint32_t lh[kWaves][kBins];
   __shared__ uint32_t s_rq[kRegions + 1];
+  __shared__ uint32_t s_mode;
   for (int i = threadIdx.x; i < kWaves * kBins; i += kBlock) (&lh[0][0])[i] = 0u;
+  if (SRC != 0 && threadIdx.x == 0)
+    s_mode = decide_k ? decide_mode(ctrl, ntiles, decide_k, blockIdx.x == 0) : ctrl->mode;
   if (SRC != 0 && threadIdx.x < kWave) {
     // exclusive prefix of the regions' whole-quad counts (candidate mode only reads it)
     const uint32_t c = threadIdx.x < kRegions ? ctrl->region_fill[threadIdx.x] >> 2 : 0u;
@@ -514,7 +541,7 @@ __global__ __launch_bounds__(kBlock) void k_hist(TopkCtrl* __restrict__ ctrl,
   BinRun run{0u, 0u};
   if (SRC == 0) {
     for (int64_t i = first; i < sample_n; i += stride) hist_add(my, run, sample_keys[i], hshift, want, shift, mask);
-  } else if (ctrl->mode == MODE_CAND) {
+  } else if (s_mode == MODE_CAND) {
     hist_pool(pool, region_cap, ctrl->region_fill, s_rq, first, stride, my, run, hshift, want, shift, mask);
   } else if (SRC == 1) {
     hist_span(full, n, first, stride, blockIdx.x == 0, my, run, hshift, want, shift, mask);
@@ -883,12 +910,15 @@ __global__ __launch_bounds__(kBlock) void k_scan_down(const uint32_t* __restrict
 
 
 // One-block exclusive scan of one or two uint32 count arrays (small counts only; b and
-// ob may be null).  A thread takes four consecutive items per round of 1024.
+// ob may be null; the count is *count_dev when given).  A thread takes four consecutive
+// items per round of 1024.
 __global__ __launch_bounds__(kBlock) void k_scan_small(const uint32_t* __restrict__ a,
-                                                       const uint32_t* __restrict__ b, int64_t count,
+                                                       const uint32_t* __restrict__ b,
+                                                       const unsigned long long* count_dev, int64_t count_host,
                                                        unsigned long long* __restrict__ oa,
                                                        unsigned long long* __restrict__ ob) {
   constexpr int kPer = 4;
+  const int64_t count = scan_count(count_dev, count_host);
   __shared__ unsigned long long s_w[2][kWaves];
   unsigned long long ca = 0, cb = 0;
   const int w = threadIdx.x / kWave;
@@ -920,20 +950,6 @@ __global__ __launch_bounds__(kBlock) void k_scan_small(const uint32_t* __restric
     ca += s_w[0][0] + s_w[0][1] + s_w[0][2] + s_w[0][3];
     cb += s_w[1][0] + s_w[1][1] + s_w[1][2] + s_w[1][3];
     __syncthreads();
-  }
-}
-
-// Choose the source of the exact selection.  Candidates hold the answer iff the pool did
-// not overflow and at least k entries reached the bound L (then T >= L).  Without
-// overflow the region counters sum to the number of candidates.
-__global__ void k_decide(TopkCtrl* __restrict__ ctrl, int64_t ntiles, unsigned long long k) {
-  if (threadIdx.x == 0) {
-    unsigned long long ncand = 0;
-    for (int i = 0; i < kRegions; ++i) ncand += ctrl->region_fill[i];
-    const bool full = ctrl->overflow != 0u || ncand < k;
-    ctrl->ncand = full ? 0ull : ncand;
-    ctrl->mode = full ? MODE_FULL : MODE_CAND;
-    ctrl->nchunks = (unsigned long long)(full ? ntiles : cdiv(ntiles, kUnit));
   }
 }
 
@@ -1016,7 +1032,7 @@ constexpr int kCountU = 4;  // entries per thread per chunk of the unit count
 
 // Candidates only: per-unit counts of key > T and key == T (units of kUnit tiles, taken
 // grid-stride: small enough that a dense layer spreads over many blocks).
-__global__ __launch_bounds__(kBlock) void k_bcount(const TopkCtrl* __restrict__ ctrl, int64_t ntiles,
+__device__ __forceinline__ void bcount_body(const TopkCtrl* __restrict__ ctrl, int64_t ntiles,
                                                    const uint32_t* __restrict__ tile_start,
                                                    const uint32_t* __restrict__ tile_count,
                                                    const float* __restrict__ pool_val,
@@ -1089,7 +1105,7 @@ __device__ __forceinline__ void small_scan(const uint32_t* s_cnt, uint32_t* s_of
 // its kept position and count the kept entries of every tile.
 // KB: tiles per batch (kBatch, or kBatchSmall when there are fewer batches than CUs).
 template <bool RAND, bool DEFER, int KB>
-__global__ __launch_bounds__(kBlock) void k_bemit(TopkCtrl* __restrict__ ctrl, int64_t ntiles,
+__device__ __forceinline__ void bemit_body(TopkCtrl* __restrict__ ctrl, int64_t ntiles,
                                                   const uint32_t* __restrict__ tile_start,
                                                   const uint32_t* __restrict__ tile_count,
                                                   const float* __restrict__ pool_val,
@@ -1213,7 +1229,7 @@ __device__ __forceinline__ void full_keys4(const float* __restrict__ full, int64
 // Fallback only: per-tile counts of key > T and key == T over the full c (RAND: over the
 // keys of all n indices, which need no load).
 template <bool RAND>
-__global__ __launch_bounds__(kBlock) void k_count(const TopkCtrl* __restrict__ ctrl,
+__device__ __forceinline__ void count_body(const TopkCtrl* __restrict__ ctrl,
                                                   const float* __restrict__ full, int64_t n,
                                                   uint32_t* __restrict__ chunk_gt,
                                                   uint32_t* __restrict__ chunk_eq, uint64_t seed,
@@ -1255,7 +1271,7 @@ __global__ __launch_bounds__(kBlock) void k_count(const TopkCtrl* __restrict__ c
 // first `need` entries with key == T.  DEFER: record offsets and per-tile counts as the
 // batch emit does.
 template <bool RAND, bool DEFER>
-__global__ __launch_bounds__(kBlock) void k_emit(const TopkCtrl* __restrict__ ctrl,
+__device__ __forceinline__ void emit_body(const TopkCtrl* __restrict__ ctrl,
                                                  float* __restrict__ r, int64_t n,
                                                  const unsigned long long* __restrict__ gt_excl,
                                                  const unsigned long long* __restrict__ eq_excl,
@@ -1345,6 +1361,45 @@ __global__ __launch_bounds__(kBlock) void k_emit(const TopkCtrl* __restrict__ ct
     }
     __syncthreads();
   }
+}
+
+// Counts for the selected source in one launch: per unit of candidates, or per tile of
+// the full source in the fallback (the body of the other mode returns at once).
+template <bool RAND>
+__global__ __launch_bounds__(kBlock) void k_count_all(const TopkCtrl* __restrict__ ctrl, int64_t ntiles,
+                                                      const uint32_t* __restrict__ tile_start,
+                                                      const uint32_t* __restrict__ tile_count,
+                                                      const float* __restrict__ pool_val,
+                                                      const float* __restrict__ full, int64_t n,
+                                                      uint32_t* __restrict__ chunk_gt, uint32_t* __restrict__ chunk_eq,
+                                                      uint64_t seed, int64_t index_base) {
+  bcount_body(ctrl, ntiles, tile_start, tile_count, pool_val, chunk_gt, chunk_eq);
+  count_body<RAND>(ctrl, full, n, chunk_gt, chunk_eq, seed, index_base);
+}
+
+// Ordered compaction from the selected source in one launch (batch emit of the pool, or
+// the fallback's tile emit).  DEFER: block 0 also writes the pending record's header for
+// this call (the streaming pass, its only reader in this call, is done).
+template <bool RAND, bool DEFER, int KB>
+__global__ __launch_bounds__(kBlock) void k_emit_all(TopkCtrl* __restrict__ ctrl, int64_t ntiles,
+                                                     const uint32_t* __restrict__ tile_start,
+                                                     const uint32_t* __restrict__ tile_count,
+                                                     const float* __restrict__ pool_val,
+                                                     const uint16_t* __restrict__ pool_off,
+                                                     const unsigned long long* __restrict__ gt_excl,
+                                                     const unsigned long long* __restrict__ eq_excl,
+                                                     float* __restrict__ r, int64_t n, int64_t index_base,
+                                                     int64_t* __restrict__ out_idx, float* __restrict__ out_val,
+                                                     int zero_residual, int64_t k, const float* __restrict__ pool_c,
+                                                     uint64_t seed, Pending pd, uint32_t has_vals) {
+  if (DEFER && blockIdx.x == 0 && threadIdx.x == 0) {
+    pd.hdr->n = (unsigned long long)n;
+    pd.hdr->count = (unsigned long long)k;
+    pd.hdr->has_vals = has_vals;
+  }
+  bemit_body<RAND, DEFER, KB>(ctrl, ntiles, tile_start, tile_count, pool_val, pool_off, gt_excl, eq_excl, r,
+                              index_base, out_idx, out_val, zero_residual, k, pool_c, pd);
+  emit_body<RAND, DEFER>(ctrl, r, n, gt_excl, eq_excl, index_base, out_idx, out_val, zero_residual, k, seed, pd);
 }
 
 // QSGD over the kept values (groups in kept order, RNG index = kept position) and the
@@ -1553,9 +1608,9 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
   const bool exact = m == n;   // the sample select is the exact select
   const int64_t nunit = cdiv(l.ntiles, kUnit);
   const int64_t nbatch = cdiv(l.ntiles, kBatch);
-  hipLaunchKernelGGL(k_init, 1, 256, 0, s, ctrl, (unsigned long long)j, (unsigned long long)nunit);
   hipLaunchKernelGGL((k_sample<RAND, DEFER>), clamp_grid(cdiv(m, 256), cus * 16), 256, 0, s, grad, res, n, m,
-                     l.sample, select_seed, index_base, pd, cap);
+                     l.sample, select_seed, index_base, pd, cap, ctrl, (unsigned long long)j,
+                     (unsigned long long)nunit);
   const int shifts[3] = {20, 9, 0}, widths[3] = {11, 11, 9};
   // pool histogram grid: each block clears and flushes a 2048-bin LDS histogram, so a
   // block takes at least 16384 of the candidates the pool is expected to hold
@@ -1565,7 +1620,8 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
   if (hgrid < 32) hgrid = 32;
   for (int p = 0; p < 3; ++p) {
     hipLaunchKernelGGL((k_hist<0>), sgrid, kBlock, 0, s, ctrl, l.sample, m, (const float*)nullptr,
-                       (int64_t)0, (const float*)nullptr, n, shifts[p], widths[p], (uint64_t)0, (int64_t)0);
+                       (int64_t)0, (const float*)nullptr, n, shifts[p], widths[p], (uint64_t)0, (int64_t)0,
+                       (int64_t)0, 0ull);
     hipLaunchKernelGGL(k_pick, 1, kBlock, 0, s, ctrl, shifts[p], p == 2 ? (exact ? 3 : 1) : 0,
                        (unsigned long long)k);
   }
@@ -1589,53 +1645,52 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
   const int cgrid = clamp_grid(l.ntiles, cus * 8);
   if (exact) {
     // T and need are known and the pool holds every candidate: count, one-block scan
-    hipLaunchKernelGGL(k_bcount, ugrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
-                       l.pool_val, l.chunk_gt, l.chunk_eq);
+    hipLaunchKernelGGL((k_count_all<RAND>), ugrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
+                       (const float*)l.pool_val, (const float*)res, n, l.chunk_gt, l.chunk_eq, select_seed,
+                       index_base);
     hipLaunchKernelGGL(k_scan_small, 1, kBlock, 0, s, (const uint32_t*)l.chunk_gt, (const uint32_t*)l.chunk_eq,
-                       nunit, l.gt_excl, l.eq_excl);
+                       (const unsigned long long*)nullptr, nunit, l.gt_excl, l.eq_excl);
   } else {
-    // 4: source decision
-    hipLaunchKernelGGL(k_decide, 1, 64, 0, s, ctrl, l.ntiles, (unsigned long long)k);
-
-    // 5: exact k-th key over the selected source
+    // 4-5: the first pool pass also decides the source; then the exact k-th key over it
     for (int p = 0; p < 3; ++p) {
       hipLaunchKernelGGL((k_hist<RAND ? 2 : 1>), hgrid, kBlock, 0, s, ctrl, (const uint32_t*)nullptr, (int64_t)0,
                          (const float*)l.pool_val, l.region_cap, (const float*)res, n, shifts[p], widths[p],
-                         select_seed, index_base);
+                         select_seed, index_base, l.ntiles, p == 0 ? (unsigned long long)k : 0ull);
       hipLaunchKernelGGL(k_pick, 1, kBlock, 0, s, ctrl, shifts[p], p == 2 ? 2 : 0, (unsigned long long)k);
     }
 
-    // 6: counts per batch (candidates) or per tile (fallback), and their scan; the kernel
-    // of the other mode returns at once
-    hipLaunchKernelGGL(k_bcount, ugrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
-                       l.pool_val, l.chunk_gt, l.chunk_eq);
-    hipLaunchKernelGGL(k_count<RAND>, cgrid, kBlock, 0, s, ctrl, res, n, l.chunk_gt, l.chunk_eq, select_seed,
+    // 6: counts per unit (candidates) or per tile (fallback), and their scan
+    hipLaunchKernelGGL((k_count_all<RAND>), cgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
+                       (const float*)l.pool_val, (const float*)res, n, l.chunk_gt, l.chunk_eq, select_seed,
                        index_base);
     const unsigned long long* nch_dev = &ctrl->nchunks;
-    const int cscan = clamp_grid(cdiv(l.max_chunks, kScanChunk), cus * 4);
-    hipLaunchKernelGGL(k_scan_up, cscan, kBlock, 0, s, l.chunk_gt, l.chunk_eq, nch_dev, (int64_t)0, l.scan_up);
-    hipLaunchKernelGGL(k_scan_mid, 1, kBlock, 0, s, nch_dev, (int64_t)0, l.scan_up);
-    hipLaunchKernelGGL(k_scan_down, cscan, kBlock, 0, s, l.chunk_gt, l.chunk_eq, nch_dev, (int64_t)0,
-                       (const unsigned long long*)l.scan_up, l.gt_excl, l.eq_excl);
+    if (l.max_chunks <= 8 * kScanChunk) {
+      hipLaunchKernelGGL(k_scan_small, 1, kBlock, 0, s, (const uint32_t*)l.chunk_gt, (const uint32_t*)l.chunk_eq,
+                         nch_dev, (int64_t)0, l.gt_excl, l.eq_excl);
+    } else {
+      const int cscan = clamp_grid(cdiv(l.max_chunks, kScanChunk), cus * 4);
+      hipLaunchKernelGGL(k_scan_up, cscan, kBlock, 0, s, l.chunk_gt, l.chunk_eq, nch_dev, (int64_t)0, l.scan_up);
+      hipLaunchKernelGGL(k_scan_mid, 1, kBlock, 0, s, nch_dev, (int64_t)0, l.scan_up);
+      hipLaunchKernelGGL(k_scan_down, cscan, kBlock, 0, s, l.chunk_gt, l.chunk_eq, nch_dev, (int64_t)0,
+                         (const unsigned long long*)l.scan_up, l.gt_excl, l.eq_excl);
+    }
   }
 
-  // 7: ordered compaction
+  // 7: ordered compaction (and, deferred, the pending record's header)
   float* vals = quant ? (out_val ? out_val : l.staging) : out_val;
   const int zero_res = (quant || DEFER) ? 0 : 1;
   if (small_batches)
-    hipLaunchKernelGGL((k_bemit<RAND, DEFER, kBatchSmall>), bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start,
+    hipLaunchKernelGGL((k_emit_all<RAND, DEFER, kBatchSmall>), bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start,
                        l.tile_count, (const float*)l.pool_val, (const uint16_t*)l.pool_off,
-                       (const unsigned long long*)l.gt_excl, (const unsigned long long*)l.eq_excl, res, index_base,
-                       out_idx, vals, zero_res, k, (const float*)l.pool_c, pd);
+                       (const unsigned long long*)l.gt_excl, (const unsigned long long*)l.eq_excl, res, n,
+                       index_base, out_idx, vals, zero_res, k, (const float*)l.pool_c, select_seed, pd,
+                       quant ? 1u : 0u);
   else
-    hipLaunchKernelGGL((k_bemit<RAND, DEFER, kBatch>), bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start,
+    hipLaunchKernelGGL((k_emit_all<RAND, DEFER, kBatch>), bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start,
                        l.tile_count, (const float*)l.pool_val, (const uint16_t*)l.pool_off,
-                       (const unsigned long long*)l.gt_excl, (const unsigned long long*)l.eq_excl, res, index_base,
-                       out_idx, vals, zero_res, k, (const float*)l.pool_c, pd);
-  if (!exact)
-    hipLaunchKernelGGL((k_emit<RAND, DEFER>), cgrid, kBlock, 0, s, ctrl, res, n,
-                       (const unsigned long long*)l.gt_excl, (const unsigned long long*)l.eq_excl, index_base,
-                       out_idx, vals, zero_res, k, select_seed, pd);
+                       (const unsigned long long*)l.gt_excl, (const unsigned long long*)l.eq_excl, res, n,
+                       index_base, out_idx, vals, zero_res, k, (const float*)l.pool_c, select_seed, pd,
+                       quant ? 1u : 0u);
 
   // 8: QSGD on the kept values and the residual of the kept set
   if (quant) {
@@ -1662,10 +1717,10 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
                        stats);
   }
   if (DEFER) {
-    // tile_first = exclusive scan of the per-tile kept counts; then the record is live
+    // tile_first = exclusive scan of the per-tile kept counts
     if (l.ntiles <= 16 * kScanChunk) {
       hipLaunchKernelGGL(k_scan_small, 1, kBlock, 0, s, (const uint32_t*)pd.tile_cnt, (const uint32_t*)nullptr,
-                         l.ntiles, pd.tile_first, (unsigned long long*)nullptr);
+                         (const unsigned long long*)nullptr, l.ntiles, pd.tile_first, (unsigned long long*)nullptr);
     } else {
       const int tscan = clamp_grid(cdiv(l.ntiles, kScanChunk), cus * 4);
       hipLaunchKernelGGL(k_scan_up, tscan, kBlock, 0, s, (const uint32_t*)pd.tile_cnt, (const uint32_t*)nullptr,
@@ -1675,8 +1730,6 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
                          (const unsigned long long*)nullptr, l.ntiles, (const unsigned long long*)l.scan_up,
                          pd.tile_first, (unsigned long long*)nullptr);
     }
-    hipLaunchKernelGGL(k_pend_set, 1, 64, 0, s, pd.hdr, (unsigned long long)n, (unsigned long long)k,
-                       quant ? 1u : 0u);
   }
   prof_mark(s, 3);
   return hipGetLastError();
