@@ -86,8 +86,10 @@ def test_monitor_deferred_three_steps_with_qsgd(gc):
     assert_bits_equal(host(rd), r, "flushed residual")
 
 
-def test_monitor_randk_deferred(gc):
-    # Random-K with the deferred residual (only reachable through the options)
+@pytest.mark.parametrize("levels", [0, 127])
+def test_monitor_randk_deferred(gc, levels):
+    # Random-K with the deferred residual (only reachable through the options), pure and
+    # with QSGD on the kept values
     n, k = 1_500_007, 15_000
     r = np.zeros(n, F32)
     rd = dev(r)
@@ -95,9 +97,11 @@ def test_monitor_randk_deferred(gc):
     st = new_stats()
     for t in range(3):
         g = workloads.bucket(n, seed=60 + t)
-        want, o_idx, o_res = oracle.monitored_step(g, r, k, select="randk", select_seed=900 + t)
-        idx, val = gc.ef_compress(dev(g), rd, k, select="randk", select_seed=900 + t, pending=pend, stats=st)
-        assert_bits_equal(host(idx), o_idx, f"step {t} idx")
+        want, o_idx, o_res = oracle.monitored_step(g, r, k, levels=levels, group=64, qsgd_seed=70 + t,
+                                                   select="randk", select_seed=900 + t)
+        out = gc.ef_compress(dev(g), rd, k, select="randk", select_seed=900 + t, pending=pend, stats=st,
+                             qsgd_levels=levels, qsgd_group=64, qsgd_seed=70 + t)
+        assert_bits_equal(host(out[0]), o_idx, f"step {t} idx")
         stats_close(host(st), want, f"step {t}")
         r = o_res
     gc.ef_flush(rd, pend)
