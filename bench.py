@@ -32,6 +32,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# Non-packed 32-bit VALU issue ceiling: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz.
+VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
+# VALU lane-instructions per element of the quantizer kernels (SQ_INSTS_VALU x 64 /
+# elements, rocprofv3 counters of bench.py --rows; profiles/compressor_rows_valu_and_traffic.md).
+VALU_LANE_OPS_PER_ELEMENT = {"minmax8": 44.5, "minmax4": 44.8, "qsgd": 59.1, "tern_max": 8.9, "tern_codes": 44.9}
 
 # HBM bytes per launch of the streaming pass on this workload, from two rocprofv3 counter
 # runs per mode (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, factors from a plain 4 GiB device
@@ -191,7 +196,7 @@ def _blas_threads():
 
 
 def _row(name, workload, unit_bytes, unit, gpu_ms, eager_ms, oracle_s=None, oracle_units=1.0,
-         sample="", cores=1, extra=None):
+         sample="", cores=1, extra=None, valu_ops=None):
     achieved = unit_bytes / (gpu_ms / 1e3) / 1e9
     line = {
         "row": name, "workload": workload, "unit": unit,
@@ -204,6 +209,13 @@ def _row(name, workload, unit_bytes, unit, gpu_ms, eager_ms, oracle_s=None, orac
         per_unit = oracle_s / oracle_units
         line["cpu_oracle"] = {"s_per_unit": round(per_unit, 4), "cores": cores, "kind": "oracle",
                               "sample": sample, "gpu_speedup": round(per_unit * 1e3 / gpu_ms, 1)}
+    if valu_ops is not None:
+        # the counted VALU work of the unit against the issue ceiling (a utilisation figure
+        # for the rows whose arithmetic, not HBM, sets the pace)
+        rate = valu_ops / (gpu_ms / 1e3)
+        line["valu_issue"] = {"lane_ops_per_unit": valu_ops, "achieved": round(rate / 1e12, 2),
+                              "peak": round(VALU_PEAK_LANE_OPS / 1e12, 2), "unit": "1e12 lane-ops/s",
+                              "frac": round(rate / VALU_PEAK_LANE_OPS, 4)}
     if extra:
         line.update(extra)
     print(json.dumps(line), flush=True)
@@ -336,7 +348,8 @@ def rows_mode(args):
         osec = _oracle_s(lambda: orc.quant_minmax(xb, 64, bits)) if orc else None
         ub = (5.0 if bits == 8 else 4.5) * n + 8.0 * ng
         _row(f"a4 min-max int{bits}, groups of 64", "25 MiB bucket: n=6,553,600 t(3)*1e-3, 40 buckets",
-             ub, "bucket", gms, eager, osec, 1.0, "one bucket")
+             ub, "bucket", gms, eager, osec, 1.0, "one bucket",
+             valu_ops=VALU_LANE_OPS_PER_ELEMENT[f"minmax{bits}"] * n)
 
     say("QSGD s=15 gs64")
     qc = torch.empty(NB * n, dtype=torch.int8, device=dev)
@@ -347,7 +360,8 @@ def rows_mode(args):
     gms, _ = _graph_ms(torch, fns)
     osec = _oracle_s(lambda: orc.qsgd(xb, 64, 15, 7)) if orc else None
     _row("a5+a6 QSGD s=15, groups of 64 (Philox4x32-10)", "25 MiB bucket, 40 buckets",
-         5.0 * n + 4.0 * ng, "bucket", gms, eager, osec, 1.0, "one bucket")
+         5.0 * n + 4.0 * ng, "bucket", gms, eager, osec, 1.0, "one bucket",
+         valu_ops=VALU_LANE_OPS_PER_ELEMENT["qsgd"] * n)
 
     say("receive: 8 QSGD payloads of one bucket, averaged")
     W = 8
@@ -503,7 +517,8 @@ def rows_mode(args):
         osec = _oracle_s(lambda: orc.terngrad(h, [0, LL3], 3))
     _row("a5+a7 TernGrad, per-layer scale", "24 layers x 14,583,333 (t(3) x lognormal(-7,1) scales)",
          4.0 * n3 + nbytes + 4.0 * L3, "call (all 24 layers)", gms, eager, osec, 1.0 / L3,
-         "one layer of 14,583,333, scaled by 24")
+         "one layer of 14,583,333, scaled by 24",
+         valu_ops=(VALU_LANE_OPS_PER_ELEMENT["tern_max"] + VALU_LANE_OPS_PER_ELEMENT["tern_codes"]) * n3)
     del xt, pk, wst
 
     # c4: PowerSGD rank 4 on the three matrix shapes, error feedback on.
