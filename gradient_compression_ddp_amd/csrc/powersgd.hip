@@ -39,7 +39,6 @@ struct PLayout {
   float* ppart;   // [ncp * rows * 4]          pass-1 partials per column panel
   float* p;       // [rows * 4]                P = M Q
   double* gram;   // [kGramBlocks * 10]        Gram partials
-  double* t;      // [16]                      P^ = P T
   float* phat;    // [rows * 4]
   float* qpart;   // [nrp * cols * 4]          pass-2 partials per row panel
   float* qn;      // [cols * 4]                Q'
@@ -61,7 +60,6 @@ PLayout make_playout(void* base, int64_t rows, int64_t cols) {
   l.ppart = (float*)take(sizeof(float) * l.ncp * rows * 4);
   l.p = (float*)take(sizeof(float) * rows * 4);
   l.gram = (double*)take(sizeof(double) * kGramBlocks * 10);
-  l.t = (double*)take(sizeof(double) * 16);
   l.phat = (float*)take(sizeof(float) * rows * 4);
   l.qpart = (float*)take(sizeof(float) * l.nrp * cols * 4);
   l.qn = (float*)take(sizeof(float) * cols * 4);
@@ -186,9 +184,9 @@ __global__ __launch_bounds__(kBlock) void k_psum_gram(const float* __restrict__ 
 // 1e-5 of its own norm (squared: 1e-10), below which its direction is rounding noise.
 // One wave: lane l sums the block partials l, l + 64, ... in order, then a fixed xor
 // butterfly combines the lanes (deterministic); lane 0 runs the 4x4 Gram-Schmidt.
-__global__ __launch_bounds__(kWave) void k_gs(const double* __restrict__ gram, int nblocks, int rank,
-                                              double* __restrict__ T) {
-  if (blockIdx.x != 0) return;
+// Called by the first wave of a block; lane 0 writes T (4 x 4, row-major) to `T`.
+__device__ __forceinline__ void gram_schmidt_t(const double* __restrict__ gram, int nblocks, int rank,
+                                               double* T) {
   double g[10];
 #pragma unroll
   for (int t = 0; t < 10; ++t) g[t] = 0.0;
@@ -232,10 +230,12 @@ __global__ __launch_bounds__(kWave) void k_gs(const double* __restrict__ gram, i
 }
 
 // P^ = P T (float64 accumulation, one rounding); padded copy plus the caller's rows x rank P.
-__global__ void k_apply_t(const float* __restrict__ p, const double* __restrict__ T, int64_t rows, int rank,
-                          float* __restrict__ phat, float* __restrict__ P_out) {
+// Every block derives T itself from the Gram partials (the same fixed order in each), which
+// saves a one-wave launch between the two kernels.
+__global__ void k_apply_t(const float* __restrict__ p, const double* __restrict__ gram, int nblocks, int64_t rows,
+                          int rank, float* __restrict__ phat, float* __restrict__ P_out) {
   __shared__ double sT[16];
-  if (threadIdx.x < 16) sT[threadIdx.x] = T[threadIdx.x];
+  if (threadIdx.x < kWave) gram_schmidt_t(gram, nblocks, rank, sT);
   __syncthreads();
   for (int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; row < rows;
        row += (int64_t)gridDim.x * blockDim.x) {
@@ -377,8 +377,8 @@ hipError_t launch_powersgd(const float* grad, float* res, int64_t rows, int64_t 
   if (res) hipLaunchKernelGGL((k_p1<true>), g1, kBlock, 0, s, grad, res, rows, cols, (const float*)Q, rank, l.ppart);
   else hipLaunchKernelGGL((k_p1<false>), g1, kBlock, 0, s, grad, res, rows, cols, (const float*)Q, rank, l.ppart);
   hipLaunchKernelGGL(k_psum_gram, kGramBlocks, kBlock, 0, s, l.ppart, l.ncp, rows, l.p, l.gram);
-  hipLaunchKernelGGL(k_gs, 1, 64, 0, s, l.gram, kGramBlocks, rank, l.t);
-  hipLaunchKernelGGL(k_apply_t, clamp_grid(cdiv(rows, 256), cus * 4), 256, 0, s, l.p, l.t, rows, rank, l.phat, P);
+  hipLaunchKernelGGL(k_apply_t, clamp_grid(cdiv(rows, 256), cus * 4), 256, 0, s, l.p, (const double*)l.gram,
+                     kGramBlocks, rows, rank, l.phat, P);
   const float* M = res ? res : grad;
   const dim3 g2((unsigned)cdiv(cols, 256), (unsigned)l.nrp);
   hipLaunchKernelGGL(k_p2, g2, kBlock, 0, s, M, rows, cols, l.phat, l.qpart);
