@@ -145,6 +145,30 @@ def test_terngrad(gc, lens, base, ef):
         assert_bits_equal(host(rd), r_new, "residual")
 
 
+@pytest.mark.parametrize("sc", [2.0, 2.0 ** -70, 3.0e30])
+def test_terngrad_decision_boundaries(gc, sc):
+    # |x| placed at U * s * (1 + d) for the element's own uniform U (taken from the oracle),
+    # with d from 0 to +-2^-19: straddles the band where the kernel leaves the product
+    # test for the division (and, with s = 2^-70, a scale below the product test's range);
+    # plus tiny values, denormals and zeros.  Codes must equal the oracle's bit for bit.
+    n, seed = 64 * 4096, 11
+    u = oracle.uniform24(seed, np.arange(n, dtype=np.int64)).astype(np.float64)
+    ds = np.array([0.0] + [sgn * 2.0 ** -e for e in range(19, 26) for sgn in (1, -1)])
+    d = ds[np.arange(n) % ds.size]
+    x = (u * sc * (1.0 + d)).astype(F32)
+    x = np.minimum(np.abs(x), F32(sc)).astype(F32)
+    x[::97] = F32(sc) * F32(2.0 ** -70) if sc > 1e-20 else F32(0.0)
+    x[5::211] = np.float32(1e-45)
+    x[7::389] = F32(0.0)
+    sign = np.where(np.random.default_rng(3).random(n) < 0.5, -1.0, 1.0).astype(F32)
+    x = (x * sign).astype(F32)
+    x[0] = F32(sc)                                      # the segment's max
+    packed, scales, _, _, _ = oracle.terngrad(x, [0, n], seed=seed)
+    p_d, s_d = gc.terngrad(dev(x), np.array([0, n], np.int64), seed)
+    assert_bits_equal(host(s_d), scales, "scale")
+    assert_bits_equal(host(p_d), packed, "packed codes")
+
+
 def test_terngrad_layers_scaled(gc):
     x, off = workloads.tern_layers(24, 145_833)        # lengths = 1 mod 4, as in the 350M case
     packed, scales, _, _, _ = oracle.terngrad(x, off, seed=3)
