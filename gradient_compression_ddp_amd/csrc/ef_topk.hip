@@ -65,6 +65,7 @@ constexpr int kBatch = 128;                  // tiles per batch of the emit (8 u
 constexpr int kBatchSmall = kUnit;           // the emit's batch when 128-tile batches are too few
 constexpr int kKeptChunk = kBlock * 4;       // kept entries per norm-monitor partial
 constexpr int kSumChunk = 4096;              // partials per block of the monitor's second level
+constexpr int kFusePickGrid = 256;           // radix pass grids up to this fold the pick in
 static_assert(kBatch % kUnit == 0 && kBatch <= 2 * kWave && kUnit <= kWave, "batch tables");
 static_assert(kBatchSmall % kUnit == 0 && kBatchSmall <= kWave, "small batch tables");
 
@@ -76,7 +77,7 @@ struct TopkCtrl {
   uint32_t mode;           // MODE_CAND or MODE_FULL
   uint32_t prefix;         // key bits fixed so far by the radix passes
   uint32_t T;              // the k-th largest key
-  uint32_t pad;
+  uint32_t ticket;         // last-block hand-off counter (zero between kernels)
   unsigned long long ncand;   // candidates found by K1
   unsigned long long krem;    // rank still to locate inside the current prefix (1-based)
   unsigned long long need;    // entries with key == T to keep
@@ -322,6 +323,7 @@ __device__ __forceinline__ void init_ctrl(TopkCtrl* __restrict__ ctrl, unsigned 
     ctrl->mode = MODE_CAND;
     ctrl->prefix = 0u;
     ctrl->T = 0u;
+    ctrl->ticket = 0u;
     ctrl->ncand = 0ull;
     ctrl->krem = krem;
     ctrl->need = 0ull;
@@ -500,69 +502,39 @@ __device__ __forceinline__ uint32_t decide_mode(TopkCtrl* __restrict__ ctrl, int
   return full ? MODE_FULL : MODE_CAND;
 }
 
-// Radix histogram pass over the key bits [shift, shift+bits) of the entries whose higher
-// bits equal the prefix fixed so far.  SRC 0: sample keys; SRC 1: the candidate pool
-// (region by region) or, in the fallback, the magnitude keys of the full c; SRC 2: the
-// pool or, in the fallback, the Random-K keys of all n indices.  decide_k > 0 (the first
-// pass over the pool): every block takes the source decision itself, and block 0 also
-// publishes it.
-template <int SRC>
-__global__ __launch_bounds__(kBlock) void k_hist(TopkCtrl* __restrict__ ctrl,
-                                                 const uint32_t* __restrict__ sample_keys,
-                                                 int64_t sample_n, const float* __restrict__ pool,
-                                                 int64_t region_cap, const float* __restrict__ full,
-                                                 int64_t n, int shift, int bits, uint64_t seed,
-                                                 int64_t index_base, int64_t ntiles, unsigned long long decide_k) {
-  __shared__ uint32_t lh[kWaves][kBins];
-  __shared__ uint32_t s_rq[kRegions + 1];
-  __shared__ uint32_t s_mode;
-  for (int i = threadIdx.x; i < kWaves * kBins; i += kBlock) (&lh[0][0])[i] = 0u;
-  if (SRC != 0 && threadIdx.x == 0)
-    s_mode = decide_k ? decide_mode(ctrl, ntiles, decide_k, blockIdx.x == 0) : ctrl->mode;
-  if (SRC != 0 && threadIdx.x < kWave) {
-    // exclusive prefix of the regions' whole-quad counts (candidate mode only reads it)
-    const uint32_t c = threadIdx.x < kRegions ? ctrl->region_fill[threadIdx.x] >> 2 : 0u;
-    uint32_t inc = c;
-#pragma unroll
-    for (int d = 1; d < kRegions; d <<= 1) {
-      const uint32_t o = (uint32_t)__shfl_up((int)inc, d, kWave);
-      if (threadIdx.x >= d) inc += o;
+// Last-block hand-off: every block of a grid calls this once, after its global writes and
+// atomics; it returns true in exactly one block, the last to arrive, which then sees the
+// writes of every block.  Nothing waits on anything, so every block runs to its end; the
+// ticket is zero again once the last block has it.  One device-scope release per block
+// (its first thread's ticket increment, after the barrier that orders the block's writes
+// before it) and one acquire in the last block: a full fence in every wave costs an L2
+// write-back and invalidate each, which measured slower than the launch this saves.
+__device__ __forceinline__ bool last_block(uint32_t* ticket) {
+  __shared__ uint32_t s_last;
+  // each wave's own global stores and atomics have completed before the barrier (the
+  // barrier alone does not wait for them), so the first thread's release covers them all
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = t == gridDim.x - 1;
+    if (last) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (threadIdx.x < kRegions) s_rq[threadIdx.x] = inc - c;
-    if (threadIdx.x == kRegions - 1) s_rq[kRegions] = inc;
+    s_last = last ? 1u : 0u;
   }
   __syncthreads();
-  const uint32_t hshift = (uint32_t)(shift + bits);
-  const uint32_t want = ctrl->prefix >> hshift;
-  const uint32_t mask = (1u << bits) - 1u;
-  uint32_t* my = lh[threadIdx.x / kWave];
-  const int64_t stride = (int64_t)gridDim.x * kBlock;
-  const int64_t first = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  BinRun run{0u, 0u};
-  if (SRC == 0) {
-    for (int64_t i = first; i < sample_n; i += stride) hist_add(my, run, sample_keys[i], hshift, want, shift, mask);
-  } else if (s_mode == MODE_CAND) {
-    hist_pool(pool, region_cap, ctrl->region_fill, s_rq, first, stride, my, run, hshift, want, shift, mask);
-  } else if (SRC == 1) {
-    hist_span(full, n, first, stride, blockIdx.x == 0, my, run, hshift, want, shift, mask);
-  } else {
-    hist_rand(n, seed, index_base, first, stride, blockIdx.x == 0, my, run, hshift, want, shift, mask);
-  }
-  run_flush(my, run);
-  __syncthreads();
-  for (int b = threadIdx.x; b < kBins; b += kBlock) {
-    const uint32_t c = lh[0][b] + lh[1][b] + lh[2][b] + lh[3][b];
-    if (c) atomicAdd(&ctrl->hist[b], (unsigned long long)c);
-  }
+  return s_last != 0u;
 }
 
-// Locate the bin holding rank `krem` (counted from the largest key) and fix its bits.
-// final_op: 0 = intermediate pass; 1 = last pass of the sample select (set L, reset for
-// the main select with rank k); 2 = last pass of the main select (set T and need);
-// 3 = last pass of a select over the whole input (L = T, and need).
-__global__ __launch_bounds__(kBlock) void k_pick(TopkCtrl* __restrict__ ctrl, int shift, int final_op,
-                                                 unsigned long long k_main) {
-  __shared__ unsigned long long s_sum[kBlock];
+// Locate the bin of the global histogram holding rank krem (counted from the largest
+// key), fix its bits in the prefix and clear the histogram (one block; s_sum holds
+// kBlock 64-bit words).  final_op: 0 = intermediate pass; 1 = last pass of the sample
+// select (set L, reset for the main select with rank k_main); 2 = last pass of the main
+// select (set T and need); 3 = last pass of a select over the whole input (L = T too).
+__device__ __forceinline__ void pick_body(TopkCtrl* __restrict__ ctrl, int shift, int final_op,
+                                          unsigned long long k_main, unsigned long long* s_sum) {
   constexpr int per = kBins / kBlock;   // 8 bins per thread, highest bins first
   const int t = threadIdx.x;
   const int hi_bin = kBins - 1 - per * t;
@@ -607,6 +579,73 @@ __global__ __launch_bounds__(kBlock) void k_pick(TopkCtrl* __restrict__ ctrl, in
       ctrl->need = ctrl->krem;
     }
   }
+}
+
+__global__ __launch_bounds__(kBlock) void k_pick(TopkCtrl* __restrict__ ctrl, int shift, int final_op,
+                                                 unsigned long long k_main) {
+  __shared__ unsigned long long s_sum[kBlock];
+  pick_body(ctrl, shift, final_op, k_main, s_sum);
+}
+
+// Radix histogram pass over the key bits [shift, shift+bits) of the entries whose higher
+// bits equal the prefix fixed so far.  SRC 0: sample keys; SRC 1: the candidate pool
+// (region by region) or, in the fallback, the magnitude keys of the full c; SRC 2: the
+// pool or, in the fallback, the Random-K keys of all n indices.  decide_k > 0 (the first
+// pass over the pool): every block takes the source decision itself, and block 0 also
+// publishes it.  fuse_pick: the last block to finish then locates the rank's bin
+// (pick_body); otherwise k_pick follows.
+template <int SRC>
+__global__ __launch_bounds__(kBlock) void k_hist(TopkCtrl* __restrict__ ctrl,
+                                                 const uint32_t* __restrict__ sample_keys,
+                                                 int64_t sample_n, const float* __restrict__ pool,
+                                                 int64_t region_cap, const float* __restrict__ full,
+                                                 int64_t n, int shift, int bits, uint64_t seed,
+                                                 int64_t index_base, int64_t ntiles, unsigned long long decide_k,
+                                                 int final_op, unsigned long long k_main, int fuse_pick) {
+  __shared__ __align__(16) uint32_t lh[kWaves][kBins];
+  __shared__ uint32_t s_rq[kRegions + 1];
+  __shared__ uint32_t s_mode;
+  for (int i = threadIdx.x; i < kWaves * kBins; i += kBlock) (&lh[0][0])[i] = 0u;
+  if (SRC != 0 && threadIdx.x == 0)
+    s_mode = decide_k ? decide_mode(ctrl, ntiles, decide_k, blockIdx.x == 0) : ctrl->mode;
+  if (SRC != 0 && threadIdx.x < kWave) {
+    // exclusive prefix of the regions' whole-quad counts (candidate mode only reads it)
+    const uint32_t c = threadIdx.x < kRegions ? ctrl->region_fill[threadIdx.x] >> 2 : 0u;
+    uint32_t inc = c;
+#pragma unroll
+    for (int d = 1; d < kRegions; d <<= 1) {
+      const uint32_t o = (uint32_t)__shfl_up((int)inc, d, kWave);
+      if (threadIdx.x >= d) inc += o;
+    }
+    if (threadIdx.x < kRegions) s_rq[threadIdx.x] = inc - c;
+    if (threadIdx.x == kRegions - 1) s_rq[kRegions] = inc;
+  }
+  __syncthreads();
+  const uint32_t hshift = (uint32_t)(shift + bits);
+  const uint32_t want = ctrl->prefix >> hshift;
+  const uint32_t mask = (1u << bits) - 1u;
+  uint32_t* my = lh[threadIdx.x / kWave];
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  const int64_t first = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  BinRun run{0u, 0u};
+  if (SRC == 0) {
+    for (int64_t i = first; i < sample_n; i += stride) hist_add(my, run, sample_keys[i], hshift, want, shift, mask);
+  } else if (s_mode == MODE_CAND) {
+    hist_pool(pool, region_cap, ctrl->region_fill, s_rq, first, stride, my, run, hshift, want, shift, mask);
+  } else if (SRC == 1) {
+    hist_span(full, n, first, stride, blockIdx.x == 0, my, run, hshift, want, shift, mask);
+  } else {
+    hist_rand(n, seed, index_base, first, stride, blockIdx.x == 0, my, run, hshift, want, shift, mask);
+  }
+  run_flush(my, run);
+  __syncthreads();
+  for (int b = threadIdx.x; b < kBins; b += kBlock) {
+    const uint32_t c = lh[0][b] + lh[1][b] + lh[2][b] + lh[3][b];
+    if (c) atomicAdd(&ctrl->hist[b], (unsigned long long)c);
+  }
+  // lh is free once every thread is past the flush (last_block's barrier)
+  if (fuse_pick && last_block(&ctrl->ticket))
+    pick_body(ctrl, shift, final_op, k_main, reinterpret_cast<unsigned long long*>(&lh[0][0]));
 }
 
 
@@ -911,14 +950,24 @@ __global__ __launch_bounds__(kBlock) void k_scan_down(const uint32_t* __restrict
 
 // One-block exclusive scan of one or two uint32 count arrays (small counts only; b and
 // ob may be null; the count is *count_dev when given).  A thread takes four consecutive
-// items per round of 1024.
-__global__ __launch_bounds__(kBlock) void k_scan_small(const uint32_t* __restrict__ a,
-                                                       const uint32_t* __restrict__ b,
-                                                       const unsigned long long* count_dev, int64_t count_host,
-                                                       unsigned long long* __restrict__ oa,
-                                                       unsigned long long* __restrict__ ob) {
+// items per round of 1024.  Runs as a kernel of its own, or as the extra job of one block
+// of the kernel that follows the one writing the counts.
+struct SmallScan {
+  const uint32_t* a;
+  const uint32_t* b;
+  const unsigned long long* count_dev;
+  int64_t count_host;
+  unsigned long long* oa;
+  unsigned long long* ob;
+};
+
+__device__ __forceinline__ void scan_small_body(const SmallScan& sc) {
   constexpr int kPer = 4;
-  const int64_t count = scan_count(count_dev, count_host);
+  const uint32_t* __restrict__ a = sc.a;
+  const uint32_t* __restrict__ b = sc.b;
+  unsigned long long* __restrict__ oa = sc.oa;
+  unsigned long long* __restrict__ ob = sc.ob;
+  const int64_t count = scan_count(sc.count_dev, sc.count_host);
   __shared__ unsigned long long s_w[2][kWaves];
   unsigned long long ca = 0, cb = 0;
   const int w = threadIdx.x / kWave;
@@ -952,6 +1001,8 @@ __global__ __launch_bounds__(kBlock) void k_scan_small(const uint32_t* __restric
     __syncthreads();
   }
 }
+
+__global__ __launch_bounds__(kBlock) void k_scan_small(SmallScan sc) { scan_small_body(sc); }
 
 // ---- the candidates of KB consecutive tiles (a unit or a batch) ------------------------
 // pre[i] is the exclusive prefix of the tile counts inside the group; past the last tile
@@ -1367,19 +1418,33 @@ __device__ __forceinline__ void emit_body(const TopkCtrl* __restrict__ ctrl,
 // two kernels (each returns at once unless the device-side mode is its own).  One
 // kernel holding both bodies measured 302 us against 186 us for the candidate count at
 // 7e9 elements, with the same code for that body, so they stay apart.
-__global__ __launch_bounds__(kBlock) void k_bcount(const TopkCtrl* __restrict__ ctrl, int64_t ntiles,
+// SCAN (small counts only): the scan of the counts is folded in.  In k_bcount (the
+// whole-input select, candidate mode) the last block to finish runs it; in k_count the
+// last counting block runs it in the fallback, and block 0 at once in candidate mode,
+// whose counts the previous kernel wrote.  Only as template variants: the extra code in
+// the candidate count's kernel alone measured 300 us against 186 us at 7e9 elements.
+template <bool SCAN>
+__global__ __launch_bounds__(kBlock) void k_bcount(TopkCtrl* __restrict__ ctrl, int64_t ntiles,
                                                    const uint32_t* __restrict__ tile_start,
                                                    const uint32_t* __restrict__ tile_count,
                                                    const float* __restrict__ pool_val,
-                                                   uint32_t* __restrict__ chunk_gt, uint32_t* __restrict__ chunk_eq) {
+                                                   uint32_t* __restrict__ chunk_gt, uint32_t* __restrict__ chunk_eq,
+                                                   SmallScan sc) {
   bcount_body(ctrl, ntiles, tile_start, tile_count, pool_val, chunk_gt, chunk_eq);
+  if (SCAN && last_block(&ctrl->ticket)) scan_small_body(sc);
 }
 
-template <bool RAND>
-__global__ __launch_bounds__(kBlock) void k_count(const TopkCtrl* __restrict__ ctrl, const float* __restrict__ full,
+template <bool RAND, bool SCAN>
+__global__ __launch_bounds__(kBlock) void k_count(TopkCtrl* __restrict__ ctrl, const float* __restrict__ full,
                                                   int64_t n, uint32_t* __restrict__ chunk_gt,
-                                                  uint32_t* __restrict__ chunk_eq, uint64_t seed, int64_t index_base) {
+                                                  uint32_t* __restrict__ chunk_eq, uint64_t seed, int64_t index_base,
+                                                  SmallScan sc) {
+  if (SCAN && ctrl->mode != MODE_FULL) {
+    if (blockIdx.x == 0) scan_small_body(sc);
+    return;
+  }
   count_body<RAND>(ctrl, full, n, chunk_gt, chunk_eq, seed, index_base);
+  if (SCAN && last_block(&ctrl->ticket)) scan_small_body(sc);
 }
 
 // Ordered compaction from the selected source in one launch (batch emit of the pool, or
@@ -1413,19 +1478,26 @@ __global__ __launch_bounds__(kBlock) void k_emit_all(TopkCtrl* __restrict__ ctrl
 // consecutive entries per wave store (neighbouring kept entries often share a sector).
 // DEFER: the residuals go to the record's values, in kept order, instead of r.
 // MON: the sum of g_hat^2 of each 1024 kept entries (float64, fixed order) goes to mon_g.
-template <bool DEFER, bool MON>
+template <bool DEFER, bool MON, bool SCAN>
 __global__ __launch_bounds__(kBlock) void k_qsgd_kept(const float* __restrict__ vals, int64_t k,
                                                       int lpg_log2, float s, uint64_t seed,
                                                       int8_t* __restrict__ codes, float* __restrict__ norms,
                                                       const int64_t* __restrict__ idx, int64_t index_base,
                                                       float* __restrict__ r, int64_t n, Pending pd,
-                                                      double* __restrict__ mon_g) {
+                                                      double* __restrict__ mon_g, SmallScan sc) {
   __shared__ float s_res[kBlock * 4];
   __shared__ double s_mon[MON ? kWaves : 1];
+  // SCAN: the grid's last block only scans the counts of sc (written by the previous
+  // kernel) while the others quantize
+  const unsigned qblocks = gridDim.x - (SCAN ? 1u : 0u);
+  if (SCAN && blockIdx.x >= qblocks) {
+    scan_small_body(sc);
+    return;
+  }
   const int64_t nquads = (k + 3) >> 2;
   const int lpg = 1 << lpg_log2;
   const int lane = lane_id();
-  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  const int64_t stride = (int64_t)qblocks * kBlock;
   for (int64_t base = (int64_t)blockIdx.x * kBlock; base < nquads; base += stride) {
     const int64_t q = base + threadIdx.x;
     const int64_t e0 = q << 2;
@@ -1624,11 +1696,12 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
   int hgrid = clamp_grid(cdiv(expect_cand, 16384), cus * 4);
   if (hgrid < 32) hgrid = 32;
   for (int p = 0; p < 3; ++p) {
+    const int op = p == 2 ? (exact ? 3 : 1) : 0;
+    const bool fuse = sgrid <= kFusePickGrid;
     hipLaunchKernelGGL((k_hist<0>), sgrid, kBlock, 0, s, ctrl, l.sample, m, (const float*)nullptr,
                        (int64_t)0, (const float*)nullptr, n, shifts[p], widths[p], (uint64_t)0, (int64_t)0,
-                       (int64_t)0, 0ull);
-    hipLaunchKernelGGL(k_pick, 1, kBlock, 0, s, ctrl, shifts[p], p == 2 ? (exact ? 3 : 1) : 0,
-                       (unsigned long long)k);
+                       (int64_t)0, 0ull, op, (unsigned long long)k, fuse ? 1 : 0);
+    if (!fuse) hipLaunchKernelGGL(k_pick, 1, kBlock, 0, s, ctrl, shifts[p], op, (unsigned long long)k);
   }
 
   // 3: the streaming pass
@@ -1649,30 +1722,36 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
   const int bgrid = clamp_grid(small_batches ? nunit : nbatch, cus * 8);
   const int cgrid = clamp_grid(l.ntiles, cus * 8);
   if (exact) {
-    // T and need are known and the pool holds every candidate: count, one-block scan
-    hipLaunchKernelGGL(k_bcount, ugrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
-                       (const float*)l.pool_val, l.chunk_gt, l.chunk_eq);
-    hipLaunchKernelGGL(k_scan_small, 1, kBlock, 0, s, (const uint32_t*)l.chunk_gt, (const uint32_t*)l.chunk_eq,
-                       (const unsigned long long*)nullptr, nunit, l.gt_excl, l.eq_excl);
+    // T and need are known and the pool holds every candidate: count, and the last block
+    // to finish scans the counts
+    const SmallScan sc{l.chunk_gt, l.chunk_eq, nullptr, nunit, l.gt_excl, l.eq_excl};
+    hipLaunchKernelGGL(k_bcount<true>, ugrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
+                       (const float*)l.pool_val, l.chunk_gt, l.chunk_eq, sc);
   } else {
     // 4-5: the first pool pass also decides the source; then the exact k-th key over it
     for (int p = 0; p < 3; ++p) {
+      const bool fuse = hgrid <= kFusePickGrid;
       hipLaunchKernelGGL((k_hist<RAND ? 2 : 1>), hgrid, kBlock, 0, s, ctrl, (const uint32_t*)nullptr, (int64_t)0,
                          (const float*)l.pool_val, l.region_cap, (const float*)res, n, shifts[p], widths[p],
-                         select_seed, index_base, l.ntiles, p == 0 ? (unsigned long long)k : 0ull);
-      hipLaunchKernelGGL(k_pick, 1, kBlock, 0, s, ctrl, shifts[p], p == 2 ? 2 : 0, (unsigned long long)k);
+                         select_seed, index_base, l.ntiles, p == 0 ? (unsigned long long)k : 0ull,
+                         p == 2 ? 2 : 0, (unsigned long long)k, fuse ? 1 : 0);
+      if (!fuse) hipLaunchKernelGGL(k_pick, 1, kBlock, 0, s, ctrl, shifts[p], p == 2 ? 2 : 0, (unsigned long long)k);
     }
 
-    // 6: counts per unit (candidates) or per tile (fallback), and their scan
-    hipLaunchKernelGGL(k_bcount, ugrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
-                       (const float*)l.pool_val, l.chunk_gt, l.chunk_eq);
-    hipLaunchKernelGGL((k_count<RAND>), cgrid, kBlock, 0, s, ctrl, (const float*)res, n, l.chunk_gt, l.chunk_eq,
-                       select_seed, index_base);
+    // 6: counts per unit (candidates) or per tile (fallback), and their scan (folded into
+    // the count kernel when the counts are few)
     const unsigned long long* nch_dev = &ctrl->nchunks;
-    if (l.max_chunks <= 8 * kScanChunk) {
-      hipLaunchKernelGGL(k_scan_small, 1, kBlock, 0, s, (const uint32_t*)l.chunk_gt, (const uint32_t*)l.chunk_eq,
-                         nch_dev, (int64_t)0, l.gt_excl, l.eq_excl);
-    } else {
+    const bool small_scan = l.max_chunks <= 8 * kScanChunk;
+    const SmallScan sc{l.chunk_gt, l.chunk_eq, nch_dev, 0, l.gt_excl, l.eq_excl};
+    hipLaunchKernelGGL(k_bcount<false>, ugrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
+                       (const float*)l.pool_val, l.chunk_gt, l.chunk_eq, sc);
+    if (small_scan)
+      hipLaunchKernelGGL((k_count<RAND, true>), cgrid, kBlock, 0, s, ctrl, (const float*)res, n, l.chunk_gt,
+                         l.chunk_eq, select_seed, index_base, sc);
+    else
+      hipLaunchKernelGGL((k_count<RAND, false>), cgrid, kBlock, 0, s, ctrl, (const float*)res, n, l.chunk_gt,
+                         l.chunk_eq, select_seed, index_base, sc);
+    if (!small_scan) {
       const int cscan = clamp_grid(cdiv(l.max_chunks, kScanChunk), cus * 4);
       hipLaunchKernelGGL(k_scan_up, cscan, kBlock, 0, s, l.chunk_gt, l.chunk_eq, nch_dev, (int64_t)0, l.scan_up);
       hipLaunchKernelGGL(k_scan_mid, 1, kBlock, 0, s, nch_dev, (int64_t)0, l.scan_up);
@@ -1697,19 +1776,29 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
                        index_base, out_idx, vals, zero_res, k, (const float*)l.pool_c, select_seed, pd,
                        quant ? 1u : 0u);
 
-  // 8: QSGD on the kept values and the residual of the kept set
+  // 8: QSGD on the kept values and the residual of the kept set; deferred, with a small
+  // tile count, one more block scans the per-tile kept counts the emit wrote
+  // (tile_first = their exclusive scan)
+  const SmallScan tsc{pd.tile_cnt, nullptr, nullptr, l.ntiles, pd.tile_first, nullptr};
+  const bool small_tiles = l.ntiles <= 16 * kScanChunk;
+  bool tile_scan_done = false;
   if (quant) {
     int lpg_log2 = 0;
     while ((int64_t(4) << lpg_log2) < qsgd_group) ++lpg_log2;
-    const int qgrid = clamp_grid(cdiv(cdiv(k, 4), kBlock), cus * 16);
-    if (mon)
-      hipLaunchKernelGGL((k_qsgd_kept<DEFER, true>), qgrid, kBlock, 0, s, (const float*)vals, k, lpg_log2,
-                         (float)qsgd_levels, qsgd_seed, out_codes, out_norms, (const int64_t*)out_idx,
-                         index_base, res, n, pd, l.mon_g);
-    else
-      hipLaunchKernelGGL((k_qsgd_kept<DEFER, false>), qgrid, kBlock, 0, s, (const float*)vals, k, lpg_log2,
-                         (float)qsgd_levels, qsgd_seed, out_codes, out_norms, (const int64_t*)out_idx,
-                         index_base, res, n, pd, (double*)nullptr);
+    const bool scan = DEFER && small_tiles;
+    const int qgrid = clamp_grid(cdiv(cdiv(k, 4), kBlock), cus * 16) + (scan ? 1 : 0);
+    double* mg = mon ? l.mon_g : nullptr;
+#define GC_QSGD_KEPT(M, S)                                                                              \
+  hipLaunchKernelGGL((k_qsgd_kept<DEFER, M, S>), qgrid, kBlock, 0, s, (const float*)vals, k, lpg_log2,   \
+                     (float)qsgd_levels, qsgd_seed, out_codes, out_norms, (const int64_t*)out_idx,       \
+                     index_base, res, n, pd, mg, tsc)
+    if (mon) {
+      if (scan) GC_QSGD_KEPT(true, true); else GC_QSGD_KEPT(true, false);
+    } else {
+      if (scan) GC_QSGD_KEPT(false, true); else GC_QSGD_KEPT(false, false);
+    }
+#undef GC_QSGD_KEPT
+    tile_scan_done = scan;
   } else if (mon) {
     // pure selection sends the kept values themselves
     hipLaunchKernelGGL(k_sq_chunks, (unsigned)l.kchunks, kBlock, 0, s, (const float*)vals, k, l.mon_g);
@@ -1721,11 +1810,10 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
     hipLaunchKernelGGL(k_mon_final, 1, kBlock, 0, s, (const double*)l.mon_c2, nc2, (const double*)l.mon_g2, ng2,
                        stats);
   }
-  if (DEFER) {
+  if (DEFER && !tile_scan_done) {
     // tile_first = exclusive scan of the per-tile kept counts
-    if (l.ntiles <= 16 * kScanChunk) {
-      hipLaunchKernelGGL(k_scan_small, 1, kBlock, 0, s, (const uint32_t*)pd.tile_cnt, (const uint32_t*)nullptr,
-                         (const unsigned long long*)nullptr, l.ntiles, pd.tile_first, (unsigned long long*)nullptr);
+    if (small_tiles) {
+      hipLaunchKernelGGL(k_scan_small, 1, kBlock, 0, s, tsc);
     } else {
       const int tscan = clamp_grid(cdiv(l.ntiles, kScanChunk), cus * 4);
       hipLaunchKernelGGL(k_scan_up, tscan, kBlock, 0, s, (const uint32_t*)pd.tile_cnt, (const uint32_t*)nullptr,
