@@ -237,7 +237,7 @@ def ddp_hook_row(torch, gc, dev, say):
     os.dup2(2, 1)
     dist.init_process_group("nccl", init_method=f"tcp://127.0.0.1:{port}", rank=0, world_size=1)
     try:
-        def build(hook):
+        def build(hook, overlap=True):
             torch.manual_seed(0)
             layers = []
             for _ in range(6):
@@ -246,7 +246,7 @@ def ddp_hook_row(torch, gc, dev, say):
                     gradient_as_bucket_view=True)
             state = None
             if hook:
-                state = CompressionHookState(ratio=0.01, qsgd_levels=127, deferred=True)
+                state = CompressionHookState(ratio=0.01, qsgd_levels=127, deferred=True, overlap=overlap)
                 m.register_comm_hook(state, ef_compress_hook)
             return m, state
 
@@ -266,6 +266,9 @@ def ddp_hook_row(torch, gc, dev, say):
         nb = len(state.buckets)
         k = sum(b.k for b in state.buckets.values())
         del m1, state
+        m2, _ = build(True, overlap=False)
+        serial = it_ms(m2)
+        del m2
     finally:
         dist.destroy_process_group()
         sys.stdout.flush()
@@ -278,7 +281,8 @@ def ddp_hook_row(torch, gc, dev, say):
     _row("next-4 DDP comm hook, world size 1 (EF Top-1% + QSGD-127, deferred)",
          f"6 x Linear(4096, 4096), {n:,} parameters in {nb} buckets of <= 25 MiB, batch 64", ub,
          "iteration (time over DDP's own hook)", extra, extra,
-         extra={"iteration_ms_allreduce_hook": round(base, 4), "iteration_ms_compression_hook": round(hooked, 4)})
+         extra={"iteration_ms_allreduce_hook": round(base, 4), "iteration_ms_compression_hook": round(hooked, 4),
+                "iteration_ms_compression_hook_same_stream": round(serial, 4)})
 
 
 def rows_mode(args):

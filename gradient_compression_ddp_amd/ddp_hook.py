@@ -7,16 +7,18 @@ memory, overlapped with the backward pass); aiqz.cc "梯度聚合通信优化实
 filled it) and "通信瓶颈分析" (the aggregate is the average over workers);
 zyxy.net/archives/25733, section 四 (compress, exchange, decompress before the update).
 
-Per bucket and step, on the stream DDP runs the hook on:
+Per bucket and step:
   1. gc_ef_compress: c = bucket + residual, exact Top-k (or Random-k) of c, QSGD of the
      kept values, written straight into this rank's payload (the 128-byte header and the
      idx / codes / norms sections of the wire format), the kept set's residual deferred
      to the bucket's next step by default;
   2. all_gather of the fixed-size payloads (every rank's k and layout are equal);
   3. gc_decompress_payloads: the bucket becomes the average of the W decoded payloads.
-The library's calls are asynchronous on the current stream, and step 3 runs as the
-continuation of the all_gather future, so the whole hook overlaps the rest of the
-backward pass the way DDP's own all-reduce does.
+The library's calls are asynchronous, and step 3 runs as the continuation of the
+all_gather future.  With `overlap` (the default) steps 1 and 2 run on a side stream of the
+hook's own (default priority) that first waits for the bucket to be ready, so the
+backward pass of the earlier layers keeps running on DDP's stream while the bucket is
+compressed; DDP waits for the returned future before it uses the bucket.
 
 State per bucket (keyed by DDP's bucket index and size; DDP may regroup buckets after its
 first iteration, and a bucket whose size changes starts from a zero residual): residual,
@@ -63,7 +65,9 @@ class CompressionHookState:
     deferred: bool = True             # kept-set residual applied by the bucket's next step
     monitor: bool = False             # keep the norm-ratio stats of every bucket
     seed: int = 0
+    overlap: bool = True              # compress and exchange on a side stream
     buckets: Dict[int, _Bucket] = field(default_factory=dict)
+    side_stream: Optional[torch.cuda.Stream] = None
     # tests: when a list, (bucket index, step, bucket before, bucket after) is appended
     capture: Optional[List[Tuple[int, int, torch.Tensor, torch.Tensor]]] = None
 
@@ -100,7 +104,9 @@ class CompressionHookState:
 
     def flush(self) -> None:
         """Apply every bucket's pending record, so each residual is exact (e.g. before a
-        checkpoint of the residuals)."""
+        checkpoint of the residuals), on the current stream, after the side stream's work."""
+        if self.side_stream is not None:
+            torch.cuda.current_stream().wait_stream(self.side_stream)
         for b in self.buckets.values():
             if b.pending is not None:
                 ef_flush(b.residual, b.pending)
@@ -114,18 +120,25 @@ def ef_compress_hook(state: CompressionHookState, bucket: dist.GradBucket) -> to
     b = state.bucket(index, buf.numel(), buf.device)
     step = b.calls
     b.calls += 1
-    before = buf.clone() if state.capture is not None else None
     sel_seed, q_seed = state.seeds(index, step)
     sec = payload_sections(b.payload, b.header)
     if state.qsgd_levels > 0:
         outs = dict(out_codes=sec["codes"], out_norms=sec["meta0"], want_values=False)
     else:
         outs = dict(out_val=sec["codes"])
-    ef_compress(buf, b.residual, b.k, select=state.select, select_seed=sel_seed, pending=b.pending, stats=b.stats,
-                qsgd_levels=state.qsgd_levels, qsgd_group=state.qsgd_group, qsgd_seed=q_seed,
-                out_idx=sec["idx"], workspace=b.workspace, **outs)
+    stream = torch.cuda.current_stream()
+    if state.overlap:
+        if state.side_stream is None:
+            state.side_stream = torch.cuda.Stream(device=buf.device)
+        state.side_stream.wait_stream(stream)      # the bucket's gradients are complete
+        stream = state.side_stream
     W = dist.get_world_size(state.process_group)
-    work = dist.all_gather_into_tensor(b.gathered, b.payload, group=state.process_group, async_op=True)
+    with torch.cuda.stream(stream):
+        before = buf.clone() if state.capture is not None else None
+        ef_compress(buf, b.residual, b.k, select=state.select, select_seed=sel_seed, pending=b.pending,
+                    stats=b.stats, qsgd_levels=state.qsgd_levels, qsgd_group=state.qsgd_group, qsgd_seed=q_seed,
+                    out_idx=sec["idx"], workspace=b.workspace, **outs)
+        work = dist.all_gather_into_tensor(b.gathered, b.payload, group=state.process_group, async_op=True)
 
     def decode(fut):
         views = [b.gathered[w * b.stride:(w + 1) * b.stride] for w in range(W)]

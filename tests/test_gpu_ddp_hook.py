@@ -1,7 +1,8 @@
 """GPU parity of the DDP communication hook at world size 1 (one process, NCCL on the one
 GPU): every bucket DDP hands to the hook, over three training iterations, is checked bit
 for bit against the oracle's EF step (carrying the oracle's residual per bucket) followed
-by the oracle's receive (average of W = 1 decoded payloads into +0.0)."""
+by the oracle's receive (average of W = 1 decoded payloads into +0.0), with the hook's
+work on its side stream and on DDP's own stream."""
 import socket
 
 import numpy as np
@@ -46,8 +47,9 @@ def oracle_bucket(before, r, k, levels, q_seed, select, sel_seed):
     return out, new_res
 
 
-@pytest.mark.parametrize("select,levels,deferred", [("topk", 127, True), ("topk", 0, False), ("randk", 15, True)])
-def test_ddp_hook_world_size_one(pg, select, levels, deferred):
+@pytest.mark.parametrize("select,levels,deferred,overlap", [("topk", 127, True, True), ("topk", 0, False, True),
+                                                             ("randk", 15, True, True), ("topk", 127, True, False)])
+def test_ddp_hook_world_size_one(pg, select, levels, deferred, overlap):
     import torch
     from torch.nn.parallel import DistributedDataParallel as DDP
     from gradient_compression_ddp_amd.ddp_hook import CompressionHookState, ef_compress_hook
@@ -56,7 +58,8 @@ def test_ddp_hook_world_size_one(pg, select, levels, deferred):
     model = torch.nn.Sequential(torch.nn.Linear(256, 512), torch.nn.ReLU(), torch.nn.Linear(512, 512),
                                 torch.nn.ReLU(), torch.nn.Linear(512, 64)).cuda()
     ddp = DDP(model, device_ids=[0], bucket_cap_mb=0.5, gradient_as_bucket_view=True)
-    state = CompressionHookState(ratio=0.02, qsgd_levels=levels, select=select, deferred=deferred, seed=3)
+    state = CompressionHookState(ratio=0.02, qsgd_levels=levels, select=select, deferred=deferred, seed=3,
+                                 overlap=overlap)
     state.capture = []
     ddp.register_comm_hook(state, ef_compress_hook)
     gen = torch.Generator(device="cuda").manual_seed(1)
