@@ -14,7 +14,10 @@ HEADER = os.path.join(ROOT, "include", "gc.h")
 @pytest.fixture(scope="module")
 def lib():
     path = ensure_built()
-    return ctypes.CDLL(path)
+    lib = ctypes.CDLL(path)
+    lib.gc_status_string.restype = ctypes.c_char_p
+    lib.gc_last_error.restype = ctypes.c_char_p
+    return lib
 
 
 def declared_functions():
