@@ -148,9 +148,9 @@ def test_terngrad(gc, lens, base, ef):
 @pytest.mark.parametrize("sc", [2.0, 2.0 ** -70, 3.0e30])
 def test_terngrad_decision_boundaries(gc, sc):
     # |x| placed at U * s * (1 + d) for the element's own uniform U (taken from the oracle),
-    # with d from 0 to +-2^-19: straddles the band where the kernel leaves the product
-    # test for the division (and, with s = 2^-70, a scale below the product test's range);
-    # plus tiny values, denormals and zeros.  Codes must equal the oracle's bit for bit.
+    # with d from 0 to +-2^-19, so that fl(|x|/s) lands on, just above and just below U;
+    # scales far from 1 (2^-70, 3e30); plus tiny values, denormals and zeros.  Codes must
+    # equal the oracle's bit for bit.
     n, seed = 64 * 4096, 11
     u = oracle.uniform24(seed, np.arange(n, dtype=np.int64)).astype(np.float64)
     ds = np.array([0.0] + [sgn * 2.0 ** -e for e in range(19, 26) for sgn in (1, -1)])
@@ -175,6 +175,30 @@ def test_terngrad_layers_scaled(gc):
     p_d, s_d = gc.terngrad(dev(x), off, 3)
     assert_bits_equal(host(p_d), packed, "packed codes")
     assert_bits_equal(host(s_d), scales, "scales")
+
+
+@pytest.mark.parametrize("ef,base", [(False, 0), (True, 3), (False, 1 << 35)])
+def test_terngrad_many_segments(gc, ef, base):
+    # 100 segments (more than one launch batch of 32): ragged lengths including empty and
+    # one-element segments, starts at every offset mod 4, scales spread over 9 decades.
+    rng = np.random.default_rng(21)
+    lens = rng.integers(0, 30_000, 100)
+    lens[::7] = 0
+    lens[3::11] = 1
+    lens[5::13] = rng.integers(4096, 70_000, lens[5::13].size)
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    n = int(off[-1])
+    x = workloads.bucket(n, seed=22)
+    for s in range(lens.size):
+        x[off[s]:off[s + 1]] *= F32(10.0 ** (s % 9 - 4))
+    r = (workloads.bucket(n, seed=23) * F32(1e-3)).astype(F32) if ef else None
+    packed, scales, _, _, r_new = oracle.terngrad(x, off, seed=13, index_base=base, residual=r)
+    rd = dev(r) if ef else None
+    p_d, s_d = gc.terngrad(dev(x), off, 13, index_base=base, residual=rd)
+    assert_bits_equal(host(s_d), scales, "scales")
+    assert_bits_equal(host(p_d), packed, "packed codes")
+    if ef:
+        assert_bits_equal(host(rd), r_new, "residual")
 
 
 # ---------------------------------------------------------------- EF Top-K ---------
