@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0
 VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
 # VALU lane-instructions per element of the quantizer kernels (SQ_INSTS_VALU x 64 /
 # elements, rocprofv3 counters of bench.py --rows; profiles/compressor_rows_valu_and_traffic.md).
-VALU_LANE_OPS_PER_ELEMENT = {"minmax8": 44.5, "minmax4": 44.8, "qsgd": 59.1, "tern_max": 8.9, "tern_codes": 44.9}
+VALU_LANE_OPS_PER_ELEMENT = {"minmax8": 44.5, "minmax4": 44.8, "qsgd": 59.1, "terngrad": 47.1}
 
 # HBM bytes per launch of the streaming pass on this workload, from two rocprofv3 counter
 # runs per mode (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, factors from a plain 4 GiB device
@@ -522,7 +522,7 @@ def rows_mode(args):
     _row("a5+a7 TernGrad, per-layer scale", "24 layers x 14,583,333 (t(3) x lognormal(-7,1) scales)",
          4.0 * n3 + nbytes + 4.0 * L3, "call (all 24 layers)", gms, eager, osec, 1.0 / L3,
          "one layer of 14,583,333, scaled by 24",
-         valu_ops=(VALU_LANE_OPS_PER_ELEMENT["tern_max"] + VALU_LANE_OPS_PER_ELEMENT["tern_codes"]) * n3)
+         valu_ops=VALU_LANE_OPS_PER_ELEMENT["terngrad"] * n3)
     del xt, pk, wst
 
     # c4: PowerSGD rank 4 on the three matrix shapes, error feedback on.
