@@ -1695,8 +1695,11 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
   const int64_t expect_cand = (int64_t)((double)j * (double)n / (double)m);
   int hgrid = clamp_grid(cdiv(expect_cand, 16384), cus * 4);
   if (hgrid < 32) hgrid = 32;
-  for (int p = 0; p < 3; ++p) {
-    const int op = p == 2 ? (exact ? 3 : 1) : 0;
+  // a bound needs only the sample key's top 22 bits (L = that prefix, its low 9 bits 0:
+  // 2^9 ulps below the sample's key); the exact select resolves all 31
+  const int spasses = exact ? 3 : 2;
+  for (int p = 0; p < spasses; ++p) {
+    const int op = p == spasses - 1 ? (exact ? 3 : 1) : 0;
     const bool fuse = sgrid <= kFusePickGrid;
     hipLaunchKernelGGL((k_hist<0>), sgrid, kBlock, 0, s, ctrl, l.sample, m, (const float*)nullptr,
                        (int64_t)0, (const float*)nullptr, n, shifts[p], widths[p], (uint64_t)0, (int64_t)0,
