@@ -101,6 +101,23 @@ __device__ __forceinline__ uint32_t philox_word(uint64_t seed, uint64_t e) {
 }
 
 // ---------------------------------------------------------------------------------
+// fl(t / s) for a QSGD level count s in [1, 127] and t = 0 or t >= 2^-100, with
+// ys = fl(1/s): the product q0 = fl(t * ys), then one correction with the exact remainder
+// fma(-q0, s, t).  On that domain it equals the IEEE quotient for every s (checked
+// exhaustively on the CPU, every binary32 t of the domain) except t = +Inf, whose
+// remainder is NaN; there, and for NaN t, q0 (+Inf or NaN) is the quotient.  Below 2^-100
+// it can miss: for even s that are not powers of two a subnormal quotient can be an exact
+// midpoint, which the correction rounds the wrong way, so callers divide there.  Three
+// full-rate operations and a select in place of the division sequence.
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ float div_level_count(float t, float s, float ys) {
+  const float q0 = t * ys;
+  const float r = __builtin_fmaf(-q0, s, t);
+  const float q = __builtin_fmaf(r, ys, q0);
+  return t <= 3.40282346638528859812e+38f ? q : q0;
+}
+
+// ---------------------------------------------------------------------------------
 // Float encodings.
 // ---------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t fbits(float f) { return __float_as_uint(f); }

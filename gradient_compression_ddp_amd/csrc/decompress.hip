@@ -37,13 +37,36 @@ __device__ __forceinline__ float decode_one(uint32_t q, float m0, float m1, floa
   return q == 1u ? m0 : (q == 3u ? -m0 : 0.f);
 }
 
+// The four QSGD values of a quad from its code bytes (word, element m in byte m) and the
+// norms of their groups: sign * fl(fl(nu * level) / s).  When every nu is >= 2^-100 each
+// t = fl(nu * level) is 0 or >= 2^-100 and the quotient comes from div_level_count (the
+// same value); otherwise from the division.
+__device__ __forceinline__ void qsgd_decode4(uint32_t word, const float nu[4], float s, float ys,
+                                             float v[4]) {
+  float t[4], mag[4];
+  bool small = false;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int c = (int)(int8_t)(uint8_t)(word >> (8 * m));
+    t[m] = nu[m] * (float)(c < 0 ? -c : c);
+    small |= !(nu[m] >= 0x1p-100f);
+    mag[m] = div_level_count(t[m], s, ys);
+  }
+  if (small) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) mag[m] = t[m] / s;
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) v[m] = (int8_t)(uint8_t)(word >> (8 * m)) < 0 ? -mag[m] : mag[m];
+}
+
 // Dense decode, entries [0, count) to out[0, count).  Requires out 16-byte aligned and
 // codes aligned to one quad's code bytes (16 for F32, 4 for 8-bit codes, 2 for int4).
 template <int KIND>
 __global__ __launch_bounds__(kBlock) void k_decompress_dense(int64_t count, const void* __restrict__ codes,
                                                              const float* __restrict__ meta0,
                                                              const float* __restrict__ meta1, int64_t G,
-                                                             int lg, float s, float alpha, int accumulate,
+                                                             int lg, float s, float ys, float alpha, int accumulate,
                                                              float* __restrict__ out) {
   const int64_t base = (int64_t)blockIdx.x * kTile;
   const uint8_t* c8 = reinterpret_cast<const uint8_t*>(codes);
@@ -79,9 +102,19 @@ __global__ __launch_bounds__(kBlock) void k_decompress_dense(int64_t count, cons
     const int64_t e0 = base + j * (kBlock * 4) + threadIdx.x * 4;
     if (e0 >= count) continue;
     float v[4];
+    if (KIND == KIND_QSGD) {
+      float nu[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int64_t e = e0 + m;
+        nu[m] = e < count ? meta0[lg >= 0 ? (e >> lg) : e / G] : 0.f;
+      }
+      qsgd_decode4(word[j], nu, s, ys, v);
+    }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      if (KIND == KIND_F32) {
+      if (KIND == KIND_QSGD) {
+      } else if (KIND == KIND_F32) {
         v[m] = fv[j][m];
       } else {
         const int64_t e = e0 + m;
@@ -174,7 +207,7 @@ struct FusedSrc {
 // cut the resident waves.)
 template <int KIND>
 __global__ __launch_bounds__(kBlock) void k_decode_sum(int W, FusedSrc src, int64_t count, int64_t G, int lg,
-                                                       float s, float alpha, int accumulate,
+                                                       float s, float ys, float alpha, int accumulate,
                                                        float* __restrict__ out) {
   const int64_t e0 = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * 4;
   if (e0 >= count) return;
@@ -222,8 +255,15 @@ __global__ __launch_bounds__(kBlock) void k_decode_sum(int W, FusedSrc src, int6
           else word |= (uint32_t)((c8[e >> 2] >> (2 * (e & 3))) & 3u) << (2 * m);
         }
       }
+      if (KIND == KIND_QSGD) {
+        float nu[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) nu[m] = e0 + m < count ? src.meta0[w][g[m]] : 0.f;
+        qsgd_decode4(word, nu, s, ys, v);
+      }
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
+        if (KIND == KIND_QSGD) continue;
         const bool in = e0 + m < count;
         const float m0 = in ? src.meta0[w][g[m]] : 0.f;
         const float m1 = (KIND == KIND_MINMAX8 || KIND == KIND_MINMAX4) && in ? src.meta1[w][g[m]] : 0.f;
@@ -271,7 +311,7 @@ hipError_t launch_decompress(int kind, const int64_t* idx, int64_t count, int64_
     const float sd = (float)(levels > 0 ? levels : 1);
 #define GC_LAUNCH_DENSE(K)                                                                          \
   hipLaunchKernelGGL((k_decompress_dense<K>), (unsigned)tiles, kBlock, 0, s, count, codes, meta0, meta1, \
-                     G, lg, sd, alpha, accumulate, out)
+                     G, lg, sd, 1.0f / sd, alpha, accumulate, out)
     switch (kind) {
       case KIND_F32: GC_LAUNCH_DENSE(KIND_F32); break;
       case KIND_MINMAX8: GC_LAUNCH_DENSE(KIND_MINMAX8); break;
@@ -335,7 +375,7 @@ hipError_t launch_decode_sum(int kind, int W, const void* const* codes, const fl
     }
     const int acc = w0 == 0 ? accumulate : 1;   // later launches add to what the first wrote
 #define GC_LAUNCH_SUM(K) \
-    hipLaunchKernelGGL((k_decode_sum<K>), blocks, kBlock, 0, s, nw, src, count, G, lg, sd, alpha, acc, out)
+    hipLaunchKernelGGL((k_decode_sum<K>), blocks, kBlock, 0, s, nw, src, count, G, lg, sd, 1.0f / sd, alpha, acc, out)
     switch (kind) {
       case KIND_F32: GC_LAUNCH_SUM(KIND_F32); break;
       case KIND_MINMAX8: GC_LAUNCH_SUM(KIND_MINMAX8); break;

@@ -1480,7 +1480,7 @@ __global__ __launch_bounds__(kBlock) void k_emit_all(TopkCtrl* __restrict__ ctrl
 // MON: the sum of g_hat^2 of each 1024 kept entries (float64, fixed order) goes to mon_g.
 template <bool DEFER, bool MON, bool SCAN>
 __global__ __launch_bounds__(kBlock) void k_qsgd_kept(const float* __restrict__ vals, int64_t k,
-                                                      int lpg_log2, float s, uint64_t seed,
+                                                      int lpg_log2, float s, float ys, uint64_t seed,
                                                       int8_t* __restrict__ codes, float* __restrict__ norms,
                                                       const int64_t* __restrict__ idx, int64_t index_base,
                                                       float* __restrict__ r, int64_t n, Pending pd,
@@ -1521,7 +1521,7 @@ __global__ __launch_bounds__(kBlock) void k_qsgd_kept(const float* __restrict__ 
       uniforms4(seed, (uint64_t)e0, u);
       int lev[4];
       float gh[4];
-      qsgd_quad(v, nu, s, u, lev, gh);
+      qsgd_quad(v, nu, s, ys, u, lev, gh);
       if (full) {
         *reinterpret_cast<uint32_t*>(codes + e0) = pack_codes4(lev);
       } else {
@@ -1793,7 +1793,8 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
     double* mg = mon ? l.mon_g : nullptr;
 #define GC_QSGD_KEPT(M, S)                                                                              \
   hipLaunchKernelGGL((k_qsgd_kept<DEFER, M, S>), qgrid, kBlock, 0, s, (const float*)vals, k, lpg_log2,   \
-                     (float)qsgd_levels, qsgd_seed, out_codes, out_norms, (const int64_t*)out_idx,       \
+                     (float)qsgd_levels, 1.0f / (float)qsgd_levels, qsgd_seed, out_codes, out_norms,     \
+                     (const int64_t*)out_idx,                                                             \
                      index_base, res, n, pd, mg, tsc)
     if (mon) {
       if (scan) GC_QSGD_KEPT(true, true); else GC_QSGD_KEPT(true, false);

@@ -30,7 +30,7 @@ constexpr int64_t kTile = (int64_t)kBlock * 4 * kRounds;   // 2048 elements
 // of the tile are issued before any arithmetic (non-temporal 16-byte loads and stores).
 template <bool EF>
 __global__ __launch_bounds__(kBlock) void k_qsgd(const float* __restrict__ x, float* __restrict__ res,
-                                                 int64_t n, int lpg_log2, float s, uint64_t seed,
+                                                 int64_t n, int lpg_log2, float s, float ys, uint64_t seed,
                                                  int64_t index_base, int8_t* __restrict__ codes,
                                                  float* __restrict__ norms) {
   const int lpg = 1 << lpg_log2;
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kBlock) void k_qsgd(const float* __restrict__ x, fl
     uniforms4(seed, (uint64_t)(index_base + e0), u);
     int lev[4];
     float gh[4];
-    qsgd_quad(v[j], nu, s, u, lev, gh);
+    qsgd_quad(v[j], nu, s, ys, u, lev, gh);
     if (full) {
       __builtin_nontemporal_store(pack_codes4(lev), reinterpret_cast<uint32_t*>(codes + e0));
       if (EF) {
@@ -103,10 +103,11 @@ hipError_t launch_qsgd(const float* x, float* res, int64_t n, int64_t group, int
   while ((int64_t(4) << lpg_log2) < group) ++lpg_log2;
   const int64_t blocks = (n + kTile - 1) / kTile;
   const float sf = (float)levels;
+  const float ys = 1.0f / sf;
   if (res)
-    hipLaunchKernelGGL((k_qsgd<true>), (int)blocks, kBlock, 0, s, x, res, n, lpg_log2, sf, seed, index_base, codes, norms);
+    hipLaunchKernelGGL((k_qsgd<true>), (int)blocks, kBlock, 0, s, x, res, n, lpg_log2, sf, ys, seed, index_base, codes, norms);
   else
-    hipLaunchKernelGGL((k_qsgd<false>), (int)blocks, kBlock, 0, s, x, res, n, lpg_log2, sf, seed, index_base, codes, norms);
+    hipLaunchKernelGGL((k_qsgd<false>), (int)blocks, kBlock, 0, s, x, res, n, lpg_log2, sf, ys, seed, index_base, codes, norms);
   return hipGetLastError();
 }
 

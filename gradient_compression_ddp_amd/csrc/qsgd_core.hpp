@@ -8,7 +8,8 @@
 
 namespace gc {
 
-__device__ __forceinline__ void qsgd_quad(const float v[4], float nu, float s, const float u[4],
+// ys = fl(1/s); the division by s goes through div_level_count (the same quotient).
+__device__ __forceinline__ void qsgd_quad(const float v[4], float nu, float s, float ys, const float u[4],
                                           int lev[4], float gh[4]) {
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -20,11 +21,19 @@ __device__ __forceinline__ void qsgd_quad(const float v[4], float nu, float s, c
       const float p = uu - l;
       level = fminf(l + (u[m] < p ? 1.f : 0.f), s);
     }
-    const float mag = (nu * level) / s;
-    const bool neg = v[m] < 0.f;
-    lev[m] = neg ? -(int)level : (int)level;
-    gh[m] = neg ? -mag : mag;
+    lev[m] = v[m] < 0.f ? -(int)level : (int)level;
+    gh[m] = nu * level;   // t, divided below
   }
+  // with nu >= 2^-100 every t = fl(nu * level) is 0 or >= 2^-100: div_level_count's domain
+  float mag[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) mag[m] = div_level_count(gh[m], s, ys);
+  if (!(nu >= 0x1p-100f)) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) mag[m] = gh[m] / s;
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) gh[m] = v[m] < 0.f ? -mag[m] : mag[m];
 }
 
 __device__ __forceinline__ uint32_t pack_codes4(const int lev[4]) {

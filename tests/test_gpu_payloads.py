@@ -171,3 +171,38 @@ def test_bucket_full_size_eight_workers(gc):
     gc.decompress_payloads(bufs, hdrs, out)
     want = expected(gc.KIND_QSGD, wants, n, 64, 15, F32(1.0) / F32(W), np.zeros(n, F32))
     assert_bits_equal(host(out), want, "bucket W=8")
+
+
+@pytest.mark.parametrize("levels", [6, 12, 126, 127])
+def test_qsgd_decode_small_norms_even_levels(gc, levels):
+    """QSGD codes with group norms from 1e-44 to 1e-28 (below and above 2^-100, where the
+    decoders switch between the division and the multiply-and-correct quotient) and level
+    counts with even factors, whose subnormal quotients can be exact rounding midpoints:
+    the dense decode and the W-payload receive must equal the oracle bit for bit."""
+    rng = np.random.default_rng(levels)
+    n, group, W = 64 * 300 + 17, 64, 3
+    ng = (n + group - 1) // group
+    bufs, hdrs, wants = [], [], []
+    for w in range(W):
+        codes = rng.integers(-levels, levels + 1, n).astype(np.int8)
+        nu = (10.0 ** rng.uniform(-44, -28, ng)).astype(F32)
+        nu[::5] = F32(2.0 ** -100)
+        nu[1::7] = np.nextafter(F32(2.0 ** -100), F32(0))
+        buf, h = new_payload(gc, gc.KIND_QSGD, n, n, group, levels)
+        sec = gc.payload_sections(buf, h)
+        sec["codes"].copy_(dev(codes.view(np.uint8)).view(sec["codes"].dtype))
+        sec["meta0"].copy_(dev(nu))
+        bufs.append(buf); hdrs.append(h); wants.append((codes, nu, None))
+    # dense decode of the first payload
+    out = dev(np.zeros(n, F32))
+    gc.decompress_scatter(gc.KIND_QSGD, gc.payload_sections(bufs[0], hdrs[0])["codes"], n, out,
+                          meta0=gc.payload_sections(bufs[0], hdrs[0])["meta0"], group=group, levels=levels)
+    want = oracle.decompress_scatter(gc.KIND_QSGD, None, n, 0, wants[0][0], wants[0][1], None, group, levels,
+                                     1.0, 0, np.zeros(n, F32))
+    assert_bits_equal(host(out), want, "dense decode")
+    # the fused receive of all three
+    out = dev(np.zeros(n, F32))
+    alpha = F32(1.0) / F32(W)
+    gc.decompress_payloads(bufs, hdrs, out, alpha=float(alpha))
+    assert_bits_equal(host(out), expected(gc.KIND_QSGD, wants, n, group, levels, alpha, np.zeros(n, F32)),
+                      "receive")
