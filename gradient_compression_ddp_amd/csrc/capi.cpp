@@ -215,6 +215,32 @@ int gc_decompress_payloads(int W, const void* const* payloads, const gc_payload_
                                             accumulate, out, s),
                       "gc_decompress_payloads launch");
   }
+  bool sparse = true;
+  for (int w = 0; w < W && sparse; ++w) sparse = (headers[w].flags & GC_PAYLOAD_SPARSE) != 0u;
+  if (sparse) {
+    // every payload sparse: merged tile by tile, out written once
+    std::vector<const int64_t*> ix(W);
+    std::vector<const void*> codes(W);
+    std::vector<const float*> m0(W), m1(W);
+    std::vector<int64_t> count(W), base(W), group(W);
+    std::vector<int> kind(W), levels(W);
+    for (int w = 0; w < W; ++w) {
+      const gc_payload_header& h = headers[w];
+      ix[w] = reinterpret_cast<const int64_t*>(at(w, h.off_idx));
+      codes[w] = at(w, h.off_codes);
+      m0[w] = reinterpret_cast<const float*>(at(w, h.off_meta0));
+      m1[w] = reinterpret_cast<const float*>(at(w, h.off_meta1));
+      count[w] = h.count;
+      base[w] = h.index_base;
+      group[w] = h.group;
+      kind[w] = h.kind;
+      levels[w] = h.levels;
+    }
+    return hip_status(gc::launch_merge_sparse(W, ix.data(), codes.data(), m0.data(), m1.data(), count.data(),
+                                              base.data(), group.data(), kind.data(), levels.data(), alpha,
+                                              accumulate, out, n_out, s),
+                      "gc_decompress_payloads launch");
+  }
   if (!accumulate) {
     const hipError_t e = gc::launch_fill_zero(out, n_out, s);
     if (e != hipSuccess) return hip_status(e, "gc_decompress_payloads launch");

@@ -286,6 +286,175 @@ __global__ __launch_bounds__(kBlock) void k_decode_sum(int W, FusedSrc src, int6
   }
 }
 
+// ---- the receive side: W sparse payloads merged tile by tile --------------------------
+// Each payload's idx is strictly ascending, so the entries of one output tile are a run of
+// consecutive entries of every payload.  A block walks kMergeTilesPerBlock tiles of 4096
+// outputs with one cursor per payload (a lower-bound search at its first tile).  Per tile,
+// wave v stages the tile's run of payload g0 + v (position in the tile and alpha * g_hat)
+// in LDS, then all threads add the staged runs into an LDS copy of the tile in payload
+// order, one barrier per payload, and the tile is written once.  A run longer than the
+// staging space is finished block-wide, in order, before the next payload.  The output
+// is written once and each payload read once, where the per-payload scatter read and wrote
+// a 64-byte sector of out for every entry (after a pass that cleared it).
+
+constexpr int kMergeTile = 4096;
+constexpr int kMergeTilesPerBlock = 8;
+constexpr int kMergeCap = 512;     // staged entries per payload per tile
+constexpr int kMergeBlock = 512;   // 8 waves: 8 payloads staged at once
+constexpr int kMergeWaves = kMergeBlock / kWave;
+
+struct SparseSrc {
+  const int64_t* idx[kMaxFused];
+  const void* codes[kMaxFused];
+  const float* meta0[kMaxFused];
+  const float* meta1[kMaxFused];
+  int64_t count[kMaxFused];
+  int64_t index_base[kMaxFused];
+  int64_t G[kMaxFused];
+  int lg[kMaxFused];      // log2(G), or -1
+  int kind[kMaxFused];
+  float s[kMaxFused];     // QSGD level count (1 for other kinds)
+};
+
+// g_hat of entry j of payload w, as k_decompress decodes it.
+__device__ __forceinline__ float decode_entry(const SparseSrc& S, int w, int64_t j) {
+  const int64_t g = S.lg[w] >= 0 ? (j >> S.lg[w]) : j / S.G[w];
+  const uint8_t* c8 = reinterpret_cast<const uint8_t*>(S.codes[w]);
+  switch (S.kind[w]) {
+    case KIND_F32:
+      return reinterpret_cast<const float*>(S.codes[w])[j];
+    case KIND_MINMAX8:
+      return (float)c8[j] * S.meta1[w][g] + S.meta0[w][g];
+    case KIND_MINMAX4: {
+      const uint32_t byte = c8[j >> 1];
+      const uint32_t q = (j & 1) ? (byte >> 4) : (byte & 15u);
+      return (float)q * S.meta1[w][g] + S.meta0[w][g];
+    }
+    case KIND_QSGD: {
+      const int c = (int)reinterpret_cast<const int8_t*>(S.codes[w])[j];
+      const float level = (float)(c < 0 ? -c : c);
+      const float mag = (S.meta0[w][g] * level) / S.s[w];
+      return c < 0 ? -mag : mag;
+    }
+    default: {
+      const uint32_t b = (c8[j >> 2] >> (2 * (j & 3))) & 3u;
+      const float sc = S.meta0[w][g];
+      return b == 1u ? sc : (b == 3u ? -sc : 0.f);
+    }
+  }
+}
+
+// First entry of idx[0, count) that is >= key.
+__device__ __forceinline__ int64_t lower_bound_i64(const int64_t* __restrict__ idx, int64_t count, int64_t key) {
+  int64_t lo = 0, hi = count;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (idx[mid] < key) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(kMergeBlock) void k_merge_sparse(int W, SparseSrc S, float alpha, int accumulate,
+                                                         int vec, float* __restrict__ out, int64_t n_out) {
+  __shared__ __align__(16) float tile[kMergeTile];
+  __shared__ uint16_t st_pos[kMergeWaves][kMergeCap];
+  __shared__ float st_val[kMergeWaves][kMergeCap];
+  __shared__ int64_t cur[kMaxFused];
+  __shared__ int st_n[kMergeWaves];
+  __shared__ int st_done[kMergeWaves];
+  __shared__ int s_cnt[kMergeWaves];
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int64_t ntiles = (n_out + kMergeTile - 1) / kMergeTile;
+  const int64_t t0 = (int64_t)blockIdx.x * kMergeTilesPerBlock;
+  const int64_t t1 = t0 + kMergeTilesPerBlock < ntiles ? t0 + kMergeTilesPerBlock : ntiles;
+  if ((int)threadIdx.x < W)
+    cur[threadIdx.x] = lower_bound_i64(S.idx[threadIdx.x], S.count[threadIdx.x],
+                                       t0 * kMergeTile + S.index_base[threadIdx.x]);
+  for (int64_t t = t0; t < t1; ++t) {
+    const int64_t q0 = t * kMergeTile;
+    const int len = n_out - q0 < kMergeTile ? (int)(n_out - q0) : kMergeTile;
+    const bool full = vec && len == kMergeTile;
+    if (full) {
+      for (int i = threadIdx.x; i < kMergeTile / 4; i += kMergeBlock)
+        reinterpret_cast<f32x4*>(tile)[i] =
+            accumulate ? reinterpret_cast<const f32x4*>(out + q0)[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
+      for (int i = threadIdx.x; i < len; i += kMergeBlock) tile[i] = accumulate ? out[q0 + i] : 0.f;
+    }
+    __syncthreads();   // the tile is initialised; cur holds this tile's first entries
+    for (int g0 = 0; g0 < W; g0 += kMergeWaves) {
+      const int w = g0 + wave;
+      if (w < W) {
+        const int64_t lo = q0 + S.index_base[w], lim = lo + len;
+        int64_t c = cur[w];
+        int n = 0;
+        bool done = false;
+        while (!done && n + kWave <= kMergeCap) {
+          const int64_t j = c + lane;
+          // the entry's code and metadata loads do not wait for its index
+          const bool in = j < S.count[w];
+          const int64_t e = in ? S.idx[w][j] : 0;
+          const float a = in ? alpha * decode_entry(S, w, j) : 0.f;
+          const bool ok = in && e >= lo && e < lim;    // ascending: the ok lanes are a prefix
+          const int cnt = __popcll(ballot(ok));
+          if (ok) {
+            st_pos[wave][n + lane] = (uint16_t)(e - lo);
+            st_val[wave][n + lane] = a;
+          }
+          n += cnt;
+          c += cnt;
+          done = cnt < kWave;
+        }
+        if (lane == 0) { st_n[wave] = n; st_done[wave] = done ? 1 : 0; cur[w] = c; }
+      }
+      __syncthreads();
+      for (int v = 0; v < kMergeWaves && g0 + v < W; ++v) {
+        const int n = st_n[v];
+        for (int i = threadIdx.x; i < n; i += kMergeBlock) {
+          const int p = st_pos[v][i];
+          tile[p] = tile[p] + st_val[v][i];
+        }
+        __syncthreads();
+        if (!st_done[v]) {
+          // the rest of payload g0 + v's run in this tile, block-wide and in order
+          const int w2 = g0 + v;
+          const int64_t lo = q0 + S.index_base[w2], lim = lo + len;
+          for (;;) {
+            const int64_t c = cur[w2];
+            const int64_t j = c + threadIdx.x;
+            int64_t e = 0;
+            bool ok = j < S.count[w2];
+            if (ok) e = S.idx[w2][j];
+            ok = ok && e >= lo && e < lim;
+            const int wc = __popcll(ballot(ok));   // every lane takes part in the ballot
+            if (lane == 0) s_cnt[wave] = wc;
+            if (ok) {
+              const int p = (int)(e - lo);
+              tile[p] = tile[p] + alpha * decode_entry(S, w2, j);
+            }
+            __syncthreads();
+            int total = 0;
+#pragma unroll
+            for (int i = 0; i < kMergeWaves; ++i) total += s_cnt[i];
+            __syncthreads();   // every thread has read cur[w2] and s_cnt
+            if (threadIdx.x == 0) cur[w2] = c + total;
+            __syncthreads();
+            if (total < kMergeBlock) break;
+          }
+        }
+      }
+    }
+    if (full) {
+      for (int i = threadIdx.x; i < kMergeTile / 4; i += kMergeBlock)
+        __builtin_nontemporal_store(reinterpret_cast<const f32x4*>(tile)[i], reinterpret_cast<f32x4*>(out + q0) + i);
+    } else {
+      for (int i = threadIdx.x; i < len; i += kMergeBlock) out[q0 + i] = tile[i];
+    }
+    __syncthreads();   // the tile is written before the next one is initialised
+  }
+}
+
 __global__ void k_fill_zero(float* __restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     p[i] = 0.f;
@@ -350,6 +519,43 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
   const int64_t cap = (int64_t)device_cu_count() * 8;
   if (blocks > cap) blocks = cap;
   hipLaunchKernelGGL(k_fill_zero, (unsigned)blocks, 256, 0, s, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_sparse(int W, const int64_t* const* idx, const void* const* codes,
+                               const float* const* meta0, const float* const* meta1, const int64_t* count,
+                               const int64_t* index_base, const int64_t* group, const int* kind,
+                               const int* levels, float alpha, int accumulate, float* out, int64_t n_out,
+                               hipStream_t s) {
+  if (n_out == 0 || W == 0) return hipSuccess;
+  const int64_t ntiles = (n_out + kMergeTile - 1) / kMergeTile;
+  const unsigned blocks = (unsigned)((ntiles + kMergeTilesPerBlock - 1) / kMergeTilesPerBlock);
+  const int vec = (reinterpret_cast<uintptr_t>(out) % 16) == 0 ? 1 : 0;
+  for (int w0 = 0; w0 < W; w0 += kMaxFused) {
+    const int nw = W - w0 < kMaxFused ? W - w0 : kMaxFused;
+    SparseSrc S{};
+    for (int i = 0; i < nw; ++i) {
+      const int w = w0 + i;
+      const int64_t G = group[w] == 0 ? (count[w] > 0 ? count[w] : 1) : group[w];
+      int lg = -1;
+      if ((G & (G - 1)) == 0) {
+        lg = 0;
+        while ((int64_t(1) << lg) < G) ++lg;
+      }
+      S.idx[i] = idx[w];
+      S.codes[i] = codes[w];
+      S.meta0[i] = meta0[w];
+      S.meta1[i] = meta1[w];
+      S.count[i] = count[w];
+      S.index_base[i] = index_base[w];
+      S.G[i] = G;
+      S.lg[i] = lg;
+      S.kind[i] = kind[w];
+      S.s[i] = (float)(levels[w] > 0 ? levels[w] : 1);
+    }
+    const int acc = w0 == 0 ? accumulate : 1;   // later launches add to what the first wrote
+    hipLaunchKernelGGL(k_merge_sparse, blocks, kMergeBlock, 0, s, nw, S, alpha, acc, vec, out, n_out);
+  }
   return hipGetLastError();
 }
 

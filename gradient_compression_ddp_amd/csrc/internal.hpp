@@ -74,6 +74,13 @@ hipError_t launch_decode_sum(int kind, int W, const void* const* codes, const fl
                              const float* const* meta1, int64_t count, int64_t group, int levels,
                              float alpha, int accumulate, float* out, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+// out[0..n_out) = (accumulate ? out : 0) + sum_w alpha * g_hat_w for W sparse payloads with
+// strictly ascending idx, merged tile by tile in payload order (16 payloads per launch).
+hipError_t launch_merge_sparse(int W, const int64_t* const* idx, const void* const* codes,
+                               const float* const* meta0, const float* const* meta1, const int64_t* count,
+                               const int64_t* index_base, const int64_t* group, const int* kind,
+                               const int* levels, float alpha, int accumulate, float* out, int64_t n_out,
+                               hipStream_t s);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

@@ -344,7 +344,7 @@ int gc_decompress_scatter(int kind, const int64_t* idx, int64_t count, int64_t i
  *
  * A payload is one contiguous byte buffer: this 128-byte header, then the sections it
  * lists, each starting at a multiple of 256 bytes from the payload start:
- *   idx    int64[count], ascending  (sparse payloads only; flags & GC_PAYLOAD_SPARSE)
+ *   idx    int64[count], strictly ascending  (sparse payloads only; flags & GC_PAYLOAD_SPARSE)
  *   codes  as for gc_decompress_scatter: float[count] (F32), uint8[count] (MINMAX8),
  *          uint8[ceil(count/2)] (MINMAX4), int8[count] (QSGD), uint8[ceil(count/4)] (TERN)
  *   meta0  float[ng]: mins (MINMAX*), norms (QSGD), scales (TERN); absent for F32
@@ -393,9 +393,13 @@ int gc_payload_layout(int kind, int64_t n, int64_t count, int64_t group, int lev
  * their W headers (the caller holds them: it built them, or read them after the gather).
  * Each payload must encode n <= n_out elements.  W in [1, 1024].
  * When every payload is dense with the same kind, count, group and levels, one pass
- * reads all W code streams and writes out once (up to 16 payloads per launch);
- * otherwise out is cleared (if accumulate == 0) and the payloads are added one launch
- * each.  Needs no workspace.
+ * reads all W code streams and writes out once (up to 16 payloads per launch).  When
+ * every payload is sparse, the payloads are merged tile by tile (their idx must be
+ * strictly ascending, as the wire format requires and gc_ef_compress writes them; with
+ * unsorted idx the result is undefined but every access stays inside its buffers), each
+ * payload read once and out written once (up to 16 payloads per launch).  Otherwise out
+ * is cleared (if accumulate == 0) and the payloads are added one launch each.  Needs no
+ * workspace.
  */
 int gc_decompress_payloads(int W, const void* const* payloads, const gc_payload_header* headers,
                            float alpha, int accumulate, float* out, int64_t n_out, void* stream);

@@ -206,3 +206,74 @@ def test_qsgd_decode_small_norms_even_levels(gc, levels):
     gc.decompress_payloads(bufs, hdrs, out, alpha=float(alpha))
     assert_bits_equal(host(out), expected(gc.KIND_QSGD, wants, n, group, levels, alpha, np.zeros(n, F32)),
                       "receive")
+
+
+def _random_sparse_payload(gc, rng, kind, n_out, count, base, dense_span=None):
+    """A hand-made sparse payload: strictly ascending idx (some positions below 0 or past
+    n_out, which the receiver skips), random codes and metadata.  Returns the buffer, its
+    header and what the oracle needs."""
+    if dense_span is not None:
+        pos = np.arange(*dense_span, dtype=np.int64)
+        count = pos.size
+    else:
+        pos = np.sort(rng.choice(np.arange(-300, n_out + 300, dtype=np.int64), count, replace=False))
+    group, levels = {gc.KIND_F32: (0, 0), gc.KIND_MINMAX8: (50, 0), gc.KIND_MINMAX4: (64, 0),
+                     gc.KIND_QSGD: (64, 127), gc.KIND_TERN: (0, 0)}[kind]
+    buf, h = new_payload(gc, kind, n_out, count, group, levels, True, base)
+    sec = gc.payload_sections(buf, h)
+    idx = pos + base
+    ng = 0 if count == 0 else (count + (group or count) - 1) // (group or count)
+    if kind == gc.KIND_F32:
+        codes = rng.standard_normal(count).astype(F32)
+    elif kind == gc.KIND_QSGD:
+        codes = rng.integers(-127, 128, count).astype(np.int8)
+    elif kind == gc.KIND_MINMAX8:
+        codes = rng.integers(0, 256, count).astype(np.uint8)
+    elif kind == gc.KIND_MINMAX4:
+        codes = rng.integers(0, 256, (count + 1) // 2).astype(np.uint8)
+    else:
+        q = rng.choice(np.array([0, 1, 3], np.uint8), (count + 3) // 4 * 4)
+        codes = (q[0::4] | (q[1::4] << 2) | (q[2::4] << 4) | (q[3::4] << 6)).astype(np.uint8)
+    m0 = (rng.standard_normal(ng) * 0.1).astype(F32)
+    m1 = np.abs(rng.standard_normal(ng) * 0.01).astype(F32) if kind in (gc.KIND_MINMAX8, gc.KIND_MINMAX4) else None
+    if count:
+        sec["idx"].copy_(dev(idx))
+        sec["codes"].copy_(dev(codes).view(sec["codes"].dtype))
+        if "meta0" in sec:
+            sec["meta0"].copy_(dev(m0 if kind != gc.KIND_QSGD else np.abs(m0)))
+        if "meta1" in sec:
+            sec["meta1"].copy_(dev(m1))
+    if kind == gc.KIND_QSGD:
+        m0 = np.abs(m0)
+    return buf, h, (kind, idx, count, base, codes, m0, m1, group, levels)
+
+
+@pytest.mark.parametrize("W,accumulate", [(8, False), (17, True), (3, False)])
+def test_sparse_merge_many_kinds(gc, W, accumulate):
+    """All-sparse receive (the tile-by-tile merge): every payload kind, ragged output,
+    positions outside [0, n_out) skipped, an empty payload, a dense run longer than the
+    staging space, more payloads than one launch takes; order of the terms per element is
+    payload order (the oracle adds them one payload at a time)."""
+    rng = np.random.default_rng(W)
+    n_out = 5 * 8 * 4096 + 1234
+    kinds = [gc.KIND_F32, gc.KIND_QSGD, gc.KIND_MINMAX8, gc.KIND_MINMAX4, gc.KIND_TERN]
+    bufs, hdrs, specs = [], [], []
+    for w in range(W):
+        kind = kinds[w % len(kinds)]
+        base = int(rng.integers(0, 1 << 40))
+        if w == 1:
+            b, h, spec = _random_sparse_payload(gc, rng, kind, n_out, 0, base, dense_span=(2 * 4096 + 100, 4 * 4096 + 50))
+        elif w == 2:
+            b, h, spec = _random_sparse_payload(gc, rng, kind, n_out, 0, base)
+        else:
+            b, h, spec = _random_sparse_payload(gc, rng, kind, n_out, int(rng.integers(100, n_out // 20)), base)
+        bufs.append(b); hdrs.append(h); specs.append(spec)
+    init = np.linspace(-1, 1, n_out, dtype=F32) if accumulate else np.zeros(n_out, F32)
+    alpha = F32(1.0) / F32(W)
+    off = 1000
+    big = np.concatenate([np.zeros(off, F32), init, np.zeros(off, F32)])
+    for kind, idx, count, base, codes, m0, m1, group, levels in specs:
+        oracle.decompress_scatter(kind, idx, count, base - off, codes, m0, m1, group, levels, alpha, True, big)
+    out = dev(init)
+    gc.decompress_payloads(bufs, hdrs, out, alpha=float(alpha), accumulate=accumulate)
+    assert_bits_equal(host(out), big[off:off + n_out], f"W {W}")
