@@ -77,14 +77,43 @@ __device__ __forceinline__ float quantize_one(float v, float mn, float scale, fl
   return q;
 }
 
-template <int BITS, bool EF>
+// RCP: the quad shares one (min, scale) and rsc = fl(1/scale).  A code needs only the
+// nearest integer of fl(d / scale), d = fl(x - min): both that quotient and q0 = fl(d * rsc)
+// lie below 256, where |q0 - fl(d / scale)| <= 2^-16 (rsc's relative error, at most 2^-24,
+// times 256) + 2^-17 + 2^-17 (the two roundings) = 2^-15.  So when q0 is at least 2^-14
+// from every half-integer, rint(q0) is the code; otherwise (and for NaN or infinite q0) the
+// quad takes the division.  Without RCP every element takes the division.
+template <int BITS, bool EF, bool RCP>
 __device__ __forceinline__ void emit_quad(const Quad& qd, int64_t e0, int64_t n, const float mn[4],
-                                          const float sc[4], uint8_t* __restrict__ codes,
+                                          const float sc[4], float rsc, uint8_t* __restrict__ codes,
                                           float* __restrict__ res) {
   uint32_t c[4];
   float gh[4];
+  if (RCP) {
+    constexpr float L = (float)((1 << BITS) - 1);
+    const float mn0 = mn[0], scale = sc[0];
+    float q[4];
+    bool slow = false;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) c[m] = (uint32_t)quantize_one<BITS>(qd.v[m], mn[m], sc[m], &gh[m]);
+    for (int m = 0; m < 4; ++m) {
+      const float q0 = (qd.v[m] - mn0) * rsc;
+      q[m] = rintf(q0);
+      slow |= !(fabsf(q0 - q[m]) <= 0.5f - 0x1p-14f);
+    }
+    if (slow && scale != 0.f) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) q[m] = rintf((qd.v[m] - mn0) / scale);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float qq = scale != 0.f ? fminf(fmaxf(q[m], 0.f), L) : 0.f;
+      gh[m] = qq * scale + mn0;
+      c[m] = (uint32_t)qq;
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) c[m] = (uint32_t)quantize_one<BITS>(qd.v[m], mn[m], sc[m], &gh[m]);
+  }
   const bool full = e0 + 4 <= n;
   if (BITS == 8) {
     if (full) {
@@ -160,7 +189,7 @@ __global__ __launch_bounds__(kBlock) void k_minmax_small(const float* __restrict
     const float mn = ord_dec(lo), mx = ord_dec(hi);
     const float scale = (mx - mn) / L;
     const float mna[4] = {mn, mn, mn, mn}, sca[4] = {scale, scale, scale, scale};
-    emit_quad<BITS, EF>(qd[j], e0, n, mna, sca, codes, res);
+    emit_quad<BITS, EF, true>(qd[j], e0, n, mna, sca, 1.0f / scale, codes, res);
     if ((lane & (lpg - 1)) == 0) {
       const int64_t g = e0 >> (lpg_log2 + 2);
       mins[g] = mn;
@@ -279,7 +308,7 @@ __global__ __launch_bounds__(kBlock) void k_minmax_quant(const float* __restrict
       mn[m] = inA ? mnA : mnB;
       sc[m] = inA ? scA : scB;
     }
-    emit_quad<BITS, EF>(qd, e0, n, mn, sc, codes, res);
+    emit_quad<BITS, EF, false>(qd, e0, n, mn, sc, 0.f, codes, res);
   }
 }
 
@@ -353,11 +382,12 @@ __global__ __launch_bounds__(kBlock) void k_minmax_tensor_quant(const float* __r
   const float scale = (mx - mn) / L;
   if (blockIdx.x == 0 && threadIdx.x == 0) { mins[0] = mn; scales[0] = scale; }
   const float mna[4] = {mn, mn, mn, mn}, sca[4] = {scale, scale, scale, scale};
+  const float rsc = 1.0f / scale;
   const int64_t nquads = (n + 3) >> 2;
   for (int64_t q = (int64_t)blockIdx.x * kBlock + threadIdx.x; q < nquads; q += (int64_t)gridDim.x * kBlock) {
     const int64_t e0 = q << 2;
     const Quad qd = load_quad<EF>(x, res, e0, n);
-    emit_quad<BITS, EF>(qd, e0, n, mna, sca, codes, res);
+    emit_quad<BITS, EF, true>(qd, e0, n, mna, sca, rsc, codes, res);
   }
 }
 

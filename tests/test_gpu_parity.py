@@ -94,6 +94,44 @@ def test_minmax_signed_zero_and_constant_groups(gc):
         assert_bits_equal(host(s_d), scales, "scales")
 
 
+@pytest.mark.parametrize("bits,group", [(8, 64), (4, 64), (8, 0), (4, 0)])
+@pytest.mark.parametrize("ef", [False, True])
+def test_minmax_half_integer_quotients(gc, bits, group, ef):
+    """Quotients (x - min) / scale exactly on, and one or two ulps either side of, k + 1/2
+    (where the kernels leave the multiply-by-reciprocal estimate for the division), with
+    scales 2^-20 .. 2^20 and one group of tiny values; codes bit-exact."""
+    L = (1 << bits) - 1
+    rng = np.random.default_rng(bits * 10 + (group > 0))
+    G = 64
+    ng = 512
+    xs = []
+    for g in range(ng):
+        sc = F32(2.0 ** rng.integers(-20, 21))
+        mn = F32(rng.integers(-5, 6)) * sc
+        k = rng.integers(0, L, G).astype(F32)
+        q = (k + F32(0.5)).astype(F32)
+        d = rng.integers(-2, 3, G)
+        q = np.array([np.nextafter(v, F32(np.inf) if dd > 0 else F32(0)) if dd else v
+                      for v, dd in zip(q, d)], F32)
+        for _ in range(1):
+            q = np.where(np.abs(d) == 2, np.nextafter(q, np.where(d > 0, F32(np.inf), F32(0))), q).astype(F32)
+        x = (mn + (q * sc).astype(F32)).astype(F32)
+        x[0] = mn
+        x[1] = (mn + F32(L) * sc).astype(F32)                 # the group's range is exactly L * scale
+        xs.append(x)
+    xs[7] = (rng.standard_normal(G) * F32(1e-41)).astype(F32)   # denormal group
+    x = np.concatenate(xs).astype(F32)
+    r = (rng.standard_normal(x.size) * F32(1e-7)).astype(F32) if ef else None
+    codes, mins, scales, _, r_new = oracle.quant_minmax(x, group, bits, residual=r)
+    rd = dev(r) if ef else None
+    c_d, m_d, s_d = gc.quant_minmax(dev(x), group, bits, residual=rd)
+    assert_bits_equal(host(c_d), codes if bits == 8 else oracle.pack_int4(codes), "codes")
+    assert_bits_equal(host(m_d), mins, "mins")
+    assert_bits_equal(host(s_d), scales, "scales")
+    if ef:
+        assert_bits_equal(host(rd), r_new, "residual")
+
+
 # ---------------------------------------------------------------- QSGD -------------
 
 @pytest.mark.parametrize("n,group,levels,base", [
