@@ -7,8 +7,8 @@
 // stored to or added into out[pos].  The receive side of a data-parallel step (aiqz.cc
 // "梯度聚合通信优化实战方案", section "通信瓶颈分析": the workers' gradients are summed and
 // averaged) adds W payloads into one vector in payload order; k_decode_sum does it for W
-// dense payloads of one shape in a single pass.  Streaming: one pass over the payload, scattered
-// 4-byte stores.  A dense decode (no idx) with aligned buffers takes the tile kernel: one
+// dense payloads of one shape in a single pass, k_merge_sparse for W sparse payloads tile
+// by tile.  Streaming: one pass over the payload, scattered 4-byte stores.  A dense decode (no idx) with aligned buffers takes the tile kernel: one
 // 4096-entry tile per block, a lane owns an aligned quad (codes loaded as one word,
 // 16-byte non-temporal stores), all loads of the tile issued before any arithmetic.
 #include "common.hpp"

@@ -4,14 +4,15 @@
 // (codes in {-1,0,+1}, layer-wise normalization), with the per-layer scheme of the
 // TernGrad paper the page cites: s = max|x|, code = sign(x) * Bernoulli(|x|/s).
 //
-// Two passes over every segment: (A) max|x'| per segment, one ordered atomic per block
+// Two passes over every segment: (A) max|x'| per segment, one ordered atomic per tile
 // (|x'| >= 0, so its bit pattern orders like the value); (B) the codes.  Pass A is bound by
 // HBM and pass B by its VALU work (a Philox4x32-10 block per quad and one IEEE division
 // per element), so they are pipelined over batches of segments: launch j runs the codes of
 // batch j-1 and the maxima of batch j, their tiles interleaved in dispatch order, so that
 // every CU mixes streaming tiles with arithmetic tiles.  Codes of batch j-1 only need
 // the scales that launch j-1 finished; the first launch only takes maxima and the last only
-// codes.  Both roles take one 4096-element tile per block on a non-persistent grid.
+// codes.  Both roles take one tile per block on a non-persistent grid (8192 elements for
+// a max tile, 4096 for a code tile).
 //
 // Pass B works in global quad space: lane L owns the aligned quad Q = qs + b0 + L, so loads
 // are 16-byte vector loads and the Philox block of the quad is shared by its 4 elements.
@@ -21,10 +22,10 @@
 // 63 only supplies the neighbour codes.  Tiles (pass A) and runs (pass B) that lie wholly
 // inside their segment skip the per-element range masks.
 //
-// Pass A spreads each segment's atomics over 64 workspace slots (one atomic per 8192-
-// element tile on a single address per segment serialised: 0.85 ms for the max pass of
-// 350M elements against 0.25 ms now), and pass B reduces the slots when it reads the
-// scale.  Pass A loads through the caches, pass B with non-temporal loads, so that pass B
+// Pass A spreads each segment's atomics over 64 workspace slots, and pass B reduces the
+// slots when it reads the scale: with one address per segment the tiles' atomics
+// serialised (the max pass of 350M elements took 0.85 ms with 4096-element tiles; about
+// 0.25 ms now).  Pass A loads through the caches, pass B with non-temporal loads, so that pass B
 // does not evict the batch that pass A has just read (0.52 against 0.56 ms).
 #include "common.hpp"
 #include "internal.hpp"
