@@ -6,8 +6,8 @@
 //
 // Two passes over every segment: (A) max|x'| per segment, one ordered atomic per tile
 // (|x'| >= 0, so its bit pattern orders like the value); (B) the codes.  Pass A is bound by
-// HBM and pass B by its VALU work (a Philox4x32-10 block per quad and one IEEE division
-// per element), so they are pipelined over batches of segments: launch j runs the codes of
+// HBM and pass B by its VALU work (a Philox4x32-10 block per quad and the decision
+// U < fl(|x|/s), from a product estimate or the IEEE division), so they are pipelined over batches of segments: launch j runs the codes of
 // batch j-1 and the maxima of batch j, their tiles interleaved in dispatch order, so that
 // every CU mixes streaming tiles with arithmetic tiles.  Codes of batch j-1 only need
 // the scales that launch j-1 finished; the first launch only takes maxima and the last only
@@ -154,7 +154,7 @@ __device__ __forceinline__ void max_tile(const float* __restrict__ x, const floa
 template <bool EF, bool FULL>
 __device__ __forceinline__ void codes_runs(const float* __restrict__ x, float* __restrict__ res,
                                            int64_t n, int64_t lo, int64_t hi, int64_t r0,
-                                           int64_t runs, float sc, uint64_t seed,
+                                           int64_t runs, float sc, float rsc, uint64_t seed,
                                            int64_t index_base, uint8_t* __restrict__ out) {
   const int64_t nb = (hi - lo + 3) >> 2;              // output bytes of the segment
   const int d = (int)(lo & 3);
@@ -190,6 +190,22 @@ __device__ __forceinline__ void codes_runs(const float* __restrict__ x, float* _
     const int64_t Q = qs + b0 + lane;
     float uu[4];
     uniforms4(seed, (uint64_t)(index_base + (Q << 2)), uu);
+    // U < p, p = fl(|x'| / sc) <= 1: d = fl(fl(|x'| * rsc) - U), rsc = fl(1/sc), lies within
+    // 2^-22 + 2^-25 + 2^-25 < 2^-21 of p - U (rsc's relative error 2^-24, two roundings
+    // below 1 and p's own), so d's sign decides when 2^-21 <= |d| <= 2; otherwise (and for
+    // NaN or infinite d) the quad divides
+    bool take[4];
+    bool slow = false;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float d = fabsf(v[u][m]) * rsc - uu[m];
+      take[m] = d > 0.f;
+      slow |= !(fabsf(d) >= 0x1p-21f && fabsf(d) <= 2.0f);
+    }
+    if (slow) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) take[m] = uu[m] < fabsf(v[u][m]) / sc;
+    }
     uint32_t c8 = 0u;
     float gh[4];
 #pragma unroll
@@ -197,8 +213,7 @@ __device__ __forceinline__ void codes_runs(const float* __restrict__ x, float* _
       uint32_t bits = 0u;
       float g = 0.f;
       if (ok[u][m] && sc > 0.f) {
-        const float p = fabsf(v[u][m]) / sc;
-        if (uu[m] < p) {
+        if (take[m]) {
           const bool neg = v[u][m] < 0.f;
           bits = neg ? 3u : 1u;
           g = neg ? -sc : sc;
@@ -248,15 +263,16 @@ __device__ __forceinline__ void codes_tile(const float* __restrict__ x, float* _
   const uint32_t sb = seg_max_u32(slots[(int64_t)B.index[si] * kSlots + lane_id()], kWave);
   const float sc = bitsf(sb);
   if (bi == 0 && threadIdx.x == 0) scales[B.index[si]] = sc;
+  const float rsc = 1.0f / sc;
   uint8_t* __restrict__ out = packed + B.out_byte[si];
   const int64_t r0 = bi * kRunsPerBlock + (threadIdx.x / kWave) * kRunsB;
   if (r0 >= runs) return;
   // the wave's runs read quads [qs + r0*step, qs + (r0 + kRunsB - 1)*step + 64)
   const int64_t qlast = qs + (r0 + kRunsB - 1) * step + kWave;
   if (((qs + r0 * step) << 2) >= lo && (qlast << 2) <= hi)
-    codes_runs<EF, true>(x, res, n, lo, hi, r0, runs, sc, seed, index_base, out);
+    codes_runs<EF, true>(x, res, n, lo, hi, r0, runs, sc, rsc, seed, index_base, out);
   else
-    codes_runs<EF, false>(x, res, n, lo, hi, r0, runs, sc, seed, index_base, out);
+    codes_runs<EF, false>(x, res, n, lo, hi, r0, runs, sc, rsc, seed, index_base, out);
 }
 
 // One pipelined launch: the codes tiles of batch B and the max tiles of batch A, mixed in

@@ -183,12 +183,14 @@ def test_terngrad(gc, lens, base, ef):
         assert_bits_equal(host(rd), r_new, "residual")
 
 
-@pytest.mark.parametrize("sc", [2.0, 2.0 ** -70, 3.0e30])
+@pytest.mark.parametrize("sc", [2.0, 2.0 ** -70, 3.0e30, 1e-40])
 def test_terngrad_decision_boundaries(gc, sc):
     # |x| placed at U * s * (1 + d) for the element's own uniform U (taken from the oracle),
-    # with d from 0 to +-2^-19, so that fl(|x|/s) lands on, just above and just below U;
-    # scales far from 1 (2^-70, 3e30); plus tiny values, denormals and zeros.  Codes must
-    # equal the oracle's bit for bit.
+    # with d from 0 to +-2^-19, so that fl(|x|/s) lands on, just above and just below U
+    # (inside the band where the kernel leaves its product estimate for the division);
+    # scales far from 1 (2^-70, 3e30) and a subnormal one (1e-40, whose reciprocal
+    # overflows); plus tiny values, denormals and zeros.  Codes must equal the oracle's
+    # bit for bit.
     n, seed = 64 * 4096, 11
     u = oracle.uniform24(seed, np.arange(n, dtype=np.int64)).astype(np.float64)
     ds = np.array([0.0] + [sgn * 2.0 ** -e for e in range(19, 26) for sgn in (1, -1)])
