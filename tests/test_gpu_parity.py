@@ -136,7 +136,8 @@ def test_minmax_half_integer_quotients(gc, bits, group, ef):
 
 @pytest.mark.parametrize("n,group,levels,base", [
     (64 * 500 + 13, 64, 15, 0), (10_000, 4, 1, 0), (10_003, 256, 127, 3), (777, 32, 7, 1 << 33),
-    (5, 64, 15, 2), (64 * 64, 64, 127, 6),
+    (5, 64, 15, 2), (64 * 64, 64, 127, 6), (64 * 300 + 5, 64, 6, 0), (20_001, 16, 12, 9),
+    (64 * 200, 128, 126, 1 << 20),
 ])
 @pytest.mark.parametrize("ef", [False, True])
 def test_qsgd(gc, n, group, levels, base, ef):
