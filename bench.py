@@ -36,7 +36,7 @@ HBM_PEAK_GBS = 8000.0
 VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
 # VALU lane-instructions per element of the quantizer kernels (SQ_INSTS_VALU x 64 /
 # elements, rocprofv3 counters of bench.py --rows; profiles/compressor_rows_valu_and_traffic.md).
-VALU_LANE_OPS_PER_ELEMENT = {"minmax8": 39.9, "minmax4": 40.1, "qsgd": 59.1, "terngrad": 42.2}
+VALU_LANE_OPS_PER_ELEMENT = {"minmax8": 39.9, "minmax4": 40.1, "qsgd": 54.9, "terngrad": 37.9}
 
 # HBM bytes per launch of the streaming pass on this workload, from two rocprofv3 counter
 # runs per mode (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, factors from a plain 4 GiB device

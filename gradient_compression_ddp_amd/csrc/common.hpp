@@ -24,19 +24,29 @@ struct Words4 {
   uint32_t w[4];
 };
 
+// gfx950's three-input bitwise op with truth table 0x96 (a ^ b ^ c) forms each new state
+// word in one instruction.
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 __device__ __forceinline__ Words4 philox10(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1) {
   constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
   constexpr uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
-  uint32_t x0 = c0, x1 = c1, x2 = 0u, x3 = 0u;
+  // round 1: the counter's words 2 and 3 are 0, so M1 * x2 = 0
+  const uint64_t q0 = (uint64_t)M0 * (uint64_t)c0;
+  uint32_t x0 = c1 ^ k0, x1 = 0u, x2 = (uint32_t)(q0 >> 32) ^ k1, x3 = (uint32_t)q0;
+  k0 += W0;
+  k1 += W1;
 #pragma unroll
-  for (int r = 0; r < 10; ++r) {
+  for (int r = 1; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)M0 * (uint64_t)x0;
     const uint64_t p1 = (uint64_t)M1 * (uint64_t)x2;
     const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
     const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
-    x0 = hi1 ^ x1 ^ k0;
+    x0 = xor3(hi1, x1, k0);
     x1 = lo1;
-    x2 = hi0 ^ x3 ^ k1;
+    x2 = xor3(hi0, x3, k1);
     x3 = lo0;
     k0 += W0;
     k1 += W1;
