@@ -259,3 +259,19 @@ def test_decompress_payloads_rejects_before_any_launch(lib):
     assert call(1, [good], [fake], n_out=999) == 1                   # n > n_out
     assert call(2, [good, bad], [fake, fake]) == 1                   # any bad header rejects the call
     assert call(1, [good], [fake], out_ptr=ctypes.c_void_p(fake + 2)) == 1   # out misaligned
+
+
+def test_terngrad_workspace_is_sized_and_checked(lib):
+    """gc_terngrad keeps 64 partial maxima per segment in the caller's workspace: the size
+    query reports it, and a missing or short workspace is rejected before any launch."""
+    size = lib.gc_workspace_size
+    size.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)]
+    b = ctypes.c_size_t(0)
+    assert size(4, 1000, 3, 0, ctypes.byref(b)) == 0 and b.value >= 3 * 64 * 4 and b.value % 256 == 0
+    assert size(4, 0, 3, 0, ctypes.byref(b)) == 0 and b.value == 0        # nothing to do, no workspace
+    t = lib.gc_terngrad
+    t.argtypes = [VP, VP, ctypes.c_int, VP, ctypes.c_uint64, ctypes.c_int64, VP, VP, VP, ctypes.c_size_t, VP]
+    off = (ctypes.c_int64 * 4)(0, 400, 700, 1000)
+    assert t(FAKE, None, 3, ctypes.cast(off, VP), 3, 0, FAKE, FAKE, None, 0, None) == 2          # GC_EWORKSPACE
+    assert t(FAKE, None, 3, ctypes.cast(off, VP), 3, 0, FAKE, FAKE, FAKE, 256, None) == 2        # too small
+    assert b"workspace" in lib.gc_last_error()
