@@ -156,8 +156,18 @@ __global__ __launch_bounds__(kBlock) void k_psum_gram(const float* __restrict__ 
   for (int t = 0; t < 10; ++t) acc[t] = 0.0;
   for (int64_t row = (int64_t)blockIdx.x * kBlock + threadIdx.x; row < rows;
        row += (int64_t)gridDim.x * kBlock) {
+    // panel partials in panel order; 8 loads are issued ahead of their additions
+    constexpr int kAhead = 8;
     float v[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t c = 0; c < ncp; ++c) {
+    int64_t c = 0;
+    for (; c + kAhead <= ncp; c += kAhead) {
+      f32x4 q[kAhead];
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) q[u] = *reinterpret_cast<const f32x4*>(ppart + ((c + u) * rows + row) * 4);
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) { v[0] += q[u].x; v[1] += q[u].y; v[2] += q[u].z; v[3] += q[u].w; }
+    }
+    for (; c < ncp; ++c) {
       const f32x4 q = *reinterpret_cast<const f32x4*>(ppart + (c * rows + row) * 4);
       v[0] += q.x; v[1] += q.y; v[2] += q.z; v[3] += q.w;
     }
