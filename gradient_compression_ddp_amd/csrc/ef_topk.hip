@@ -1224,22 +1224,36 @@ __device__ __forceinline__ void bemit_body(TopkCtrl* __restrict__ ctrl, int64_t 
       __syncthreads();
 #pragma unroll
       for (int u = 0; u < kEmitU; ++u) {
-        if (!flag[u]) continue;
-        const uint32_t o = s_off[u * kWaves + w];
-        const unsigned long long gb = gt_run + (o & 0xFFFFu) + gpre[u];
-        const unsigned long long eb = eq_run + (o >> 16) + epre[u];
-        if ((flag[u] & 1u) || eb < need) {
-          const unsigned long long pos = gb + (eb < need ? eb : need);
-          const int64_t e = tbase[u] + off[u];
-          if (pos < (unsigned long long)k) {   // exactly k are kept; the guard only bounds stores
-            out_idx[pos] = e + index_base;
-            out_val[pos] = RAND ? pool_c[src[u]] : v[u];
-            if (DEFER) {
-              *pend_off(pd.chunks, pos) = off[u];
-              atomicAdd(&s_kc[tlo[u]], 1u);
+        bool kept = false;
+        if (flag[u]) {
+          const uint32_t o = s_off[u * kWaves + w];
+          const unsigned long long gb = gt_run + (o & 0xFFFFu) + gpre[u];
+          const unsigned long long eb = eq_run + (o >> 16) + epre[u];
+          if ((flag[u] & 1u) || eb < need) {
+            const unsigned long long pos = gb + (eb < need ? eb : need);
+            const int64_t e = tbase[u] + off[u];
+            if (pos < (unsigned long long)k) {   // exactly k are kept; the guard only bounds stores
+              kept = true;
+              out_idx[pos] = e + index_base;
+              out_val[pos] = RAND ? pool_c[src[u]] : v[u];
+              if (DEFER) *pend_off(pd.chunks, pos) = off[u];
             }
+            if (!DEFER && zero_residual) r[e] = 0.f;
           }
-          if (!DEFER && zero_residual) r[e] = 0.f;
+        }
+        if (DEFER) {
+          // per-tile kept counts: the wave's entries are in index order, so each tile's
+          // lanes form one run; the run's first lane adds the run's kept count (one LDS
+          // atomic per tile and wave, not one per entry on a shared address)
+          const uint64_t km = ballot(kept);
+          const int prev = __shfl_up(tlo[u], 1, kWave);
+          const uint64_t heads = ballot(lane == 0 || prev != tlo[u]);
+          if (km != 0ull && ((heads >> lane) & 1ull)) {
+            const uint64_t above = heads & ~((2ull << lane) - 1ull);   // heads of later runs (lane 63: none)
+            const uint64_t upto = above ? (above & (0ull - above)) - 1ull : ~0ull;   // lanes below the next head
+            const uint32_t c = (uint32_t)__popcll(km & upto & ~((1ull << lane) - 1ull));
+            if (c) atomicAdd(&s_kc[tlo[u]], c);
+          }
         }
       }
       const uint32_t tot = s_total;
