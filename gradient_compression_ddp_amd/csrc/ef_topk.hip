@@ -950,8 +950,8 @@ __global__ __launch_bounds__(kBlock) void k_scan_down(const uint32_t* __restrict
 
 // One-block exclusive scan of one or two uint32 count arrays (small counts only; b and
 // ob may be null; the count is *count_dev when given).  A thread takes four consecutive
-// items per round of 1024.  Runs as a kernel of its own, or as the extra job of one block
-// of the kernel that follows the one writing the counts.
+// items per round of 1024.  Runs as the extra job of one block of the kernel that
+// follows the one writing the counts.
 struct SmallScan {
   const uint32_t* a;
   const uint32_t* b;
@@ -1002,7 +1002,6 @@ __device__ __forceinline__ void scan_small_body(const SmallScan& sc) {
   }
 }
 
-__global__ __launch_bounds__(kBlock) void k_scan_small(SmallScan sc) { scan_small_body(sc); }
 
 // ---- the candidates of KB consecutive tiles (a unit or a batch) ------------------------
 // pre[i] is the exclusive prefix of the tile counts inside the group; past the last tile
@@ -1153,7 +1152,8 @@ __device__ __forceinline__ void small_scan(const uint32_t* s_cnt, uint32_t* s_of
 // the high 16 bits key == T (a chunk holds 2048 entries, so neither field carries).
 // RAND: the pool holds key bits, and the kept value is read from pool_c.
 // DEFER: instead of writing the kept residual, record each kept entry's tile offset at
-// its kept position and count the kept entries of every tile.
+// its kept position, and write every tile's kept count and the kept position of its
+// first entry (the batch's first position plus the prefix of its tiles' counts).
 // KB: tiles per batch (kBatch, or kBatchSmall when there are fewer batches than CUs).
 template <bool RAND, bool DEFER, int KB>
 __device__ __forceinline__ void bemit_body(TopkCtrl* __restrict__ ctrl, int64_t ntiles,
@@ -1173,6 +1173,7 @@ __device__ __forceinline__ void bemit_body(TopkCtrl* __restrict__ ctrl, int64_t 
   __shared__ uint32_t s_total;
   __shared__ int64_t s_b;
   __shared__ uint32_t s_kc[DEFER ? KB : 1];
+  __shared__ uint32_t s_kw[2];
   if (ctrl->mode != MODE_CAND) return;
   const uint32_t T = ctrl->T;
   const unsigned long long need = ctrl->need;
@@ -1186,6 +1187,8 @@ __device__ __forceinline__ void bemit_body(TopkCtrl* __restrict__ ctrl, int64_t 
     const uint32_t total = load_batch(bt, t0, nt, tile_start, tile_count);
     // the exclusive prefixes of the batch's first unit
     unsigned long long gt_run = gt_excl[b * (KB / kUnit)], eq_run = eq_excl[b * (KB / kUnit)];
+    // kept entries before the batch: its first kept position
+    const unsigned long long pos0 = gt_run + (eq_run < need ? eq_run : need);
     for (uint32_t j0 = 0; j0 < total; j0 += kBlock * kEmitU) {
       uint32_t src[kEmitU];
       int64_t tbase[kEmitU];
@@ -1261,7 +1264,27 @@ __device__ __forceinline__ void bemit_body(TopkCtrl* __restrict__ ctrl, int64_t 
       eq_run += tot >> 16;
       __syncthreads();   // s_cnt / s_off / s_total are rewritten by the next chunk
     }
-    if (DEFER && threadIdx.x < nt) pd.tile_cnt[t0 + threadIdx.x] = s_kc[threadIdx.x];
+    if (DEFER) {
+      // the batch's tiles: kept counts, and the kept position of each tile's first entry
+      // (pos0 plus the exclusive prefix of the counts); the last chunk's barrier ordered
+      // the count atomics before these reads
+      const uint32_t c = threadIdx.x < KB ? s_kc[threadIdx.x] : 0u;
+      uint32_t inc = c;
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t o = (uint32_t)__shfl_up((int)inc, d, kWave);
+        if (lane >= d) inc += o;
+      }
+      if (KB > kWave) {
+        if (threadIdx.x == kWave - 1) s_kw[0] = inc;
+        __syncthreads();
+        if (threadIdx.x >= kWave) inc += s_kw[0];
+      }
+      if (threadIdx.x < nt) {
+        pd.tile_cnt[t0 + threadIdx.x] = c;
+        pd.tile_first[t0 + threadIdx.x] = pos0 + (inc - c);
+      }
+    }
   }
 }
 
@@ -1333,8 +1356,8 @@ __device__ __forceinline__ void count_body(const TopkCtrl* __restrict__ ctrl,
 }
 
 // Fallback only: ordered compaction of the full c, tile by tile: keep key > T, and the
-// first `need` entries with key == T.  DEFER: record offsets and per-tile counts as the
-// batch emit does.
+// first `need` entries with key == T.  DEFER: record offsets, per-tile counts and first
+// positions as the batch emit does.
 template <bool RAND, bool DEFER>
 __device__ __forceinline__ void emit_body(const TopkCtrl* __restrict__ ctrl,
                                                  float* __restrict__ r, int64_t n,
@@ -1405,7 +1428,10 @@ __device__ __forceinline__ void emit_body(const TopkCtrl* __restrict__ ctrl,
     block_scan32(s_cnt, s_off, &s_total);
     __syncthreads();
     const unsigned long long kept0 = gt_excl[ch] + (eq0 < need ? eq0 : need);
-    if (DEFER && threadIdx.x == 0) pd.tile_cnt[ch] = s_total;
+    if (DEFER && threadIdx.x == 0) {
+      pd.tile_cnt[ch] = s_total;
+      pd.tile_first[ch] = kept0;
+    }
 #pragma unroll
     for (int j = 0; j < kRounds; ++j) {
       if (keep[j]) {
@@ -1492,26 +1518,19 @@ __global__ __launch_bounds__(kBlock) void k_emit_all(TopkCtrl* __restrict__ ctrl
 // consecutive entries per wave store (neighbouring kept entries often share a sector).
 // DEFER: the residuals go to the record's values, in kept order, instead of r.
 // MON: the sum of g_hat^2 of each 1024 kept entries (float64, fixed order) goes to mon_g.
-template <bool DEFER, bool MON, bool SCAN>
+template <bool DEFER, bool MON>
 __global__ __launch_bounds__(kBlock) void k_qsgd_kept(const float* __restrict__ vals, int64_t k,
                                                       int lpg_log2, float s, float ys, uint64_t seed,
                                                       int8_t* __restrict__ codes, float* __restrict__ norms,
                                                       const int64_t* __restrict__ idx, int64_t index_base,
                                                       float* __restrict__ r, int64_t n, Pending pd,
-                                                      double* __restrict__ mon_g, SmallScan sc) {
+                                                      double* __restrict__ mon_g) {
   __shared__ float s_res[kBlock * 4];
   __shared__ double s_mon[MON ? kWaves : 1];
-  // SCAN: the grid's last block only scans the counts of sc (written by the previous
-  // kernel) while the others quantize
-  const unsigned qblocks = gridDim.x - (SCAN ? 1u : 0u);
-  if (SCAN && blockIdx.x >= qblocks) {
-    scan_small_body(sc);
-    return;
-  }
   const int64_t nquads = (k + 3) >> 2;
   const int lpg = 1 << lpg_log2;
   const int lane = lane_id();
-  const int64_t stride = (int64_t)qblocks * kBlock;
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
   for (int64_t base = (int64_t)blockIdx.x * kBlock; base < nquads; base += stride) {
     const int64_t q = base + threadIdx.x;
     const int64_t e0 = q << 2;
@@ -1793,30 +1812,19 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
                        index_base, out_idx, vals, zero_res, k, (const float*)l.pool_c, select_seed, pd,
                        quant ? 1u : 0u);
 
-  // 8: QSGD on the kept values and the residual of the kept set; deferred, with a small
-  // tile count, one more block scans the per-tile kept counts the emit wrote
-  // (tile_first = their exclusive scan)
-  const SmallScan tsc{pd.tile_cnt, nullptr, nullptr, l.ntiles, pd.tile_first, nullptr};
-  const bool small_tiles = l.ntiles <= 16 * kScanChunk;
-  bool tile_scan_done = false;
+  // 8: QSGD on the kept values and the residual of the kept set (deferred: into the
+  // record, whose per-tile counts and first positions the emit wrote)
   if (quant) {
     int lpg_log2 = 0;
     while ((int64_t(4) << lpg_log2) < qsgd_group) ++lpg_log2;
-    const bool scan = DEFER && small_tiles;
-    const int qgrid = clamp_grid(cdiv(cdiv(k, 4), kBlock), cus * 16) + (scan ? 1 : 0);
+    const int qgrid = clamp_grid(cdiv(cdiv(k, 4), kBlock), cus * 16);
     double* mg = mon ? l.mon_g : nullptr;
-#define GC_QSGD_KEPT(M, S)                                                                              \
-  hipLaunchKernelGGL((k_qsgd_kept<DEFER, M, S>), qgrid, kBlock, 0, s, (const float*)vals, k, lpg_log2,   \
+#define GC_QSGD_KEPT(M)                                                                                 \
+  hipLaunchKernelGGL((k_qsgd_kept<DEFER, M>), qgrid, kBlock, 0, s, (const float*)vals, k, lpg_log2,      \
                      (float)qsgd_levels, 1.0f / (float)qsgd_levels, qsgd_seed, out_codes, out_norms,     \
-                     (const int64_t*)out_idx,                                                             \
-                     index_base, res, n, pd, mg, tsc)
-    if (mon) {
-      if (scan) GC_QSGD_KEPT(true, true); else GC_QSGD_KEPT(true, false);
-    } else {
-      if (scan) GC_QSGD_KEPT(false, true); else GC_QSGD_KEPT(false, false);
-    }
+                     (const int64_t*)out_idx, index_base, res, n, pd, mg)
+    if (mon) GC_QSGD_KEPT(true); else GC_QSGD_KEPT(false);
 #undef GC_QSGD_KEPT
-    tile_scan_done = scan;
   } else if (mon) {
     // pure selection sends the kept values themselves
     hipLaunchKernelGGL(k_sq_chunks, (unsigned)l.kchunks, kBlock, 0, s, (const float*)vals, k, l.mon_g);
@@ -1827,20 +1835,6 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
     hipLaunchKernelGGL(k_sum_f64, (unsigned)ng2, kBlock, 0, s, (const double*)l.mon_g, l.kchunks, l.mon_g2);
     hipLaunchKernelGGL(k_mon_final, 1, kBlock, 0, s, (const double*)l.mon_c2, nc2, (const double*)l.mon_g2, ng2,
                        stats);
-  }
-  if (DEFER && !tile_scan_done) {
-    // tile_first = exclusive scan of the per-tile kept counts
-    if (small_tiles) {
-      hipLaunchKernelGGL(k_scan_small, 1, kBlock, 0, s, tsc);
-    } else {
-      const int tscan = clamp_grid(cdiv(l.ntiles, kScanChunk), cus * 4);
-      hipLaunchKernelGGL(k_scan_up, tscan, kBlock, 0, s, (const uint32_t*)pd.tile_cnt, (const uint32_t*)nullptr,
-                         (const unsigned long long*)nullptr, l.ntiles, l.scan_up);
-      hipLaunchKernelGGL(k_scan_mid, 1, kBlock, 0, s, (const unsigned long long*)nullptr, l.ntiles, l.scan_up);
-      hipLaunchKernelGGL(k_scan_down, tscan, kBlock, 0, s, (const uint32_t*)pd.tile_cnt, (const uint32_t*)nullptr,
-                         (const unsigned long long*)nullptr, l.ntiles, (const unsigned long long*)l.scan_up,
-                         pd.tile_first, (unsigned long long*)nullptr);
-    }
   }
   prof_mark(s, 3);
   return hipGetLastError();
