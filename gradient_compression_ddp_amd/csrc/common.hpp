@@ -33,7 +33,7 @@ __device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
 __device__ __forceinline__ Words4 philox10(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1) {
   constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
   constexpr uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
-  // round 1: the counter's words 2 and 3 are 0, so M1 * x2 = 0
+  // the first Philox round: the counter's words 2 and 3 are 0, so M1 * x2 = 0
   const uint64_t q0 = (uint64_t)M0 * (uint64_t)c0;
   uint32_t x0 = c1 ^ k0, x1 = 0u, x2 = (uint32_t)(q0 >> 32) ^ k1, x3 = (uint32_t)q0;
   k0 += W0;

@@ -53,7 +53,7 @@ enum gc_status {
   GC_OK = 0,
   GC_EINVAL = 1,        /* bad argument: null pointer, size, k, bits, levels, group, alignment */
   GC_EWORKSPACE = 2,    /* workspace missing or smaller than gc_workspace_size() */
-  GC_EUNSUPPORTED = 3,  /* valid request this build does not implement */
+  GC_EUNSUPPORTED = 3,  /* valid request the library does not implement */
   GC_EHIP = 4           /* a HIP runtime call or kernel launch failed */
 };
 
