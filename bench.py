@@ -16,9 +16,12 @@ cycles through them), the residual carried from step to step starting at 0, QSGD
 500 + t.
 
 Printed: one JSON line.  value = input fp32 GB/s (4 n bytes per step / step time);
-roofline = the streaming pass (the dominant kernel), 12 algorithmic bytes per element,
-timed with HIP events recorded by the library on the launch stream inside the timed
-region; cpu_baseline = the numpy oracle on a bounded sample of the same workload.
+ms_per_step = the bracketed wall time of the K steps (and the final flush) / K, with each
+step's own event time summarised as median, p10 and p90; roofline = the streaming pass
+(the dominant kernel), 12 algorithmic bytes per element (read g and r, write c), timed with
+HIP events recorded by the library on the launch stream inside the timed region, the
+deferred record's bytes reported apart; cpu_baseline = the numpy oracle on a bounded
+sample of the same workload.
 """
 from __future__ import annotations
 
@@ -103,14 +106,18 @@ def cpu_baseline(args, n_layers):
     t0 = time.perf_counter()
     oracle.ef_topk_qsgd(g, r, k, levels=127, group=64, seed=501)
     dt = time.perf_counter() - t0
+    n_full = args.layers * args.layer_len
     return {
         "value": round(4.0 * g.size / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": 1,
+        "cpus_usable": len(os.sched_getaffinity(0)),
+        "cpus_host": os.cpu_count(),
         "kind": "oracle",
+        "sample_fraction": round(g.size / n_full, 5),
         "sample": (f"{g.size} elements ({n_layers} layers x {layer_len}) of the same layered t(3) x "
                    f"lognormal recipe drawn on the host, k = {k} (1%), one EF-Top-k + QSGD-127 step; "
-                   f"{dt:.2f} s on one core (numpy sort-based oracle); host has {os.cpu_count()} cpus"),
+                   f"{dt:.2f} s in one thread (numpy elementwise work and sort run single-threaded)"),
     }
 
 # ---------------------------------------------------------------------------
@@ -600,13 +607,19 @@ def main():
     gc.profile_collect()              # discard anything recorded before the timed region
     gc.profile_enable(True)
     torch.cuda.synchronize()
+    # one event pair per step on the launch stream (the binding launches on torch's
+    # current stream), so each step's own GPU time is known besides the bracketed total
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    for i in range(args.warmup, args.warmup + args.steps):
+    ev[0].record()
+    for j, i in enumerate(range(args.warmup, args.warmup + args.steps)):
         step(i)
+        ev[j + 1].record()
     if pend is not None:
         gc.ef_flush(res, pend)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    step_ms = sorted(ev[j].elapsed_time(ev[j + 1]) for j in range(args.steps))
     gc.profile_enable(False)
     calls, ms_before, ms_pass, ms_after = gc.profile_collect()
     print(f"[bench] timed {args.steps} steps in {elapsed:.4f} s", file=sys.stderr, flush=True)
@@ -616,10 +629,15 @@ def main():
     alg_step = 12.0 * n + 8.0 * k + 1.0 * k + 4.0 * ((k + 63) // 64)
     value = in_bytes / (ms_step / 1e3) / 1e9
     pass_ms = ms_pass / max(calls, 1)
-    # read g and r, write c; deferred: also the record of the previous step (a 4-byte
-    # offset and a 4-byte value per kept entry, 12 bytes of tile table per tile)
-    pass_bytes = 12.0 * n + (0.0 if args.direct else 8.0 * k + 12.0 * ((n + 4095) // 4096))
+    # the method's own bytes: read g and r, write c.  Deferred mode also reads the record
+    # of the previous step (a 4-byte offset and a 4-byte value per kept entry, 12 bytes of
+    # tile table per tile): reported apart, as overhead of the design, not in the fraction
+    pass_bytes = 12.0 * n
+    record_bytes = 0.0 if args.direct else 8.0 * k + 12.0 * ((n + 4095) // 4096)
     achieved = pass_bytes / (pass_ms / 1e3) / 1e9
+
+    def pct(q):
+        return round(step_ms[min(len(step_ms) - 1, int(q * (len(step_ms) - 1) + 0.5))], 4)
     traffic = K1_TRAFFIC_BYTES[mode] if k1_source_digest() == K1_SOURCE_SHA256 else None
     line = {
         "metric": METRIC,
@@ -641,6 +659,7 @@ def main():
             "qsgd_levels": 127, "qsgd_group": 64, "step_gradients": 3,
             "parallelism": "single GPU",
         },
+        "step_ms_events": {"median": pct(0.5), "p10": pct(0.1), "p90": pct(0.9), "reps": len(step_ms)},
         "hbm_frac_step": round(alg_step / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": alg_step,
         "stage_ms_per_step": {"before_pass": round(ms_before / max(calls, 1), 4),
@@ -658,6 +677,7 @@ def main():
             "traffic": round(traffic / 1e9 / (pass_ms / 1e3), 1) if traffic else None,
             "traffic_bytes_per_launch": traffic,
             "bytes_per_launch": pass_bytes,
+            "record_bytes_per_launch": record_bytes,
             "avg_launch_ms": round(pass_ms, 4),
         },
     }

@@ -4,16 +4,20 @@ The oracle cannot sort 7e9 elements, so:
 * the Top-K set is checked with the exact O(n) invariant, evaluated with torch on the
   GPU (an independent library), layer by layer;
 * every QSGD code and norm of the 7e7 kept values, and the residual at every kept
-  position, are compared bit for bit with the oracle on the host;
-* TernGrad at 350M elements: scales against torch's max|x|, codes of sampled runs of
-  every layer against the oracle.
+  position, are compared bit for bit with the oracle on the host, for each of the three
+  steps of the 7e9 workload (the third consumes a record written by a step that itself
+  consumed one);
+* TernGrad at 350M elements (24 layers of 14,583,333): every packed byte and every
+  scale, and with error feedback every element of the new residual, against the oracle
+  run layer by layer on the host.  Only at this size does the library close its
+  layer batches by element count rather than by layer count.
 """
 import numpy as np
 import pytest
 
 import oracle
 import workloads
-from gc_testlib import assert_bits_equal
+from gc_testlib import assert_bits_equal, oracle_qsgd_threaded, oracle_terngrad_layers
 
 pytestmark = pytest.mark.gpu
 
@@ -32,7 +36,7 @@ def keys(t):
 
 
 @pytest.mark.parametrize("mode", ["direct", "deferred"])
-def test_metric_path_7e9_two_steps(gc, mode):
+def test_metric_path_7e9_three_steps(gc, mode):
     # deferred: the call bench.py times (gc_ef_compress with a pending record); the true
     # residual before a step is rebuilt by flushing copies of the residual and the record
     import torch
@@ -47,7 +51,8 @@ def test_metric_path_7e9_two_steps(gc, mode):
     out_norms = torch.empty((k + 63) // 64, dtype=torch.float32, device=dev)
     ws = torch.empty(gc.workspace_size(gc.OP_EF_TOPK, n, k, 127), dtype=torch.uint8, device=dev)
     pend = gc.pending_record(n, k, dev) if mode == "deferred" else None
-    for t in (1, 2):
+    for t in (1, 2, 3):
+        print(f"[7e9 {mode}] step {t}", flush=True)
         workloads.layered_torch(L, LL, step=t, device=dev, out=g)
         r_prev.copy_(r)
         if pend is not None:
@@ -90,7 +95,7 @@ def test_metric_path_7e9_two_steps(gc, mode):
         del mask
         # QSGD of every kept value and the residual at the kept positions, against the oracle
         v_h = v.cpu().numpy()
-        codes, norms, ghat, _ = oracle.qsgd(v_h, 64, 127, seed=500 + t)
+        codes, norms, ghat = oracle_qsgd_threaded(v_h, 64, 127, seed=500 + t)
         assert_bits_equal(out_codes.cpu().numpy(), codes, f"step {t} codes")
         assert_bits_equal(out_norms.cpu().numpy(), norms, f"step {t} norms")
         if pend is None:
@@ -104,34 +109,32 @@ def test_metric_path_7e9_two_steps(gc, mode):
         del v, kv
 
 
-def test_terngrad_350m(gc):
+@pytest.mark.parametrize("ef", [False, True], ids=["plain", "error_feedback"])
+def test_terngrad_350m(gc, ef):
     import torch
     dev = torch.device("cuda:0")
     L, LL = workloads.TERN_LAYERS, workloads.TERN_LAYER_LEN
+    print(f"[terngrad 350M ef={ef}]", flush=True)
     x = workloads.layered_torch(L, LL, step=0, device=dev, seed=3)
+    r = None
+    if ef:
+        # a residual of the same recipe, a quarter the size: x + r moves the layer maxima
+        r = workloads.layered_torch(L, LL, step=1, device=dev, seed=3).mul_(0.25)
+        r_h = r.cpu().numpy()
     off = np.arange(L + 1, dtype=np.int64) * LL
-    packed, scales = gc.terngrad(x, off, 3)
+    packed, scales = gc.terngrad(x, off, 3, residual=r)
     torch.cuda.synchronize()
     nb = (LL + 3) // 4
     assert packed.numel() == L * nb
-    want_scales = torch.stack([x[l * LL:(l + 1) * LL].abs().max() for l in range(L)])
-    assert_bits_equal(scales.cpu().numpy(), want_scales.cpu().numpy(), "scales")
-    p = packed.cpu().numpy()
-    assert not np.any(((p[:, None] >> np.array([0, 2, 4, 6], np.uint8)) & 3) == 2)
-    rng = np.random.default_rng(0)
-    sc = scales.cpu().numpy()
+    x_h = x.cpu().numpy()
+    del x
+    want_packed, want_scales, want_r = oracle_terngrad_layers(x_h, LL, 3, residual=r_h if ef else None)
+    assert_bits_equal(scales.cpu().numpy(), want_scales, "scales")
+    got = packed.cpu().numpy()
     for l in range(L):
-        starts = np.concatenate([[0, nb - 64], rng.integers(0, nb - 64, 8)]) * 4
-        for s0 in starts:
-            lo = l * LL + int(s0)
-            hi = min(lo + 256, (l + 1) * LL)
-            xs = x[lo:hi].cpu().numpy()
-            # a trailing +scale element pins the oracle's per-segment scale to the layer's
-            probe = np.concatenate([xs, [sc[l]]]).astype(F32)
-            _, _, codes, _, _ = oracle.terngrad(probe, [0, probe.size], seed=3, index_base=lo)
-            want = oracle.pack_ternary(codes[:-1])
-            b0 = int(s0) // 4
-            got = p[l * nb + b0: l * nb + b0 + want.size]
-            if hi == (l + 1) * LL:
-                want = want[:got.size]
-            assert_bits_equal(got, want, f"layer {l} bytes from {b0}")
+        assert_bits_equal(got[l * nb:(l + 1) * nb], want_packed[l * nb:(l + 1) * nb], f"layer {l} codes")
+    if ef:
+        got_r = r.cpu().numpy()
+        for l in range(L):
+            sl = slice(l * LL, (l + 1) * LL)
+            assert_bits_equal(got_r[sl], want_r[sl], f"layer {l} residual")

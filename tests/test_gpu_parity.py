@@ -242,6 +242,28 @@ def test_terngrad_many_segments(gc, ef, base):
         assert_bits_equal(host(rd), r_new, "residual")
 
 
+@pytest.mark.parametrize("ef", [False, True])
+def test_terngrad_batches_closed_by_size(gc, ef):
+    # segments of 2^24 + 5, 9,000,001, 9,000,003, 2^23 + 7 and 3 elements: starts at four
+    # different offsets mod 4, and batches of layers that close once they hold 2^24
+    # elements (the first segment alone, then two, then two), so launches mix max tiles and
+    # code tiles of segments of different sizes, as at 24 x 14,583,333
+    lens = np.array([(1 << 24) + 5, 9_000_001, 9_000_003, (1 << 23) + 7, 3], dtype=np.int64)
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    n = int(off[-1])
+    x = workloads.bucket(n, seed=31)
+    for s in range(lens.size):
+        x[off[s]:off[s + 1]] *= F32(10.0 ** (s - 2))
+    r = (workloads.bucket(n, seed=32) * F32(1e-2)).astype(F32) if ef else None
+    packed, scales, _, _, r_new = oracle.terngrad(x, off, seed=17, index_base=5, residual=r)
+    rd = dev(r) if ef else None
+    p_d, s_d = gc.terngrad(dev(x), off, 17, index_base=5, residual=rd)
+    assert_bits_equal(host(s_d), scales, "scales")
+    assert_bits_equal(host(p_d), packed, "packed codes")
+    if ef:
+        assert_bits_equal(host(rd), r_new, "residual")
+
+
 # ---------------------------------------------------------------- EF Top-K ---------
 
 def run_topk(gc, g, r, k, base=0):

@@ -1,38 +1,16 @@
 """Pins for the oracle's Philox4x32-10 stream (CPU only).
 
 The reference is rocRAND's own Philox4x32-10 engine, run as a library on the host
-(tests/pins/philox_rocrand_ref.cpp): a different implementation of the SC'11
+(tests/pins/philox_rocrand_ref.cpp, built by the
+`rocrand_ref` fixture in conftest.py): a different implementation of the SC'11
 definition, so a wrong constant, a swapped word or a wrong counter/key layout
 fails here.
 """
-import os
-import shutil
-import subprocess
-
 import numpy as np
 import pytest
 
 import oracle
 from oracle.philox import random_words
-
-HERE = os.path.dirname(os.path.abspath(__file__))
-
-
-@pytest.fixture(scope="session")
-def rocrand_ref(tmp_path_factory):
-    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-    if not os.path.exists(hipcc) or not os.path.exists("/opt/rocm/include/rocrand/rocrand_kernel.h"):
-        pytest.skip("hipcc / rocRAND headers not available")
-    exe = str(tmp_path_factory.mktemp("philox") / "philox_ref")
-    subprocess.run([hipcc, "-O1", "-o", exe, os.path.join(HERE, "pins", "philox_rocrand_ref.cpp")],
-                   check=True, capture_output=True)
-
-    def run(pairs):
-        text = "".join(f"{s} {c}\n" for s, c in pairs)
-        out = subprocess.run([exe], input=text, capture_output=True, text=True, check=True).stdout
-        return np.array([[int(w, 16) for w in line.split()] for line in out.strip().splitlines()],
-                        dtype=np.uint64)
-    return run
 
 
 def test_blocks_match_rocrand(rocrand_ref):
