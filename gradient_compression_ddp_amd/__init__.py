@@ -14,7 +14,8 @@ import os
 import torch
 
 __all__ = [
-    "lib_path", "GCError", "workspace_size", "ef_compress", "EfOptions", "ef_topk", "ef_topk_deferred",
+    "lib_path", "GCError", "workspace_size", "ef_compress", "ef_compress_noalloc", "noalloc_scratch_bytes",
+    "EfOptions", "ef_topk", "ef_topk_deferred",
     "ef_flush", "pending_record",
     "ef_randk", "quant_minmax", "qsgd", "terngrad",
     "powersgd_step", "decompress_scatter", "KIND_F32", "KIND_MINMAX8", "KIND_MINMAX4",
@@ -71,6 +72,9 @@ _SIGS = {
     "gc_ef_topk": ([_p, _p, _i64, _i64, _i64, _p, _p, _i32, _i64, _u64, _p, _p, _p, _sz, _p], _i32),
     "gc_ef_compress": ([_p, _p, _i64, _i64, _i64, _p, _p, _i32, _i64, _u64, _p, _p, ctypes.POINTER(EfOptions),
                         _p, _sz, _p], _i32),
+    "gc_ef_compress_noalloc": ([_p, _p, _i64, _i64, _i64, _p, _p, _i32, _i64, _u64, _p, _p,
+                                ctypes.POINTER(EfOptions), _p], _i32),
+    "gc_noalloc_scratch_bytes": ([], _sz),
     "gc_ef_topk_deferred": ([_p, _p, _i64, _i64, _i64, _p, _p, _i32, _i64, _u64, _p, _p, _p, _sz, _p, _sz, _p],
                             _i32),
     "gc_ef_flush": ([_p, _i64, _p, _sz, _p], _i32),
@@ -160,10 +164,14 @@ def _sparsify(name, op, grad, residual, k, index_base, extra, qsgd_levels, qsgd_
             out_codes = torch.empty(k, dtype=torch.int8, device=dev)
         if out_norms is None:
             out_norms = torch.empty((k + qsgd_group - 1) // qsgd_group, dtype=torch.float32, device=dev)
-    ws, ws_bytes = _workspace(op, n, k, qsgd_levels, dev, workspace)
+    if op is None:       # the entry point brings its own workspace
+        ws_args = ()
+    else:
+        ws, ws_bytes = _workspace(op, n, k, qsgd_levels, dev, workspace)
+        ws_args = (_ptr(ws), ws_bytes)
     _check(getattr(_lib, name)(_ptr(grad), _ptr(residual), n, k, index_base, *extra, _ptr(out_idx),
                                _ptr(out_val), qsgd_levels, qsgd_group, qsgd_seed, _ptr(out_codes),
-                               _ptr(out_norms), *tail, _ptr(ws), ws_bytes, _stream(stream)), name)
+                               _ptr(out_norms), *tail, *ws_args, _stream(stream)), name)
     if quant:
         return out_idx, out_codes, out_norms, out_val
     return out_idx, out_val
@@ -191,6 +199,14 @@ def ef_compress(grad, residual, k, index_base=0, *, select="topk", select_seed=0
     :func:`ef_flush`); stats: a float64 GPU tensor of 3 that receives the norm monitor
     (sum c^2, sum g_hat^2, ratio).  Outputs as :func:`ef_topk`.
     """
+    opts = _ef_options(select, select_seed, pending, stats)
+    op = OP_EF_RANDK if select == "randk" else OP_EF_TOPK
+    return _sparsify("gc_ef_compress", op, grad, residual, k, index_base, (), qsgd_levels, qsgd_group, qsgd_seed,
+                     out_idx, out_val, out_codes, out_norms, want_values, workspace, stream,
+                     tail=(ctypes.byref(opts),))
+
+
+def _ef_options(select, select_seed, pending, stats):
     if select not in ("topk", "randk"):
         raise ValueError("select must be 'topk' or 'randk'")
     opts = EfOptions(size=ctypes.sizeof(EfOptions), select=SELECT_RANDK if select == "randk" else SELECT_TOPK,
@@ -203,9 +219,24 @@ def ef_compress(grad, residual, k, index_base=0, *, select="topk", select_seed=0
         if stats.numel() < 3:
             raise ValueError("stats must hold 3 doubles")
         opts.stats = stats.data_ptr()
-    op = OP_EF_RANDK if select == "randk" else OP_EF_TOPK
-    return _sparsify("gc_ef_compress", op, grad, residual, k, index_base, (), qsgd_levels, qsgd_group, qsgd_seed,
-                     out_idx, out_val, out_codes, out_norms, want_values, workspace, stream,
+    return opts
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the fixed per-GPU array that :func:`ef_compress_noalloc` works in."""
+    return int(_lib.gc_noalloc_scratch_bytes())
+
+
+def ef_compress_noalloc(grad, residual, k, index_base=0, *, select="topk", select_seed=0, pending=None,
+                        stats=None, qsgd_levels=0, qsgd_group=64, qsgd_seed=0, out_idx=None, out_val=None,
+                        out_codes=None, out_norms=None, want_values=True, stream=None):
+    """:func:`ef_compress` without a workspace (gc_ef_compress_noalloc): the library
+    works in its own fixed per-GPU array and allocates nothing.  Pass every output
+    tensor to keep this wrapper from allocating them; calls beyond the array's size
+    raise GCError (GC_EWORKSPACE)."""
+    opts = _ef_options(select, select_seed, pending, stats)
+    return _sparsify("gc_ef_compress_noalloc", None, grad, residual, k, index_base, (), qsgd_levels, qsgd_group,
+                     qsgd_seed, out_idx, out_val, out_codes, out_norms, want_values, None, stream,
                      tail=(ctypes.byref(opts),))
 
 

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libgc.so")
 ARCH = "gfx950"
 
 SOURCES = ["capi.cpp", "minmax.hip", "qsgd.hip", "terngrad.hip", "ef_topk.hip",
-           "powersgd.hip", "decompress.hip"]
+           "powersgd.hip", "decompress.hip", "noalloc.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -58,6 +58,14 @@ int check_workspace(void* ws, size_t have, size_t need) {
 
 namespace gc {
 
+int report(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
 int device_cu_count() {
   static std::mutex mu;
   static int cache[64] = {0};
@@ -370,10 +378,16 @@ static int check_sparsify(const float* grad, float* residual, int64_t n, int64_t
 
 static_assert(sizeof(gc_ef_options) == 40, "gc_ef_options layout");
 
-int gc_ef_compress(const float* grad, float* residual, int64_t n, int64_t k, int64_t index_base,
-                   int64_t* out_idx, float* out_val, int qsgd_levels, int64_t qsgd_group, uint64_t qsgd_seed,
-                   int8_t* out_codes, float* out_norms, const gc_ef_options* opts, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace gc {
+
+// Every check of gc_ef_compress except the workspace's; *need receives the workspace
+// bytes the call needs (0 when it touches none).
+int ef_compress_check(const float* grad, float* residual, int64_t n, int64_t k, int64_t index_base,
+                      int64_t* out_idx, float* out_val, int qsgd_levels, int64_t qsgd_group, int8_t* out_codes,
+                      float* out_norms, const gc_ef_options* opts, size_t* need) {
+  *need = 0;
   gc_ef_options o{};
   if (opts) {
     GC_REQUIRE(opts->size >= sizeof(gc_ef_options), "opts->size must be sizeof(gc_ef_options)");
@@ -391,9 +405,28 @@ int gc_ef_compress(const float* grad, float* residual, int64_t n, int64_t k, int
       return fail(GC_EWORKSPACE, "pending record of %zu bytes is smaller than the %zu this n and k need",
                   o.pending_bytes, gc::ef_pending_bytes(n, k));
   }
+  if (k > 0)
+    *need = o.select == GC_SELECT_RANDK ? gc::ef_randk_workspace(n, k, qsgd_levels)
+                                        : gc::ef_topk_workspace(n, k, qsgd_levels);
+  return ok();
+}
+
+}  // namespace gc
+
+extern "C" {
+
+int gc_ef_compress(const float* grad, float* residual, int64_t n, int64_t k, int64_t index_base,
+                   int64_t* out_idx, float* out_val, int qsgd_levels, int64_t qsgd_group, uint64_t qsgd_seed,
+                   int8_t* out_codes, float* out_norms, const gc_ef_options* opts, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  const int c = gc::ef_compress_check(grad, residual, n, k, index_base, out_idx, out_val, qsgd_levels, qsgd_group,
+                                      out_codes, out_norms, opts, &need);
+  if (c != GC_OK || n == 0) return c;
+  gc_ef_options o{};
+  if (opts) o = *opts;
   const bool randk = o.select == GC_SELECT_RANDK;
   if (k > 0) {
-    const size_t need = randk ? gc::ef_randk_workspace(n, k, qsgd_levels) : gc::ef_topk_workspace(n, k, qsgd_levels);
     const int w = check_workspace(workspace, workspace_bytes, need);
     if (w != GC_OK) return w;
   }

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+struct gc_ef_options;   // include/gc.h
+
 namespace gc {
 
 // Round a byte count up to the 256-byte alignment used for every workspace carve-out.
@@ -81,6 +83,16 @@ hipError_t launch_merge_sparse(int W, const int64_t* const* idx, const void* con
                                const int64_t* index_base, const int64_t* group, const int* kind,
                                const int* levels, float alpha, int accumulate, float* out, int64_t n_out,
                                hipStream_t s);
+
+// Every argument check of gc_ef_compress except the workspace's (a rejected call makes no
+// HIP call); *need receives the workspace bytes the call needs.
+int ef_compress_check(const float* grad, float* residual, int64_t n, int64_t k, int64_t index_base,
+                      int64_t* out_idx, float* out_val, int qsgd_levels, int64_t qsgd_group, int8_t* out_codes,
+                      float* out_norms, const ::gc_ef_options* opts, size_t* need);
+
+// Sets the calling thread's gc_last_error text and returns `status` (for entry points
+// defined outside capi.cpp).
+int report(int status, const char* fmt, ...);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

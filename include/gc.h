@@ -173,6 +173,35 @@ int gc_ef_compress(const float* grad, float* residual, int64_t n, int64_t k, int
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gc_ef_compress_noalloc -- gc_ef_compress with no workspace argument, for callers that
+ * cannot allocate device memory: code under HIP stream capture, serving loops and
+ * harnesses that must not call the allocator.
+ *
+ * Same operation, arguments (less workspace and workspace_bytes), outputs and errors as
+ * gc_ef_compress.  Its workspace is a fixed array of gc_noalloc_scratch_bytes() bytes
+ * (32 MiB) inside the library's code object, one copy per GPU, held until the process
+ * ends.  The call allocates and frees nothing.  The first call on a device looks up that
+ * device's copy (hipGetSymbolAddress, with the device current) and keeps its address.
+ * Every call resets whatever part of the array must start at zero, so it does not depend
+ * on what an earlier call left there.
+ *
+ * Limit: a call whose gc_workspace_size(GC_OP_EF_TOPK or GC_OP_EF_RANDK, n, k,
+ * qsgd_levels) exceeds the array returns GC_EWORKSPACE before any HIP call.  At k = 1%
+ * of n with QSGD that allows n up to about 1.5e8 (Top-K) or 1.0e8 (Random-K), so a
+ * 25 MiB bucket (6,553,600 elements) fits at any k up to a quarter of it.  Calls that overlap
+ * in time on one GPU (two streams or threads at once) share the array and race: the
+ * caller serializes them, e.g. by issuing them on one stream.
+ */
+int gc_ef_compress_noalloc(const float* grad, float* residual, int64_t n, int64_t k, int64_t index_base,
+                           int64_t* out_idx, float* out_val,
+                           int qsgd_levels, int64_t qsgd_group, uint64_t qsgd_seed,
+                           int8_t* out_codes, float* out_norms, const gc_ef_options* opts,
+                           void* stream);
+
+/* Size in bytes of gc_ef_compress_noalloc's fixed per-GPU array. */
+size_t gc_noalloc_scratch_bytes(void);
+
+/*
  * gc_ef_topk_deferred -- gc_ef_topk with the residual update of the kept set deferred to
  * the next call on the same residual.
  *

@@ -275,3 +275,27 @@ def test_terngrad_workspace_is_sized_and_checked(lib):
     assert t(FAKE, None, 3, ctypes.cast(off, VP), 3, 0, FAKE, FAKE, None, 0, None) == 2          # GC_EWORKSPACE
     assert t(FAKE, None, 3, ctypes.cast(off, VP), 3, 0, FAKE, FAKE, FAKE, 256, None) == 2        # too small
     assert b"workspace" in lib.gc_last_error()
+
+
+def test_noalloc_rejects_on_the_host(lib):
+    # gc_ef_compress_noalloc validates like gc_ef_compress, then refuses any call whose
+    # workspace would not fit its fixed array, all before its first HIP call
+    lib.gc_last_error.restype = ctypes.c_char_p
+    lib.gc_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    f = lib.gc_ef_compress_noalloc
+    f.argtypes = [VP, VP, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, VP, VP, ctypes.c_int,
+                  ctypes.c_int64, ctypes.c_uint64, VP, VP, VP, VP]
+    cap = lib.gc_noalloc_scratch_bytes()
+    assert cap == 32 << 20
+    n = 1 << 28
+    st, need = _ws(lib, 1, n, n // 100, 127)
+    assert st == 0 and need > cap
+    assert f(FAKE, FAKE, n, n // 100, 0, FAKE, None, 127, 64, 1, FAKE, FAKE, None, None) == 2   # GC_EWORKSPACE
+    assert b"fixed scratch" in lib.gc_last_error()
+    # bad arguments are reported as by gc_ef_compress, before the size check
+    assert f(None, FAKE, 10, 1, 0, FAKE, FAKE, 0, 64, 0, None, None, None, None) == 1
+    assert f(FAKE, FAKE, 10, 11, 0, FAKE, FAKE, 0, 64, 0, None, None, None, None) == 1
+    assert b"k must" in lib.gc_last_error()
+    assert f(FAKE, FAKE, n, n // 100, 0, FAKE, None, 127, 100, 1, FAKE, FAKE, None, None) == 1   # group
+    # n == 0 and k == 0 need no workspace and touch nothing
+    assert f(None, None, 0, 0, 0, None, None, 0, 64, 0, None, None, None, None) == 0
