@@ -8,7 +8,10 @@ LIB = os.path.join(ROOT, "gradient_compression_ddp_amd", "libgc.so")
 
 
 def ensure_built():
-    """Build libgc.so only if it is not there yet."""
+    """Build libgc.so only if it is not there yet.  GC_LIB_PATH, when set, names another
+    build of the library to test instead (the host AddressSanitizer build)."""
+    if os.environ.get("GC_LIB_PATH"):
+        return os.environ["GC_LIB_PATH"]
     if not os.path.exists(LIB):
         # by path: importing the package would load the library that is missing
         import importlib.util
