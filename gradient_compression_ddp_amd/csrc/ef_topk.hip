@@ -66,6 +66,10 @@ constexpr int kBatchSmall = kUnit;           // the emit's batch when 128-tile b
 constexpr int kKeptChunk = kBlock * 4;       // kept entries per norm-monitor partial
 constexpr int kSumChunk = 4096;              // partials per block of the monitor's second level
 constexpr int kFusePickGrid = 256;           // radix pass grids up to this fold the pick in
+// The emit's look-back words hold counts in 31-bit fields, so it serves k below 2^31.
+constexpr unsigned long long kLbField = (1ull << 31) - 1ull;
+// The smallest sample: inputs up to this size are sampled whole (the select is exact).
+constexpr int kSampleMin = 1 << 15;
 static_assert(kBatch % kUnit == 0 && kBatch <= 2 * kWave && kUnit <= kWave, "batch tables");
 static_assert(kBatchSmall % kUnit == 0 && kBatchSmall <= kWave, "small batch tables");
 
@@ -116,13 +120,14 @@ __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 
 // Sample size and the sample rank whose key is taken as the candidate bound L.
 // The rank sits 2% above the expected sample rank plus 8 standard deviations, so the
 // candidates hold the k largest unless the sample is off by far more than sampling error.
-// Up to 2^20 elements the sample is the whole input, which gives the exact k-th key.
-// Above, one element in 64 is drawn, between 2^18 and 2^20: the draw costs two random
-// sectors per point, which a call on a 25 MB bucket would otherwise spend mostly here.
+// Up to 2^15 elements the sample is the whole input, which gives the exact k-th key.
+// Above, one element in 64 is drawn, between 2^15 and 2^20 points: the draw costs two
+// random sectors per point, and a whole-input select of a million keys costs more than
+// the small candidate pool a sample leaves (1e6 elements: 1.7% of them at k = 1%).
 int64_t sample_size(int64_t n) {
-  if (n <= kSampleMax) return n;
+  if (n <= kSampleMin) return n;
   const int64_t m = n >> 6;
-  return m < (kSampleMax >> 2) ? (kSampleMax >> 2) : (m > kSampleMax ? kSampleMax : m);
+  return m < kSampleMin ? kSampleMin : (m > kSampleMax ? kSampleMax : m);
 }
 int64_t sample_rank(int64_t n, int64_t k) {
   const int64_t m = sample_size(n);
@@ -669,7 +674,8 @@ __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g,
                                                     uint16_t* __restrict__ pool_off,
                                                     uint32_t region_cap, float* __restrict__ pool_c,
                                                     uint64_t seed, int64_t index_base, Pending pd,
-                                                    unsigned long long cap, double* __restrict__ mon_c) {
+                                                    unsigned long long cap, double* __restrict__ mon_c,
+                                                    unsigned long long* __restrict__ lb_status) {
   __shared__ uint32_t s_cnt[kRounds * kWaves];
   __shared__ double s_mon[MON ? kWaves : 1];
   __shared__ uint32_t s_off[kRounds * kWaves];
@@ -678,11 +684,12 @@ __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g,
   __shared__ uint32_t s_ok;
   __shared__ float s_cv[DEFER ? kTile : 1];
   __shared__ uint32_t s_cf[DEFER ? kTile / 32 : 1];
-  const uint32_t L = ctrl->L;
   const int w = threadIdx.x / kWave;
   const int lane = lane_id();
   const int64_t tile = blockIdx.x;
   const int64_t base = tile * kTile;
+  const uint32_t L = ctrl->L;
+  if (threadIdx.x == 0) lb_status[tile] = 0ull;   // the emit's look-back word of this tile
   unsigned long long pf = 0;
   uint32_t pc = 0u, has_vals = 0u;
   if (DEFER && pd.hdr->n == (unsigned long long)n) {
@@ -1077,6 +1084,138 @@ __device__ __forceinline__ int64_t next_batch(TopkCtrl* ctrl, int64_t nbatch, in
   return b < nbatch ? b : -1;
 }
 
+// ---- decoupled look-back over the emit's work queue -----------------------------------
+// Items (batches of the pool, or tiles of the full c) are claimed in increasing order.
+// Each item publishes a status word as soon as it knows its own counts (kLbAgg: key > T,
+// key == T), then walks back over its predecessors for their sum and publishes the
+// inclusive prefix (kLbIncl).  A predecessor that has not published yet is counted by
+// the walking block itself, so no block ever waits for another.  Counts are 31-bit
+// fields (gt <= k < 2^31; eq is clamped at need <= k, which leaves
+// min(eq_before, need), all the emit uses, unchanged).  The words are relaxed agent-scope
+// atomics: the word alone carries the data, so no fence is needed.  The stream pass
+// zeroes one word per tile before the emit runs.
+constexpr unsigned long long kLbAgg = 1ull << 62, kLbIncl = 2ull << 62;
+constexpr int kLbPolls = 512;   // reads of an unpublished word before the walker counts it
+
+__device__ __forceinline__ unsigned long long lb_pack(unsigned long long flag, unsigned long long gt,
+                                                      unsigned long long eq) {
+  return flag | (gt << 31) | eq;
+}
+__device__ __forceinline__ void lb_publish(unsigned long long* st, unsigned long long v) {
+  __hip_atomic_store(st, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long lb_read(const unsigned long long* st) {
+  return __hip_atomic_load(st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct LbShared {
+  unsigned long long gt, eq;   // running sums of the walk
+  long long next;              // -1: done; otherwise the next item to look at
+  long long count_item;        // >= 0: an unpublished item the block counts itself
+  unsigned long long wg[kWaves], we[kWaves];   // per wave: sums of its lanes before its stop
+  int wstop[kWaves];           // per wave: its first stopping lane (kWave: none)
+  uint32_t wincl[kWaves];      // per wave: 1 if that lane holds an inclusive prefix
+};
+
+// Exclusive prefix of item i over items 0..i-1: every thread calls it and gets
+// (*gx, *ex) with ex clamped at need.  Each step reads the kBlock nearest predecessors
+// not yet summed (one per thread) and stops at the nearest inclusive word, or at the
+// nearest unpublished item: that one is polled up to kLbPolls times and, if still
+// unpublished, counted by count(p, &gt, &eq) block-wide (it may use barriers).  Every
+// step sums at least one item, ends the walk, or leaves the next step an item that is
+// published or counted, so the walk ends within 2i steps.
+template <typename CountFn>
+__device__ __forceinline__ void lookback(const unsigned long long* __restrict__ st, int64_t i,
+                                         unsigned long long need, LbShared* sh, CountFn count,
+                                         unsigned long long* gx, unsigned long long* ex) {
+  if (threadIdx.x == 0) { sh->gt = 0ull; sh->eq = 0ull; sh->next = i - 1; sh->count_item = -1; }
+  __syncthreads();
+  const int w = threadIdx.x / kWave;
+  const int lane = lane_id();
+  for (;;) {
+    const long long p = sh->next;
+    __syncthreads();    // every thread has p before sh is rewritten
+    if (p < 0) break;   // uniform: the walk reached item 0's inclusive prefix (or item -1)
+    // thread t reads item p - t: wave w covers p - 64w - lane
+    const long long q = p - (long long)threadIdx.x;
+    const unsigned long long v = q >= 0 ? lb_read(st + q) : kLbIncl;   // before item 0: 0, 0
+    const uint32_t flag = (uint32_t)(v >> 62);
+    const uint64_t incl = ballot(flag == 2u), none = ballot(flag == 0u);
+    const uint64_t stop = incl | none;
+    const int f = stop ? __ffsll((unsigned long long)stop) - 1 : kWave;
+    // lanes below the wave's stop hold aggregates; an inclusive stop adds its own word
+    const bool add = lane < f || (lane == f && ((incl >> lane) & 1ull));
+    unsigned long long ag = add ? ((v >> 31) & kLbField) : 0ull;
+    unsigned long long ae = add ? (v & kLbField) : 0ull;
+    ag = wave_sum_u64(ag);
+    ae = wave_sum_u64(ae);
+    if (lane == 0) {
+      sh->wg[w] = ag;
+      sh->we[w] = ae;
+      sh->wstop[w] = f;
+      sh->wincl[w] = (f < kWave && ((incl >> f) & 1ull)) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      // waves in order: whole waves of aggregates, then the first wave with a stop
+      long long nxt = p - kBlock;                 // no stop in kBlock items: keep walking
+      for (int x = 0; x < kWaves; ++x) {
+        sh->gt += sh->wg[x];
+        sh->eq += sh->we[x];
+        if (sh->wstop[x] < kWave) {
+          if (sh->wincl[x]) {
+            nxt = -1;                             // an inclusive prefix ends the walk
+          } else {
+            // unpublished: its block has claimed it and publishes its counts without
+            // waiting on anything, so poll its word a bounded number of times; if it is
+            // still unpublished after that, count it here
+            const long long q = p - (kWave * x + sh->wstop[x]);
+            bool seen = false;
+            for (int it = 0; it < kLbPolls && !seen; ++it) seen = (lb_read(st + q) >> 62) != 0ull;
+            if (seen) {
+              nxt = q;                            // read it again as the next step's first item
+            } else {
+              sh->count_item = q;
+              nxt = q - 1;
+            }
+          }
+          break;
+        }
+      }
+      sh->next = nxt;
+    }
+    __syncthreads();
+    const long long c = sh->count_item;
+    if (c >= 0) {
+      unsigned long long cg = 0ull, ce = 0ull;
+      count((int64_t)c, &cg, &ce);
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        // The item's owner may have published meanwhile, and may since have changed what
+        // it counts (the full-c emit zeroes the residual at kept positions).  An owner
+        // publishes its counts, and that store completes, before it writes anything else,
+        // so: published now -> take the published word; still unpublished -> nothing was
+        // written before this count read it, and the count stands.
+        const unsigned long long v = lb_read(st + c);
+        const uint32_t flag = (uint32_t)(v >> 62);
+        if (flag == 0u) {
+          sh->gt += cg;
+          sh->eq += ce;
+        } else {
+          sh->gt += (v >> 31) & kLbField;
+          sh->eq += v & kLbField;
+          if (flag == 2u) sh->next = -1;   // an inclusive prefix covers everything below
+        }
+        sh->count_item = -1;
+      }
+      __syncthreads();
+    }
+  }
+  *gx = sh->gt;
+  *ex = sh->eq < need ? sh->eq : need;
+  __syncthreads();   // sh is free again once every thread has read it
+}
+
 constexpr int kEmitU = 8;   // entries per thread per chunk of the batch emit
 constexpr int kCountU = 4;  // entries per thread per chunk of the unit count
 
@@ -1454,6 +1593,358 @@ __device__ __forceinline__ void emit_body(const TopkCtrl* __restrict__ ctrl,
   }
 }
 
+// ---- the emit with look-back: no separate count and scan -----------------------------
+// Counts of key > T and key == T over tile ch of the full source (block-wide; every
+// thread gets them).
+template <bool RAND>
+__device__ __forceinline__ void count_tile(const float* __restrict__ full, int64_t n, int64_t ch, uint32_t T,
+                                           uint64_t seed, int64_t index_base, uint32_t (*s_red)[kWaves],
+                                           unsigned long long* gt_out, unsigned long long* eq_out) {
+  const int64_t base = ch * kTile;
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < kRounds; ++j) {
+    const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4;
+    if (e >= n) continue;
+    float v[4];
+    uint32_t key[4];
+    full_keys4<RAND>(full, n, e, seed, index_base, false, v, key);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      if (e + m < n) {
+        gt += key[m] > T;
+        eq += key[m] == T;
+      }
+  }
+  gt = (uint32_t)wave_sum_u64(gt);
+  eq = (uint32_t)wave_sum_u64(eq);
+  if (lane_id() == 0) { s_red[0][threadIdx.x / kWave] = gt; s_red[1][threadIdx.x / kWave] = eq; }
+  __syncthreads();
+  *gt_out = (unsigned long long)s_red[0][0] + s_red[0][1] + s_red[0][2] + s_red[0][3];
+  *eq_out = (unsigned long long)s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
+  __syncthreads();
+}
+
+// Counts of key > T and key == T over the pool entries of the batch whose table is bt
+// (block-wide; every thread gets them).
+template <int KB>
+__device__ __forceinline__ void count_pool_batch(const BatchTable<KB>& bt, uint32_t total,
+                                                 const float* __restrict__ pool_val, uint32_t T,
+                                                 uint32_t (*s_red)[kWaves], unsigned long long* gt_out,
+                                                 unsigned long long* eq_out) {
+  uint32_t gt = 0, eq = 0;
+  for (uint32_t j0 = 0; j0 < total; j0 += kBlock * kCountU) {
+    uint32_t src[kCountU];
+    bool live[kCountU];
+#pragma unroll
+    for (int u = 0; u < kCountU; ++u) {
+      const uint32_t j = j0 + u * kBlock + threadIdx.x;
+      live[u] = j < total;
+      const int lo = live[u] ? batch_tile<KB>(bt, j) : 0;
+      src[u] = bt.start[lo] + (j - bt.pre[lo]);
+    }
+#pragma unroll
+    for (int u = 0; u < kCountU; ++u)
+      if (live[u]) {
+        const uint32_t key = mag_key(pool_val[src[u]]);
+        gt += key > T;
+        eq += key == T;
+      }
+  }
+  gt = (uint32_t)wave_sum_u64(gt);
+  eq = (uint32_t)wave_sum_u64(eq);
+  if (lane_id() == 0) { s_red[0][threadIdx.x / kWave] = gt; s_red[1][threadIdx.x / kWave] = eq; }
+  __syncthreads();
+  *gt_out = (unsigned long long)s_red[0][0] + s_red[0][1] + s_red[0][2] + s_red[0][3];
+  *eq_out = (unsigned long long)s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
+  __syncthreads();
+}
+
+// Ordered compaction of the full c, tile by tile from the work queue, each tile's
+// exclusive counts found by look-back (status word per tile): keep key > T, and the
+// entries with key == T whose rank among them is below need.  DEFER: record offsets,
+// per-tile counts and first positions.
+template <bool RAND, bool DEFER>
+__device__ __forceinline__ void emit_full_lb(TopkCtrl* __restrict__ ctrl, float* __restrict__ r, int64_t n,
+                                             unsigned long long* __restrict__ st, int64_t index_base,
+                                             int64_t* __restrict__ out_idx, float* __restrict__ out_val,
+                                             int zero_residual, int64_t k, uint64_t seed, Pending pd) {
+  __shared__ uint32_t s_cnt[kRounds * kWaves];
+  __shared__ uint32_t s_off[kRounds * kWaves];
+  __shared__ uint32_t s_total;
+  __shared__ uint32_t s_red[2][kWaves];
+  __shared__ LbShared s_lb;
+  __shared__ int64_t s_b;
+  const int64_t nch = cdiv(n, kTile);
+  const uint32_t T = ctrl->T;
+  const unsigned long long need = ctrl->need;
+  const int w = threadIdx.x / kWave;
+  const int lane = lane_id();
+  for (int64_t ch; (ch = next_batch(ctrl, nch, &s_b)) >= 0;) {
+    const int64_t base = ch * kTile;
+    float v[kRounds][4];
+    uint32_t gtn[kRounds], eqn[kRounds], pre[kRounds];
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4;
+      uint32_t key[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) v[j][m] = 0.f;
+      if (e < n) full_keys4<RAND>(r, n, e, seed, index_base, true, v[j], key);
+      uint32_t gb = 0, qb = 0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const bool in = e + m < n;
+        gb |= (in && key[m] > T) ? (1u << m) : 0u;
+        qb |= (in && key[m] == T) ? (1u << m) : 0u;
+      }
+      gtn[j] = gb;
+      eqn[j] = qb;
+      uint32_t wq, wg;
+      pre[j] = rank_round(qb, &wq);
+      (void)rank_round(gb, &wg);
+      // packed (key > T) << 16 | (key == T): a tile holds 4096 entries, so neither carries
+      if (lane == 0) s_cnt[j * kWaves + w] = (wg << 16) | wq;
+    }
+    __syncthreads();
+    block_scan32(s_cnt, s_off, &s_total);
+    __syncthreads();
+    const unsigned long long gt_t = s_total >> 16, eq_t = s_total & 0xFFFFu;
+    if (threadIdx.x == 0) lb_publish(st + ch, lb_pack(kLbAgg, gt_t, eq_t < need ? eq_t : need));
+    unsigned long long gx, ex;
+    lookback(st, ch, need, &s_lb,
+             [&](int64_t p, unsigned long long* cg, unsigned long long* ce) {
+               count_tile<RAND>(r, n, p, T, seed, index_base, s_red, cg, ce);
+             },
+             &gx, &ex);
+    if (threadIdx.x == 0) {
+      const unsigned long long ei = ex + eq_t;
+      lb_publish(st + ch, lb_pack(kLbIncl, gx + gt_t, ei < need ? ei : need));
+      // both status stores complete before the block writes anything (the barrier below
+      // holds every other thread): a block that counts this tile itself then finds the
+      // status published whenever it could have read a zeroed residual
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    // ties: an entry with key == T is kept iff its rank among them is below need
+    uint32_t keep[kRounds];
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      uint32_t kb = gtn[j];
+      unsigned long long r0 = ex + (s_off[j * kWaves + w] & 0xFFFFu) + pre[j];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        if (eqn[j] & (1u << m)) {
+          if (r0 < need) kb |= 1u << m;
+          ++r0;
+        }
+      keep[j] = kb;
+    }
+    __syncthreads();   // s_cnt / s_off are rewritten below
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      uint32_t wc;
+      pre[j] = rank_round(keep[j], &wc);
+      if (lane == 0) s_cnt[j * kWaves + w] = wc;
+    }
+    __syncthreads();
+    block_scan32(s_cnt, s_off, &s_total);
+    __syncthreads();
+    const unsigned long long kept0 = gx + ex;
+    if (DEFER && threadIdx.x == 0) {
+      pd.tile_cnt[ch] = s_total;
+      pd.tile_first[ch] = kept0;
+    }
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      if (keep[j]) {
+        unsigned long long pos = kept0 + s_off[j * kWaves + w] + pre[j];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          if (keep[j] & (1u << m)) {
+            const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4 + m;
+            if (pos < (unsigned long long)k) {   // exactly k are kept; the guard only bounds stores
+              out_idx[pos] = e + index_base;
+              out_val[pos] = v[j][m];
+              if (DEFER) *pend_off(pd.chunks, pos) = (uint32_t)(j * (kBlock * 4) + threadIdx.x * 4 + m);
+            }
+            if (!DEFER && zero_residual) r[e] = 0.f;
+            ++pos;
+          }
+      }
+    }
+  }
+}
+
+// Ordered compaction straight from the pool, batch by batch from the work queue, each
+// batch's exclusive counts found by look-back (status word per batch): a first pass
+// over the batch's candidates counts them, the emit proper then reads them again (now
+// in the cache).  Otherwise as bemit_body.
+template <bool RAND, bool DEFER, int KB>
+__device__ __forceinline__ void bemit_lb(TopkCtrl* __restrict__ ctrl, int64_t ntiles,
+                                         const uint32_t* __restrict__ tile_start,
+                                         const uint32_t* __restrict__ tile_count,
+                                         const float* __restrict__ pool_val, const uint16_t* __restrict__ pool_off,
+                                         unsigned long long* __restrict__ st, float* __restrict__ r,
+                                         int64_t index_base, int64_t* __restrict__ out_idx,
+                                         float* __restrict__ out_val, int zero_residual, int64_t k,
+                                         const float* __restrict__ pool_c, Pending pd) {
+  __shared__ BatchTable<KB> bt;
+  __shared__ BatchTable<KB> bt2;   // a predecessor counted during the look-back
+  __shared__ uint32_t s_cnt[kEmitU * kWaves];
+  __shared__ uint32_t s_off[kEmitU * kWaves];
+  __shared__ uint32_t s_total;
+  __shared__ uint32_t s_red[2][kWaves];
+  __shared__ LbShared s_lb;
+  __shared__ int64_t s_b;
+  __shared__ uint32_t s_kc[DEFER ? KB : 1];
+  __shared__ uint32_t s_kw[2];
+  const uint32_t T = ctrl->T;
+  const unsigned long long need = ctrl->need;
+  const int w = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int64_t nbatch = cdiv(ntiles, KB);
+  for (int64_t b; (b = next_batch(ctrl, nbatch, &s_b)) >= 0;) {
+    const int64_t t0 = b * KB;
+    const int nt = (int)(ntiles - t0 < KB ? ntiles - t0 : KB);
+    if (DEFER && threadIdx.x < KB) s_kc[threadIdx.x] = 0u;   // visible after load_batch's barrier
+    const uint32_t total = load_batch(bt, t0, nt, tile_start, tile_count);
+    unsigned long long gt_b, eq_b;
+    count_pool_batch<KB>(bt, total, pool_val, T, s_red, &gt_b, &eq_b);
+    if (threadIdx.x == 0) lb_publish(st + b, lb_pack(kLbAgg, gt_b, eq_b < need ? eq_b : need));
+    unsigned long long gt_run, eq_run;
+    lookback(st, b, need, &s_lb,
+             [&](int64_t p, unsigned long long* cg, unsigned long long* ce) {
+               const int64_t p0 = p * KB;
+               const int pn = (int)(ntiles - p0 < KB ? ntiles - p0 : KB);
+               const uint32_t ptot = load_batch(bt2, p0, pn, tile_start, tile_count);
+               count_pool_batch<KB>(bt2, ptot, pool_val, T, s_red, cg, ce);
+             },
+             &gt_run, &eq_run);
+    if (threadIdx.x == 0) {
+      const unsigned long long ei = eq_run + eq_b;
+      lb_publish(st + b, lb_pack(kLbIncl, gt_run + gt_b, ei < need ? ei : need));
+    }
+    // kept entries before the batch: its first kept position (eq_run is clamped at need)
+    const unsigned long long pos0 = gt_run + eq_run;
+    for (uint32_t j0 = 0; j0 < total; j0 += kBlock * kEmitU) {
+      uint32_t src[kEmitU];
+      int64_t tbase[kEmitU];
+      int tlo[kEmitU];
+      bool live[kEmitU];
+#pragma unroll
+      for (int u = 0; u < kEmitU; ++u) {
+        const uint32_t j = j0 + u * kBlock + threadIdx.x;
+        live[u] = j < total;
+        const int lo = live[u] ? batch_tile<KB>(bt, j) : 0;
+        src[u] = bt.start[lo] + (j - bt.pre[lo]);
+        tbase[u] = (t0 + lo) * kTile;
+        tlo[u] = lo;
+      }
+      float v[kEmitU];
+      uint32_t off[kEmitU];
+#pragma unroll
+      for (int u = 0; u < kEmitU; ++u) {
+        v[u] = live[u] ? pool_val[src[u]] : 0.f;
+        off[u] = live[u] ? (uint32_t)pool_off[src[u]] : 0u;
+      }
+      uint32_t flag[kEmitU], gpre[kEmitU], epre[kEmitU];
+#pragma unroll
+      for (int u = 0; u < kEmitU; ++u) {
+        const uint32_t key = mag_key(v[u]);
+        const bool gtf = live[u] && key > T;
+        const bool eqf = live[u] && key == T;
+        const uint64_t bg = ballot(gtf), be = ballot(eqf);
+        gpre[u] = mbcnt(bg);
+        epre[u] = mbcnt(be);
+        flag[u] = (gtf ? 1u : 0u) | (eqf ? 2u : 0u);
+        if (lane == 0) s_cnt[u * kWaves + w] = ((uint32_t)__popcll(be) << 16) | (uint32_t)__popcll(bg);
+      }
+      __syncthreads();
+      small_scan<kEmitU * kWaves>(s_cnt, s_off, &s_total);
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kEmitU; ++u) {
+        bool kept = false;
+        if (flag[u]) {
+          const uint32_t o = s_off[u * kWaves + w];
+          const unsigned long long gb = gt_run + (o & 0xFFFFu) + gpre[u];
+          const unsigned long long eb = eq_run + (o >> 16) + epre[u];
+          if ((flag[u] & 1u) || eb < need) {
+            const unsigned long long pos = gb + (eb < need ? eb : need);
+            const int64_t e = tbase[u] + off[u];
+            if (pos < (unsigned long long)k) {   // exactly k are kept; the guard only bounds stores
+              kept = true;
+              out_idx[pos] = e + index_base;
+              out_val[pos] = RAND ? pool_c[src[u]] : v[u];
+              if (DEFER) *pend_off(pd.chunks, pos) = off[u];
+            }
+            if (!DEFER && zero_residual) r[e] = 0.f;
+          }
+        }
+        if (DEFER) {
+          const uint64_t km = ballot(kept);
+          const int prev = __shfl_up(tlo[u], 1, kWave);
+          const uint64_t heads = ballot(lane == 0 || prev != tlo[u]);
+          if (km != 0ull && ((heads >> lane) & 1ull)) {
+            const uint64_t above = heads & ~((2ull << lane) - 1ull);
+            const uint64_t upto = above ? (above & (0ull - above)) - 1ull : ~0ull;
+            const uint32_t c = (uint32_t)__popcll(km & upto & ~((1ull << lane) - 1ull));
+            if (c) atomicAdd(&s_kc[tlo[u]], c);
+          }
+        }
+      }
+      const uint32_t tot = s_total;
+      gt_run += tot & 0xFFFFu;
+      eq_run += tot >> 16;
+      __syncthreads();
+    }
+    if (DEFER) {
+      const uint32_t c = threadIdx.x < KB ? s_kc[threadIdx.x] : 0u;
+      uint32_t inc = c;
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const uint32_t o = (uint32_t)__shfl_up((int)inc, d, kWave);
+        if (lane >= d) inc += o;
+      }
+      if (KB > kWave) {
+        if (threadIdx.x == kWave - 1) s_kw[0] = inc;
+        __syncthreads();
+        if (threadIdx.x >= kWave) inc += s_kw[0];
+      }
+      if (threadIdx.x < nt) {
+        pd.tile_cnt[t0 + threadIdx.x] = c;
+        pd.tile_first[t0 + threadIdx.x] = pos0 + (inc - c);
+      }
+    }
+  }
+}
+
+// The emit with look-back, either source (the mode the selection left in the control
+// block).  zero_residual (pure Top-K, residual written directly): the kept positions'
+// residual becomes +0.0.  DEFER: block 0 also writes the pending record's header.
+template <bool RAND, bool DEFER, int KB>
+__global__ __launch_bounds__(kBlock) void k_emit_lb(TopkCtrl* __restrict__ ctrl, int64_t ntiles,
+                                                    const uint32_t* __restrict__ tile_start,
+                                                    const uint32_t* __restrict__ tile_count,
+                                                    const float* __restrict__ pool_val,
+                                                    const uint16_t* __restrict__ pool_off,
+                                                    unsigned long long* __restrict__ st, float* __restrict__ r,
+                                                    int64_t n, int64_t index_base, int64_t* __restrict__ out_idx,
+                                                    float* __restrict__ out_val, int zero_residual, int64_t k,
+                                                    const float* __restrict__ pool_c, uint64_t seed, Pending pd,
+                                                    uint32_t has_vals) {
+  if (DEFER && blockIdx.x == 0 && threadIdx.x == 0) {
+    pd.hdr->n = (unsigned long long)n;
+    pd.hdr->count = (unsigned long long)k;
+    pd.hdr->has_vals = has_vals;
+  }
+  if (ctrl->mode == MODE_CAND)
+    bemit_lb<RAND, DEFER, KB>(ctrl, ntiles, tile_start, tile_count, pool_val, pool_off, st, r, index_base, out_idx,
+                              out_val, zero_residual, k, pool_c, pd);
+  else
+    emit_full_lb<RAND, DEFER>(ctrl, r, n, st, index_base, out_idx, out_val, zero_residual, k, seed, pd);
+}
+
 // Counts of the candidates per unit, and of the full source per tile in the fallback:
 // two kernels (each returns at once unless the device-side mode is its own).  One
 // kernel holding both bodies measured 302 us against 186 us for the candidate count at
@@ -1711,6 +2202,11 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
   // not, the carve-outs stay where the size query put them
   const Layout l = make_layout(ws, n, k, quant, RAND);
   TopkCtrl* ctrl = l.ctrl;
+  unsigned long long* lb_status = l.gt_excl;   // the emit's look-back words, one per tile
+  float* vals = quant ? (out_val ? out_val : l.staging) : out_val;
+  const int zero_res = (quant || DEFER) ? 0 : 1;
+  const uint32_t has_vals = quant ? 1u : 0u;
+  double* mon_c = mon ? l.mon_c : nullptr;
 
   // 1-2: sample and conservative bound L on the k-th largest key
   const int64_t m = sample_size(n);
@@ -1742,29 +2238,18 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
 
   // 3: the streaming pass
   prof_mark(s, 1);
-  if (mon)
-    hipLaunchKernelGGL((k_ef_cand<RAND, DEFER, true>), (unsigned)l.ntiles, kBlock, 0, s, grad, res, n, ctrl,
-                       l.tile_start, l.tile_count, l.pool_val, l.pool_off, (uint32_t)l.region_cap, l.pool_c,
-                       select_seed, index_base, pd, cap, l.mon_c);
-  else
-    hipLaunchKernelGGL((k_ef_cand<RAND, DEFER, false>), (unsigned)l.ntiles, kBlock, 0, s, grad, res, n, ctrl,
-                       l.tile_start, l.tile_count, l.pool_val, l.pool_off, (uint32_t)l.region_cap, l.pool_c,
-                       select_seed, index_base, pd, cap, (double*)nullptr);
+#define GC_CAND_PASS(M)                                                                                  \
+  hipLaunchKernelGGL((k_ef_cand<RAND, DEFER, M>), (unsigned)l.ntiles, kBlock, 0, s, grad, res, n, ctrl,        \
+                     l.tile_start, l.tile_count, l.pool_val, l.pool_off, (uint32_t)l.region_cap, l.pool_c,       \
+                     select_seed, index_base, pd, cap, mon_c, lb_status)
+  if (mon) GC_CAND_PASS(true); else GC_CAND_PASS(false);
+#undef GC_CAND_PASS
   prof_mark(s, 2);
 
-  const int ugrid = clamp_grid(nunit, cus * 8);
-  // fewer 128-tile batches than CUs: batches of one unit keep the emit spread out
-  const bool small_batches = nbatch < cus;
-  const int bgrid = clamp_grid(small_batches ? nunit : nbatch, cus * 8);
-  const int cgrid = clamp_grid(l.ntiles, cus * 8);
-  if (exact) {
-    // T and need are known and the pool holds every candidate: count, and the last block
-    // to finish scans the counts
-    const SmallScan sc{l.chunk_gt, l.chunk_eq, nullptr, nunit, l.gt_excl, l.eq_excl};
-    hipLaunchKernelGGL(k_bcount<true>, ugrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start, l.tile_count,
-                       (const float*)l.pool_val, l.chunk_gt, l.chunk_eq, sc);
-  } else {
-    // 4-5: the first pool pass also decides the source; then the exact k-th key over it
+  // 4-5: unless the sample was the whole input (T and need already exact, and every
+  // candidate is kept or a tie), the first pool pass decides the source; then the exact
+  // k-th key over it
+  if (!exact) {
     for (int p = 0; p < 3; ++p) {
       const bool fuse = hgrid <= kFusePickGrid;
       hipLaunchKernelGGL((k_hist<RAND ? 2 : 1>), hgrid, kBlock, 0, s, ctrl, (const uint32_t*)nullptr, (int64_t)0,
@@ -1773,9 +2258,29 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
                          p == 2 ? 2 : 0, (unsigned long long)k, fuse ? 1 : 0);
       if (!fuse) hipLaunchKernelGGL(k_pick, 1, kBlock, 0, s, ctrl, shifts[p], p == 2 ? 2 : 0, (unsigned long long)k);
     }
+  }
 
-    // 6: counts per unit (candidates) or per tile (fallback), and their scan (folded into
-    // the count kernel when the counts are few)
+  // 6-7: ordered compaction.  Few work items (batches of the pool; tiles in the
+  // fallback): each finds its exclusive counts by look-back inside the emit.  Many: a
+  // count kernel and a scan first (the look-back's extra pass per item and its walks
+  // measured slower than those at 7e9 elements, 13,672 batches).
+  const bool small_batches = nbatch < cus;
+  const int64_t items = small_batches ? nunit : nbatch;
+  const int bgrid = clamp_grid(items, cus * 8);
+  if (k <= (int64_t)kLbField && items <= 2 * (int64_t)cus) {
+    if (small_batches)
+      hipLaunchKernelGGL((k_emit_lb<RAND, DEFER, kBatchSmall>), bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start,
+                         l.tile_count, (const float*)l.pool_val, (const uint16_t*)l.pool_off, lb_status, res, n,
+                         index_base, out_idx, vals, zero_res, k, (const float*)l.pool_c, select_seed, pd, has_vals);
+    else
+      hipLaunchKernelGGL((k_emit_lb<RAND, DEFER, kBatch>), bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start,
+                         l.tile_count, (const float*)l.pool_val, (const uint16_t*)l.pool_off, lb_status, res, n,
+                         index_base, out_idx, vals, zero_res, k, (const float*)l.pool_c, select_seed, pd, has_vals);
+  } else {
+    const int ugrid = clamp_grid(nunit, cus * 8);
+    const int cgrid = clamp_grid(l.ntiles, cus * 8);
+    // counts per unit (candidates) or per tile (fallback), and their scan (folded into the
+    // count kernel when the counts are few)
     const unsigned long long* nch_dev = &ctrl->nchunks;
     const bool small_scan = l.max_chunks <= 8 * kScanChunk;
     const SmallScan sc{l.chunk_gt, l.chunk_eq, nch_dev, 0, l.gt_excl, l.eq_excl};
@@ -1794,23 +2299,17 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
       hipLaunchKernelGGL(k_scan_down, cscan, kBlock, 0, s, l.chunk_gt, l.chunk_eq, nch_dev, (int64_t)0,
                          (const unsigned long long*)l.scan_up, l.gt_excl, l.eq_excl);
     }
+    if (small_batches)
+      hipLaunchKernelGGL((k_emit_all<RAND, DEFER, kBatchSmall>), bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start,
+                         l.tile_count, (const float*)l.pool_val, (const uint16_t*)l.pool_off,
+                         (const unsigned long long*)l.gt_excl, (const unsigned long long*)l.eq_excl, res, n,
+                         index_base, out_idx, vals, zero_res, k, (const float*)l.pool_c, select_seed, pd, has_vals);
+    else
+      hipLaunchKernelGGL((k_emit_all<RAND, DEFER, kBatch>), bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start,
+                         l.tile_count, (const float*)l.pool_val, (const uint16_t*)l.pool_off,
+                         (const unsigned long long*)l.gt_excl, (const unsigned long long*)l.eq_excl, res, n,
+                         index_base, out_idx, vals, zero_res, k, (const float*)l.pool_c, select_seed, pd, has_vals);
   }
-
-  // 7: ordered compaction (and, deferred, the pending record's header)
-  float* vals = quant ? (out_val ? out_val : l.staging) : out_val;
-  const int zero_res = (quant || DEFER) ? 0 : 1;
-  if (small_batches)
-    hipLaunchKernelGGL((k_emit_all<RAND, DEFER, kBatchSmall>), bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start,
-                       l.tile_count, (const float*)l.pool_val, (const uint16_t*)l.pool_off,
-                       (const unsigned long long*)l.gt_excl, (const unsigned long long*)l.eq_excl, res, n,
-                       index_base, out_idx, vals, zero_res, k, (const float*)l.pool_c, select_seed, pd,
-                       quant ? 1u : 0u);
-  else
-    hipLaunchKernelGGL((k_emit_all<RAND, DEFER, kBatch>), bgrid, kBlock, 0, s, ctrl, l.ntiles, l.tile_start,
-                       l.tile_count, (const float*)l.pool_val, (const uint16_t*)l.pool_off,
-                       (const unsigned long long*)l.gt_excl, (const unsigned long long*)l.eq_excl, res, n,
-                       index_base, out_idx, vals, zero_res, k, (const float*)l.pool_c, select_seed, pd,
-                       quant ? 1u : 0u);
 
   // 8: QSGD on the kept values and the residual of the kept set (deferred: into the
   // record, whose per-tile counts and first positions the emit wrote)

@@ -101,10 +101,12 @@ def test_ef_randk_rejects_bad_arguments(lib):
     assert f(FAKE, FAKE, 10, 1, 1 << 62, 3, FAKE, FAKE, 0, 64, 0, None, None, FAKE, 1 << 20, None) == 1
     assert f(FAKE, FAKE, 10, 1, 0, 3, FAKE, FAKE, 0, 64, 0, None, None, None, 0, None) == 2
     assert f(None, None, 0, 0, 0, 3, None, None, 0, 64, 0, None, None, None, 0, None) == 0
-    # the pool also keeps each candidate's value: more workspace than Top-K of the same size
-    st_t, b_t = _ws(lib, 1, 5_000_000, 50_000, 0)
-    st_r, b_r = _ws(lib, 7, 5_000_000, 50_000, 0)
+    # above 2^25 elements the Random-K pool also keeps each candidate's value: more
+    # workspace than Top-K of the same size; below, both select over c itself
+    st_t, b_t = _ws(lib, 1, 50_000_000, 500_000, 0)
+    st_r, b_r = _ws(lib, 7, 50_000_000, 500_000, 0)
     assert st_t == 0 and st_r == 0 and b_r > b_t
+    assert _ws(lib, 1, 5_000_000, 50_000, 0) == _ws(lib, 7, 5_000_000, 50_000, 0)
     assert _ws(lib, 7, 100, 0, 0) == (0, 0)
     assert _ws(lib, 7, 100, 101, 0)[0] == 1
 
@@ -150,8 +152,10 @@ def test_ef_compress_rejects_bad_options(lib):
     assert f(FAKE, FAKE, 100_000, 0, 0, FAKE, FAKE, 0, 64, 0, None, None, ctypes.byref(o), None, 0, None) == 1
     assert b"k > 0" in lib.gc_last_error()
     o = gcm.EfOptions(size=ctypes.sizeof(gcm.EfOptions), select=1)
-    need_t = _ws(lib, 1, 100_000, 1000, 0)[1]
-    assert f(*args, ctypes.byref(o), FAKE, need_t, None) == 2                      # Random-K needs more
+    big = (FAKE, FAKE, 50_000_000, 500_000, 0, FAKE, FAKE, 0, 64, 0, None, None)
+    need_t = _ws(lib, 1, 50_000_000, 500_000, 0)[1]
+    assert f(*big, ctypes.byref(o), FAKE, need_t, None) == 2                       # Random-K needs more
+    assert f(*big, ctypes.byref(o), FAKE, need_t - 256, None) == 2
     o = gcm.EfOptions(size=ctypes.sizeof(gcm.EfOptions), pending=0x200000, pending_bytes=64)
     assert f(*args, ctypes.byref(o), FAKE, 1 << 30, None) == 2                     # record too small
 
