@@ -171,6 +171,58 @@ __device__ __forceinline__ uint32_t seg_max_u32(uint32_t v, int width) {
   return v;
 }
 
+// Butterfly partner of compile-time step S (partner lane = lane ^ 2^S) for reductions in
+// which every lane of a segment ends with the segment's result.  Steps 0 and 1 are DPP
+// quad permutes ([1,0,3,2], [2,3,0,1]).  Once every quad holds one value, the half-row
+// mirror (lane i <-> 7 - i within 8) pairs each lane with a lane of the other quad, and
+// once every 8 lanes hold one value the row mirror (i <-> 15 - i within 16) pairs each
+// with a lane of the other half: the same partial results the xor steps 2 and 3 pair, so
+// the combined values are identical.  All four are DPP operand modifiers, with no LDS
+// traffic; steps 4 and 5 (16 and 32 lanes) shuffle.
+template <int S>
+__device__ __forceinline__ uint32_t bfly_u32(uint32_t v) {
+  static_assert(S >= 0 && S <= 5, "butterfly step");
+  if constexpr (S == 0) return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false);
+  else if constexpr (S == 1) return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false);
+  else if constexpr (S == 2) return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false);
+  else if constexpr (S == 3) return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false);
+  else return (uint32_t)__shfl_xor((int)v, 1 << S, kWave);
+}
+
+// Min / max / pairwise-tree sum over aligned segments of 2^W lanes, W known at compile time.
+template <int W>
+__device__ __forceinline__ uint32_t seg_min_c(uint32_t v) {
+  if constexpr (W > 0) v = min(v, bfly_u32<0>(v));
+  if constexpr (W > 1) v = min(v, bfly_u32<1>(v));
+  if constexpr (W > 2) v = min(v, bfly_u32<2>(v));
+  if constexpr (W > 3) v = min(v, bfly_u32<3>(v));
+  if constexpr (W > 4) v = min(v, bfly_u32<4>(v));
+  if constexpr (W > 5) v = min(v, bfly_u32<5>(v));
+  return v;
+}
+template <int W>
+__device__ __forceinline__ uint32_t seg_max_c(uint32_t v) {
+  if constexpr (W > 0) v = max(v, bfly_u32<0>(v));
+  if constexpr (W > 1) v = max(v, bfly_u32<1>(v));
+  if constexpr (W > 2) v = max(v, bfly_u32<2>(v));
+  if constexpr (W > 3) v = max(v, bfly_u32<3>(v));
+  if constexpr (W > 4) v = max(v, bfly_u32<4>(v));
+  if constexpr (W > 5) v = max(v, bfly_u32<5>(v));
+  return v;
+}
+// the tree's level-S additions: a + b and b + a are the same IEEE result, so each lane's
+// sum equals the tree's node
+template <int W>
+__device__ __forceinline__ float seg_tree_sum_c(float v) {
+  if constexpr (W > 0) v = v + __uint_as_float(bfly_u32<0>(__float_as_uint(v)));
+  if constexpr (W > 1) v = v + __uint_as_float(bfly_u32<1>(__float_as_uint(v)));
+  if constexpr (W > 2) v = v + __uint_as_float(bfly_u32<2>(__float_as_uint(v)));
+  if constexpr (W > 3) v = v + __uint_as_float(bfly_u32<3>(__float_as_uint(v)));
+  if constexpr (W > 4) v = v + __uint_as_float(bfly_u32<4>(__float_as_uint(v)));
+  if constexpr (W > 5) v = v + __uint_as_float(bfly_u32<5>(__float_as_uint(v)));
+  return v;
+}
+
 // Float sum over aligned segments of `width` lanes as a balanced pairwise tree in lane
 // order: the xor butterfly with offsets 1, 2, 4, ... adds exactly the pairs of the
 // tree (a + b and b + a are the same IEEE result), and every lane ends with the sum.

@@ -2009,9 +2009,9 @@ __global__ __launch_bounds__(kBlock) void k_emit_all(TopkCtrl* __restrict__ ctrl
 // consecutive entries per wave store (neighbouring kept entries often share a sector).
 // DEFER: the residuals go to the record's values, in kept order, instead of r.
 // MON: the sum of g_hat^2 of each 1024 kept entries (float64, fixed order) goes to mon_g.
-template <bool DEFER, bool MON>
+template <bool DEFER, bool MON, int LPG_LOG2>
 __global__ __launch_bounds__(kBlock) void k_qsgd_kept(const float* __restrict__ vals, int64_t k,
-                                                      int lpg_log2, float s, float ys, uint64_t seed,
+                                                      float s, float ys, uint64_t seed,
                                                       int8_t* __restrict__ codes, float* __restrict__ norms,
                                                       const int64_t* __restrict__ idx, int64_t index_base,
                                                       float* __restrict__ r, int64_t n, Pending pd,
@@ -2019,7 +2019,8 @@ __global__ __launch_bounds__(kBlock) void k_qsgd_kept(const float* __restrict__ 
   __shared__ float s_res[kBlock * 4];
   __shared__ double s_mon[MON ? kWaves : 1];
   const int64_t nquads = (k + 3) >> 2;
-  const int lpg = 1 << lpg_log2;
+  constexpr int lpg_log2 = LPG_LOG2;
+  constexpr int lpg = 1 << LPG_LOG2;
   const int lane = lane_id();
   const int64_t stride = (int64_t)gridDim.x * kBlock;
   for (int64_t base = (int64_t)blockIdx.x * kBlock; base < nquads; base += stride) {
@@ -2036,7 +2037,7 @@ __global__ __launch_bounds__(kBlock) void k_qsgd_kept(const float* __restrict__ 
       for (int m = 0; m < 4; ++m) v[m] = (live && e0 + m < k) ? vals[e0 + m] : 0.f;
     }
     float ss = quad_sumsq(v);
-    ss = seg_tree_sum(ss, lpg);
+    ss = seg_tree_sum_c<LPG_LOG2>(ss);
     __syncthreads();   // s_res is still being read by the previous iteration's scatter
     double gg = 0.0;
     if (live) {
@@ -2318,11 +2319,22 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
     while ((int64_t(4) << lpg_log2) < qsgd_group) ++lpg_log2;
     const int qgrid = clamp_grid(cdiv(cdiv(k, 4), kBlock), cus * 16);
     double* mg = mon ? l.mon_g : nullptr;
-#define GC_QSGD_KEPT(M)                                                                                 \
-  hipLaunchKernelGGL((k_qsgd_kept<DEFER, M>), qgrid, kBlock, 0, s, (const float*)vals, k, lpg_log2,      \
+#define GC_QSGD_KEPT(M, W)                                                                              \
+  hipLaunchKernelGGL((k_qsgd_kept<DEFER, M, W>), qgrid, kBlock, 0, s, (const float*)vals, k,               \
                      (float)qsgd_levels, 1.0f / (float)qsgd_levels, qsgd_seed, out_codes, out_norms,     \
                      (const int64_t*)out_idx, index_base, res, n, pd, mg)
-    if (mon) GC_QSGD_KEPT(true); else GC_QSGD_KEPT(false);
+#define GC_QSGD_KEPT_W(M)                     \
+  switch (lpg_log2) {                         \
+    case 0: GC_QSGD_KEPT(M, 0); break;        \
+    case 1: GC_QSGD_KEPT(M, 1); break;        \
+    case 2: GC_QSGD_KEPT(M, 2); break;        \
+    case 3: GC_QSGD_KEPT(M, 3); break;        \
+    case 4: GC_QSGD_KEPT(M, 4); break;        \
+    case 5: GC_QSGD_KEPT(M, 5); break;        \
+    default: GC_QSGD_KEPT(M, 6); break;       \
+  }
+    if (mon) { GC_QSGD_KEPT_W(true) } else { GC_QSGD_KEPT_W(false) }
+#undef GC_QSGD_KEPT_W
 #undef GC_QSGD_KEPT
   } else if (mon) {
     // pure selection sends the kept values themselves

@@ -77,43 +77,11 @@ __device__ __forceinline__ float quantize_one(float v, float mn, float scale, fl
   return q;
 }
 
-// RCP: the quad shares one (min, scale) and rsc = fl(1/scale).  A code needs only the
-// nearest integer of fl(d / scale), d = fl(x - min): both that quotient and q0 = fl(d * rsc)
-// lie below 256, where |q0 - fl(d / scale)| <= 2^-16 (rsc's relative error, at most 2^-24,
-// times 256) + 2^-17 + 2^-17 (the two roundings) = 2^-15.  So when q0 is at least 2^-14
-// from every half-integer, rint(q0) is the code; otherwise (and for NaN or infinite q0) the
-// quad takes the division.  Without RCP every element takes the division.
-template <int BITS, bool EF, bool RCP>
-__device__ __forceinline__ void emit_quad(const Quad& qd, int64_t e0, int64_t n, const float mn[4],
-                                          const float sc[4], float rsc, uint8_t* __restrict__ codes,
-                                          float* __restrict__ res) {
-  uint32_t c[4];
-  float gh[4];
-  if (RCP) {
-    constexpr float L = (float)((1 << BITS) - 1);
-    const float mn0 = mn[0], scale = sc[0];
-    float q[4];
-    bool slow = false;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float q0 = (qd.v[m] - mn0) * rsc;
-      q[m] = rintf(q0);
-      slow |= !(fabsf(q0 - q[m]) <= 0.5f - 0x1p-14f);
-    }
-    if (slow && scale != 0.f) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) q[m] = rintf((qd.v[m] - mn0) / scale);
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float qq = scale != 0.f ? fminf(fmaxf(q[m], 0.f), L) : 0.f;
-      gh[m] = qq * scale + mn0;
-      c[m] = (uint32_t)qq;
-    }
-  } else {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) c[m] = (uint32_t)quantize_one<BITS>(qd.v[m], mn[m], sc[m], &gh[m]);
-  }
+// Stores a quad's codes and (EF) residuals.
+template <int BITS, bool EF>
+__device__ __forceinline__ void store_quad(const Quad& qd, int64_t e0, int64_t n, const uint32_t c[4],
+                                           const float gh[4], uint8_t* __restrict__ codes,
+                                           float* __restrict__ res) {
   const bool full = e0 + 4 <= n;
   if (BITS == 8) {
     if (full) {
@@ -147,17 +115,70 @@ __device__ __forceinline__ void emit_quad(const Quad& qd, int64_t e0, int64_t n,
   }
 }
 
-// One pass for groups of 4..256 elements: a group is `lpg` = G/4 consecutive lanes.
-// One tile per block; a round covers 1024 elements starting at a multiple of 1024, so
-// every group lies inside one wave of one round.
+// A quad whose elements may belong to two groups: each divides by its own scale.
 template <int BITS, bool EF>
+__device__ __forceinline__ void emit_quad_mixed(const Quad& qd, int64_t e0, int64_t n, const float mn[4],
+                                                const float sc[4], uint8_t* __restrict__ codes,
+                                                float* __restrict__ res) {
+  uint32_t c[4];
+  float gh[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) c[m] = (uint32_t)quantize_one<BITS>(qd.v[m], mn[m], sc[m], &gh[m]);
+  store_quad<BITS, EF>(qd, e0, n, c, gh, codes, res);
+}
+
+// Codes (and residuals) of a quad sharing one (min, scale).  rsc estimates 1/scale well
+// enough (rsc_ok) that q0 = fl(fl(x - min) * rsc) lies within 2^-13 of fl(fl(x - min) /
+// scale) for codes below 256; when q0 is at least 2^-13 from every half-integer,
+// rint(q0) is the code, otherwise (or for NaN or infinite q0, or !rsc_ok) the quad divides.
+template <int BITS, bool EF>
+__device__ __forceinline__ void emit_quad(const Quad& qd, int64_t e0, int64_t n, float mn0, float scale,
+                                          float rsc, bool rsc_ok, uint8_t* __restrict__ codes,
+                                          float* __restrict__ res) {
+  constexpr float L = (float)((1 << BITS) - 1);
+  uint32_t c[4];
+  float gh[4];
+  float q[4];
+  bool slow = !rsc_ok;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const float q0 = (qd.v[m] - mn0) * rsc;
+    q[m] = rintf(q0);
+    slow |= !(fabsf(q0 - q[m]) <= 0.5f - 0x1p-13f);
+  }
+  if (slow && scale != 0.f) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) q[m] = rintf((qd.v[m] - mn0) / scale);
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const float qq = scale != 0.f ? fminf(fmaxf(q[m], 0.f), L) : 0.f;
+    gh[m] = qq * scale + mn0;
+    c[m] = (uint32_t)qq;
+  }
+  store_quad<BITS, EF>(qd, e0, n, c, gh, codes, res);
+}
+
+// One pass for groups of 4..256 elements: a group is 2^LPG_LOG2 = G/4 consecutive
+// lanes, reduced with the compile-time butterflies of common.hpp (DPP, no LDS for up to
+// 16 lanes).  One tile per block; a round covers 1024 elements starting at a multiple of
+// 1024, so every group lies inside one wave of one round.
+//   scale = fl(range / L) through the corrected reciprocal div_level_count (equal to the
+//           IEEE quotient for range >= 2^-100, checked for every binary32 range at
+//           L = 15 and 255; smaller ranges divide);
+//   rsc   = v_rcp_f32(scale), within 1 ulp of 1/scale, for the code estimate (see below):
+//           for normal scales in [2^-126, 2^126) its error adds at most 2^-14.4 to the
+//           estimate below 256 (with q0's rounding and the quotient's own 2^-16, less than
+//           2^-13 in all), so a code is taken from q0 when q0 is at least 2^-13 from every
+//           half-integer; a quad with any other q0, or a scale outside that range, divides.
+template <int BITS, bool EF, int LPG_LOG2>
 __global__ __launch_bounds__(kBlock) void k_minmax_small(const float* __restrict__ x,
                                                          float* __restrict__ res, int64_t n,
-                                                         int lpg_log2, uint8_t* __restrict__ codes,
+                                                         uint8_t* __restrict__ codes,
                                                          float* __restrict__ mins,
                                                          float* __restrict__ scales) {
   constexpr float L = (float)((1 << BITS) - 1);
-  const int lpg = 1 << lpg_log2;
+  constexpr int lpg = 1 << LPG_LOG2;
   const int lane = lane_id();
   const int64_t base = (int64_t)blockIdx.x * kTile;
   Quad qd[kRounds];
@@ -183,15 +204,17 @@ __global__ __launch_bounds__(kBlock) void k_minmax_small(const float* __restrict
         lo = min(lo, e);
         hi = max(hi, e);
       }
-    lo = seg_min_u32(lo, lpg);
-    hi = seg_max_u32(hi, lpg);
+    lo = seg_min_c<LPG_LOG2>(lo);
+    hi = seg_max_c<LPG_LOG2>(hi);
     if (e0 >= n) continue;
     const float mn = ord_dec(lo), mx = ord_dec(hi);
-    const float scale = (mx - mn) / L;
-    const float mna[4] = {mn, mn, mn, mn}, sca[4] = {scale, scale, scale, scale};
-    emit_quad<BITS, EF, true>(qd[j], e0, n, mna, sca, 1.0f / scale, codes, res);
+    const float range = mx - mn;
+    const float scale = range >= 0x1p-100f ? div_level_count(range, L, 1.0f / L) : range / L;
+    const bool rsc_ok = scale >= 0x1p-126f && scale < 0x1p126f;
+    const float rsc = __builtin_amdgcn_rcpf(scale);
+    emit_quad<BITS, EF>(qd[j], e0, n, mn, scale, rsc, rsc_ok, codes, res);
     if ((lane & (lpg - 1)) == 0) {
-      const int64_t g = e0 >> (lpg_log2 + 2);
+      const int64_t g = e0 >> (LPG_LOG2 + 2);
       mins[g] = mn;
       scales[g] = scale;
     }
@@ -308,7 +331,7 @@ __global__ __launch_bounds__(kBlock) void k_minmax_quant(const float* __restrict
       mn[m] = inA ? mnA : mnB;
       sc[m] = inA ? scA : scB;
     }
-    emit_quad<BITS, EF, false>(qd, e0, n, mn, sc, 0.f, codes, res);
+    emit_quad_mixed<BITS, EF>(qd, e0, n, mn, sc, codes, res);
   }
 }
 
@@ -381,13 +404,13 @@ __global__ __launch_bounds__(kBlock) void k_minmax_tensor_quant(const float* __r
   const float mn = ord_dec(lo), mx = ord_dec(hi);
   const float scale = (mx - mn) / L;
   if (blockIdx.x == 0 && threadIdx.x == 0) { mins[0] = mn; scales[0] = scale; }
-  const float mna[4] = {mn, mn, mn, mn}, sca[4] = {scale, scale, scale, scale};
-  const float rsc = 1.0f / scale;
+  const bool rsc_ok = scale >= 0x1p-126f && scale < 0x1p126f;
+  const float rsc = __builtin_amdgcn_rcpf(scale);
   const int64_t nquads = (n + 3) >> 2;
   for (int64_t q = (int64_t)blockIdx.x * kBlock + threadIdx.x; q < nquads; q += (int64_t)gridDim.x * kBlock) {
     const int64_t e0 = q << 2;
     const Quad qd = load_quad<EF>(x, res, e0, n);
-    emit_quad<BITS, EF, true>(qd, e0, n, mna, sca, rsc, codes, res);
+    emit_quad<BITS, EF>(qd, e0, n, mn, scale, rsc, rsc_ok, codes, res);
   }
 }
 
@@ -406,13 +429,24 @@ hipError_t launch_minmax_small(const float* x, float* res, int64_t n, int64_t gr
   const int64_t tiles = (n + kTile - 1) / kTile;
   if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   const int grid = (int)tiles;
-  if (bits == 8) {
-    if (res) hipLaunchKernelGGL((k_minmax_small<8, true>), grid, kBlock, 0, s, x, res, n, lpg_log2, codes, mins, scales);
-    else hipLaunchKernelGGL((k_minmax_small<8, false>), grid, kBlock, 0, s, x, res, n, lpg_log2, codes, mins, scales);
-  } else {
-    if (res) hipLaunchKernelGGL((k_minmax_small<4, true>), grid, kBlock, 0, s, x, res, n, lpg_log2, codes, mins, scales);
-    else hipLaunchKernelGGL((k_minmax_small<4, false>), grid, kBlock, 0, s, x, res, n, lpg_log2, codes, mins, scales);
+#define GC_MM_SMALL(B, E, W) hipLaunchKernelGGL((k_minmax_small<B, E, W>), grid, kBlock, 0, s, x, res, n, codes, mins, scales)
+#define GC_MM_WIDTH(B, E)                       \
+  switch (lpg_log2) {                           \
+    case 0: GC_MM_SMALL(B, E, 0); break;        \
+    case 1: GC_MM_SMALL(B, E, 1); break;        \
+    case 2: GC_MM_SMALL(B, E, 2); break;        \
+    case 3: GC_MM_SMALL(B, E, 3); break;        \
+    case 4: GC_MM_SMALL(B, E, 4); break;        \
+    case 5: GC_MM_SMALL(B, E, 5); break;        \
+    default: GC_MM_SMALL(B, E, 6); break;       \
   }
+  if (bits == 8) {
+    if (res) { GC_MM_WIDTH(8, true) } else { GC_MM_WIDTH(8, false) }
+  } else {
+    if (res) { GC_MM_WIDTH(4, true) } else { GC_MM_WIDTH(4, false) }
+  }
+#undef GC_MM_WIDTH
+#undef GC_MM_SMALL
   return hipGetLastError();
 }
 

@@ -11,9 +11,11 @@
 // The random draw of element e is word (e&3) of the Philox block at counter e>>2, so an
 // aligned quad costs one Philox call.  One pass: 4 B read, 1 B code written per element
 // (+4 B read and written for the residual), 4 B per group for the norm.  The pass is
-// bound by VALU work more than by HBM: a Philox4x32-10 block per quad (20 64-bit integer
-// multiply-adds) and two correctly rounded divisions per element; on a 25 MiB bucket two
-// quads per lane measured fastest (12.9 us against 14.8 with one and 14.4 with four).
+// bound by VALU work more than by HBM: a Philox4x32-10 block per quad (19 64-bit integer
+// multiply-adds, each issued at the full rate on gfx950) and the level decision, taken from
+// a reciprocal estimate except near its boundaries (qsgd_core.hpp); the group's butterfly
+// is compile-time (DPP steps for up to 16 lanes).  On a 25 MiB bucket two quads per lane
+// measured fastest (12.9 us against 14.8 with one and 14.4 with four, with the divisions).
 #include "common.hpp"
 #include "internal.hpp"
 #include "qsgd_core.hpp"
@@ -28,12 +30,13 @@ constexpr int64_t kTile = (int64_t)kBlock * 4 * kRounds;   // 2048 elements
 // One 2048-element tile per block: 2 rounds of 1024 elements, each starting at a multiple
 // of 1024 so that every group (G <= 256) lies inside one wave of one round.  All loads
 // of the tile are issued before any arithmetic (non-temporal 16-byte loads and stores).
-template <bool EF>
+template <bool EF, int LPG_LOG2>
 __global__ __launch_bounds__(kBlock) void k_qsgd(const float* __restrict__ x, float* __restrict__ res,
-                                                 int64_t n, int lpg_log2, float s, float ys, uint64_t seed,
+                                                 int64_t n, float s, float ys, uint64_t seed,
                                                  int64_t index_base, int8_t* __restrict__ codes,
                                                  float* __restrict__ norms) {
-  const int lpg = 1 << lpg_log2;
+  constexpr int lpg_log2 = LPG_LOG2;
+  constexpr int lpg = 1 << LPG_LOG2;
   const int lane = lane_id();
   const int64_t base = (int64_t)blockIdx.x * kTile;
   float v[kRounds][4];
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(kBlock) void k_qsgd(const float* __restrict__ x, fl
     // pairwise tree: lane-local levels, then the lane butterfly (every lane takes part;
     // lanes past the end hold +0.0)
     float ss = quad_sumsq(v[j]);
-    ss = seg_tree_sum(ss, lpg);
+    ss = seg_tree_sum_c<LPG_LOG2>(ss);
     if (e0 >= n) continue;
     const bool full = e0 + 4 <= n;
     const float nu = sqrtf(ss);
@@ -104,10 +107,20 @@ hipError_t launch_qsgd(const float* x, float* res, int64_t n, int64_t group, int
   const int64_t blocks = (n + kTile - 1) / kTile;
   const float sf = (float)levels;
   const float ys = 1.0f / sf;
-  if (res)
-    hipLaunchKernelGGL((k_qsgd<true>), (int)blocks, kBlock, 0, s, x, res, n, lpg_log2, sf, ys, seed, index_base, codes, norms);
-  else
-    hipLaunchKernelGGL((k_qsgd<false>), (int)blocks, kBlock, 0, s, x, res, n, lpg_log2, sf, ys, seed, index_base, codes, norms);
+#define GC_QSGD(E, W) hipLaunchKernelGGL((k_qsgd<E, W>), (int)blocks, kBlock, 0, s, x, res, n, sf, ys, seed, index_base, codes, norms)
+#define GC_QSGD_WIDTH(E)                  \
+  switch (lpg_log2) {                     \
+    case 0: GC_QSGD(E, 0); break;         \
+    case 1: GC_QSGD(E, 1); break;         \
+    case 2: GC_QSGD(E, 2); break;         \
+    case 3: GC_QSGD(E, 3); break;         \
+    case 4: GC_QSGD(E, 4); break;         \
+    case 5: GC_QSGD(E, 5); break;         \
+    default: GC_QSGD(E, 6); break;        \
+  }
+  if (res) { GC_QSGD_WIDTH(true) } else { GC_QSGD_WIDTH(false) }
+#undef GC_QSGD_WIDTH
+#undef GC_QSGD
   return hipGetLastError();
 }
 

@@ -9,18 +9,45 @@
 namespace gc {
 
 // ys = fl(1/s); the division by s goes through div_level_count (the same quotient).
+//
+// The level needs floor(u) and the decision U < p of u = fl(fl(|v| / nu) * s).  An
+// estimate u' = fl(fl(|v| * rnu) * s) with rnu = v_rcp_f32(nu) (within 1 ulp of 1/nu, for
+// nu in [2^-126, 2^126)) lies within u * (2^-22 + 2^-23) < 2^-14 of u, since u <= s <= 127
+// (|v| <= nu).  So when p' = u' - floor(u') is at least 2^-13 from 0, from 1 and from U,
+// floor(u) = floor(u') and (U < p) = (U < p'); a quad with any element outside that band
+// (or nu outside the range, or nu = 0) divides.  One reciprocal per quad replaces four
+// IEEE divisions on almost every quad.
 __device__ __forceinline__ void qsgd_quad(const float v[4], float nu, float s, float ys, const float u[4],
                                           int lev[4], float gh[4]) {
+  const float rnu = __builtin_amdgcn_rcpf(nu);
+  bool slow = !(nu >= 0x1p-126f && nu < 0x1p126f);
+  float lf[4], up[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    float level = 0.f;
-    if (nu > 0.f) {
-      const float a = fabsf(v[m]) / nu;
-      const float uu = a * s;
-      const float l = floorf(uu);
-      const float p = uu - l;
-      level = fminf(l + (u[m] < p ? 1.f : 0.f), s);
+    const float uu = (fabsf(v[m]) * rnu) * s;
+    const float l = floorf(uu);
+    const float p = uu - l;
+    slow |= !(p >= 0x1p-13f && p <= 1.0f - 0x1p-13f && fabsf(u[m] - p) >= 0x1p-13f);
+    lf[m] = l;
+    up[m] = u[m] < p ? 1.f : 0.f;
+  }
+  if (slow) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      float l = 0.f, up1 = 0.f;
+      if (nu > 0.f) {
+        const float a = fabsf(v[m]) / nu;
+        const float uu = a * s;
+        l = floorf(uu);
+        up1 = u[m] < (uu - l) ? 1.f : 0.f;
+      }
+      lf[m] = l;
+      up[m] = up1;
     }
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const float level = nu > 0.f ? fminf(lf[m] + up[m], s) : 0.f;
     lev[m] = v[m] < 0.f ? -(int)level : (int)level;
     gh[m] = nu * level;   // t, divided below
   }

@@ -1,10 +1,11 @@
 """The quotient form of QSGD's dequantization, fl(fl(nu * level) / s), in the kernels.
 
-For a level count s in [1, 127] and t = 0 or t >= 2^-100, the kernels compute fl(t / s)
+For a level count s in [1, 127] (and the min-max level counts 15 and 255) and t = 0 or
+t >= 2^-100, the kernels compute fl(t / s)
 as q0 = fl(t * fl(1/s)) followed by one correction with the exact remainder
 fma(-q0, s, t), and divide for t below 2^-100.  tests/pins/level_count_division.c
 compares that form with the IEEE binary32 division bit for bit: here over every t of the
-domain for the level counts of the configurations (15, 127), and over whole binades of t
+domain for the level counts of the configurations (15, 127, 255), and over whole binades of t
 for every s in [1, 127] (the form scales with t's exponent inside the normal range).  The
 last case shows why the domain stops at 2^-100: for even s that are not powers of two a
 subnormal quotient can be an exact midpoint that the correction rounds the wrong way.
@@ -40,7 +41,9 @@ def checker(tmp_path_factory):
 
 
 def test_domain_exact(checker):
-    jobs = [(15, 15, LO, INF), (127, 127, LO, INF), (1, 127, 0, 1),            # t = 0
+    # 15 and 127: the QSGD level counts of the configurations; 15 and 255 also divide the
+    # min-max range into its scale (int4, int8)
+    jobs = [(15, 15, LO, INF), (127, 127, LO, INF), (255, 255, LO, INF), (1, 255, 0, 1),   # t = 0
             (1, 127, LO, LO + (1 << 23)),                                      # [2^-100, 2^-99)
             (1, 127, 127 << 23, 128 << 23),                                    # [1, 2)
             (1, 127, 254 << 23, INF)]                                          # [2^127, max]
