@@ -99,6 +99,33 @@ __device__ __forceinline__ void uniforms4(uint64_t seed, uint64_t e0, float u[4]
   for (int m = 0; m < 4; ++m) u[m] = u24(w[m]);
 }
 
+// Raw words of e0..e0+3 when the caller knows at compile time whether e0 % 4 == 0.
+template <bool ALIGNED>
+__device__ __forceinline__ void words4_t(uint64_t seed, uint64_t e0, uint32_t out[4]) {
+  if constexpr (ALIGNED) {
+    const Words4 a = philox_block(seed, e0 >> 2);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) out[m] = a.w[m];
+  } else {
+    words4(seed, e0, out);
+  }
+}
+
+// The same when the caller knows at compile time whether e0 % 4 == 0 (ALIGNED: one
+// Philox block).  Kernels whose element indices are index_base + a multiple of 4 choose
+// the variant at launch from index_base % 4: the alignment is uniform, yet with only the
+// general form the compiler computed both blocks of words4 on every quad.
+template <bool ALIGNED>
+__device__ __forceinline__ void uniforms4_t(uint64_t seed, uint64_t e0, float u[4]) {
+  if constexpr (ALIGNED) {
+    const Words4 a = philox_block(seed, e0 >> 2);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) u[m] = u24(a.w[m]);
+  } else {
+    uniforms4(seed, e0, u);
+  }
+}
+
 // The word of one element index.
 __device__ __forceinline__ uint32_t philox_word(uint64_t seed, uint64_t e) {
   const Words4 a = philox_block(seed, e >> 2);

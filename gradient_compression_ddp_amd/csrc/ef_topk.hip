@@ -665,7 +665,7 @@ __global__ __launch_bounds__(kBlock) void k_hist(TopkCtrl* __restrict__ ctrl,
 // DEFER: the previous call's recorded corrections of this tile are spread into LDS
 // while the loads are in flight and replace r at their positions before the add.
 // MON: the tile's sum of c^2 in float64 (exact squares, fixed order) goes to mon_c.
-template <bool RAND, bool DEFER, bool MON>
+template <bool RAND, bool DEFER, bool MON, bool ALIGNED>
 __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g, float* __restrict__ r,
                                                     int64_t n, TopkCtrl* __restrict__ ctrl,
                                                     uint32_t* __restrict__ tile_start,
@@ -762,7 +762,7 @@ __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g,
 #pragma unroll
   for (int j = 0; j < kRounds; ++j) {
     if (RAND) {
-      words4(seed, (uint64_t)(index_base + base + j * (kBlock * 4) + threadIdx.x * 4), key[j]);
+      words4_t<ALIGNED>(seed, (uint64_t)(index_base + base + j * (kBlock * 4) + threadIdx.x * 4), key[j]);
 #pragma unroll
       for (int m = 0; m < 4; ++m) key[j][m] = rand_key(key[j][m]);
     } else {
@@ -2043,7 +2043,7 @@ __global__ __launch_bounds__(kBlock) void k_qsgd_kept(const float* __restrict__ 
     if (live) {
       const float nu = sqrtf(ss);
       float u[4];
-      uniforms4(seed, (uint64_t)e0, u);
+      uniforms4_t<true>(seed, (uint64_t)e0, u);   // e0 is a multiple of 4
       int lev[4];
       float gh[4];
       qsgd_quad(v, nu, s, ys, u, lev, gh);
@@ -2239,11 +2239,18 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
 
   // 3: the streaming pass
   prof_mark(s, 1);
-#define GC_CAND_PASS(M)                                                                                  \
-  hipLaunchKernelGGL((k_ef_cand<RAND, DEFER, M>), (unsigned)l.ntiles, kBlock, 0, s, grad, res, n, ctrl,        \
+  // Random-K keys: a lane's quad draws one Philox block when index_base % 4 == 0
+#define GC_CAND_PASS(M, A)                                                                               \
+  hipLaunchKernelGGL((k_ef_cand<RAND, DEFER, M, A>), (unsigned)l.ntiles, kBlock, 0, s, grad, res, n, ctrl,     \
                      l.tile_start, l.tile_count, l.pool_val, l.pool_off, (uint32_t)l.region_cap, l.pool_c,       \
                      select_seed, index_base, pd, cap, mon_c, lb_status)
-  if (mon) GC_CAND_PASS(true); else GC_CAND_PASS(false);
+  if (!RAND || (index_base & 3) == 0) {
+    if (mon) GC_CAND_PASS(true, true); else GC_CAND_PASS(false, true);
+  } else {
+    if constexpr (RAND) {
+      if (mon) GC_CAND_PASS(true, false); else GC_CAND_PASS(false, false);
+    }
+  }
 #undef GC_CAND_PASS
   prof_mark(s, 2);
 

@@ -30,7 +30,7 @@ constexpr int64_t kTile = (int64_t)kBlock * 4 * kRounds;   // 2048 elements
 // One 2048-element tile per block: 2 rounds of 1024 elements, each starting at a multiple
 // of 1024 so that every group (G <= 256) lies inside one wave of one round.  All loads
 // of the tile are issued before any arithmetic (non-temporal 16-byte loads and stores).
-template <bool EF, int LPG_LOG2>
+template <bool EF, int LPG_LOG2, bool ALIGNED>
 __global__ __launch_bounds__(kBlock) void k_qsgd(const float* __restrict__ x, float* __restrict__ res,
                                                  int64_t n, float s, float ys, uint64_t seed,
                                                  int64_t index_base, int8_t* __restrict__ codes,
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kBlock) void k_qsgd(const float* __restrict__ x, fl
     const bool full = e0 + 4 <= n;
     const float nu = sqrtf(ss);
     float u[4];
-    uniforms4(seed, (uint64_t)(index_base + e0), u);
+    uniforms4_t<ALIGNED>(seed, (uint64_t)(index_base + e0), u);
     int lev[4];
     float gh[4];
     qsgd_quad(v[j], nu, s, ys, u, lev, gh);
@@ -107,7 +107,16 @@ hipError_t launch_qsgd(const float* x, float* res, int64_t n, int64_t group, int
   const int64_t blocks = (n + kTile - 1) / kTile;
   const float sf = (float)levels;
   const float ys = 1.0f / sf;
-#define GC_QSGD(E, W) hipLaunchKernelGGL((k_qsgd<E, W>), (int)blocks, kBlock, 0, s, x, res, n, sf, ys, seed, index_base, codes, norms)
+  // element e0 of a lane is a multiple of 4: its draw is one Philox block exactly when
+  // index_base is a multiple of 4
+  const bool aligned = (index_base & 3) == 0;
+#define GC_QSGD(E, W)                                                                                        \
+  do {                                                                                                      \
+    if (aligned) hipLaunchKernelGGL((k_qsgd<E, W, true>), (int)blocks, kBlock, 0, s, x, res, n, sf, ys, seed,  \
+                                    index_base, codes, norms);                                              \
+    else hipLaunchKernelGGL((k_qsgd<E, W, false>), (int)blocks, kBlock, 0, s, x, res, n, sf, ys, seed,         \
+                            index_base, codes, norms);                                                      \
+  } while (0)
 #define GC_QSGD_WIDTH(E)                  \
   switch (lpg_log2) {                     \
     case 0: GC_QSGD(E, 0); break;         \

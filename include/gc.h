@@ -318,8 +318,10 @@ int gc_qsgd(const float* x, float* residual, int64_t n, int64_t group, int level
  *   element t of the segment sits in bits 2(t%4)..2(t%4)+1 of byte B_s + t/4, with
  *   0 -> 00, +1 -> 01, -1 -> 11; unused bits are 0.  scales: float[nseg].
  * x, residual: 16-byte aligned.  index_base >= 0.
- * Workspace: gc_workspace_size(GC_OP_TERNGRAD, n, nseg, 0) bytes (64 partial maxima per
- * segment; 0 when n == 0).  Calls that share a workspace must not overlap on the device.
+ * Workspace: gc_workspace_size(GC_OP_TERNGRAD, n, nseg, 0) bytes, about 0.64 bytes per
+ * element (two sets of 64 partial maxima per segment, and per tile of 4032 elements a
+ * list of up to 128 bytes whose codes the streaming pass could not settle, with their
+ * values); 0 when n == 0.  Calls that share a workspace must not overlap on the device.
  */
 int gc_terngrad(const float* x, float* residual, int nseg, const int64_t* seg_offsets,
                 uint64_t seed, int64_t index_base, uint8_t* packed, float* scales,

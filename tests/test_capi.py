@@ -101,12 +101,12 @@ def test_ef_randk_rejects_bad_arguments(lib):
     assert f(FAKE, FAKE, 10, 1, 1 << 62, 3, FAKE, FAKE, 0, 64, 0, None, None, FAKE, 1 << 20, None) == 1
     assert f(FAKE, FAKE, 10, 1, 0, 3, FAKE, FAKE, 0, 64, 0, None, None, None, 0, None) == 2
     assert f(None, None, 0, 0, 0, 3, None, None, 0, 64, 0, None, None, None, 0, None) == 0
-    # above 2^25 elements the Random-K pool also keeps each candidate's value: more
-    # workspace than Top-K of the same size; below, both select over c itself
-    st_t, b_t = _ws(lib, 1, 50_000_000, 500_000, 0)
-    st_r, b_r = _ws(lib, 7, 50_000_000, 500_000, 0)
-    assert st_t == 0 and st_r == 0 and b_r > b_t
-    assert _ws(lib, 1, 5_000_000, 50_000, 0) == _ws(lib, 7, 5_000_000, 50_000, 0)
+    # the Random-K candidate pool also keeps each candidate's value: more workspace than
+    # Top-K of the same size, at every size
+    for n, k in ((50_000_000, 500_000), (5_000_000, 50_000), (1000, 10)):
+        st_t, b_t = _ws(lib, 1, n, k, 0)
+        st_r, b_r = _ws(lib, 7, n, k, 0)
+        assert st_t == 0 and st_r == 0 and b_r > b_t
     assert _ws(lib, 7, 100, 0, 0) == (0, 0)
     assert _ws(lib, 7, 100, 101, 0)[0] == 1
 
@@ -266,12 +266,13 @@ def test_decompress_payloads_rejects_before_any_launch(lib):
 
 
 def test_terngrad_workspace_is_sized_and_checked(lib):
-    """gc_terngrad keeps 64 partial maxima per segment in the caller's workspace: the size
-    query reports it, and a missing or short workspace is rejected before any launch."""
+    """gc_terngrad keeps two sets of 64 partial maxima per segment and the per-tile lists of
+    unsettled bytes in the caller's workspace: the size query reports it, and a missing or
+    short workspace is rejected before any launch."""
     size = lib.gc_workspace_size
     size.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.POINTER(ctypes.c_size_t)]
     b = ctypes.c_size_t(0)
-    assert size(4, 1000, 3, 0, ctypes.byref(b)) == 0 and b.value >= 3 * 64 * 4 and b.value % 256 == 0
+    assert size(4, 1000, 3, 0, ctypes.byref(b)) == 0 and b.value >= 2 * 3 * 64 * 4 + 128 * 20 and b.value % 256 == 0
     assert size(4, 0, 3, 0, ctypes.byref(b)) == 0 and b.value == 0        # nothing to do, no workspace
     t = lib.gc_terngrad
     t.argtypes = [VP, VP, ctypes.c_int, VP, ctypes.c_uint64, ctypes.c_int64, VP, VP, VP, ctypes.c_size_t, VP]
