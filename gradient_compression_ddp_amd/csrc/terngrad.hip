@@ -47,9 +47,10 @@ constexpr int kBlock = 256;
 constexpr int kWaves = kBlock / kWave;                  // 4
 constexpr int kSegBatch = 32;                           // segments per launch at most
 constexpr int kSlots = kWave;                           // maximum slots per segment
-constexpr int kRunsB = 4;                               // wave runs per wave per tile
+constexpr int kRunsB = 8;                               // wave runs per wave per tile
 constexpr int kRunsPerBlock = kWaves * kRunsB;          // 16 runs of 64 quads per tile
-constexpr int kCap = 128;                               // listed bytes per tile
+constexpr int kCap = 64;                                // listed bytes per wave list
+constexpr int kFixLists = 16;                           // wave lists per fix-up wave
 constexpr int kSampleChunkQuads = kWave;                // a sampled chunk: 64 quads = 1 KB
 constexpr int kSampleEvery = 32;                        // one chunk in 32
 
@@ -66,7 +67,7 @@ struct SegList {
 __host__ __device__ inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Tiles of a segment [lo, hi): runs of 64 quads (63 bytes when the start is not
-// quad-aligned), 16 runs per tile.
+// quad-aligned), 16 runs per tile, 4 per wave.
 __host__ __device__ inline int64_t seg_runs(int64_t lo, int64_t hi) {
   const int64_t nq = ((hi + 3) >> 2) - (lo >> 2);
   return hi > lo ? cdiv64(nq, (lo & 3) ? kWave - 1 : kWave) : 0;
@@ -78,12 +79,13 @@ int64_t tiles_bound(int64_t n, int nseg) {
   return cdiv64(n / 4 + 2 * (int64_t)nseg, (int64_t)(kWave - 1) * kRunsPerBlock) + 2 * (int64_t)nseg + 1;
 }
 
+// One list per wave of the pass: wave w of tile t owns list t * kWaves + w.
 struct Work {
   uint32_t* samp;     // [nseg * kSlots] sampled maxima (|x| bits), written before the pass
   uint32_t* slots;    // [nseg * kSlots] the pass's maxima (|x| bits)
-  uint32_t* tile_cnt; // [tiles] listed bytes of each tile (> kCap: overflowed)
-  uint32_t* lst_b;    // [tiles * kCap] byte within its segment
-  f32x4* lst_x;       // [tiles * kCap] the byte's 4 values (x + r), byte order
+  uint32_t* cnt;      // [lists] listed bytes of each wave list (> kCap: overflowed)
+  uint32_t* lst_b;    // [lists * kCap] byte within its segment
+  f32x4* lst_x;       // [lists * kCap] the byte's 4 values (x + r), byte order
   size_t bytes;
 };
 
@@ -99,9 +101,10 @@ Work work_layout(void* base, int64_t n, int nseg) {
   };
   w.samp = (uint32_t*)take((size_t)nseg * kSlots * sizeof(uint32_t));
   w.slots = (uint32_t*)take((size_t)nseg * kSlots * sizeof(uint32_t));
-  w.tile_cnt = (uint32_t*)take((size_t)tiles * sizeof(uint32_t));
-  w.lst_b = (uint32_t*)take((size_t)tiles * kCap * sizeof(uint32_t));
-  w.lst_x = (f32x4*)take((size_t)tiles * kCap * sizeof(f32x4));
+  const size_t lists = (size_t)tiles * kWaves;
+  w.cnt = (uint32_t*)take(lists * sizeof(uint32_t));
+  w.lst_b = (uint32_t*)take(lists * kCap * sizeof(uint32_t));
+  w.lst_x = (f32x4*)take(lists * kCap * sizeof(f32x4));
   w.bytes = off;
   return w;
 }
@@ -140,11 +143,16 @@ __device__ __forceinline__ void load_quad_masked(const float* __restrict__ x,
   for (int m = 0; m < 4; ++m) ok[m] = (p0 + m >= lo) && (p0 + m < hi);
 }
 
-// The segment of a launch's block (or wave) t: the largest si with blk[si] <= t.
+// The segment of a launch's block (or wave) t: the largest si < count with blk[si] <= t
+// (blk is nondecreasing, blk[0] = 0), by bisection: at most 5 dependent reads of the
+// kernel argument instead of one per segment.
 __device__ __forceinline__ int seg_of(const SegList& L, uint32_t t) {
-  int si = 0;
-  while (si + 1 < L.count && L.blk[si + 1] <= t) ++si;
-  return si;
+  int a = 0, b = L.count - 1;
+  while (a < b) {
+    const int mid = (a + b + 1) >> 1;
+    if (L.blk[mid] <= t) a = mid; else b = mid - 1;
+  }
+  return a;
 }
 
 // The 4 elements of packed byte b of a segment starting at lo: element j is position
@@ -167,6 +175,11 @@ __device__ __forceinline__ uint32_t byte_codes(const float xs[4], int nvalid, fl
     }
   }
   return byte;
+}
+
+// The value of the next lane (lane 63 gets 0): a DPP wave shift by one lane.
+__device__ __forceinline__ float next_lane(float v) {
+  return bitsf((uint32_t)__builtin_amdgcn_update_dpp(0, (int)fbits(v), 0x130, 0xF, 0xF, false));
 }
 
 // ---- 1: sampled maxima --------------------------------------------------------------
@@ -202,192 +215,259 @@ __global__ __launch_bounds__(kBlock) void k_tern_sample(const float* __restrict_
 }
 
 // ---- 2: the pass --------------------------------------------------------------------
-// One wave's 4 runs.  FULL: every quad of the runs lies inside the segment (no masks, no
-// bounds).  Every wave of the block calls this once and meets its one barrier, where the
-// block's maximum is combined into the bound s_lo.
-template <bool EF, bool ALIGNED, bool FULL>
-__device__ __forceinline__ void pass_wave(const float* __restrict__ x, float* __restrict__ res, int64_t n,
-                                          int64_t lo, int64_t hi, int64_t r0, int64_t runs, uint32_t sampled,
-                                          uint32_t* __restrict__ slot, uint32_t* s_max, uint32_t* s_n,
-                                          uint64_t seed, int64_t index_base, uint8_t* __restrict__ out,
-                                          int64_t tile, uint32_t* __restrict__ lst_b, f32x4* __restrict__ lst_x) {
-  const int d = (int)(lo & 3);
-  const int step = d == 0 ? kWave : kWave - 1;   // bytes per wave run
-  const int64_t qs = lo >> 2;
-  const int64_t nb = (hi - lo + 3) >> 2;         // output bytes of the segment
-  const int lane = lane_id();
-  const int w = threadIdx.x / kWave;
-  float v[kRunsB][4];
-  bool ok[kRunsB][4];
-#pragma unroll
-  for (int u = 0; u < kRunsB; ++u) {
-    const int64_t Q = qs + (r0 + u) * step + lane;
-    if (FULL) {
-      const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x + (Q << 2)));
-      v[u][0] = a.x; v[u][1] = a.y; v[u][2] = a.z; v[u][3] = a.w;
-      if (EF) {
-        const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(res + (Q << 2)));
-        v[u][0] = v[u][0] + b.x; v[u][1] = v[u][1] + b.y; v[u][2] = v[u][2] + b.z; v[u][3] = v[u][3] + b.w;
-      }
-#pragma unroll
-      for (int m = 0; m < 4; ++m) ok[u][m] = true;
-    } else if (r0 + u < runs) {
-      load_quad_masked<EF>(x, res, Q, lo, hi, n, v[u], ok[u]);
-    } else {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) { v[u][m] = 0.f; ok[u][m] = false; }
-    }
-  }
-  // the block's maximum (with the sampled maxima, one slot per lane) into the pass's
-  // slots, and the bound s_lo
-  uint32_t mx = sampled;
-#pragma unroll
-  for (int u = 0; u < kRunsB; ++u)
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      if (ok[u][m]) mx = max(mx, fbits(fabsf(v[u][m])));
-  mx = seg_max_c<6>(mx);
-  if (lane == 0) s_max[w] = mx;
+// Segments whose start is D elements past a multiple of 4 (D is a template argument: the
+// byte stitching and the masks below are then fixed at compile time).
+
+// The block's bound s_lo: the maximum of fm over the block (fm holds a wave's |x| maximum
+// and the sampled maxima) goes to the pass's slots; returns fl(1/s_lo) * 2^32 (inf when
+// s_lo is 0 or below 2^-96).  Every wave of the block calls this once.
+__device__ __forceinline__ float block_bound(float fm, uint32_t* __restrict__ slot, uint32_t* s_max) {
+  // |x| >= 0, so the order of the bit patterns is the order of the values
+  const uint32_t mx = seg_max_c<6>(fbits(fm));
+  if (lane_id() == 0) s_max[threadIdx.x / kWave] = mx;
   __syncthreads();
   const uint32_t lo_bits = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
   if (threadIdx.x == 0 && lo_bits) atomicMax(slot + (blockIdx.x & (kSlots - 1)), lo_bits);
-  const float rsc = 1.0f / bitsf(lo_bits);
+  return (1.0f / bitsf(lo_bits)) * 0x1p32f;
+}
+
+// One wave run: bytes b0 .. b0 + 62 (or 63) of the segment from the lane's quad q0 + lane
+// (values vq, ok: inside the segment).  Writes the bytes as 0, lists the unsettled ones
+// (nl: the wave's count so far, uniform) and, with error feedback, r = x + r.
+template <bool EF, bool ALIGNED, int D, bool FULL>
+__device__ __forceinline__ void run_pass(f32x4 vq, const bool ok[4], int64_t b0, int64_t q0, int64_t nb,
+                                         float rsc32, uint64_t seed, int64_t index_base, uint8_t* __restrict__ out,
+                                         float* __restrict__ res, uint32_t& nl, uint32_t* __restrict__ lst_b,
+                                         f32x4* __restrict__ lst_x) {
+  constexpr int step = D == 0 ? kWave : kWave - 1;
+  const int lane = lane_id();
+  uint32_t wd[4];
+  if constexpr (ALIGNED) {
+    // index_base % 4 == 0: the lane's quad is Philox block index_base / 4 + q0 + lane
+    const Words4 a = philox_block(seed, (uint64_t)((index_base >> 2) + q0) + (uint32_t)lane);
 #pragma unroll
-  for (int u = 0; u < kRunsB; ++u) {
-    const int64_t ru = r0 + u;
-    if (!FULL && ru >= runs) break;   // uniform across the wave
-    const int64_t b0 = ru * step;
-    const int64_t Q = qs + b0 + lane;
-    float uu[4];
-    uniforms4_t<ALIGNED>(seed, (uint64_t)(index_base + (Q << 2)), uu);
-    // settled: x = 0, or U >= fl(|x| / s_lo) (so code 0 under every s >= s_lo).
-    // d = fl(fl(|x| * rsc) - U) lies within 2^-21 of fl(|x|/s_lo) - U (rsc's relative
-    // error 2^-24, two roundings below 1 and the quotient's own), so d <= -2^-21 settles it
-    uint32_t open = 0u;   // bit m: element m of the quad is not settled
+    for (int m = 0; m < 4; ++m) wd[m] = a.w[m];
+  } else {
+    words4_t<false>(seed, (uint64_t)(index_base + ((q0 + lane) << 2)), wd);
+  }
+  // Settled: U >= q = fl(|x| / s_lo), U = (w >> 8) * 2^-24; then the code is 0 under
+  // every scale s >= s_lo, since fl(|x| / s) <= q.  Let Q = |x| / s_lo <= 1 (s_lo is at
+  // least this block's own maximum).  rsc32 is within 2^-24 relative (or 2^-118
+  // absolute, in the subnormal range) of 2^32 / s_lo, the fused add rounds once, and q
+  // is within 2^-24 relative of Q, so F = fl(|x| * rsc32 + 8192) >= q * 2^32 + 6000.
+  // fl(w) is within 128 of w and (w >> 8) * 2^8 >= w - 255, so fl(w) > F gives U > q.
+  // An element is open (unsettled) when F >= fl(w); x = 0 with rsc32 = inf gives
+  // F = NaN: settled, correctly (its code is 0).  Each element's test is a lane mask,
+  // and a byte's mask is stitched from them with scalar operations.
+  uint64_t om[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float ax = fabsf(v[u][m]);
-      const float dd = ax * rsc - uu[m];
-      const bool settled = !ok[u][m] || ax == 0.f || dd <= -0x1p-21f;
-      open |= settled ? 0u : (1u << m);
+  for (int m = 0; m < 4; ++m) om[m] = ballot(ok[m] && fmaf(fabsf(vq[m]), rsc32, 8192.0f) >= (float)wd[m]);
+  // byte b0 + lane: elements m >= D of this lane's quad and m < D of the next lane's
+  uint64_t hi_m = 0ull, lo_m = 0ull;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    if (m >= D) hi_m |= om[m]; else lo_m |= om[m];
+  }
+  const uint64_t own = FULL ? (D == 0 ? ~0ull : (~0ull >> 1)) : ballot(lane < step && b0 + lane < nb);
+  const uint64_t lm = (hi_m | (lo_m >> 1)) & own;
+  if (__builtin_amdgcn_inverse_ballot_w64(own)) (out + b0)[lane] = 0;
+  if (lm) {
+    // the byte's values: elements D.. of this quad, then elements ..D-1 of the next
+    // lane's quad (a wave shift by one lane)
+    f32x4 xs;
+    if constexpr (D == 0) {
+      xs = vq;
+    } else if constexpr (D == 1) {
+      xs = f32x4{vq.y, vq.z, vq.w, next_lane(vq.x)};
+    } else if constexpr (D == 2) {
+      xs = f32x4{vq.z, vq.w, next_lane(vq.x), next_lane(vq.y)};
+    } else {
+      xs = f32x4{vq.w, next_lane(vq.x), next_lane(vq.y), next_lane(vq.z)};
     }
-    // byte b0 + lane: elements m >= d of this quad and m < d of the next
-    const uint32_t nxt = (uint32_t)__shfl_down((int)open, 1, kWave);
-    const uint32_t bopen = d == 0 ? open : (((open >> d) | (nxt << (4 - d))) & 0xFu);
-    const bool owner = lane < step && (FULL || b0 + lane < nb);
-    const bool listed = owner && bopen != 0u;
-    if (owner) out[b0 + lane] = 0;
-    const uint64_t lm = ballot(listed);
-    if (lm) {
-      // the byte's values: xs[j] = element j + d of this quad (j < 4 - d), else element
-      // j + d - 4 of the next lane's quad.  d is uniform, and each case indexes with
-      // constants (an index computed from d would put the arrays in scratch memory)
-      float xs[4];
-      if (d == 0) {
-        xs[0] = v[u][0]; xs[1] = v[u][1]; xs[2] = v[u][2]; xs[3] = v[u][3];
-      } else {
-        float nv[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) nv[m] = __shfl_down(v[u][m], 1, kWave);
-        if (d == 1) {
-          xs[0] = v[u][1]; xs[1] = v[u][2]; xs[2] = v[u][3]; xs[3] = nv[0];
-        } else if (d == 2) {
-          xs[0] = v[u][2]; xs[1] = v[u][3]; xs[2] = nv[0]; xs[3] = nv[1];
-        } else {
-          xs[0] = v[u][3]; xs[1] = nv[0]; xs[2] = nv[1]; xs[3] = nv[2];
-        }
-      }
-      uint32_t base = 0u;
-      if (lane == 0) base = atomicAdd(s_n, (uint32_t)__popcll(lm));
-      base = (uint32_t)__shfl((int)base, 0, kWave);
-      const uint32_t pos = base + mbcnt(lm);
-      if (listed && pos < kCap) {
-        lst_b[tile * kCap + pos] = (uint32_t)(b0 + lane);
-        lst_x[tile * kCap + pos] = f32x4{xs[0], xs[1], xs[2], xs[3]};
-      }
+    const uint32_t pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(lm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)lm, nl));
+    if (__builtin_amdgcn_inverse_ballot_w64(lm) && pos < kCap) {
+      lst_b[pos] = (uint32_t)b0 + (uint32_t)lane;
+      lst_x[pos] = xs;
     }
-    if (EF) {
-      // element m of this lane's quad belongs to byte lane (m >= d) or byte lane-1 (m < d);
-      // the lane owning that byte writes its residual, so a quad shared by two runs is
-      // split between them and no lane writes an element another lane writes
-      if (FULL && (d == 0 || (lane >= 1 && lane <= kWave - 2))) {
-        __builtin_nontemporal_store(f32x4{v[u][0], v[u][1], v[u][2], v[u][3]},
-                                    reinterpret_cast<f32x4*>(res + (Q << 2)));
-      } else {
+    nl += (uint32_t)__popcll(lm);
+  }
+  if (EF) {
+    // element m of this lane's quad belongs to byte lane (m >= D) or byte lane-1 (m < D);
+    // the lane owning that byte writes its residual, so a quad shared by two runs is
+    // split between them and no lane writes an element another lane writes
+    float* __restrict__ rq = res + (q0 << 2);
+    if (FULL && (D == 0 || (lane >= 1 && lane <= kWave - 2))) {
+      __builtin_nontemporal_store(vq, reinterpret_cast<f32x4*>(rq) + lane);
+    } else {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const bool mine = d == 0 || (m >= d ? lane <= kWave - 2 : lane >= 1);
-          if (ok[u][m] && mine) res[(Q << 2) + m] = v[u][m];
-        }
+      for (int m = 0; m < 4; ++m) {
+        const bool mine = D == 0 || (m >= D ? lane <= kWave - 2 : lane >= 1);
+        if (ok[m] && mine) rq[4 * lane + m] = vq[m];
       }
     }
   }
 }
 
-// Block t of the launch: tile bi of its segment, 16 runs of 64 quads (4 per wave).
-template <bool EF, bool ALIGNED>
+// A wave's 4 runs when every quad of them lies inside the segment: loaded once, kept in
+// registers across the block's barrier.
+template <bool EF, bool ALIGNED, int D>
+__device__ __forceinline__ void pass_wave_full(const float* __restrict__ x, float* __restrict__ res, int64_t lo,
+                                               int64_t hi, int64_t r0, uint32_t sampled, uint32_t* __restrict__ slot,
+                                               uint32_t* s_max, uint64_t seed, int64_t index_base,
+                                               uint8_t* __restrict__ out, uint32_t* __restrict__ cnt_out,
+                                               uint32_t* __restrict__ lst_b, f32x4* __restrict__ lst_x) {
+  constexpr int step = D == 0 ? kWave : kWave - 1;
+  const int64_t qs = lo >> 2;
+  const int64_t nb = (hi - lo + 3) >> 2;
+  const int lane = lane_id();
+  f32x4 v[kRunsB];
+#pragma unroll
+  for (int u = 0; u < kRunsB; ++u) {
+    const int64_t q0 = qs + (r0 + u) * step;   // the run's first quad (uniform)
+    v[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x + (q0 << 2)) + lane);
+    if (EF) v[u] = v[u] + __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(res + (q0 << 2)) + lane);
+  }
+  float fm = bitsf(sampled);
+#pragma unroll
+  for (int u = 0; u < kRunsB; ++u)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) fm = fmaxf(fm, fabsf(v[u][m]));
+  const float rsc32 = block_bound(fm, slot, s_max);
+  const bool all[4] = {true, true, true, true};
+  uint32_t nl = 0u;
+#pragma unroll
+  for (int u = 0; u < kRunsB; ++u) {
+    const int64_t b0 = (r0 + u) * step;
+    run_pass<EF, ALIGNED, D, true>(v[u], all, b0, qs + b0, nb, rsc32, seed, index_base, out, res, nl, lst_b, lst_x);
+  }
+  if (lane == 0) *cnt_out = nl;
+}
+
+// A wave's runs at a segment's edges (masked to the segment, possibly fewer than 4): the
+// values are loaded for the maximum, then again run by run after the barrier, so that few
+// registers stay live (the kernel's register count, and so its occupancy, is the larger
+// of this path's and the full path's).
+template <bool EF, bool ALIGNED, int D>
+__device__ __forceinline__ void pass_wave_edge(const float* __restrict__ x, float* __restrict__ res, int64_t n,
+                                            int64_t lo, int64_t hi, int64_t r0, int64_t runs, uint32_t sampled,
+                                            uint32_t* __restrict__ slot, uint32_t* s_max, uint64_t seed,
+                                            int64_t index_base, uint8_t* __restrict__ out,
+                                            uint32_t* __restrict__ cnt_out, uint32_t* __restrict__ lst_b,
+                                            f32x4* __restrict__ lst_x) {
+  constexpr int step = D == 0 ? kWave : kWave - 1;
+  const int64_t qs = lo >> 2;
+  const int64_t nb = (hi - lo + 3) >> 2;
+  const int lane = lane_id();
+  const int nr = (int)(runs - r0 < kRunsB ? (runs - r0 > 0 ? runs - r0 : 0) : kRunsB);
+  float fm = bitsf(sampled);
+#pragma unroll 1
+  for (int u = 0; u < nr; ++u) {
+    float t[4];
+    bool ok[4];
+    load_quad_masked<EF>(x, res, qs + (r0 + u) * step + lane, lo, hi, n, t, ok);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) fm = fmaxf(fm, ok[m] ? fabsf(t[m]) : 0.f);
+  }
+  const float rsc32 = block_bound(fm, slot, s_max);
+  uint32_t nl = 0u;
+#pragma unroll 1
+  for (int u = 0; u < nr; ++u) {
+    const int64_t b0 = (r0 + u) * step;
+    float t[4];
+    bool ok[4];
+    load_quad_masked<EF>(x, res, qs + b0 + lane, lo, hi, n, t, ok);
+    run_pass<EF, ALIGNED, D, false>(f32x4{t[0], t[1], t[2], t[3]}, ok, b0, qs + b0, nb, rsc32, seed, index_base,
+                                    out, res, nl, lst_b, lst_x);
+  }
+  if (lane == 0) *cnt_out = nl;
+}
+
+// Block t of the launch: tile bi of its segment, 16 runs of 64 quads (4 per wave).  Every
+// segment of the launch starts D elements past a multiple of 4.
+template <bool EF, bool ALIGNED, int D>
 __global__ __launch_bounds__(kBlock) void k_tern_pass(const float* __restrict__ x, float* __restrict__ res,
                                                       int64_t n, SegList S, const uint32_t* __restrict__ samp,
                                                       uint32_t* __restrict__ slots, uint64_t seed, int64_t index_base,
-                                                      uint8_t* __restrict__ packed, uint32_t* __restrict__ tile_cnt,
+                                                      uint8_t* __restrict__ packed, uint32_t* __restrict__ cnt,
                                                       uint32_t* __restrict__ lst_b, f32x4* __restrict__ lst_x) {
+  constexpr int step = D == 0 ? kWave : kWave - 1;
   __shared__ uint32_t s_max[kWaves];
-  __shared__ uint32_t s_n;
   const int si = seg_of(S, blockIdx.x);
   const int64_t bi = (int64_t)blockIdx.x - S.blk[si];
   const int64_t lo = S.start[si], hi = S.end[si];
-  const int step = (lo & 3) == 0 ? kWave : kWave - 1;
   const int64_t qs = lo >> 2;
   const int64_t runs = seg_runs(lo, hi);
-  const int64_t r0 = bi * kRunsPerBlock + (threadIdx.x / kWave) * kRunsB;
-  const int64_t tile = S.tile0[si] + bi;
+  const int w = threadIdx.x / kWave;
+  const int64_t r0 = bi * kRunsPerBlock + w * kRunsB;
+  const int64_t list = (S.tile0[si] + bi) * kWaves + w;
   uint32_t* __restrict__ slot = slots + (int64_t)S.index[si] * kSlots;
   // the sampled maxima: written by the sample launch, only read here (the pass's own
   // atomics go to the other slots, so these lines stay cached and uncontended)
   const uint32_t sampled = samp[(int64_t)S.index[si] * kSlots + lane_id()];
   uint8_t* __restrict__ out = packed + S.out_byte[si];
-  if (threadIdx.x == 0) s_n = 0u;
   // the wave's runs read quads [qs + r0*step, qs + (r0 + kRunsB - 1)*step + 64)
   const bool full = ((qs + r0 * step) << 2) >= lo && ((qs + (r0 + kRunsB - 1) * step + kWave) << 2) <= hi;
   if (full)
-    pass_wave<EF, ALIGNED, true>(x, res, n, lo, hi, r0, runs, sampled, slot, s_max, &s_n, seed, index_base, out,
-                                 tile, lst_b, lst_x);
+    pass_wave_full<EF, ALIGNED, D>(x, res, lo, hi, r0, sampled, slot, s_max, seed, index_base, out, cnt + list,
+                                   lst_b + list * kCap, lst_x + list * kCap);
   else
-    pass_wave<EF, ALIGNED, false>(x, res, n, lo, hi, r0, runs, sampled, slot, s_max, &s_n, seed, index_base, out,
-                                  tile, lst_b, lst_x);
-  __syncthreads();
-  if (threadIdx.x == 0) tile_cnt[tile] = s_n;
+    pass_wave_edge<EF, ALIGNED, D>(x, res, n, lo, hi, r0, runs, sampled, slot, s_max, seed, index_base, out,
+                                   cnt + list, lst_b + list * kCap, lst_x + list * kCap);
 }
 
 // ---- 3: the fix-up ------------------------------------------------------------------
-// Wave t of the launch: tile t of the batch.  Listed bytes are decided exactly; an
-// overflowed tile is redone byte by byte over the bytes it owns.  Tile 0 of a segment
-// also writes the segment's scale.
+// Wave t of the launch: kFixLists consecutive wave lists of one segment.  Their entries
+// are laid out densely over the lanes (an LDS table maps entry f to its list and slot),
+// decided exactly and written.  A list that overflowed is redone byte by byte over the
+// bytes of its wave's runs.  The first wave of a segment also writes the segment's scale.
 template <bool EF>
 __global__ __launch_bounds__(kBlock) void k_tern_fix(const float* __restrict__ x, float* __restrict__ res,
                                                      SegList S, const uint32_t* __restrict__ samp,
                                                      const uint32_t* __restrict__ slots,
                                                      float* __restrict__ scales, uint64_t seed, int64_t index_base,
-                                                     uint8_t* __restrict__ packed, const uint32_t* __restrict__ tile_cnt,
+                                                     uint8_t* __restrict__ packed, const uint32_t* __restrict__ cnt,
                                                      const uint32_t* __restrict__ lst_b,
                                                      const f32x4* __restrict__ lst_x) {
+  static_assert(kFixLists * kCap <= 65536, "table entries fit 16 bits");
+  __shared__ uint16_t s_tab[kWaves][kFixLists * kCap];
   const uint32_t wt = (uint32_t)((blockIdx.x * kBlock + threadIdx.x) / kWave);
   if (wt >= S.blk[S.count]) return;
   const int si = seg_of(S, wt);
-  const int64_t bi = (int64_t)(wt - S.blk[si]);
+  const int64_t fw = (int64_t)(wt - S.blk[si]);
   const int64_t lo = S.start[si], hi = S.end[si];
   const int64_t nb = (hi - lo + 3) >> 2;
   const int lane = lane_id();
+  uint16_t* tab = s_tab[threadIdx.x / kWave];
+  // lists [L0, L0 + ng) of the segment's [tile0 * kWaves, (tile0 + tiles) * kWaves)
+  const int64_t L0 = S.tile0[si] * kWaves + fw * kFixLists;
+  const int64_t Lend = (S.tile0[si] + seg_tiles(lo, hi)) * kWaves;
+  const int ng = (int)(Lend - L0 < kFixLists ? Lend - L0 : kFixLists);
+  const uint32_t craw = lane < ng ? cnt[L0 + lane] : 0u;
   const int64_t sl = (int64_t)S.index[si] * kSlots + lane;
   const float sc = bitsf(seg_max_c<6>(max(slots[sl], samp[sl])));
-  if (bi == 0 && lane == 0) scales[S.index[si]] = sc;
-  const int64_t tile = S.tile0[si] + bi;
+  if (fw == 0 && lane == 0) scales[S.index[si]] = sc;
   uint8_t* __restrict__ out = packed + S.out_byte[si];
-  const uint32_t cnt = tile_cnt[tile];
-  if (cnt <= (uint32_t)kCap) {
-    for (uint32_t i = lane; i < cnt; i += kWave) {
-      const int64_t b = lst_b[tile * kCap + i];
-      const f32x4 q = lst_x[tile * kCap + i];
+  // the table: entry pre_g + i of the wave's entries is slot i of list g.  An overflowed
+  // list takes no entries: it is redone below from x (or the residual, which its entries
+  // would otherwise have changed first)
+  const uint32_t c = craw <= (uint32_t)kCap ? craw : 0u;
+  uint32_t total = 0u;
+#pragma unroll
+  for (int g = 0; g < kFixLists; ++g) {
+    const uint32_t cg = (uint32_t)__builtin_amdgcn_readlane((int)c, g);
+    for (uint32_t i = (uint32_t)lane; i < cg; i += kWave) tab[total + i] = (uint16_t)(g * kCap + i);
+    total += cg;
+  }
+  // the table is read by other lanes of the same wave
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (uint32_t f0 = 0; f0 < total; f0 += kWave) {
+    const uint32_t f = f0 + (uint32_t)lane;
+    if (f < total) {
+      const int64_t e = L0 * kCap + tab[f];   // list L0 + g, slot i
+      const int64_t b = lst_b[e];
+      const f32x4 q = lst_x[e];
       const float xs[4] = {q.x, q.y, q.z, q.w};
       const int64_t p0 = lo + 4 * b;
       const int nvalid = (int)(hi - p0 < 4 ? hi - p0 : 4);
@@ -400,28 +480,36 @@ __global__ __launch_bounds__(kBlock) void k_tern_fix(const float* __restrict__ x
           if (take[j]) res[p0 + j] = rnew[j];
       }
     }
-    return;
   }
-  // overflowed: every byte this tile owns, from x (or from the residual, which holds x + r)
+  // overflowed lists: every byte of the wave's runs, from x (or from the residual, which
+  // holds x + r after the pass)
+  uint64_t ovf = ballot(craw > (uint32_t)kCap);
+  if (!ovf) return;
   const int d = (int)(lo & 3);
   const int step = d == 0 ? kWave : kWave - 1;
-  const int64_t b_first = bi * kRunsPerBlock * step;
-  int64_t b_last = b_first + (int64_t)kRunsPerBlock * step;
-  if (b_last > nb) b_last = nb;
   const float* __restrict__ src = EF ? res : x;
-  for (int64_t b = b_first + lane; b < b_last; b += kWave) {
-    const int64_t p0 = lo + 4 * b;
-    const int nvalid = (int)(hi - p0 < 4 ? hi - p0 : 4);
-    float xs[4];
+  while (ovf) {
+    const int g = __builtin_ctzll(ovf);
+    ovf &= ovf - 1;
+    const int64_t lr = L0 + g - S.tile0[si] * kWaves;   // the list's wave within the segment
+    const int64_t r0 = (lr / kWaves) * kRunsPerBlock + (lr % kWaves) * kRunsB;
+    const int64_t b_first = r0 * step;
+    int64_t b_last = b_first + (int64_t)kRunsB * step;
+    if (b_last > nb) b_last = nb;
+    for (int64_t b = b_first + lane; b < b_last; b += kWave) {
+      const int64_t p0 = lo + 4 * b;
+      const int nvalid = (int)(hi - p0 < 4 ? hi - p0 : 4);
+      float xs[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xs[j] = j < nvalid ? src[p0 + j] : 0.f;
-    float rnew[4];
-    bool take[4];
-    out[b] = (uint8_t)byte_codes(xs, nvalid, sc, seed, (uint64_t)(index_base + p0), rnew, take);
-    if (EF) {
+      for (int j = 0; j < 4; ++j) xs[j] = j < nvalid ? src[p0 + j] : 0.f;
+      float rnew[4];
+      bool take[4];
+      out[b] = (uint8_t)byte_codes(xs, nvalid, sc, seed, (uint64_t)(index_base + p0), rnew, take);
+      if (EF) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (take[j]) res[p0 + j] = rnew[j];
+        for (int j = 0; j < 4; ++j)
+          if (take[j]) res[p0 + j] = rnew[j];
+      }
     }
   }
 }
@@ -476,29 +564,48 @@ hipError_t launch_terngrad(const float* x, float* res, int nseg, const int64_t* 
     if (res) hipLaunchKernelGGL((k_tern_sample<true>), (unsigned)cdiv64(waves, kWaves), kBlock, 0, s, x, res, n, L, w.samp);
     else hipLaunchKernelGGL((k_tern_sample<false>), (unsigned)cdiv64(waves, kWaves), kBlock, 0, s, x, res, n, L, w.samp);
   }
-  for (SegList L : batches) {
-    L.blk[0] = 0;
-    for (int c = 0; c < L.count; ++c) L.blk[c + 1] = L.blk[c] + (uint32_t)seg_tiles(L.start[c], L.end[c]);
-    const int64_t blocks = L.blk[L.count];
-    if (blocks == 0) continue;
-#define GC_TERN_PASS(E, A)                                                                                    \
-  hipLaunchKernelGGL((k_tern_pass<E, A>), (unsigned)blocks, kBlock, 0, s, x, res, n, L, (const uint32_t*)w.samp, \
-                     w.slots, seed, index_base, packed, w.tile_cnt, w.lst_b, w.lst_x)
-    // a lane's quad starts at a multiple of 4, so its element indices are aligned blocks of
-    // the stream exactly when index_base is a multiple of 4
-    const bool aligned = (index_base & 3) == 0;
-    if (res) { if (aligned) GC_TERN_PASS(true, true); else GC_TERN_PASS(true, false); }
-    else { if (aligned) GC_TERN_PASS(false, true); else GC_TERN_PASS(false, false); }
+  // the passes: one launch per batch and start phase d = start % 4 (the pass kernel is
+  // compiled for each d)
+  for (const SegList& B : batches) {
+    for (int d = 0; d < 4; ++d) {
+      SegList L{};
+      for (int c = 0; c < B.count; ++c) {
+        if ((B.start[c] & 3) != d) continue;
+        const int k = L.count++;
+        L.index[k] = B.index[c];
+        L.start[k] = B.start[c];
+        L.end[k] = B.end[c];
+        L.out_byte[k] = B.out_byte[c];
+        L.tile0[k] = B.tile0[c];
+        L.blk[k + 1] = L.blk[k] + (uint32_t)seg_tiles(B.start[c], B.end[c]);
+      }
+      const int64_t blocks = L.blk[L.count];
+      if (blocks == 0) continue;
+      // a lane's quad starts at a multiple of 4, so its element indices are aligned blocks
+      // of the stream exactly when index_base is a multiple of 4
+      const bool aligned = (index_base & 3) == 0;
+#define GC_TERN_PASS(E, A, D)                                                                                    \
+  hipLaunchKernelGGL((k_tern_pass<E, A, D>), (unsigned)blocks, kBlock, 0, s, x, res, n, L,                       \
+                     (const uint32_t*)w.samp, w.slots, seed, index_base, packed, w.cnt, w.lst_b, w.lst_x)
+#define GC_TERN_PASS_D(E, A) \
+  switch (d) { case 0: GC_TERN_PASS(E, A, 0); break; case 1: GC_TERN_PASS(E, A, 1); break; \
+               case 2: GC_TERN_PASS(E, A, 2); break; default: GC_TERN_PASS(E, A, 3); break; }
+      if (res) { if (aligned) { GC_TERN_PASS_D(true, true) } else { GC_TERN_PASS_D(true, false) } }
+      else { if (aligned) { GC_TERN_PASS_D(false, true) } else { GC_TERN_PASS_D(false, false) } }
+#undef GC_TERN_PASS_D
 #undef GC_TERN_PASS
+    }
   }
   for (SegList L : batches) {
-    // one wave per tile; segments without tiles still get their scale (0) from k_zero2
+    // one wave per kFixLists wave lists of a segment; segments without tiles still get
+    // their scale (0) from k_zero2
     L.blk[0] = 0;
-    for (int c = 0; c < L.count; ++c) L.blk[c + 1] = L.blk[c] + (uint32_t)seg_tiles(L.start[c], L.end[c]);
+    for (int c = 0; c < L.count; ++c)
+      L.blk[c + 1] = L.blk[c] + (uint32_t)cdiv64(seg_tiles(L.start[c], L.end[c]) * kWaves, kFixLists);
     const int64_t waves = L.blk[L.count];
     if (waves == 0) continue;
-    if (res) hipLaunchKernelGGL((k_tern_fix<true>), (unsigned)cdiv64(waves, kWaves), kBlock, 0, s, x, res, L, (const uint32_t*)w.samp, (const uint32_t*)w.slots, scales, seed, index_base, packed, w.tile_cnt, w.lst_b, w.lst_x);
-    else hipLaunchKernelGGL((k_tern_fix<false>), (unsigned)cdiv64(waves, kWaves), kBlock, 0, s, x, res, L, (const uint32_t*)w.samp, (const uint32_t*)w.slots, scales, seed, index_base, packed, w.tile_cnt, w.lst_b, w.lst_x);
+    if (res) hipLaunchKernelGGL((k_tern_fix<true>), (unsigned)cdiv64(waves, kWaves), kBlock, 0, s, x, res, L, (const uint32_t*)w.samp, (const uint32_t*)w.slots, scales, seed, index_base, packed, w.cnt, w.lst_b, w.lst_x);
+    else hipLaunchKernelGGL((k_tern_fix<false>), (unsigned)cdiv64(waves, kWaves), kBlock, 0, s, x, res, L, (const uint32_t*)w.samp, (const uint32_t*)w.slots, scales, seed, index_base, packed, w.cnt, w.lst_b, w.lst_x);
   }
   return hipGetLastError();
 }
