@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0
 VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
 # VALU lane-instructions per element of the quantizer kernels (SQ_INSTS_VALU x 64 /
 # elements, rocprofv3 counters of bench.py --rows; profiles/compressor_rows_valu_and_traffic.md).
-VALU_LANE_OPS_PER_ELEMENT = {"minmax8": 39.9, "minmax4": 40.1, "qsgd": 54.9, "terngrad": 37.9}
+VALU_LANE_OPS_PER_ELEMENT = {"minmax8": 32.4, "minmax4": 32.7, "qsgd": 47.7, "terngrad": 23.3}
 
 # HBM bytes per launch of the streaming pass on this workload, from two rocprofv3 counter
 # runs per mode (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, factors from a plain 4 GiB device
@@ -47,8 +47,8 @@ VALU_LANE_OPS_PER_ELEMENT = {"minmax8": 39.9, "minmax4": 40.1, "qsgd": 54.9, "te
 # only for the kernel source it was measured on: the digest covers the tile constants,
 # the pending-record helpers, the block-rank helpers and the kernel itself, and a
 # mismatch reports the traffic as null.
-K1_TRAFFIC_BYTES = {"deferred": 8.5718e10, "direct": 8.4612e10}
-K1_SOURCE_SHA256 = "ebddc6a2a4d31de1dbf741e7a83f8d2d470564d67a5efd71841c34eb0ecdca0d"
+K1_TRAFFIC_BYTES = {"deferred": 8.5774e10, "direct": 8.4667e10}
+K1_SOURCE_SHA256 = "0f92c752ab8319c3fcdcf1eab02579fb474fe5945e34567e3c44d5c6a3806cb5"
 METRIC = "EF-Top-1%+int8 compress GB/s of fp32 grad input; % of HBM peak"
 
 
