@@ -507,32 +507,6 @@ __device__ __forceinline__ uint32_t decide_mode(TopkCtrl* __restrict__ ctrl, int
   return full ? MODE_FULL : MODE_CAND;
 }
 
-// Last-block hand-off: every block of a grid calls this once, after its global writes and
-// atomics; it returns true in exactly one block, the last to arrive, which then sees the
-// writes of every block.  Nothing waits on anything, so every block runs to its end; the
-// ticket is zero again once the last block has it.  One device-scope release per block
-// (its first thread's ticket increment, after the barrier that orders the block's writes
-// before it) and one acquire in the last block: a full fence in every wave costs an L2
-// write-back and invalidate each, which measured slower than the launch this saves.
-__device__ __forceinline__ bool last_block(uint32_t* ticket) {
-  __shared__ uint32_t s_last;
-  // each wave's own global stores and atomics have completed before the barrier (the
-  // barrier alone does not wait for them), so the first thread's release covers them all
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = t == gridDim.x - 1;
-    if (last) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    s_last = last ? 1u : 0u;
-  }
-  __syncthreads();
-  return s_last != 0u;
-}
-
 // Locate the bin of the global histogram holding rank krem (counted from the largest
 // key), fix its bits in the prefix and clear the histogram (one block; s_sum holds
 // kBlock 64-bit words).  final_op: 0 = intermediate pass; 1 = last pass of the sample

@@ -31,7 +31,7 @@ constexpr int kP1Cols = 256;      // column panel of pass 1 (4 steps of 64)
 constexpr int kRowsPerWave = 16;  // pass 1 and 2: 16 rows per wave, 64 per block
 constexpr int kRowsPerBlock = 64;
 constexpr int kP3Rows = 16;       // pass 3 rows per block
-constexpr int kGramBlocks = 256;
+constexpr int kGramBlocks = 64;    // the last one sums their Gram partials, one per lane
 
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -42,6 +42,8 @@ struct PLayout {
   float* phat;    // [rows * 4]
   float* qpart;   // [nrp * cols * 4]          pass-2 partials per row panel
   float* qn;      // [cols * 4]                Q'
+  double* T;      // [16]                      Gram-Schmidt coefficients, row-major
+  uint32_t* ticket;   // last-block hand-off of the Gram reduction
   int64_t ncp, nrp;
   size_t bytes;
 };
@@ -63,6 +65,8 @@ PLayout make_playout(void* base, int64_t rows, int64_t cols) {
   l.phat = (float*)take(sizeof(float) * rows * 4);
   l.qpart = (float*)take(sizeof(float) * l.nrp * cols * 4);
   l.qn = (float*)take(sizeof(float) * cols * 4);
+  l.T = (double*)take(sizeof(double) * 16);
+  l.ticket = (uint32_t*)take(sizeof(uint32_t));
   l.bytes = off;
   return l;
 }
@@ -83,7 +87,9 @@ __device__ __forceinline__ f32x4 load4_or_zero(const float* p, bool ok) {
 template <bool EF>
 __global__ __launch_bounds__(kBlock) void k_p1(const float* __restrict__ G, float* __restrict__ E,
                                                int64_t rows, int64_t cols, const float* __restrict__ Q,
-                                               int rank, float* __restrict__ ppart) {
+                                               int rank, float* __restrict__ ppart, uint32_t* __restrict__ ticket) {
+  // the Gram reduction's hand-off ticket starts at zero (the workspace is the caller's)
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *ticket = 0u;
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
   const int64_t cp = blockIdx.x;
@@ -146,49 +152,6 @@ __global__ __launch_bounds__(kBlock) void k_p1(const float* __restrict__ G, floa
   }
 }
 
-// P = sum of the panel partials (in panel order); float64 partials of the Gram matrix.
-__global__ __launch_bounds__(kBlock) void k_psum_gram(const float* __restrict__ ppart, int64_t ncp,
-                                                      int64_t rows, float* __restrict__ p,
-                                                      double* __restrict__ gram) {
-  __shared__ double s[kBlock / kWave][10];
-  double acc[10];
-#pragma unroll
-  for (int t = 0; t < 10; ++t) acc[t] = 0.0;
-  for (int64_t row = (int64_t)blockIdx.x * kBlock + threadIdx.x; row < rows;
-       row += (int64_t)gridDim.x * kBlock) {
-    // panel partials in panel order; 8 loads are issued ahead of their additions
-    constexpr int kAhead = 8;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    int64_t c = 0;
-    for (; c + kAhead <= ncp; c += kAhead) {
-      f32x4 q[kAhead];
-#pragma unroll
-      for (int u = 0; u < kAhead; ++u) q[u] = *reinterpret_cast<const f32x4*>(ppart + ((c + u) * rows + row) * 4);
-#pragma unroll
-      for (int u = 0; u < kAhead; ++u) { v[0] += q[u].x; v[1] += q[u].y; v[2] += q[u].z; v[3] += q[u].w; }
-    }
-    for (; c < ncp; ++c) {
-      const f32x4 q = *reinterpret_cast<const f32x4*>(ppart + (c * rows + row) * 4);
-      v[0] += q.x; v[1] += q.y; v[2] += q.z; v[3] += q.w;
-    }
-    *reinterpret_cast<f32x4*>(p + row * 4) = f32x4{v[0], v[1], v[2], v[3]};
-    int t = 0;
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int bb = a; bb < 4; ++bb) acc[t++] += (double)v[a] * (double)v[bb];
-  }
-#pragma unroll
-  for (int t = 0; t < 10; ++t)
-    for (int m = 1; m < kWave; m <<= 1) acc[t] += __shfl_xor(acc[t], m, kWave);
-  if (lane_id() == 0)
-    for (int t = 0; t < 10; ++t) s[threadIdx.x / kWave][t] = acc[t];
-  __syncthreads();
-  if (threadIdx.x < 10)
-    gram[blockIdx.x * 10 + threadIdx.x] = ((s[0][threadIdx.x] + s[1][threadIdx.x]) + s[2][threadIdx.x]) +
-                                          s[3][threadIdx.x];
-}
-
 // Modified Gram-Schmidt in coefficient space: columns of T give P^ = P T.  A column in the
 // span of the previous ones becomes 0; numerically, one whose projected norm is at most
 // 1e-5 of its own norm (squared: 1e-10), below which its direction is rounding noise.
@@ -239,35 +202,77 @@ __device__ __forceinline__ void gram_schmidt_t(const double* __restrict__ gram, 
     for (int bb = 0; bb < 4; ++bb) T[a * 4 + bb] = Tm[a][bb];
 }
 
-// P^ = P T (float64 accumulation, one rounding); padded copy plus the caller's rows x rank P.
-// Every block derives T itself from the Gram partials (the same fixed order in each), which
-// saves a one-wave launch between the two kernels.
-__global__ void k_apply_t(const float* __restrict__ p, const double* __restrict__ gram, int nblocks, int64_t rows,
-                          int rank, float* __restrict__ phat, float* __restrict__ P_out) {
-  __shared__ double sT[16];
-  if (threadIdx.x < kWave) gram_schmidt_t(gram, nblocks, rank, sT);
-  __syncthreads();
-  for (int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; row < rows;
-       row += (int64_t)gridDim.x * blockDim.x) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(p + row * 4);
-    const double pv[4] = {v.x, v.y, v.z, v.w};
-    float o[4];
+// P = sum of the panel partials (in panel order); float64 partials of the Gram matrix.
+// The last block to finish sums the partials and derives T (gram_schmidt_t), so pass 2
+// can form P^ = P T row by row.
+__global__ __launch_bounds__(kBlock) void k_psum_gram(const float* __restrict__ ppart, int64_t ncp,
+                                                      int64_t rows, float* __restrict__ p,
+                                                      double* __restrict__ gram, int rank,
+                                                      double* __restrict__ T, uint32_t* __restrict__ ticket) {
+  __shared__ double s[kBlock / kWave][10];
+  double acc[10];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      double a = 0.0;
+  for (int t = 0; t < 10; ++t) acc[t] = 0.0;
+  for (int64_t row = (int64_t)blockIdx.x * kBlock + threadIdx.x; row < rows;
+       row += (int64_t)gridDim.x * kBlock) {
+    // panel partials in panel order; 8 loads are issued ahead of their additions
+    constexpr int kAhead = 8;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    int64_t c = 0;
+    for (; c + kAhead <= ncp; c += kAhead) {
+      f32x4 q[kAhead];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a += pv[i] * sT[i * 4 + j];
-      o[j] = j < rank ? (float)a : 0.f;
+      for (int u = 0; u < kAhead; ++u) q[u] = *reinterpret_cast<const f32x4*>(ppart + ((c + u) * rows + row) * 4);
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) { v[0] += q[u].x; v[1] += q[u].y; v[2] += q[u].z; v[3] += q[u].w; }
     }
-    *reinterpret_cast<f32x4*>(phat + row * 4) = f32x4{o[0], o[1], o[2], o[3]};
-    for (int j = 0; j < rank; ++j) P_out[row * rank + j] = o[j];
+    for (; c < ncp; ++c) {
+      const f32x4 q = *reinterpret_cast<const f32x4*>(ppart + (c * rows + row) * 4);
+      v[0] += q.x; v[1] += q.y; v[2] += q.z; v[3] += q.w;
+    }
+    *reinterpret_cast<f32x4*>(p + row * 4) = f32x4{v[0], v[1], v[2], v[3]};
+    int t = 0;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int bb = a; bb < 4; ++bb) acc[t++] += (double)v[a] * (double)v[bb];
   }
+#pragma unroll
+  for (int t = 0; t < 10; ++t)
+    for (int m = 1; m < kWave; m <<= 1) acc[t] += __shfl_xor(acc[t], m, kWave);
+  if (lane_id() == 0)
+    for (int t = 0; t < 10; ++t) s[threadIdx.x / kWave][t] = acc[t];
+  __syncthreads();
+  if (threadIdx.x < 10)
+    gram[blockIdx.x * 10 + threadIdx.x] = ((s[0][threadIdx.x] + s[1][threadIdx.x]) + s[2][threadIdx.x]) +
+                                          s[3][threadIdx.x];
+  if (last_block(ticket) && threadIdx.x < kWave) gram_schmidt_t(gram, (int)gridDim.x, rank, T);
 }
 
-// Pass 2: Q' partials per row panel, Q'[c][j] = sum_rows M[row][c] * P^[row][j].
+// Row `row` of P^ = P T, component j (float64 accumulation in i order, one rounding;
+// components j >= rank are 0).
+__device__ __forceinline__ float phat_of(const float* __restrict__ p, const double* __restrict__ T, int64_t row,
+                                         int j, int rank) {
+  const f32x4 v = *reinterpret_cast<const f32x4*>(p + row * 4);
+  const double pv[4] = {v.x, v.y, v.z, v.w};
+  double a = 0.0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a += pv[i] * T[i * 4 + j];
+  return j < rank ? (float)a : 0.f;
+}
+
+// Pass 2: Q' partials per row panel, Q'[c][j] = sum_rows M[row][c] * P^[row][j], with
+// P^ = P T formed here for the block's 64 rows (one value per thread, into LDS); the
+// first column panel also writes P^ (padded, for pass 3) and the caller's rows x rank P.
 __global__ __launch_bounds__(kBlock) void k_p2(const float* __restrict__ M, int64_t rows, int64_t cols,
-                                               const float* __restrict__ phat, float* __restrict__ qpart) {
+                                               const float* __restrict__ p, const double* __restrict__ Tg,
+                                               int rank, float* __restrict__ phat, float* __restrict__ P_out,
+                                               float* __restrict__ qpart) {
   __shared__ float s_acc[kBlock / kWave][kWave][16];
+  __shared__ double sT[16];
+  __shared__ float s_ph[kRowsPerBlock * 4];
+  constexpr int kPre = 4;   // rows of M loaded before P^ is formed
+  static_assert(kRowsPerBlock * 4 == kBlock, "one P^ value per thread");
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
   const int64_t c0 = (int64_t)blockIdx.x * 256;
@@ -275,15 +280,39 @@ __global__ __launch_bounds__(kBlock) void k_p2(const float* __restrict__ M, int6
   const int64_t r0 = rp * kRowsPerBlock + w * kRowsPerWave;
   const int64_t col = c0 + 4 * lane;
   const bool col_ok = col < cols;
+  f32x4 pre[kPre];
+#pragma unroll
+  for (int rr = 0; rr < kPre; ++rr) pre[rr] = load4_or_zero(M + (r0 + rr) * cols + col, r0 + rr < rows && col_ok);
+  if (threadIdx.x < 16) sT[threadIdx.x] = Tg[threadIdx.x];
+  __syncthreads();
+  {
+    const int64_t row = rp * kRowsPerBlock + (threadIdx.x >> 2);
+    const int j = threadIdx.x & 3;
+    const float v = row < rows ? phat_of(p, sT, row, j, rank) : 0.f;
+    s_ph[threadIdx.x] = v;
+    if (blockIdx.x == 0 && row < rows) {
+      phat[row * 4 + j] = v;
+      if (j < rank) P_out[row * rank + j] = v;
+    }
+  }
+  __syncthreads();
   f32x4 acc[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int rr = 0; rr < kPre; ++rr) {
+    const float bv = s_ph[(w * kRowsPerWave + rr) * 4 + (lane & 3)];
+    acc[0] = mfma4(pre[rr].x, bv, acc[0]);
+    acc[1] = mfma4(pre[rr].y, bv, acc[1]);
+    acc[2] = mfma4(pre[rr].z, bv, acc[2]);
+    acc[3] = mfma4(pre[rr].w, bv, acc[3]);
+  }
 #pragma unroll 4
-  for (int rr = 0; rr < kRowsPerWave; ++rr) {
+  for (int rr = kPre; rr < kRowsPerWave; ++rr) {
     const int64_t row = r0 + rr;
     const bool ok = row < rows;
     const f32x4 m = load4_or_zero(M + row * cols + col, ok && col_ok);
-    const float bv = ok ? phat[row * 4 + (lane & 3)] : 0.f;
+    const float bv = s_ph[(w * kRowsPerWave + rr) * 4 + (lane & 3)];
     acc[0] = mfma4(m.x, bv, acc[0]);
     acc[1] = mfma4(m.y, bv, acc[1]);
     acc[2] = mfma4(m.z, bv, acc[2]);
@@ -384,14 +413,15 @@ hipError_t launch_powersgd(const float* grad, float* res, int64_t rows, int64_t 
   const PLayout l = make_playout(ws, rows, cols);
   const int cus = device_cu_count();
   const dim3 g1((unsigned)l.ncp, (unsigned)l.nrp);
-  if (res) hipLaunchKernelGGL((k_p1<true>), g1, kBlock, 0, s, grad, res, rows, cols, (const float*)Q, rank, l.ppart);
-  else hipLaunchKernelGGL((k_p1<false>), g1, kBlock, 0, s, grad, res, rows, cols, (const float*)Q, rank, l.ppart);
-  hipLaunchKernelGGL(k_psum_gram, kGramBlocks, kBlock, 0, s, l.ppart, l.ncp, rows, l.p, l.gram);
-  hipLaunchKernelGGL(k_apply_t, clamp_grid(cdiv(rows, 256), cus * 4), 256, 0, s, l.p, (const double*)l.gram,
-                     kGramBlocks, rows, rank, l.phat, P);
+  if (res)
+    hipLaunchKernelGGL((k_p1<true>), g1, kBlock, 0, s, grad, res, rows, cols, (const float*)Q, rank, l.ppart, l.ticket);
+  else
+    hipLaunchKernelGGL((k_p1<false>), g1, kBlock, 0, s, grad, res, rows, cols, (const float*)Q, rank, l.ppart, l.ticket);
+  hipLaunchKernelGGL(k_psum_gram, kGramBlocks, kBlock, 0, s, l.ppart, l.ncp, rows, l.p, l.gram, rank, l.T, l.ticket);
   const float* M = res ? res : grad;
   const dim3 g2((unsigned)cdiv(cols, 256), (unsigned)l.nrp);
-  hipLaunchKernelGGL(k_p2, g2, kBlock, 0, s, M, rows, cols, l.phat, l.qpart);
+  hipLaunchKernelGGL(k_p2, g2, kBlock, 0, s, M, rows, cols, (const float*)l.p, (const double*)l.T, rank, l.phat, P,
+                     l.qpart);
   hipLaunchKernelGGL(k_qsum, clamp_grid(cdiv(cols * 4, 256), cus * 8), 256, 0, s, l.qpart, l.nrp, cols, rank, l.qn, Q);
   if (res) {
     const dim3 g3((unsigned)cdiv(cols, kBlock * 4), (unsigned)cdiv(rows, kP3Rows));
