@@ -12,6 +12,8 @@ constexpr int kWave = 64;
 
 // Native 4 x fp32 vector (usable with the nontemporal load/store builtins).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11).  One block: counter

@@ -286,6 +286,142 @@ __global__ __launch_bounds__(kBlock) void k_decode_sum(int W, FusedSrc src, int6
   }
 }
 
+// The same sum for packed codes (8-, 4- or 2-bit) whose groups are a power of two of at
+// least 16 entries: a lane owns 16 entries of one group, so each payload costs it one
+// load of its codes (16, 8 or 4 bytes) and one of each metadata array, and the loads of
+// kSumChunk payloads are issued together before they are decoded and added in payload
+// order (the same values and the same order of additions as k_decode_sum).  Requires
+// out 16-byte aligned and every codes pointer aligned to 16 entries' code bytes; the
+// lane holding the ragged end goes entry by entry.
+constexpr int kEpl = 16;
+constexpr int kSumChunk = 8;
+
+template <int KIND>
+__device__ __forceinline__ void decode16(const uint32_t cw[4], float m0, float m1, float s, float ys, float v[kEpl]) {
+  if (KIND == KIND_QSGD) {
+    // sign * fl(fl(nu * level) / s) = fl(fl(nu * code) / s): multiplication and division
+    // round symmetrically, so the signed code gives the same bits; one norm per lane, so
+    // the choice of quotient (div_level_count's domain, |t| >= 2^-100 or 0) is per lane
+    float t[kEpl];
+#pragma unroll
+    for (int i = 0; i < kEpl; ++i) t[i] = m0 * (float)(int)(int8_t)(uint8_t)(cw[i >> 2] >> (8 * (i & 3)));
+    if (m0 >= 0x1p-100f) {
+#pragma unroll
+      for (int i = 0; i < kEpl; ++i) {
+        const float q0 = t[i] * ys;
+        const float q = __builtin_fmaf(__builtin_fmaf(-q0, s, t[i]), ys, q0);
+        v[i] = fabsf(t[i]) <= 3.40282346638528859812e+38f ? q : q0;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kEpl; ++i) v[i] = t[i] / s;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kEpl; ++i) {
+      uint32_t q;
+      if (KIND == KIND_MINMAX8) q = (cw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+      else if (KIND == KIND_MINMAX4) q = (cw[i >> 3] >> (4 * (i & 7))) & 15u;
+      else q = (cw[0] >> (2 * i)) & 3u;
+      v[i] = decode_one<KIND>(q, m0, m1, s);
+    }
+  }
+}
+
+template <int KIND>
+__global__ __launch_bounds__(kBlock) void k_decode_sum16(int W, FusedSrc src, int64_t count, int lg, float s,
+                                                         float ys, float alpha, int accumulate,
+                                                         float* __restrict__ out) {
+  __shared__ __align__(16) float s_tr[kBlock / kWave][kWave * kEpl];
+  const int64_t e0 = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * kEpl;
+  if (e0 >= count) return;
+  if (e0 + kEpl > count) {
+    // the ragged end: entry by entry, payloads in order
+    for (int64_t e = e0; e < count; ++e) {
+      float o = accumulate ? out[e] : 0.f;
+      const int64_t g = e >> lg;
+      for (int w = 0; w < W; ++w) {
+        const uint8_t* c8 = reinterpret_cast<const uint8_t*>(src.codes[w]);
+        uint32_t q;
+        if (KIND == KIND_MINMAX8 || KIND == KIND_QSGD) q = c8[e];
+        else if (KIND == KIND_MINMAX4) q = (c8[e >> 1] >> (4 * (e & 1))) & 15u;
+        else q = (c8[e >> 2] >> (2 * (e & 3))) & 3u;
+        const float m1 = (KIND == KIND_MINMAX8 || KIND == KIND_MINMAX4) ? src.meta1[w][g] : 0.f;
+        o = o + alpha * decode_one<KIND>(q, src.meta0[w][g], m1, s);
+      }
+      out[e] = o;
+    }
+    return;
+  }
+  const int64_t g = e0 >> lg;
+  float o[kEpl];
+  if (accumulate) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 p = *reinterpret_cast<const f32x4*>(out + e0 + 4 * q);
+      o[4 * q] = p.x; o[4 * q + 1] = p.y; o[4 * q + 2] = p.z; o[4 * q + 3] = p.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kEpl; ++i) o[i] = 0.f;
+  }
+  for (int w0 = 0; w0 < W; w0 += kSumChunk) {
+    uint32_t cw[kSumChunk][4];
+    float m0[kSumChunk], m1[kSumChunk];
+#pragma unroll
+    for (int c = 0; c < kSumChunk; ++c) {
+      const int w = w0 + c;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cw[c][q] = 0u;
+      m0[c] = 0.f;
+      m1[c] = 0.f;
+      if (w < W) {
+        const uint8_t* c8 = reinterpret_cast<const uint8_t*>(src.codes[w]);
+        if (KIND == KIND_MINMAX8 || KIND == KIND_QSGD) {
+          const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(c8 + e0));
+          cw[c][0] = a.x; cw[c][1] = a.y; cw[c][2] = a.z; cw[c][3] = a.w;
+        } else if (KIND == KIND_MINMAX4) {
+          const u32x2 a = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(c8 + (e0 >> 1)));
+          cw[c][0] = a.x; cw[c][1] = a.y;
+        } else {
+          cw[c][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(c8 + (e0 >> 2)));
+        }
+        m0[c] = src.meta0[w][g];
+        if (KIND == KIND_MINMAX8 || KIND == KIND_MINMAX4) m1[c] = src.meta1[w][g];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kSumChunk; ++c) {
+      if (w0 + c >= W) break;   // uniform
+      float v[kEpl];
+      decode16<KIND>(cw[c], m0[c], m1[c], s, ys, v);
+#pragma unroll
+      for (int i = 0; i < kEpl; ++i) o[i] = o[i] + alpha * v[i];
+    }
+  }
+  // a wave inside the range stores through LDS, so each store instruction writes 1 KB of
+  // consecutive floats (a lane's own 16 floats would make every instruction touch 64 lines)
+  const int64_t ew = e0 - (int64_t)lane_id() * kEpl;   // the wave's first entry
+  if (ew + kWave * kEpl <= count) {
+    float* t = s_tr[threadIdx.x / kWave];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<f32x4*>(t + lane_id() * kEpl + 4 * q) = f32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]};
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(t + q * (kWave * 4) + lane_id() * 4),
+                                  reinterpret_cast<f32x4*>(out + ew + q * (kWave * 4)) + lane_id());
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_nontemporal_store(f32x4{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]},
+                                  reinterpret_cast<f32x4*>(out + e0 + 4 * q));
+  }
+}
+
 // ---- the receive side: W sparse payloads merged tile by tile --------------------------
 // Each payload's idx is strictly ascending, so the entries of one output tile are a run of
 // consecutive entries of every payload.  A block walks kMergeTilesPerBlock tiles of 4096
@@ -571,6 +707,12 @@ hipError_t launch_decode_sum(int kind, int W, const void* const* codes, const fl
   }
   const float sd = (float)(levels > 0 ? levels : 1);
   const unsigned blocks = (unsigned)((count + kBlock * 4 - 1) / (kBlock * 4));
+  // the 16-entry path: packed codes, groups of a power of two >= 16, codes aligned to 16
+  // entries' code bytes
+  const int cbytes16 = kind == KIND_MINMAX8 || kind == KIND_QSGD ? 16 : (kind == KIND_MINMAX4 ? 8 : 4);
+  bool wide = kind != KIND_F32 && lg >= 4;
+  for (int i = 0; wide && i < W; ++i) wide = (reinterpret_cast<uintptr_t>(codes[i]) % cbytes16) == 0;
+  const unsigned blocks16 = (unsigned)((count + kBlock * kEpl - 1) / (kBlock * kEpl));
   for (int w0 = 0; w0 < W; w0 += kMaxFused) {
     const int nw = W - w0 < kMaxFused ? W - w0 : kMaxFused;
     FusedSrc src{};
@@ -580,6 +722,18 @@ hipError_t launch_decode_sum(int kind, int W, const void* const* codes, const fl
       src.meta1[i] = meta1 ? meta1[w0 + i] : nullptr;
     }
     const int acc = w0 == 0 ? accumulate : 1;   // later launches add to what the first wrote
+#define GC_LAUNCH_SUM16(K) \
+    hipLaunchKernelGGL((k_decode_sum16<K>), blocks16, kBlock, 0, s, nw, src, count, lg, sd, 1.0f / sd, alpha, acc, out)
+    if (wide) {
+      switch (kind) {
+        case KIND_MINMAX8: GC_LAUNCH_SUM16(KIND_MINMAX8); break;
+        case KIND_MINMAX4: GC_LAUNCH_SUM16(KIND_MINMAX4); break;
+        case KIND_QSGD: GC_LAUNCH_SUM16(KIND_QSGD); break;
+        default: GC_LAUNCH_SUM16(KIND_TERN); break;
+      }
+      continue;
+    }
+#undef GC_LAUNCH_SUM16
 #define GC_LAUNCH_SUM(K) \
     hipLaunchKernelGGL((k_decode_sum<K>), blocks, kBlock, 0, s, nw, src, count, G, lg, sd, 1.0f / sd, alpha, acc, out)
     switch (kind) {

@@ -93,6 +93,26 @@ def test_dense_payloads_fused(gc, kind, group, levels, W, accumulate):
     assert_bits_equal(host(out), want, f"kind {kind} W {W}")
 
 
+@pytest.mark.parametrize("kind,group,levels,n", [(1, 64, 0, 3 * 4096 + 1003), (2, 128, 0, 3 * 4096 + 1003),
+                                                  (3, 16, 127, 3 * 4096 + 1003), (4, 0, 0, 1 << 14)])
+@pytest.mark.parametrize("W,accumulate", [(5, False), (17, True)])
+def test_dense_payloads_sixteen_entry_path(gc, kind, group, levels, n, W, accumulate):
+    """Packed codes in groups of a power of two >= 16 (TernGrad: one group of 2^14) take the
+    path where a lane sums 16 entries of one group over chunks of payloads; ragged ends,
+    a chunk cut short (W = 5), a second launch (W = 17) and accumulation included."""
+    bufs, hdrs, wants = [], [], []
+    for w in range(W):
+        x = workloads.bucket(n, seed=500 + w)
+        b, h, want = dense_payload(gc, kind, x, group, levels, seed=11 + w)
+        bufs.append(b); hdrs.append(h); wants.append(want)
+    init = np.linspace(-2, 2, n, dtype=F32) if accumulate else np.zeros(n, F32)
+    out = dev(init)
+    alpha = F32(1.0) / F32(W)
+    gc.decompress_payloads(bufs, hdrs, out, alpha=float(alpha), accumulate=accumulate)
+    want = expected(kind, wants, n, group, levels, alpha, init)
+    assert_bits_equal(host(out), want, f"kind {kind} W {W}")
+
+
 def test_dense_payloads_unaligned_out_takes_the_sequential_path(gc):
     import torch
     n, W = 5000, 4
