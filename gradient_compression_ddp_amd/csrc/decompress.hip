@@ -480,12 +480,26 @@ __device__ __forceinline__ float decode_entry(const SparseSrc& S, int w, int64_t
   }
 }
 
-// First entry of idx[0, count) that is >= key.
-__device__ __forceinline__ int64_t lower_bound_i64(const int64_t* __restrict__ idx, int64_t count, int64_t key) {
-  int64_t lo = 0, hi = count;
+// First entry of idx[0, count) that is >= key, by one wave: each step probes 64 evenly
+// spaced entries of the open range and keeps the gap between the last probe below key and
+// the first at or above it (the probes ascend, so the ones below key are a prefix of the
+// lanes), a 64-fold cut per dependent load (4 loads for a million entries) instead of
+// 2-fold.  Every lane of the wave calls it and gets the answer.
+__device__ __forceinline__ int64_t lower_bound_wave(const int64_t* __restrict__ idx, int64_t count, int64_t key) {
+  const int lane = lane_id();
+  int64_t lo = 0, hi = count;   // the answer lies in [lo, hi]
   while (lo < hi) {
-    const int64_t mid = (lo + hi) >> 1;
-    if (idx[mid] < key) lo = mid + 1; else hi = mid;
+    const int64_t span = hi - lo;
+    const int64_t step = span <= kWave ? 1 : (span + kWave - 1) / kWave;
+    const int64_t p = lo + (int64_t)lane * step;
+    const bool valid = p < hi;
+    const uint64_t below = ballot(valid && idx[p] < key);
+    const int m = __popcll(below);
+    if (m == 0) return lo;
+    const int nvalid = __popcll(ballot(valid));
+    const int64_t last = lo + (int64_t)(m - 1) * step;   // the last probe below key
+    hi = m < nvalid ? lo + (int64_t)m * step : hi;
+    lo = last + 1;
   }
   return lo;
 }
@@ -504,9 +518,10 @@ __global__ __launch_bounds__(kMergeBlock) void k_merge_sparse(int W, SparseSrc S
   const int64_t ntiles = (n_out + kMergeTile - 1) / kMergeTile;
   const int64_t t0 = (int64_t)blockIdx.x * kMergeTilesPerBlock;
   const int64_t t1 = t0 + kMergeTilesPerBlock < ntiles ? t0 + kMergeTilesPerBlock : ntiles;
-  if ((int)threadIdx.x < W)
-    cur[threadIdx.x] = lower_bound_i64(S.idx[threadIdx.x], S.count[threadIdx.x],
-                                       t0 * kMergeTile + S.index_base[threadIdx.x]);
+  for (int w = wave; w < W; w += kMergeWaves) {
+    const int64_t c = lower_bound_wave(S.idx[w], S.count[w], t0 * kMergeTile + S.index_base[w]);
+    if (lane == 0) cur[w] = c;
+  }
   for (int64_t t = t0; t < t1; ++t) {
     const int64_t q0 = t * kMergeTile;
     const int len = n_out - q0 < kMergeTile ? (int)(n_out - q0) : kMergeTile;
