@@ -40,6 +40,12 @@ VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
 # VALU lane-instructions per element of the quantizer kernels (SQ_INSTS_VALU x 64 /
 # elements, rocprofv3 counters of bench.py --rows; profiles/compressor_rows_valu_and_traffic.md).
 VALU_LANE_OPS_PER_ELEMENT = {"minmax8": 32.4, "minmax4": 32.7, "qsgd": 47.7, "terngrad": 23.3}
+# Issue slots beyond one per instruction: v_mad_u64_u32 (the Philox4x32-10 multiplies, 20
+# of the about 66 instructions of a block of 4 draws) occupies a SIMD for two full-rate
+# slots (a kernel of Philox blocks alone measured 5.4 cycles per wave instruction against
+# 4 for a full-rate one).  QSGD draws one block per quad; TernGrad one per quad in its
+# pass and two per listed byte (3.7M of 87.5M) in the fix-up.
+VALU_EXTRA_SLOTS_PER_ELEMENT = {"minmax8": 0.0, "minmax4": 0.0, "qsgd": 5.0, "terngrad": 5.4}
 
 # HBM bytes per launch of the streaming pass on this workload, from two rocprofv3 counter
 # runs per mode (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, factors from a plain 4 GiB device
@@ -343,6 +349,17 @@ def rows_mode(args):
     ng = n // 64
     x40 = torch.from_numpy(xb).to(dev).repeat(NB)
     xs = [x40[i * n:(i + 1) * n] for i in range(NB)]
+    # the size's floor: a pass that only reads the 4-byte inputs and writes one byte each
+    say("floor: read 4 B, write 1 B per element")
+    fl = torch.empty(NB * n, dtype=torch.uint8, device=dev)
+    fns = [lambda i=i: gc.stream_floor(xs[i], fl[i * n:(i + 1) * n]) for i in range(NB)]
+    eager = _eager_ms(torch, fns[0])
+    gms, _ = _graph_ms(torch, fns)
+    floor_ms = gms
+    _row("a4-a6 floor: plain pass reading 4 B and writing 1 B per element", "25 MiB bucket, 40 buckets",
+         5.0 * n, "bucket", gms, eager, None, 1.0, "one bucket")
+    del fl
+
     for bits in (8, 4):
         say(f"min-max int{bits} gs64")
         nc = n if bits == 8 else (n + 1) // 2
@@ -359,8 +376,8 @@ def rows_mode(args):
         osec = _oracle_s(lambda: orc.quant_minmax(xb, 64, bits)) if orc else None
         ub = (5.0 if bits == 8 else 4.5) * n + 8.0 * ng
         _row(f"a4 min-max int{bits}, groups of 64", "25 MiB bucket: n=6,553,600 t(3)*1e-3, 40 buckets",
-             ub, "bucket", gms, eager, osec, 1.0, "one bucket",
-             valu_ops=VALU_LANE_OPS_PER_ELEMENT[f"minmax{bits}"] * n)
+             ub, "bucket", gms, eager, osec, 1.0, "one bucket", extra={"vs_floor": round(gms / floor_ms, 3)},
+             valu_ops=(VALU_LANE_OPS_PER_ELEMENT[f"minmax{bits}"] + VALU_EXTRA_SLOTS_PER_ELEMENT[f"minmax{bits}"]) * n)
 
     say("QSGD s=15 gs64")
     qc = torch.empty(NB * n, dtype=torch.int8, device=dev)
@@ -371,8 +388,8 @@ def rows_mode(args):
     gms, _ = _graph_ms(torch, fns)
     osec = _oracle_s(lambda: orc.qsgd(xb, 64, 15, 7)) if orc else None
     _row("a5+a6 QSGD s=15, groups of 64 (Philox4x32-10)", "25 MiB bucket, 40 buckets",
-         5.0 * n + 4.0 * ng, "bucket", gms, eager, osec, 1.0, "one bucket",
-         valu_ops=VALU_LANE_OPS_PER_ELEMENT["qsgd"] * n)
+         5.0 * n + 4.0 * ng, "bucket", gms, eager, osec, 1.0, "one bucket", extra={"vs_floor": round(gms / floor_ms, 3)},
+         valu_ops=(VALU_LANE_OPS_PER_ELEMENT["qsgd"] + VALU_EXTRA_SLOTS_PER_ELEMENT["qsgd"]) * n)
 
     say("receive: 8 QSGD payloads of one bucket, averaged")
     W = 8
@@ -529,7 +546,7 @@ def rows_mode(args):
     _row("a5+a7 TernGrad, per-layer scale", "24 layers x 14,583,333 (t(3) x lognormal(-7,1) scales)",
          4.0 * n3 + nbytes + 4.0 * L3, "call (all 24 layers)", gms, eager, osec, 1.0 / L3,
          "one layer of 14,583,333, scaled by 24",
-         valu_ops=VALU_LANE_OPS_PER_ELEMENT["terngrad"] * n3)
+         valu_ops=(VALU_LANE_OPS_PER_ELEMENT["terngrad"] + VALU_EXTRA_SLOTS_PER_ELEMENT["terngrad"]) * n3)
     del xt, pk, wst
 
     # c4: PowerSGD rank 4 on the three matrix shapes, error feedback on.

@@ -22,7 +22,7 @@ __all__ = [
     "KIND_QSGD", "KIND_TERN", "OP_EF_TOPK", "OP_QUANT_MINMAX", "OP_QSGD", "OP_TERNGRAD",
     "OP_POWERSGD", "OP_DECOMPRESS", "OP_EF_RANDK", "OP_EF_PENDING", "profile_enable", "profile_collect", "PayloadHeader",
     "PAYLOAD_MAGIC", "PAYLOAD_SPARSE", "payload_layout", "payload_sections", "write_payload_header",
-    "read_payload_header", "decompress_payloads",
+    "read_payload_header", "decompress_payloads", "stream_floor",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -81,6 +81,7 @@ _SIGS = {
     "gc_ef_randk": ([_p, _p, _i64, _i64, _i64, _u64, _p, _p, _i32, _i64, _u64, _p, _p, _p, _sz, _p], _i32),
     "gc_quant_minmax": ([_p, _p, _i64, _i64, _i32, _p, _p, _p, _p, _sz, _p], _i32),
     "gc_qsgd": ([_p, _p, _i64, _i64, _i32, _u64, _i64, _p, _p, _p], _i32),
+    "gc_stream_floor": ([_p, _p, _i64, _p], _i32),
     "gc_terngrad": ([_p, _p, _i32, _p, _u64, _i64, _p, _p, _p, _sz, _p], _i32),
     "gc_powersgd_step": ([_p, _p, _i64, _i64, _i32, _p, _p, _p, _sz, _p], _i32),
     "gc_decompress_scatter": ([_i32, _p, _i64, _i64, _p, _p, _p, _i64, _i32, _f32, _i32, _p, _i64, _p],
@@ -313,6 +314,16 @@ def qsgd(x, group, levels, seed, index_base=0, residual=None, *, codes=None, nor
     _check(_lib.gc_qsgd(_ptr(x), _ptr(residual), n, group, levels, seed, index_base, _ptr(codes),
                         _ptr(norms), _stream(stream)), "gc_qsgd")
     return codes, norms
+
+
+def stream_floor(x, out=None, *, stream=None):
+    """Benchmark calibration: out[i] = (x[i] > 0) as uint8, nothing else (the bytes a
+    one-pass 8-bit quantizer moves).  Returns out."""
+    _dev(x, torch.float32, "x")
+    if out is None:
+        out = torch.empty(x.numel(), dtype=torch.uint8, device=x.device)
+    _check(_lib.gc_stream_floor(_ptr(x), _ptr(out), x.numel(), _stream(stream)), "gc_stream_floor")
+    return out
 
 
 def terngrad(x, seg_offsets, seed, index_base=0, residual=None, *, packed=None, scales=None,

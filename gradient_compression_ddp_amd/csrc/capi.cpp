@@ -523,6 +523,15 @@ int gc_qsgd(const float* x, float* residual, int64_t n, int64_t group, int level
                     "gc_qsgd launch");
 }
 
+int gc_stream_floor(const float* x, uint8_t* out, int64_t n, void* stream) {
+  GC_REQUIRE(n >= 0 && n <= kMaxN, "n must lie in [0, 2^40]");
+  if (n == 0) return ok();
+  GC_REQUIRE(x && aligned(x, 16), "x must be non-NULL and 16-byte aligned");
+  GC_REQUIRE(out && aligned(out, 4), "out must be non-NULL and 4-byte aligned");
+  return hip_status(gc::launch_stream_floor(x, out, n, reinterpret_cast<hipStream_t>(stream)),
+                    "gc_stream_floor launch");
+}
+
 int gc_terngrad(const float* x, float* residual, int nseg, const int64_t* seg_offsets, uint64_t seed,
                 int64_t index_base, uint8_t* packed, float* scales, void* workspace,
                 size_t workspace_bytes, void* stream) {

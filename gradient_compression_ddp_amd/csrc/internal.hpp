@@ -23,6 +23,9 @@ hipError_t launch_minmax_large(const float* x, float* res, int64_t n, int64_t gr
                                uint8_t* codes, float* mins, float* scales, void* ws,
                                hipStream_t s);
 
+// out[i] = (x[i] > 0): the 4 B -> 1 B streaming floor benchmarks time beside the quantizers.
+hipError_t launch_stream_floor(const float* x, uint8_t* out, int64_t n, hipStream_t s);
+
 // ---- QSGD ----------------------------------------------------------------------
 hipError_t launch_qsgd(const float* x, float* res, int64_t n, int64_t group, int levels,
                        uint64_t seed, int64_t index_base, int8_t* codes, float* norms,

@@ -305,6 +305,16 @@ int gc_qsgd(const float* x, float* residual, int64_t n, int64_t group, int level
             uint64_t seed, int64_t index_base, int8_t* codes, float* norms, void* stream);
 
 /*
+ * gc_stream_floor -- calibration for benchmarks, not part of any compressor:
+ * out[i] = (x[i] > 0) ? 1 : 0 for i < n, and nothing else.  It moves the bytes a one-pass
+ * 8-bit quantizer of x moves (4 read and 1 written per element, 16-byte loads, 4-byte
+ * stores), so its time at a given size is the floor such a pass is measured against.
+ * x: float[n], 16-byte aligned.  out: uint8[n], 4-byte aligned.  n in [0, 2^40].
+ * Errors: GC_EINVAL (checked on the host), GC_EHIP.
+ */
+int gc_stream_floor(const float* x, uint8_t* out, int64_t n, void* stream);
+
+/*
  * gc_terngrad -- TernGrad ternary codes with one scale per segment (layer).
  *
  * Operation ([P1] section 1.1: codes in {-1,0,+1}, layer-wise normalization; the scheme

@@ -282,6 +282,18 @@ def test_terngrad_workspace_is_sized_and_checked(lib):
     assert b"workspace" in lib.gc_last_error()
 
 
+def test_stream_floor_rejects_on_the_host(lib):
+    f = lib.gc_stream_floor
+    f.argtypes = [VP, VP, ctypes.c_int64, VP]
+    lib.gc_last_error.restype = ctypes.c_char_p
+    assert f(None, None, 0, None) == 0                      # nothing to do
+    assert f(None, FAKE, 10, None) == 1
+    assert f(MISALIGNED, FAKE, 10, None) == 1
+    assert b"16-byte" in lib.gc_last_error()
+    assert f(FAKE, VP(FAKE.value + 2), 10, None) == 1                 # out not 4-byte aligned
+    assert f(FAKE, FAKE, -1, None) == 1
+
+
 def test_noalloc_rejects_on_the_host(lib):
     # gc_ef_compress_noalloc validates like gc_ef_compress, then refuses any call whose
     # workspace would not fit its fixed array, all before its first HIP call

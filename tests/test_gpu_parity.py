@@ -34,6 +34,19 @@ def host(t):
     return t.cpu().numpy()
 
 
+# ---------------------------------------------------------------- calibration -------
+
+@pytest.mark.parametrize("n", [1, 4, 4096 * 3 + 7, 16384, 1 << 20])
+def test_stream_floor(gc, n):
+    """The benchmark floor pass: out[i] = (x[i] > 0), ragged ends included, signed zeros
+    and negative values giving 0."""
+    x = workloads.bucket(n, seed=n)
+    x[: min(n, 3)] = np.array([0.0, -0.0, 1e-45], F32)[: min(n, 3)]
+    out = host(gc.stream_floor(dev(x)))
+    assert out.dtype == np.uint8
+    assert_bits_equal(out, (x > 0).astype(np.uint8), "floor bytes")
+
+
 # ---------------------------------------------------------------- min-max ----------
 
 MINMAX_CASES = [
