@@ -87,8 +87,11 @@ struct TopkCtrl {
   unsigned long long need;    // entries with key == T to keep
   unsigned long long nchunks; // tiles of the full fallback source
   unsigned long long hist[kBins];
-  uint32_t region_fill[kRegions];
+  // per region: candidates appended (low 32 bits) and, of those, keys whose first radix
+  // digit (bits 20..30) is above L's (high 32 bits)
+  unsigned long long region_fill[kRegions];
   uint32_t emit_next;         // work queue of the batch emit
+  uint32_t pass;              // the main select's next digit (0, 1, 2; 3: T found)
 };
 
 struct Layout {
@@ -320,8 +323,9 @@ __device__ __forceinline__ void block_scan32(const uint32_t* s_cnt, uint32_t* s_
 __device__ __forceinline__ void init_ctrl(TopkCtrl* __restrict__ ctrl, unsigned long long krem,
                                           unsigned long long nchunks) {
   for (int i = threadIdx.x; i < kBins; i += blockDim.x) ctrl->hist[i] = 0ull;
-  for (int i = threadIdx.x; i < kRegions; i += blockDim.x) ctrl->region_fill[i] = 0u;
+  for (int i = threadIdx.x; i < kRegions; i += blockDim.x) ctrl->region_fill[i] = 0ull;
   if (threadIdx.x == 0) ctrl->emit_next = 0u;
+  if (threadIdx.x == 0) ctrl->pass = 0u;
   if (threadIdx.x == 0) {
     ctrl->L = 0u;
     ctrl->overflow = 0u;
@@ -438,7 +442,7 @@ __device__ __forceinline__ void hist_span(const float* __restrict__ src, int64_t
 // its loads at once however the candidates are spread over the regions.  The 0-3
 // trailing candidates of region r are counted by block r % gridDim.x.
 __device__ __forceinline__ void hist_pool(const float* __restrict__ pool, int64_t region_cap,
-                                          const uint32_t* __restrict__ region_fill, const uint32_t* s_rq,
+                                          const unsigned long long* __restrict__ region_fill, const uint32_t* s_rq,
                                           int64_t first, int64_t stride, uint32_t* my, BinRun& r,
                                           uint32_t hshift, uint32_t want, int shift, uint32_t mask) {
   constexpr int kAhead = 4;
@@ -468,7 +472,7 @@ __device__ __forceinline__ void hist_pool(const float* __restrict__ pool, int64_
     }
   }
   for (int rg = blockIdx.x; rg < kRegions; rg += gridDim.x) {
-    const uint32_t fill = region_fill[rg];
+    const uint32_t fill = (uint32_t)region_fill[rg];
     if (threadIdx.x < (fill & 3u))
       hist_add(my, r, mag_key(pool[rg * region_cap + (fill & ~3u) + threadIdx.x]), hshift, want, shift, mask);
   }
@@ -494,27 +498,56 @@ __device__ __forceinline__ void hist_rand(int64_t n, uint64_t seed, int64_t inde
 // the pool did not overflow and at least k entries reached the bound L (then T >= L).
 // Without overflow the region counters sum to the number of candidates.  `publish`
 // stores the decision in the control block for the kernels that follow.
+//
+// First digit from the counters: every candidate's key is >= L, so when fewer than k of
+// them have a first digit (bits 20..30) above L's, the k-th key's first digit is L's,
+// and its rank among the candidates of that digit is k minus that count.  The select
+// then starts at the second digit (*skip = true; publish also records the prefix, the
+// remaining rank and the next digit for the passes and picks that follow).
 __device__ __forceinline__ uint32_t decide_mode(TopkCtrl* __restrict__ ctrl, int64_t ntiles,
-                                                unsigned long long k, bool publish) {
-  unsigned long long ncand = 0;
-  for (int i = 0; i < kRegions; ++i) ncand += ctrl->region_fill[i];
+                                                unsigned long long k, bool publish, bool* skip) {
+  unsigned long long ncand = 0, above = 0;
+  for (int i = 0; i < kRegions; ++i) {
+    const unsigned long long f = ctrl->region_fill[i];
+    ncand += f & 0xFFFFFFFFull;
+    above += f >> 32;
+  }
   const bool full = ctrl->overflow != 0u || ncand < k;
+  *skip = !full && above < k;
   if (publish) {
     ctrl->ncand = full ? 0ull : ncand;
     ctrl->mode = full ? MODE_FULL : MODE_CAND;
     ctrl->nchunks = (unsigned long long)(full ? ntiles : cdiv(ntiles, kUnit));
+    if (*skip) {
+      ctrl->prefix = (ctrl->L >> 20) << 20;
+      ctrl->krem = k - above;
+      ctrl->pass = 1u;
+    }
   }
   return full ? MODE_FULL : MODE_CAND;
 }
+
+// The main select's digits: bits 20..30, 9..19 and 0..8 of the 31-bit key.
+__host__ __device__ constexpr int main_shift(uint32_t pass) { return pass == 0u ? 20 : (pass == 1u ? 9 : 0); }
+__host__ __device__ constexpr int main_bits(uint32_t pass) { return pass == 2u ? 9 : 11; }
 
 // Locate the bin of the global histogram holding rank krem (counted from the largest
 // key), fix its bits in the prefix and clear the histogram (one block; s_sum holds
 // kBlock 64-bit words).  final_op: 0 = intermediate pass; 1 = last pass of the sample
 // select (set L, reset for the main select with rank k_main); 2 = last pass of the main
 // select (set T and need); 3 = last pass of a select over the whole input (L = T too).
+// dyn: the main select over the pool or the full c, whose digit (and so shift and
+// final_op) is the control block's pass, advanced here; nothing to do once it is 3.
 __device__ __forceinline__ void pick_body(TopkCtrl* __restrict__ ctrl, int shift, int final_op,
-                                          unsigned long long k_main, unsigned long long* s_sum) {
+                                          unsigned long long k_main, unsigned long long* s_sum, int dyn) {
   constexpr int per = kBins / kBlock;   // 8 bins per thread, highest bins first
+  uint32_t pass = 0u;
+  if (dyn) {
+    pass = ctrl->pass;
+    if (pass >= 3u) return;   // uniform: every thread read the same word
+    shift = main_shift(pass);
+    final_op = pass == 2u ? 2 : 0;
+  }
   const int t = threadIdx.x;
   const int hi_bin = kBins - 1 - per * t;
   unsigned long long c[per];
@@ -546,6 +579,7 @@ __device__ __forceinline__ void pick_body(TopkCtrl* __restrict__ ctrl, int shift
   }
   for (int i = 0; i < per; ++i) ctrl->hist[hi_bin - i] = 0ull;
   __syncthreads();
+  if (t == 0 && dyn) ctrl->pass = pass + 1u;
   if (t == 0 && final_op != 0) {
     const uint32_t T = ctrl->prefix;
     if (final_op == 1) {
@@ -561,9 +595,9 @@ __device__ __forceinline__ void pick_body(TopkCtrl* __restrict__ ctrl, int shift
 }
 
 __global__ __launch_bounds__(kBlock) void k_pick(TopkCtrl* __restrict__ ctrl, int shift, int final_op,
-                                                 unsigned long long k_main) {
+                                                 unsigned long long k_main, int dyn) {
   __shared__ unsigned long long s_sum[kBlock];
-  pick_body(ctrl, shift, final_op, k_main, s_sum);
+  pick_body(ctrl, shift, final_op, k_main, s_sum, dyn);
 }
 
 // Radix histogram pass over the key bits [shift, shift+bits) of the entries whose higher
@@ -572,7 +606,9 @@ __global__ __launch_bounds__(kBlock) void k_pick(TopkCtrl* __restrict__ ctrl, in
 // pool or, in the fallback, the Random-K keys of all n indices.  decide_k > 0 (the first
 // pass over the pool): every block takes the source decision itself, and block 0 also
 // publishes it.  fuse_pick: the last block to finish then locates the rank's bin
-// (pick_body); otherwise k_pick follows.
+// (pick_body); otherwise k_pick follows.  dyn (the main select over the pool or the full
+// c): the digit is the control block's pass, not the arguments (the first launch may
+// start at the second digit, see decide_mode), and a launch past the last digit returns.
 template <int SRC>
 __global__ __launch_bounds__(kBlock) void k_hist(TopkCtrl* __restrict__ ctrl,
                                                  const uint32_t* __restrict__ sample_keys,
@@ -580,16 +616,30 @@ __global__ __launch_bounds__(kBlock) void k_hist(TopkCtrl* __restrict__ ctrl,
                                                  int64_t region_cap, const float* __restrict__ full,
                                                  int64_t n, int shift, int bits, uint64_t seed,
                                                  int64_t index_base, int64_t ntiles, unsigned long long decide_k,
-                                                 int final_op, unsigned long long k_main, int fuse_pick) {
+                                                 int final_op, unsigned long long k_main, int fuse_pick, int dyn) {
   __shared__ __align__(16) uint32_t lh[kWaves][kBins];
   __shared__ uint32_t s_rq[kRegions + 1];
-  __shared__ uint32_t s_mode;
+  __shared__ uint32_t s_mode, s_pass, s_prefix;
   for (int i = threadIdx.x; i < kWaves * kBins; i += kBlock) (&lh[0][0])[i] = 0u;
-  if (SRC != 0 && threadIdx.x == 0)
-    s_mode = decide_k ? decide_mode(ctrl, ntiles, decide_k, blockIdx.x == 0) : ctrl->mode;
+  if (threadIdx.x == 0) {
+    uint32_t pass = 0u, prefix = ctrl->prefix;
+    if (SRC != 0) {
+      bool skip = false;
+      s_mode = decide_k ? decide_mode(ctrl, ntiles, decide_k, blockIdx.x == 0, &skip) : ctrl->mode;
+      if (dyn && decide_k) {
+        // every block decides the same from the counters; block 0 published it
+        pass = skip ? 1u : 0u;
+        prefix = skip ? ((ctrl->L >> 20) << 20) : 0u;
+      } else if (dyn) {
+        pass = ctrl->pass;
+      }
+    }
+    s_pass = pass;
+    s_prefix = prefix;
+  }
   if (SRC != 0 && threadIdx.x < kWave) {
     // exclusive prefix of the regions' whole-quad counts (candidate mode only reads it)
-    const uint32_t c = threadIdx.x < kRegions ? ctrl->region_fill[threadIdx.x] >> 2 : 0u;
+    const uint32_t c = threadIdx.x < kRegions ? (uint32_t)ctrl->region_fill[threadIdx.x] >> 2 : 0u;
     uint32_t inc = c;
 #pragma unroll
     for (int d = 1; d < kRegions; d <<= 1) {
@@ -600,8 +650,14 @@ __global__ __launch_bounds__(kBlock) void k_hist(TopkCtrl* __restrict__ ctrl,
     if (threadIdx.x == kRegions - 1) s_rq[kRegions] = inc;
   }
   __syncthreads();
+  if (dyn) {
+    if (s_pass >= 3u) return;   // the select ended in an earlier launch (same for every block)
+    shift = main_shift(s_pass);
+    bits = main_bits(s_pass);
+    final_op = s_pass == 2u ? 2 : 0;
+  }
   const uint32_t hshift = (uint32_t)(shift + bits);
-  const uint32_t want = ctrl->prefix >> hshift;
+  const uint32_t want = s_prefix >> hshift;
   const uint32_t mask = (1u << bits) - 1u;
   uint32_t* my = lh[threadIdx.x / kWave];
   const int64_t stride = (int64_t)gridDim.x * kBlock;
@@ -624,7 +680,7 @@ __global__ __launch_bounds__(kBlock) void k_hist(TopkCtrl* __restrict__ ctrl,
   }
   // lh is free once every thread is past the flush (last_block's barrier)
   if (fuse_pick && last_block(&ctrl->ticket))
-    pick_body(ctrl, shift, final_op, k_main, reinterpret_cast<unsigned long long*>(&lh[0][0]));
+    pick_body(ctrl, shift, final_op, k_main, reinterpret_cast<unsigned long long*>(&lh[0][0]), dyn);
 }
 
 
@@ -744,29 +800,36 @@ __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g,
       for (int m = 0; m < 4; ++m) key[j][m] = mag_key(c[j][m]);
     }
   }
+  // candidates (key >= L) and, in the high 16 bits of each wave's count, those whose first
+  // radix digit is above L's (key >= A; counts stay below 2^13 per tile, so the packed
+  // scan never carries)
+  const uint32_t A = ((L >> 20) + 1u) << 20;
   uint32_t nib[kRounds], pre[kRounds];
 #pragma unroll
   for (int j = 0; j < kRounds; ++j) {
-    uint32_t b = 0u;
+    uint32_t b = 0u, wa = 0u;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int64_t e = base + j * (kBlock * 4) + threadIdx.x * 4 + m;
-      b |= ((key[j][m] >= L) && e < n) ? (1u << m) : 0u;
+      const bool in = e < n;
+      b |= ((key[j][m] >= L) && in) ? (1u << m) : 0u;
+      wa += (uint32_t)__popcll(ballot((key[j][m] >= A) && in));
     }
     nib[j] = b;
     uint32_t wc;
     pre[j] = rank_round(b, &wc);
-    if (lane == 0) s_cnt[j * kWaves + w] = wc;
+    if (lane == 0) s_cnt[j * kWaves + w] = wc | (wa << 16);
   }
   __syncthreads();
   block_scan32(s_cnt, s_off, &s_total);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t total = s_total;
+    const uint32_t total = s_total & 0xFFFFu, above = s_total >> 16;
     uint32_t start = 0u, ok = 1u;
     if (total) {
       const uint32_t region = (uint32_t)(tile & (kRegions - 1));
-      const uint32_t at = atomicAdd(&ctrl->region_fill[region], total);
+      const uint32_t at = (uint32_t)atomicAdd(&ctrl->region_fill[region],
+                                              ((unsigned long long)above << 32) | (unsigned long long)total);
       if (at + total > region_cap) {
         atomicOr(&ctrl->overflow, 1u);
         ok = 0u;
@@ -785,7 +848,7 @@ __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g,
 #pragma unroll
     for (int j = 0; j < kRounds; ++j) {
       if (nib[j]) {
-        uint32_t pos = s_base + s_off[j * kWaves + w] + pre[j];
+        uint32_t pos = s_base + (s_off[j * kWaves + w] & 0xFFFFu) + pre[j];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           if (nib[j] & (1u << m)) {
@@ -2215,8 +2278,8 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
     const bool fuse = sgrid <= kFusePickGrid;
     hipLaunchKernelGGL((k_hist<0>), sgrid, kBlock, 0, s, ctrl, l.sample, m, (const float*)nullptr,
                        (int64_t)0, (const float*)nullptr, n, shifts[p], widths[p], (uint64_t)0, (int64_t)0,
-                       (int64_t)0, 0ull, op, (unsigned long long)k, fuse ? 1 : 0);
-    if (!fuse) hipLaunchKernelGGL(k_pick, 1, kBlock, 0, s, ctrl, shifts[p], op, (unsigned long long)k);
+                       (int64_t)0, 0ull, op, (unsigned long long)k, fuse ? 1 : 0, 0);
+    if (!fuse) hipLaunchKernelGGL(k_pick, 1, kBlock, 0, s, ctrl, shifts[p], op, (unsigned long long)k, 0);
   }
 
   // 3: the streaming pass
@@ -2238,15 +2301,18 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
 
   // 4-5: unless the sample was the whole input (T and need already exact, and every
   // candidate is kept or a tie), the first pool pass decides the source; then the exact
-  // k-th key over it
+  // k-th key over it.  The digits come from the control block: when the streaming pass's
+  // counts already fix the first digit, the first launch takes the second and the third
+  // launch (and its pick) returns at once
   if (!exact) {
     for (int p = 0; p < 3; ++p) {
       const bool fuse = hgrid <= kFusePickGrid;
       hipLaunchKernelGGL((k_hist<RAND ? 2 : 1>), hgrid, kBlock, 0, s, ctrl, (const uint32_t*)nullptr, (int64_t)0,
                          (const float*)l.pool_val, l.region_cap, (const float*)res, n, shifts[p], widths[p],
                          select_seed, index_base, l.ntiles, p == 0 ? (unsigned long long)k : 0ull,
-                         p == 2 ? 2 : 0, (unsigned long long)k, fuse ? 1 : 0);
-      if (!fuse) hipLaunchKernelGGL(k_pick, 1, kBlock, 0, s, ctrl, shifts[p], p == 2 ? 2 : 0, (unsigned long long)k);
+                         p == 2 ? 2 : 0, (unsigned long long)k, fuse ? 1 : 0, 1);
+      if (!fuse)
+        hipLaunchKernelGGL(k_pick, 1, kBlock, 0, s, ctrl, shifts[p], p == 2 ? 2 : 0, (unsigned long long)k, 1);
     }
   }
 
