@@ -135,6 +135,34 @@ def test_topk_forced_fallback_deferred(gc):
     assert_bits_equal(host(rd), r, "flushed residual")
 
 
+@pytest.mark.parametrize("fill", ["ones", "random"])
+def test_topk_workspace_of_other_data(gc, fill):
+    # The workspace holds whatever its memory held before (here all ones, or random
+    # bytes): the control block, the counters and the pool are set by the call itself
+    # before they are read, so both calls are exact and take the candidate path.
+    import torch
+    n, k = N_LARGE, N_LARGE // 100
+    print(f"[large] workspace of other data ({fill}) n={n} k={k}", flush=True)
+    g, r = inputs(n, 53)
+    rd = dev(r)
+    ws = workspace(gc, gc.OP_EF_TOPK, n, k)
+    if fill == "ones":
+        ws.fill_(255)
+    else:
+        gen = torch.Generator(device="cuda:0").manual_seed(5)
+        ws.copy_(torch.randint(0, 256, ws.shape, generator=gen, device="cuda:0", dtype=torch.int32).to(torch.uint8))
+    for step in (1, 2):
+        if step == 2:
+            g = (g * F32(0.9)).astype(F32)
+        o_idx, o_val, o_res = oracle.ef_topk(g, r, k)
+        idx, val = gc.ef_topk(dev(g), rd, k, workspace=ws)
+        assert_bits_equal(host(idx), o_idx, f"step {step} idx")
+        assert_bits_equal(host(val), o_val, f"step {step} values")
+        assert_bits_equal(host(rd), o_res, f"step {step} residual")
+        assert mode_of(ws) == 0
+        r = o_res
+
+
 @pytest.mark.parametrize("k,mode", [(N_LARGE // 100, 0), (N_LARGE, 1)])
 def test_randk_with_qsgd(gc, k, mode):
     # k = n: some keys fall below the smallest of the 2^19 sampled keys, so the candidates
