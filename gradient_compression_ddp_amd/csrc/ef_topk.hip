@@ -9,9 +9,9 @@
 // index wins among equal magnitudes, and the indices come out ascending.
 //
 // Pipeline (all on the caller's stream, no host synchronization):
-//  1. sample   key(g+r) at m <= 2^20 jittered positions;
+//  1. sample   key(g+r) at m <= 2^19 jittered positions;
 //  2. select   a conservative lower bound L on the k-th largest key from the sample.
-//              When n <= 2^20 the sample is the whole input and this select is already
+//              When n <= 2^15 the sample is the whole input and this select is already
 //              exact (T and need); the pool then has room for all n elements and steps
 //              4-5 and the fallback are skipped, which halves the kernel count of a
 //              small call;
@@ -57,7 +57,10 @@ constexpr int kWaves = kBlock / kWave;       // 4
 constexpr int kRounds = 4;                   // quads per thread per tile
 constexpr int64_t kTile = (int64_t)kBlock * 4 * kRounds;   // 4096 elements
 constexpr int kRegions = 32;                 // candidate-pool regions (tile % 32)
-constexpr int kSampleMax = 1 << 20;
+// At 7e9 elements a draw of 2^20 points (about ten random 64-byte sectors each, with the
+// record lookup) took 0.10 ms; 2^19 points took the sample and its select 0.145 -> 0.100 ms
+// while the looser bound grew the pool passes and the emit by about 0.015 ms.
+constexpr int kSampleMax = 1 << 19;
 constexpr int kScanChunk = 1024;             // items per block in the multi-block scan
 constexpr int kBins = 2048;
 constexpr int kUnit = 16;                    // tiles per unit of the candidate count and scan
@@ -124,7 +127,7 @@ __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 
 // The rank sits 2% above the expected sample rank plus 8 standard deviations, so the
 // candidates hold the k largest unless the sample is off by far more than sampling error.
 // Up to 2^15 elements the sample is the whole input, which gives the exact k-th key.
-// Above, one element in 64 is drawn, between 2^15 and 2^20 points: the draw costs two
+// Above, one element in 64 is drawn, between 2^15 and 2^19 points: the draw costs two
 // random sectors per point, and a whole-input select of a million keys costs more than
 // the small candidate pool a sample leaves (1e6 elements: 1.7% of them at k = 1%).
 int64_t sample_size(int64_t n) {

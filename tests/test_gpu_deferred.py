@@ -4,7 +4,7 @@ Every call's indices, values, codes and norms are compared bit for bit with the 
 EF Top-K step; after gc_ef_flush the residual is compared bit for bit with the oracle's
 residual.  Between calls the residual holds c = g + r at every position (the kept
 entries' residuals sit in the pending record), which is checked too.  Cases cover the
-whole-input select (n <= 2^20), the sampled candidate path, the exact fallback, k = 0,
+whole-input select (n <= 2^15), the sampled candidate path, the exact fallback, k = 0,
 and a 2^30-element bucket against the direct call.
 """
 import numpy as np

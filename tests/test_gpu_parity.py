@@ -323,8 +323,9 @@ def test_topk_ties_and_specials(gc):
 
 
 def test_topk_whole_input_select_all_ties(gc):
-    # n = 2^20: the sample is the whole input, so the select is exact and the pool must
-    # hold every element when all of them tie with the k-th key
+    # n = 2^20 (sampled) with every element, or all but five, tied with the k-th key:
+    # every element reaches the bound, the pool overflows and the exact fallback over the
+    # full c selects, ties to the lower index
     n = 1 << 20
     check_topk(gc, np.full(n, 0.5, F32), np.zeros(n, F32), 3)
     g = np.full(n, -0.25, F32)

@@ -2,7 +2,7 @@
 
 Indices, kept values, QSGD codes and norms, and the residual are compared bit for bit.
 Sizes span several 4096-element tiles with ragged tails, the whole-input select
-(n <= 2^20), the sampled candidate path, and the exact fallback over all n keys.
+(n <= 2^15), the sampled candidate path, and the exact fallback over all n keys.
 """
 import numpy as np
 import pytest
