@@ -22,7 +22,7 @@ __all__ = [
     "KIND_QSGD", "KIND_TERN", "OP_EF_TOPK", "OP_QUANT_MINMAX", "OP_QSGD", "OP_TERNGRAD",
     "OP_POWERSGD", "OP_DECOMPRESS", "OP_EF_RANDK", "OP_EF_PENDING", "profile_enable", "profile_collect", "PayloadHeader",
     "PAYLOAD_MAGIC", "PAYLOAD_SPARSE", "payload_layout", "payload_sections", "write_payload_header",
-    "read_payload_header", "decompress_payloads", "stream_floor",
+    "read_payload_header", "decompress_payloads", "stream_floor", "PreparedEfCompress", "PreparedDecompress",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -221,6 +221,69 @@ def _ef_options(select, select_seed, pending, stats):
             raise ValueError("stats must hold 3 doubles")
         opts.stats = stats.data_ptr()
     return opts
+
+
+class PreparedEfCompress:
+    """One gc_ef_compress call set up for repeated use on the same buffers (one DDP bucket
+    every step): every argument but the gradient, the two seeds and the stream is checked
+    and converted once, so a call costs the ctypes call and little else.  Same operation
+    and outputs as :func:`ef_compress` with ``index_base = 0``."""
+
+    def __init__(self, n, residual, k, *, select="topk", pending=None, stats=None, qsgd_levels=0, qsgd_group=64,
+                 out_idx, out_val=None, out_codes=None, out_norms=None, workspace=None):
+        _dev(residual, torch.float32, "residual")
+        if residual.numel() != n:
+            raise ValueError("residual differs in size from n")
+        _dev(out_idx, torch.int64, "out_idx")
+        quant = qsgd_levels > 0
+        if quant:
+            if out_codes is None or out_norms is None:
+                raise ValueError("QSGD needs out_codes and out_norms")
+        elif out_val is None:
+            raise ValueError("pure selection needs out_val")
+        self.n = n
+        self._dev = residual.device
+        self._opts = _ef_options(select, 0, pending, stats)
+        op = OP_EF_RANDK if select == "randk" else OP_EF_TOPK
+        ws, ws_bytes = _workspace(op, n, k, qsgd_levels, residual.device, workspace)
+        self._keep = (residual, pending, stats, out_idx, out_val, out_codes, out_norms, ws)   # alive while prepared
+        p = lambda t: None if t is None else t.data_ptr()
+        self._head = (p(residual), n, k, 0, p(out_idx), p(out_val), qsgd_levels, qsgd_group)
+        self._tail = (p(out_codes), p(out_norms), ctypes.byref(self._opts), p(ws), ws_bytes)
+        self._fn = _lib.gc_ef_compress
+
+    def __call__(self, grad, select_seed, qsgd_seed, stream_handle):
+        """grad: float32 GPU tensor of n elements; stream_handle: the raw hipStream_t."""
+        if grad.numel() != self.n or grad.dtype != torch.float32 or grad.device != self._dev:
+            raise ValueError("grad must be a float32 tensor of n elements on the residual's device")
+        self._opts.select_seed = select_seed
+        _check(self._fn(grad.data_ptr(), *self._head, qsgd_seed, *self._tail, stream_handle), "gc_ef_compress")
+
+
+class PreparedDecompress:
+    """One gc_decompress_payloads call over fixed payload buffers, set up once: a call
+    passes only the output and the stream.  Same operation as :func:`decompress_payloads`."""
+
+    def __init__(self, payloads, headers, *, alpha=None, accumulate=False):
+        W = len(payloads)
+        if W != len(headers):
+            raise ValueError("one header per payload")
+        for b in payloads:
+            _dev(b, torch.uint8, "payload")
+        self._keep = list(payloads)
+        self._ptrs = (ctypes.c_void_p * W)(*[b.data_ptr() for b in payloads])
+        self._hdrs = (PayloadHeader * W)(*headers)
+        self._W = W
+        self._alpha = 1.0 / W if alpha is None else alpha
+        self._acc = 1 if accumulate else 0
+        self._pp = ctypes.cast(self._ptrs, ctypes.POINTER(ctypes.c_void_p))
+        self._fn = _lib.gc_decompress_payloads
+
+    def __call__(self, out, stream_handle):
+        if out.dtype != torch.float32 or not out.is_contiguous():
+            raise ValueError("out must be a contiguous float32 tensor")
+        _check(self._fn(self._W, self._pp, self._hdrs, self._alpha, self._acc, out.data_ptr(), out.numel(),
+                        stream_handle), "gc_decompress_payloads")
 
 
 def noalloc_scratch_bytes() -> int:

@@ -14,15 +14,22 @@ Per bucket and step:
      to the bucket's next step by default;
   2. all_gather of the fixed-size payloads (every rank's k and layout are equal);
   3. gc_decompress_payloads: the bucket becomes the average of the W decoded payloads.
-The library's calls are asynchronous, and step 3 runs as the continuation of the
-all_gather future.  With `overlap` (the default) steps 1 and 2 run on a side stream of the
-hook's own (default priority) that first waits for the bucket to be ready, so the
-backward pass of the earlier layers keeps running on DDP's stream while the bucket is
-compressed; DDP waits for the returned future before it uses the bucket.
+Every step is enqueued on one stream and nothing waits on the host: the stream waits
+for the all_gather's work before the decode, and the hook returns a future that is
+already complete, since whatever DDP runs next on that stream comes after the decode.
+With `overlap` (the default) the three steps run on a side stream of the hook's own
+(default priority), which first waits for an event recorded on DDP's stream (the bucket's
+gradients are complete), so the backward pass of the earlier layers keeps running while
+the bucket is compressed; DDP's stream then waits for an event recorded after the decode.
+
+The iteration of a small model is bound by the host: each bucket's library calls are set
+up once (PreparedEfCompress, PreparedDecompress: arguments checked and converted when the
+bucket is created), so a step costs two ctypes calls, the collective and two events.
 
 State per bucket (keyed by DDP's bucket index and size; DDP may regroup buckets after its
 first iteration, and a bucket whose size changes starts from a zero residual): residual,
-pending record, workspace, this rank's payload and the gathered payloads.
+pending record, workspace, this rank's payload and the gathered payloads, and the
+prepared calls over them.
 """
 # No postponed annotations here: DDP checks the hook's annotations at run time.
 from dataclasses import dataclass, field
@@ -31,7 +38,7 @@ from typing import Dict, List, Optional, Tuple
 import torch
 import torch.distributed as dist
 
-from . import (KIND_F32, KIND_QSGD, OP_EF_RANDK, OP_EF_TOPK, decompress_payloads, ef_compress, ef_flush,
+from . import (KIND_F32, KIND_QSGD, OP_EF_RANDK, OP_EF_TOPK, PreparedDecompress, PreparedEfCompress, ef_flush,
                payload_layout, payload_sections, pending_record, workspace_size, write_payload_header)
 
 
@@ -51,6 +58,10 @@ class _Bucket:
     gathered: torch.Tensor
     stride: int
     stats: Optional[torch.Tensor]
+    compress: PreparedEfCompress      # the bucket's library calls, set up once
+    decode: PreparedDecompress
+    ready: torch.cuda.Event           # side stream: the bucket's gradients are complete
+    done: torch.cuda.Event            # side stream: the bucket holds the average
     calls: int = 0
 
 
@@ -94,11 +105,22 @@ class CompressionHookState:
         write_payload_header(payload, h)
         op = OP_EF_RANDK if self.select == "randk" else OP_EF_TOPK
         ws = torch.empty(max(workspace_size(op, n, k, self.qsgd_levels), 1), dtype=torch.uint8, device=device)
-        b = _Bucket(n=n, k=k, header=h, residual=torch.zeros(n, dtype=torch.float32, device=device),
-                    pending=pending_record(n, k, device) if self.deferred else None, workspace=ws,
-                    payload=payload, gathered=torch.empty(W * stride, dtype=torch.uint8, device=device),
-                    stride=stride,
-                    stats=torch.zeros(3, dtype=torch.float64, device=device) if self.monitor else None)
+        residual = torch.zeros(n, dtype=torch.float32, device=device)
+        pending = pending_record(n, k, device) if self.deferred else None
+        stats = torch.zeros(3, dtype=torch.float64, device=device) if self.monitor else None
+        gathered = torch.empty(W * stride, dtype=torch.uint8, device=device)
+        sec = payload_sections(payload, h)
+        if self.qsgd_levels > 0:
+            outs = dict(out_codes=sec["codes"], out_norms=sec["meta0"])
+        else:
+            outs = dict(out_val=sec["codes"])
+        compress = PreparedEfCompress(n, residual, k, select=self.select, pending=pending, stats=stats,
+                                      qsgd_levels=self.qsgd_levels, qsgd_group=self.qsgd_group, out_idx=sec["idx"],
+                                      workspace=ws, **outs)
+        decode = PreparedDecompress([gathered[w * stride:(w + 1) * stride] for w in range(W)], [h] * W)
+        b = _Bucket(n=n, k=k, header=h, residual=residual, pending=pending, workspace=ws, payload=payload,
+                    gathered=gathered, stride=stride, stats=stats, compress=compress, decode=decode,
+                    ready=torch.cuda.Event(), done=torch.cuda.Event())
         self.buckets[index] = b
         return b
 
@@ -112,6 +134,11 @@ class CompressionHookState:
                 ef_flush(b.residual, b.pending)
 
 
+def _raw_stream(device_index: int) -> int:
+    """The current stream's raw handle, without building a Stream object."""
+    return torch._C._cuda_getCurrentRawStream(device_index)
+
+
 def ef_compress_hook(state: CompressionHookState, bucket: dist.GradBucket) -> torch.futures.Future[torch.Tensor]:
     buf = bucket.buffer()
     if buf.dtype != torch.float32:
@@ -121,30 +148,31 @@ def ef_compress_hook(state: CompressionHookState, bucket: dist.GradBucket) -> to
     step = b.calls
     b.calls += 1
     sel_seed, q_seed = state.seeds(index, step)
-    sec = payload_sections(b.payload, b.header)
-    if state.qsgd_levels > 0:
-        outs = dict(out_codes=sec["codes"], out_norms=sec["meta0"], want_values=False)
-    else:
-        outs = dict(out_val=sec["codes"])
-    stream = torch.cuda.current_stream()
     if state.overlap:
+        cur = torch.cuda.current_stream()
         if state.side_stream is None:
             state.side_stream = torch.cuda.Stream(device=buf.device)
-        state.side_stream.wait_stream(stream)      # the bucket's gradients are complete
         stream = state.side_stream
-    W = dist.get_world_size(state.process_group)
-    with torch.cuda.stream(stream):
-        before = buf.clone() if state.capture is not None else None
-        ef_compress(buf, b.residual, b.k, select=state.select, select_seed=sel_seed, pending=b.pending,
-                    stats=b.stats, qsgd_levels=state.qsgd_levels, qsgd_group=state.qsgd_group, qsgd_seed=q_seed,
-                    out_idx=sec["idx"], workspace=b.workspace, **outs)
-        work = dist.all_gather_into_tensor(b.gathered, b.payload, group=state.process_group, async_op=True)
+        b.ready.record(cur)              # the bucket's gradients are complete
+        stream.wait_event(b.ready)
+        with torch.cuda.stream(stream):  # the collective orders itself after the current stream
+            _exchange(state, b, buf, index, step, sel_seed, q_seed, stream.cuda_stream)
+        b.done.record(stream)
+        cur.wait_event(b.done)           # DDP reads the bucket on its own stream
+    else:
+        _exchange(state, b, buf, index, step, sel_seed, q_seed, _raw_stream(buf.device.index))
+    # every step is stream-ordered, so the result is ready for whatever DDP runs next
+    fut = torch.futures.Future()
+    fut.set_result(buf)
+    return fut
 
-    def decode(fut):
-        views = [b.gathered[w * b.stride:(w + 1) * b.stride] for w in range(W)]
-        decompress_payloads(views, [b.header] * W, buf)
-        if state.capture is not None:
-            state.capture.append((index, step, before, buf.clone()))
-        return buf
 
-    return work.get_future().then(decode)
+def _exchange(state, b, buf, index, step, sel_seed, q_seed, h):
+    """Compress, all_gather and decode one bucket on the current stream (raw handle h)."""
+    before = buf.clone() if state.capture is not None else None
+    b.compress(buf, sel_seed, q_seed, h)
+    work = dist.all_gather_into_tensor(b.gathered, b.payload, group=state.process_group, async_op=True)
+    work.wait()                          # the stream waits for the gathered payloads; the host does not
+    b.decode(buf, h)
+    if state.capture is not None:
+        state.capture.append((index, step, before, buf.clone()))
