@@ -20,11 +20,13 @@ already complete, since whatever DDP runs next on that stream comes after the de
 With `overlap` (the default) the three steps run on a side stream of the hook's own
 (default priority), which first waits for an event recorded on DDP's stream (the bucket's
 gradients are complete), so the backward pass of the earlier layers keeps running while
-the bucket is compressed; DDP's stream then waits for an event recorded after the decode.
+the bucket is compressed and exchanged; the returned future is device-aware and set on
+the side stream, so DDP's stream waits for the decode only when DDP waits for the future.
+Without it, every step runs on DDP's stream, which then also waits for the collective.
 
 The iteration of a small model is bound by the host: each bucket's library calls are set
 up once (PreparedEfCompress, PreparedDecompress: arguments checked and converted when the
-bucket is created), so a step costs two ctypes calls, the collective and two events.
+bucket is created), so a step costs two ctypes calls, the collective and an event.
 
 State per bucket (keyed by DDP's bucket index and size; DDP may regroup buckets after its
 first iteration, and a bucket whose size changes starts from a zero residual): residual,
@@ -61,7 +63,6 @@ class _Bucket:
     compress: PreparedEfCompress      # the bucket's library calls, set up once
     decode: PreparedDecompress
     ready: torch.cuda.Event           # side stream: the bucket's gradients are complete
-    done: torch.cuda.Event            # side stream: the bucket holds the average
     calls: int = 0
 
 
@@ -120,7 +121,7 @@ class CompressionHookState:
         decode = PreparedDecompress([gathered[w * stride:(w + 1) * stride] for w in range(W)], [h] * W)
         b = _Bucket(n=n, k=k, header=h, residual=residual, pending=pending, workspace=ws, payload=payload,
                     gathered=gathered, stride=stride, stats=stats, compress=compress, decode=decode,
-                    ready=torch.cuda.Event(), done=torch.cuda.Event())
+                    ready=torch.cuda.Event())
         self.buckets[index] = b
         return b
 
@@ -157,11 +158,14 @@ def ef_compress_hook(state: CompressionHookState, bucket: dist.GradBucket) -> to
         stream.wait_event(b.ready)
         with torch.cuda.stream(stream):  # the collective orders itself after the current stream
             _exchange(state, b, buf, index, step, sel_seed, q_seed, stream.cuda_stream)
-        b.done.record(stream)
-        cur.wait_event(b.done)           # DDP reads the bucket on its own stream
-    else:
-        _exchange(state, b, buf, index, step, sel_seed, q_seed, _raw_stream(buf.device.index))
-    # every step is stream-ordered, so the result is ready for whatever DDP runs next
+            # a device-aware future set here records the side stream: DDP's stream waits
+            # for the decode only when DDP waits for the future, at the end of backward,
+            # so the backward of earlier layers is not held behind this bucket's exchange
+            fut = torch.futures.Future(devices=[buf.device])
+            fut.set_result(buf)
+        return fut
+    _exchange(state, b, buf, index, step, sel_seed, q_seed, _raw_stream(buf.device.index))
+    # everything is ordered on DDP's stream, so the result is ready for what DDP runs next
     fut = torch.futures.Future()
     fut.set_result(buf)
     return fut
