@@ -316,3 +316,19 @@ def test_noalloc_rejects_on_the_host(lib):
     assert f(FAKE, FAKE, n, n // 100, 0, FAKE, None, 127, 100, 1, FAKE, FAKE, None, None) == 1   # group
     # n == 0 and k == 0 need no workspace and touch nothing
     assert f(None, None, 0, 0, 0, None, None, 0, 64, 0, None, None, None, None) == 0
+
+
+def test_prepared_calls_check_their_buffers(lib):
+    # the prepared calls of the DDP hook check every buffer when they are set up, on the
+    # host: host tensors, wrong dtypes and missing outputs raise before any library call
+    import torch
+    import gradient_compression_ddp_amd as gcm
+    n, k = 10_000, 100
+    cpu_res = torch.zeros(n)
+    idx = torch.zeros(k, dtype=torch.int64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        gcm.PreparedEfCompress(n, cpu_res, k, out_idx=idx, out_val=torch.zeros(k))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        gcm.PreparedDecompress([torch.zeros(256, dtype=torch.uint8)], [gcm.PayloadHeader()])
+    with pytest.raises(ValueError, match="one header per payload"):
+        gcm.PreparedDecompress([], [gcm.PayloadHeader()])
