@@ -94,6 +94,11 @@ struct TopkCtrl {
   // per region: candidates appended (low 32 bits) and, of those, keys whose first radix
   // digit (bits 20..30) is above L's (high 32 bits)
   unsigned long long region_fill[kRegions];
+  // per region, when the streaming pass is asked for it, keys whose first digit is at
+  // least two above L's: region r's count at [16 r], each on a 64-byte line of its own
+  // (atomics on one line serialize whatever their addresses; the region fills above keep
+  // 8 to a line, which measured faster at 7e9 than one line each)
+  alignas(64) uint32_t region_above2[kRegions * 16];
   uint32_t emit_next;         // work queue of the look-back emits (claims in increasing order)
   uint32_t pass;              // the main select's next digit (0, 1, 2; 3: T found)
   uint32_t emit_sub[kQueues * 16];   // the batch emit's sub-queues, one per 64-byte line
@@ -328,7 +333,10 @@ __device__ __forceinline__ void block_scan32(const uint32_t* s_cnt, uint32_t* s_
 __device__ __forceinline__ void init_ctrl(TopkCtrl* __restrict__ ctrl, unsigned long long krem,
                                           unsigned long long nchunks) {
   for (int i = threadIdx.x; i < kBins; i += blockDim.x) ctrl->hist[i] = 0ull;
-  for (int i = threadIdx.x; i < kRegions; i += blockDim.x) ctrl->region_fill[i] = 0ull;
+  for (int i = threadIdx.x; i < kRegions; i += blockDim.x) {
+    ctrl->region_fill[i] = 0ull;
+    ctrl->region_above2[i * 16] = 0u;
+  }
   if (threadIdx.x == 0) ctrl->emit_next = 0u;
   for (int i = threadIdx.x; i < kQueues; i += blockDim.x) ctrl->emit_sub[i * 16] = 0u;
   if (threadIdx.x == 0) ctrl->pass = 0u;
@@ -507,26 +515,31 @@ __device__ __forceinline__ void hist_rand(int64_t n, uint64_t seed, int64_t inde
 //
 // First digit from the counters: every candidate's key is >= L, so when fewer than k of
 // them have a first digit (bits 20..30) above L's, the k-th key's first digit is L's,
-// and its rank among the candidates of that digit is k minus that count.  The select
-// then starts at the second digit (*skip = true; publish also records the prefix, the
-// remaining rank and the next digit for the passes and picks that follow).
+// and its rank among the candidates of that digit is k minus that count.  With the
+// second count (count2: keys whose first digit is at least two above L's), when at least
+// k keys have a digit above L's but fewer than k one two above, the k-th key's first
+// digit is L's plus one, at rank k minus the second count.  Either way the select then
+// starts at the second digit (*skip = true, *prefix = the first digit in place; publish
+// also records the prefix, the remaining rank and the next digit for the passes and picks
+// that follow).
+// ncand, above and above2 are the sums of the region counters.
 __device__ __forceinline__ uint32_t decide_mode(TopkCtrl* __restrict__ ctrl, int64_t ntiles,
-                                                unsigned long long k, bool publish, bool* skip) {
-  unsigned long long ncand = 0, above = 0;
-  for (int i = 0; i < kRegions; ++i) {
-    const unsigned long long f = ctrl->region_fill[i];
-    ncand += f & 0xFFFFFFFFull;
-    above += f >> 32;
-  }
+                                                unsigned long long k, bool publish, int count2,
+                                                unsigned long long ncand, unsigned long long above,
+                                                unsigned long long above2, bool* skip, uint32_t* prefix) {
   const bool full = ctrl->overflow != 0u || ncand < k;
-  *skip = !full && above < k;
+  const uint32_t dL = ctrl->L >> 20;
+  const bool skip1 = !full && above < k;
+  const bool skip2 = !full && !skip1 && count2 != 0 && dL + 1u < (uint32_t)kBins && above2 < k;
+  *skip = skip1 || skip2;
+  *prefix = skip1 ? (dL << 20) : (skip2 ? ((dL + 1u) << 20) : 0u);
   if (publish) {
     ctrl->ncand = full ? 0ull : ncand;
     ctrl->mode = full ? MODE_FULL : MODE_CAND;
     ctrl->nchunks = (unsigned long long)(full ? ntiles : cdiv(ntiles, kUnit));
     if (*skip) {
-      ctrl->prefix = (ctrl->L >> 20) << 20;
-      ctrl->krem = k - above;
+      ctrl->prefix = *prefix;
+      ctrl->krem = k - (skip1 ? above : above2);
       ctrl->pass = 1u;
     }
   }
@@ -622,38 +635,64 @@ __global__ __launch_bounds__(kBlock) void k_hist(TopkCtrl* __restrict__ ctrl,
                                                  int64_t region_cap, const float* __restrict__ full,
                                                  int64_t n, int shift, int bits, uint64_t seed,
                                                  int64_t index_base, int64_t ntiles, unsigned long long decide_k,
-                                                 int final_op, unsigned long long k_main, int fuse_pick, int dyn) {
+                                                 int final_op, unsigned long long k_main, int fuse_pick, int dyn,
+                                                 int count2) {
   __shared__ __align__(16) uint32_t lh[kWaves][kBins];
   __shared__ uint32_t s_rq[kRegions + 1];
   __shared__ uint32_t s_mode, s_pass, s_prefix;
   for (int i = threadIdx.x; i < kWaves * kBins; i += kBlock) (&lh[0][0])[i] = 0u;
-  if (threadIdx.x == 0) {
-    uint32_t pass = 0u, prefix = ctrl->prefix;
+  if (threadIdx.x < kWave) {
+    // wave 0: the region counters, one lane each, for the prefix of the regions' whole-quad
+    // counts and, in the deciding pass, the decision
+    const int lane = (int)threadIdx.x;
+    uint32_t pass = 0u, prefix = 0u, mode = MODE_CAND;
     if (SRC != 0) {
-      bool skip = false;
-      s_mode = decide_k ? decide_mode(ctrl, ntiles, decide_k, blockIdx.x == 0, &skip) : ctrl->mode;
-      if (dyn && decide_k) {
-        // every block decides the same from the counters; block 0 published it
-        pass = skip ? 1u : 0u;
-        prefix = skip ? ((ctrl->L >> 20) << 20) : 0u;
-      } else if (dyn) {
-        pass = ctrl->pass;
+      unsigned long long f = 0ull;
+      uint32_t a2 = 0u;
+      if (lane < kRegions) {
+        f = ctrl->region_fill[lane];
+        a2 = ctrl->region_above2[lane * 16];
       }
-    }
-    s_pass = pass;
-    s_prefix = prefix;
-  }
-  if (SRC != 0 && threadIdx.x < kWave) {
-    // exclusive prefix of the regions' whole-quad counts (candidate mode only reads it)
-    const uint32_t c = threadIdx.x < kRegions ? (uint32_t)ctrl->region_fill[threadIdx.x] >> 2 : 0u;
-    uint32_t inc = c;
+      // exclusive prefix of the regions' whole-quad counts (candidate mode only reads it)
+      const uint32_t c = (uint32_t)f >> 2;
+      uint32_t inc = c;
 #pragma unroll
-    for (int d = 1; d < kRegions; d <<= 1) {
-      const uint32_t o = (uint32_t)__shfl_up((int)inc, d, kWave);
-      if (threadIdx.x >= d) inc += o;
+      for (int d = 1; d < kRegions; d <<= 1) {
+        const uint32_t o = (uint32_t)__shfl_up((int)inc, d, kWave);
+        if (lane >= d) inc += o;
+      }
+      if (lane < kRegions) s_rq[lane] = inc - c;
+      if (lane == kRegions - 1) s_rq[kRegions] = inc;
+      if (decide_k) {
+        const unsigned long long ncand = wave_sum_u64(f & 0xFFFFFFFFull);
+        const unsigned long long above = wave_sum_u64(f >> 32);
+        const unsigned long long above2 = wave_sum_u64((unsigned long long)a2);
+        if (lane == 0) {
+          // every block decides the same from the counters; block 0 publishes it
+          bool skip = false;
+          uint32_t skip_prefix = 0u;
+          mode = decide_mode(ctrl, ntiles, decide_k, blockIdx.x == 0, count2, ncand, above, above2, &skip,
+                             &skip_prefix);
+          if (dyn) {
+            pass = skip ? 1u : 0u;
+            prefix = skip_prefix;
+          } else {
+            prefix = ctrl->prefix;
+          }
+        }
+      } else if (lane == 0) {
+        mode = ctrl->mode;
+        prefix = ctrl->prefix;
+        if (dyn) pass = ctrl->pass;
+      }
+    } else if (lane == 0) {
+      prefix = ctrl->prefix;
     }
-    if (threadIdx.x < kRegions) s_rq[threadIdx.x] = inc - c;
-    if (threadIdx.x == kRegions - 1) s_rq[kRegions] = inc;
+    if (lane == 0) {
+      s_mode = mode;
+      s_pass = pass;
+      s_prefix = prefix;
+    }
   }
   __syncthreads();
   if (dyn) {
@@ -701,7 +740,7 @@ __global__ __launch_bounds__(kBlock) void k_hist(TopkCtrl* __restrict__ ctrl,
 // DEFER: the previous call's recorded corrections of this tile are spread into LDS
 // while the loads are in flight and replace r at their positions before the add.
 // MON: the tile's sum of c^2 in float64 (exact squares, fixed order) goes to mon_c.
-template <bool RAND, bool DEFER, bool MON, bool ALIGNED>
+template <bool RAND, bool DEFER, bool MON, bool ALIGNED, bool COUNT2>
 __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g, float* __restrict__ r,
                                                     int64_t n, TopkCtrl* __restrict__ ctrl,
                                                     uint32_t* __restrict__ tile_start,
@@ -713,6 +752,7 @@ __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g,
                                                     unsigned long long cap, double* __restrict__ mon_c,
                                                     unsigned long long* __restrict__ lb_status) {
   __shared__ uint32_t s_cnt[kRounds * kWaves];
+  __shared__ uint32_t s_a2[kWaves];
   __shared__ double s_mon[MON ? kWaves : 1];
   __shared__ uint32_t s_off[kRounds * kWaves];
   __shared__ uint32_t s_total;
@@ -808,8 +848,11 @@ __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g,
   }
   // candidates (key >= L) and, in the high 16 bits of each wave's count, those whose first
   // radix digit is above L's (key >= A; counts stay below 2^13 per tile, so the packed
-  // scan never carries)
+  // scan never carries); COUNT2: also those whose first digit is two or more above L's
+  // (key >= A2, with L's digit below 2047 at most 2049 << 20), summed per wave
   const uint32_t A = ((L >> 20) + 1u) << 20;
+  const uint32_t A2 = ((L >> 20) + 2u) << 20;
+  uint32_t wa2 = 0u;
   uint32_t nib[kRounds], pre[kRounds];
 #pragma unroll
   for (int j = 0; j < kRounds; ++j) {
@@ -820,12 +863,14 @@ __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g,
       const bool in = e < n;
       b |= ((key[j][m] >= L) && in) ? (1u << m) : 0u;
       wa += (uint32_t)__popcll(ballot((key[j][m] >= A) && in));
+      if (COUNT2) wa2 += (uint32_t)__popcll(ballot((key[j][m] >= A2) && in));
     }
     nib[j] = b;
     uint32_t wc;
     pre[j] = rank_round(b, &wc);
     if (lane == 0) s_cnt[j * kWaves + w] = wc | (wa << 16);
   }
+  if (COUNT2 && lane == 0) s_a2[w] = wa2;
   __syncthreads();
   block_scan32(s_cnt, s_off, &s_total);
   __syncthreads();
@@ -836,6 +881,10 @@ __global__ __launch_bounds__(kBlock) void k_ef_cand(const float* __restrict__ g,
       const uint32_t region = (uint32_t)(tile & (kRegions - 1));
       const uint32_t at = (uint32_t)atomicAdd(&ctrl->region_fill[region],
                                               ((unsigned long long)above << 32) | (unsigned long long)total);
+      if (COUNT2) {
+        const uint32_t above2 = (s_a2[0] + s_a2[1]) + (s_a2[2] + s_a2[3]);
+        if (above2) atomicAdd(&ctrl->region_above2[region * 16], above2);
+      }
       if (at + total > region_cap) {
         atomicOr(&ctrl->overflow, 1u);
         ok = 0u;
@@ -2299,17 +2348,28 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
     const bool fuse = sgrid <= kFusePickGrid;
     hipLaunchKernelGGL((k_hist<0>), sgrid, kBlock, 0, s, ctrl, l.sample, m, (const float*)nullptr,
                        (int64_t)0, (const float*)nullptr, n, shifts[p], widths[p], (uint64_t)0, (int64_t)0,
-                       (int64_t)0, 0ull, op, (unsigned long long)k, fuse ? 1 : 0, 0);
+                       (int64_t)0, 0ull, op, (unsigned long long)k, fuse ? 1 : 0, 0, 0);
     if (!fuse) hipLaunchKernelGGL(k_pick, 1, kBlock, 0, s, ctrl, shifts[p], op, (unsigned long long)k, 0);
   }
 
-  // 3: the streaming pass
+  // 3: the streaming pass.  On small calls the bound's slack, relative to the sample size,
+  // often puts the k-th key one first digit above L's: up to 2^22 elements the pass then
+  // also counts the keys two digits above, so that the pool select can still start at the
+  // second digit (1e6 elements: 63.9 -> 58.7 us a call).  At 6.5M and 16.8M the second
+  // count cost the streaming pass about what the skipped pool pass saved, and at 7e9 the
+  // first count settles the digit
+  const int count2 = n <= (int64_t(1) << 22) ? 1 : 0;
   prof_mark(s, 1);
   // Random-K keys: a lane's quad draws one Philox block when index_base % 4 == 0
-#define GC_CAND_PASS(M, A)                                                                               \
-  hipLaunchKernelGGL((k_ef_cand<RAND, DEFER, M, A>), (unsigned)l.ntiles, kBlock, 0, s, grad, res, n, ctrl,     \
+#define GC_CAND_PASS3(M, A, C)                                                                            \
+  hipLaunchKernelGGL((k_ef_cand<RAND, DEFER, M, A, C>), (unsigned)l.ntiles, kBlock, 0, s, grad, res, n, ctrl,  \
                      l.tile_start, l.tile_count, l.pool_val, l.pool_off, (uint32_t)l.region_cap, l.pool_c,       \
                      select_seed, index_base, pd, cap, mon_c, lb_status)
+#define GC_CAND_PASS(M, A)                                  \
+  do {                                                      \
+    if (count2) GC_CAND_PASS3(M, A, true);                  \
+    else GC_CAND_PASS3(M, A, false);                        \
+  } while (0)
   if (!RAND || (index_base & 3) == 0) {
     if (mon) GC_CAND_PASS(true, true); else GC_CAND_PASS(false, true);
   } else {
@@ -2318,6 +2378,7 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
     }
   }
 #undef GC_CAND_PASS
+#undef GC_CAND_PASS3
   prof_mark(s, 2);
 
   // 4-5: unless the sample was the whole input (T and need already exact, and every
@@ -2331,7 +2392,7 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
       hipLaunchKernelGGL((k_hist<RAND ? 2 : 1>), hgrid, kBlock, 0, s, ctrl, (const uint32_t*)nullptr, (int64_t)0,
                          (const float*)l.pool_val, l.region_cap, (const float*)res, n, shifts[p], widths[p],
                          select_seed, index_base, l.ntiles, p == 0 ? (unsigned long long)k : 0ull,
-                         p == 2 ? 2 : 0, (unsigned long long)k, fuse ? 1 : 0, 1);
+                         p == 2 ? 2 : 0, (unsigned long long)k, fuse ? 1 : 0, 1, count2);
       if (!fuse)
         hipLaunchKernelGGL(k_pick, 1, kBlock, 0, s, ctrl, shifts[p], p == 2 ? 2 : 0, (unsigned long long)k, 1);
     }
