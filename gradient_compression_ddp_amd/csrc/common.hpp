@@ -165,10 +165,12 @@ __device__ __forceinline__ float bitsf(uint32_t u) { return __uint_as_float(u); 
 // Magnitude key: bit pattern with the sign cleared.
 __device__ __forceinline__ uint32_t mag_key(float f) { return fbits(f) & 0x7FFFFFFFu; }
 
-// Monotone map float -> uint32 for the total order -inf < ... < -0 < +0 < ... < +inf.
+// Monotone map float -> uint32 for the total order -inf < ... < -0 < +0 < ... < +inf:
+// a negative pattern has all its bits flipped, any other gets the sign bit set (one xor
+// with the sign spread by an arithmetic shift).
 __device__ __forceinline__ uint32_t ord_enc(float f) {
   const uint32_t b = fbits(f);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
 }
 __device__ __forceinline__ float ord_dec(uint32_t e) {
   return bitsf((e & 0x80000000u) ? (e & 0x7FFFFFFFu) : ~e);
@@ -207,14 +209,16 @@ __device__ __forceinline__ uint32_t seg_max_u32(uint32_t v, int width) {
 // once every 8 lanes hold one value the row mirror (i <-> 15 - i within 16) pairs each
 // with a lane of the other half: the same partial results the xor steps 2 and 3 pair, so
 // the combined values are identical.  All four are DPP operand modifiers, with no LDS
-// traffic; steps 4 and 5 (16 and 32 lanes) shuffle.
+// traffic; steps 4 and 5 (16 and 32 lanes) shuffle.  None of these permutes reads a lane
+// outside its row, so bound_ctrl never applies, and leaving the old value undefined lets
+// the compiler fold each move into the min, max or add that uses it (one instruction a step).
 template <int S>
 __device__ __forceinline__ uint32_t bfly_u32(uint32_t v) {
   static_assert(S >= 0 && S <= 5, "butterfly step");
-  if constexpr (S == 0) return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false);
-  else if constexpr (S == 1) return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false);
-  else if constexpr (S == 2) return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false);
-  else if constexpr (S == 3) return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false);
+  if constexpr (S == 0) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+  else if constexpr (S == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
+  else if constexpr (S == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true);
+  else if constexpr (S == 3) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, true);
   else return (uint32_t)__shfl_xor((int)v, 1 << S, kWave);
 }
 

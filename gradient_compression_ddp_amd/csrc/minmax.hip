@@ -77,12 +77,12 @@ __device__ __forceinline__ float quantize_one(float v, float mn, float scale, fl
   return q;
 }
 
-// Stores a quad's codes and (EF) residuals.
-template <int BITS, bool EF>
+// Stores a quad's codes and (EF) residuals (FULL: the caller knows all four are in range).
+template <int BITS, bool EF, bool FULL = false>
 __device__ __forceinline__ void store_quad(const Quad& qd, int64_t e0, int64_t n, const uint32_t c[4],
                                            const float gh[4], uint8_t* __restrict__ codes,
                                            float* __restrict__ res) {
-  const bool full = e0 + 4 <= n;
+  const bool full = FULL || e0 + 4 <= n;
   if (BITS == 8) {
     if (full) {
       __builtin_nontemporal_store(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
@@ -131,7 +131,7 @@ __device__ __forceinline__ void emit_quad_mixed(const Quad& qd, int64_t e0, int6
 // enough (rsc_ok) that q0 = fl(fl(x - min) * rsc) lies within 2^-13 of fl(fl(x - min) /
 // scale) for codes below 256; when q0 is at least 2^-13 from every half-integer,
 // rint(q0) is the code, otherwise (or for NaN or infinite q0, or !rsc_ok) the quad divides.
-template <int BITS, bool EF>
+template <int BITS, bool EF, bool FULL = false>
 __device__ __forceinline__ void emit_quad(const Quad& qd, int64_t e0, int64_t n, float mn0, float scale,
                                           float rsc, bool rsc_ok, uint8_t* __restrict__ codes,
                                           float* __restrict__ res) {
@@ -156,7 +156,27 @@ __device__ __forceinline__ void emit_quad(const Quad& qd, int64_t e0, int64_t n,
     gh[m] = qq * scale + mn0;
     c[m] = (uint32_t)qq;
   }
-  store_quad<BITS, EF>(qd, e0, n, c, gh, codes, res);
+  store_quad<BITS, EF, FULL>(qd, e0, n, c, gh, codes, res);
+}
+
+// A group's (min, scale) from its reduced ordered-encoded bounds, then the quad's codes
+// and (EF) residuals, and the group's metadata from the group's first lane.
+template <int BITS, bool EF, int LPG_LOG2, bool FULL>
+__device__ __forceinline__ void finish_quad(const Quad& qd, int64_t e0, int64_t n, uint32_t lo, uint32_t hi,
+                                            int lane, uint8_t* __restrict__ codes, float* __restrict__ res,
+                                            float* __restrict__ mins, float* __restrict__ scales) {
+  constexpr float L = (float)((1 << BITS) - 1);
+  const float mn = ord_dec(lo), mx = ord_dec(hi);
+  const float range = mx - mn;
+  const float scale = range >= 0x1p-100f ? div_level_count(range, L, 1.0f / L) : range / L;
+  const bool rsc_ok = scale >= 0x1p-126f && scale < 0x1p126f;
+  const float rsc = __builtin_amdgcn_rcpf(scale);
+  emit_quad<BITS, EF, FULL>(qd, e0, n, mn, scale, rsc, rsc_ok, codes, res);
+  if ((lane & ((1 << LPG_LOG2) - 1)) == 0) {
+    const int64_t g = e0 >> (LPG_LOG2 + 2);
+    mins[g] = mn;
+    scales[g] = scale;
+  }
 }
 
 // One pass for groups of 4..256 elements: a group is 2^LPG_LOG2 = G/4 consecutive
@@ -177,11 +197,37 @@ __global__ __launch_bounds__(kBlock) void k_minmax_small(const float* __restrict
                                                          uint8_t* __restrict__ codes,
                                                          float* __restrict__ mins,
                                                          float* __restrict__ scales) {
-  constexpr float L = (float)((1 << BITS) - 1);
-  constexpr int lpg = 1 << LPG_LOG2;
   const int lane = lane_id();
   const int64_t base = (int64_t)blockIdx.x * kTile;
   Quad qd[kRounds];
+  if (base + kTile <= n) {
+    // the whole tile is in range (a block-uniform branch): straight-line code, no
+    // per-element masks
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      const int64_t e0 = base + j * (kBlock * 4) + threadIdx.x * 4;
+      const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x + e0));
+      qd[j].v[0] = a.x; qd[j].v[1] = a.y; qd[j].v[2] = a.z; qd[j].v[3] = a.w;
+      if (EF) {
+        const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(res + e0));
+        qd[j].v[0] = qd[j].v[0] + b.x; qd[j].v[1] = qd[j].v[1] + b.y;
+        qd[j].v[2] = qd[j].v[2] + b.z; qd[j].v[3] = qd[j].v[3] + b.w;
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) qd[j].ok[m] = true;
+    }
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      const int64_t e0 = base + j * (kBlock * 4) + threadIdx.x * 4;
+      uint32_t e[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) e[m] = ord_enc(qd[j].v[m]);
+      const uint32_t lo = seg_min_c<LPG_LOG2>(min(min(e[0], e[1]), min(e[2], e[3])));
+      const uint32_t hi = seg_max_c<LPG_LOG2>(max(max(e[0], e[1]), max(e[2], e[3])));
+      finish_quad<BITS, EF, LPG_LOG2, true>(qd[j], e0, n, lo, hi, lane, codes, res, mins, scales);
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < kRounds; ++j) {
     const int64_t e0 = base + j * (kBlock * 4) + threadIdx.x * 4;
@@ -207,17 +253,7 @@ __global__ __launch_bounds__(kBlock) void k_minmax_small(const float* __restrict
     lo = seg_min_c<LPG_LOG2>(lo);
     hi = seg_max_c<LPG_LOG2>(hi);
     if (e0 >= n) continue;
-    const float mn = ord_dec(lo), mx = ord_dec(hi);
-    const float range = mx - mn;
-    const float scale = range >= 0x1p-100f ? div_level_count(range, L, 1.0f / L) : range / L;
-    const bool rsc_ok = scale >= 0x1p-126f && scale < 0x1p126f;
-    const float rsc = __builtin_amdgcn_rcpf(scale);
-    emit_quad<BITS, EF>(qd[j], e0, n, mn, scale, rsc, rsc_ok, codes, res);
-    if ((lane & (lpg - 1)) == 0) {
-      const int64_t g = e0 >> (LPG_LOG2 + 2);
-      mins[g] = mn;
-      scales[g] = scale;
-    }
+    finish_quad<BITS, EF, LPG_LOG2, false>(qd[j], e0, n, lo, hi, lane, codes, res, mins, scales);
   }
 }
 

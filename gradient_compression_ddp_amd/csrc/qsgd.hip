@@ -40,6 +40,38 @@ __global__ __launch_bounds__(kBlock) void k_qsgd(const float* __restrict__ x, fl
   const int lane = lane_id();
   const int64_t base = (int64_t)blockIdx.x * kTile;
   float v[kRounds][4];
+  if (base + kTile <= n) {
+    // the whole tile is in range (a block-uniform branch): straight-line code, no
+    // per-element masks
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      const int64_t e0 = base + j * (kBlock * 4) + threadIdx.x * 4;
+      const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(x + e0));
+      v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
+      if (EF) {
+        const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(res + e0));
+        v[j][0] = v[j][0] + b.x; v[j][1] = v[j][1] + b.y; v[j][2] = v[j][2] + b.z; v[j][3] = v[j][3] + b.w;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      const int64_t e0 = base + j * (kBlock * 4) + threadIdx.x * 4;
+      const float nu = sqrtf(seg_tree_sum_c<LPG_LOG2>(quad_sumsq(v[j])));
+      float u[4];
+      uniforms4_t<ALIGNED>(seed, (uint64_t)(index_base + e0), u);
+      int lev[4];
+      float gh[4];
+      qsgd_quad(v[j], nu, s, ys, u, lev, gh);
+      __builtin_nontemporal_store(pack_codes4(lev), reinterpret_cast<uint32_t*>(codes + e0));
+      if (EF) {
+        f32x4 r;
+        r.x = v[j][0] - gh[0]; r.y = v[j][1] - gh[1]; r.z = v[j][2] - gh[2]; r.w = v[j][3] - gh[3];
+        __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(res + e0));
+      }
+      if ((lane & (lpg - 1)) == 0) norms[e0 >> (lpg_log2 + 2)] = nu;
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < kRounds; ++j) {
     const int64_t e0 = base + j * (kBlock * 4) + threadIdx.x * 4;
