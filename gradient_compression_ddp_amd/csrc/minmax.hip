@@ -9,10 +9,12 @@
 // A group of G elements spans G/4 consecutive lanes, so for G <= 256 a group is
 // reduced inside one wave with a lane butterfly and everything happens in one pass:
 // 4 B read (+4 B read/write of the residual) and 1 B (int8) or 0.5 B (int4) written per
-// element, 8 B per group.  That pass runs one 1024-element tile per block (one quad per
-// lane, non-temporal 16-byte loads and stores).  On a 25 MiB bucket, 1, 2 and 4 quads per
-// lane measured 10.9, 12.2 and 13.6 us on MI355X: at this size the launch ramp and load
-// latency dominate, and more resident waves hide them best.
+// element, 8 B per group.  That pass runs one 2048-element tile per block (two quads per
+// lane, non-temporal 16-byte loads and stores); a tile wholly inside the input takes a
+// straight-line path that computes both rounds before its first store.  On a 25 MiB
+// bucket (int8, groups of 64), 1, 2 and 4 quads per lane measured 8.57, 8.38 and 8.69 us
+// on MI355X, against 7.2 us for a kernel that only reads the bucket and writes a byte per
+// element on the same grid shape.
 // Larger groups take a reduce pass with ordered-integer atomics, a per-group finalize and
 // a quantize pass.  A single group (the whole tensor) takes two kernels and no atomics:
 // per-block partial min/max, then a quantize pass in which every block first combines the
@@ -28,8 +30,8 @@ namespace gc {
 namespace {
 
 constexpr int kBlock = 256;
-constexpr int kRounds = 1;                                 // quads per thread per tile
-constexpr int64_t kTile = (int64_t)kBlock * 4 * kRounds;   // 1024 elements
+constexpr int kRounds = 2;                                 // quads per thread per tile
+constexpr int64_t kTile = (int64_t)kBlock * 4 * kRounds;   // 2048 elements
 
 struct Quad {
   float v[4];
@@ -127,17 +129,14 @@ __device__ __forceinline__ void emit_quad_mixed(const Quad& qd, int64_t e0, int6
   store_quad<BITS, EF>(qd, e0, n, c, gh, codes, res);
 }
 
-// Codes (and residuals) of a quad sharing one (min, scale).  rsc estimates 1/scale well
+// Codes (and g_hat) of a quad sharing one (min, scale).  rsc estimates 1/scale well
 // enough (rsc_ok) that q0 = fl(fl(x - min) * rsc) lies within 2^-13 of fl(fl(x - min) /
 // scale) for codes below 256; when q0 is at least 2^-13 from every half-integer,
 // rint(q0) is the code, otherwise (or for NaN or infinite q0, or !rsc_ok) the quad divides.
-template <int BITS, bool EF, bool FULL = false>
-__device__ __forceinline__ void emit_quad(const Quad& qd, int64_t e0, int64_t n, float mn0, float scale,
-                                          float rsc, bool rsc_ok, uint8_t* __restrict__ codes,
-                                          float* __restrict__ res) {
+template <int BITS>
+__device__ __forceinline__ void quant_quad(const Quad& qd, float mn0, float scale, float rsc, bool rsc_ok,
+                                           uint32_t c[4], float gh[4]) {
   constexpr float L = (float)((1 << BITS) - 1);
-  uint32_t c[4];
-  float gh[4];
   float q[4];
   bool slow = !rsc_ok;
 #pragma unroll
@@ -156,7 +155,19 @@ __device__ __forceinline__ void emit_quad(const Quad& qd, int64_t e0, int64_t n,
     gh[m] = qq * scale + mn0;
     c[m] = (uint32_t)qq;
   }
-  store_quad<BITS, EF, FULL>(qd, e0, n, c, gh, codes, res);
+}
+
+// A group's min and scale from its reduced ordered-encoded bounds, and the reciprocal
+// estimate of the scale with its validity.
+template <int BITS>
+__device__ __forceinline__ void group_params(uint32_t lo, uint32_t hi, float* mn, float* scale, float* rsc,
+                                             bool* rsc_ok) {
+  constexpr float L = (float)((1 << BITS) - 1);
+  *mn = ord_dec(lo);
+  const float range = ord_dec(hi) - *mn;
+  *scale = range >= 0x1p-100f ? div_level_count(range, L, 1.0f / L) : range / L;
+  *rsc_ok = *scale >= 0x1p-126f && *scale < 0x1p126f;
+  *rsc = __builtin_amdgcn_rcpf(*scale);
 }
 
 // A group's (min, scale) from its reduced ordered-encoded bounds, then the quad's codes
@@ -165,13 +176,13 @@ template <int BITS, bool EF, int LPG_LOG2, bool FULL>
 __device__ __forceinline__ void finish_quad(const Quad& qd, int64_t e0, int64_t n, uint32_t lo, uint32_t hi,
                                             int lane, uint8_t* __restrict__ codes, float* __restrict__ res,
                                             float* __restrict__ mins, float* __restrict__ scales) {
-  constexpr float L = (float)((1 << BITS) - 1);
-  const float mn = ord_dec(lo), mx = ord_dec(hi);
-  const float range = mx - mn;
-  const float scale = range >= 0x1p-100f ? div_level_count(range, L, 1.0f / L) : range / L;
-  const bool rsc_ok = scale >= 0x1p-126f && scale < 0x1p126f;
-  const float rsc = __builtin_amdgcn_rcpf(scale);
-  emit_quad<BITS, EF, FULL>(qd, e0, n, mn, scale, rsc, rsc_ok, codes, res);
+  float mn, scale, rsc;
+  bool rsc_ok;
+  group_params<BITS>(lo, hi, &mn, &scale, &rsc, &rsc_ok);
+  uint32_t c[4];
+  float gh[4];
+  quant_quad<BITS>(qd, mn, scale, rsc, rsc_ok, c, gh);
+  store_quad<BITS, EF, FULL>(qd, e0, n, c, gh, codes, res);
   if ((lane & ((1 << LPG_LOG2) - 1)) == 0) {
     const int64_t g = e0 >> (LPG_LOG2 + 2);
     mins[g] = mn;
@@ -216,15 +227,31 @@ __global__ __launch_bounds__(kBlock) void k_minmax_small(const float* __restrict
 #pragma unroll
       for (int m = 0; m < 4; ++m) qd[j].ok[m] = true;
     }
+    // every round's results before the first store: the wait for a later round's load
+    // would otherwise also wait for the earlier stores (the counter retires in order)
+    uint32_t c[kRounds][4];
+    float gh[kRounds][4], gmn[kRounds], gsc[kRounds];
 #pragma unroll
     for (int j = 0; j < kRounds; ++j) {
-      const int64_t e0 = base + j * (kBlock * 4) + threadIdx.x * 4;
       uint32_t e[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) e[m] = ord_enc(qd[j].v[m]);
       const uint32_t lo = seg_min_c<LPG_LOG2>(min(min(e[0], e[1]), min(e[2], e[3])));
       const uint32_t hi = seg_max_c<LPG_LOG2>(max(max(e[0], e[1]), max(e[2], e[3])));
-      finish_quad<BITS, EF, LPG_LOG2, true>(qd[j], e0, n, lo, hi, lane, codes, res, mins, scales);
+      float rsc;
+      bool rsc_ok;
+      group_params<BITS>(lo, hi, &gmn[j], &gsc[j], &rsc, &rsc_ok);
+      quant_quad<BITS>(qd[j], gmn[j], gsc[j], rsc, rsc_ok, c[j], gh[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      const int64_t e0 = base + j * (kBlock * 4) + threadIdx.x * 4;
+      store_quad<BITS, EF, true>(qd[j], e0, n, c[j], gh[j], codes, res);
+      if ((lane & ((1 << LPG_LOG2) - 1)) == 0) {
+        const int64_t g = e0 >> (LPG_LOG2 + 2);
+        mins[g] = gmn[j];
+        scales[g] = gsc[j];
+      }
     }
     return;
   }
@@ -446,7 +473,10 @@ __global__ __launch_bounds__(kBlock) void k_minmax_tensor_quant(const float* __r
   for (int64_t q = (int64_t)blockIdx.x * kBlock + threadIdx.x; q < nquads; q += (int64_t)gridDim.x * kBlock) {
     const int64_t e0 = q << 2;
     const Quad qd = load_quad<EF>(x, res, e0, n);
-    emit_quad<BITS, EF>(qd, e0, n, mn, scale, rsc, rsc_ok, codes, res);
+    uint32_t c[4];
+    float gh[4];
+    quant_quad<BITS>(qd, mn, scale, rsc, rsc_ok, c, gh);
+    store_quad<BITS, EF>(qd, e0, n, c, gh, codes, res);
   }
 }
 

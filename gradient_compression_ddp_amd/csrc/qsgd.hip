@@ -15,7 +15,8 @@
 // multiply-adds, each issued at the full rate on gfx950) and the level decision, taken from
 // a reciprocal estimate except near its boundaries (qsgd_core.hpp); the group's butterfly
 // is compile-time (DPP steps for up to 16 lanes).  On a 25 MiB bucket two quads per lane
-// measured fastest (12.9 us against 14.8 with one and 14.4 with four, with the divisions).
+// measured fastest (9.88 us against 9.94 with one and 11.1 with four); a tile wholly
+// inside the input computes both rounds before its first store (10.42 -> 9.88 us).
 #include "common.hpp"
 #include "internal.hpp"
 #include "qsgd_core.hpp"
@@ -53,22 +54,32 @@ __global__ __launch_bounds__(kBlock) void k_qsgd(const float* __restrict__ x, fl
         v[j][0] = v[j][0] + b.x; v[j][1] = v[j][1] + b.y; v[j][2] = v[j][2] + b.z; v[j][3] = v[j][3] + b.w;
       }
     }
+    // every round's results before the first store: the wait for a later round's load
+    // would otherwise also wait for the earlier stores (the counter retires in order)
+    uint32_t cw[kRounds];
+    float nus[kRounds];
+    f32x4 rr[kRounds];
 #pragma unroll
     for (int j = 0; j < kRounds; ++j) {
       const int64_t e0 = base + j * (kBlock * 4) + threadIdx.x * 4;
-      const float nu = sqrtf(seg_tree_sum_c<LPG_LOG2>(quad_sumsq(v[j])));
+      nus[j] = sqrtf(seg_tree_sum_c<LPG_LOG2>(quad_sumsq(v[j])));
       float u[4];
       uniforms4_t<ALIGNED>(seed, (uint64_t)(index_base + e0), u);
       int lev[4];
       float gh[4];
-      qsgd_quad(v[j], nu, s, ys, u, lev, gh);
-      __builtin_nontemporal_store(pack_codes4(lev), reinterpret_cast<uint32_t*>(codes + e0));
+      qsgd_quad(v[j], nus[j], s, ys, u, lev, gh);
+      cw[j] = pack_codes4(lev);
       if (EF) {
-        f32x4 r;
-        r.x = v[j][0] - gh[0]; r.y = v[j][1] - gh[1]; r.z = v[j][2] - gh[2]; r.w = v[j][3] - gh[3];
-        __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(res + e0));
+        rr[j].x = v[j][0] - gh[0]; rr[j].y = v[j][1] - gh[1];
+        rr[j].z = v[j][2] - gh[2]; rr[j].w = v[j][3] - gh[3];
       }
-      if ((lane & (lpg - 1)) == 0) norms[e0 >> (lpg_log2 + 2)] = nu;
+    }
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      const int64_t e0 = base + j * (kBlock * 4) + threadIdx.x * 4;
+      __builtin_nontemporal_store(cw[j], reinterpret_cast<uint32_t*>(codes + e0));
+      if (EF) __builtin_nontemporal_store(rr[j], reinterpret_cast<f32x4*>(res + e0));
+      if ((lane & (lpg - 1)) == 0) norms[e0 >> (lpg_log2 + 2)] = nus[j];
     }
     return;
   }
