@@ -133,6 +133,10 @@ __device__ __forceinline__ void emit_quad_mixed(const Quad& qd, int64_t e0, int6
 // enough (rsc_ok) that q0 = fl(fl(x - min) * rsc) lies within 2^-13 of fl(fl(x - min) /
 // scale) for codes below 256; when q0 is at least 2^-13 from every half-integer,
 // rint(q0) is the code, otherwise (or for NaN or infinite q0, or !rsc_ok) the quad divides.
+// The estimate needs no clamp: with rsc_ok every element of the group is finite and in
+// [min, max], so 0 <= q0 <= fl(max - min) * rsc * (1 + 2^-24) < L * (1 + 2^-22), whose
+// rounding is at most L.  (Elements outside the group, the padding of a partial quad, are
+// never stored.)  The divided codes are clamped to [0, L], and are 0 when scale == 0.
 template <int BITS>
 __device__ __forceinline__ void quant_quad(const Quad& qd, float mn0, float scale, float rsc, bool rsc_ok,
                                            uint32_t c[4], float gh[4]) {
@@ -145,15 +149,15 @@ __device__ __forceinline__ void quant_quad(const Quad& qd, float mn0, float scal
     q[m] = rintf(q0);
     slow |= !(fabsf(q0 - q[m]) <= 0.5f - 0x1p-13f);
   }
-  if (slow && scale != 0.f) {
+  if (slow) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) q[m] = rintf((qd.v[m] - mn0) / scale);
+    for (int m = 0; m < 4; ++m)
+      q[m] = scale != 0.f ? fminf(fmaxf(rintf((qd.v[m] - mn0) / scale), 0.f), L) : 0.f;
   }
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const float qq = scale != 0.f ? fminf(fmaxf(q[m], 0.f), L) : 0.f;
-    gh[m] = qq * scale + mn0;
-    c[m] = (uint32_t)qq;
+    gh[m] = q[m] * scale + mn0;
+    c[m] = (uint32_t)q[m];
   }
 }
 

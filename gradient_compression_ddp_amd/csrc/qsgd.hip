@@ -54,6 +54,17 @@ __global__ __launch_bounds__(kBlock) void k_qsgd(const float* __restrict__ x, fl
         v[j][0] = v[j][0] + b.x; v[j][1] = v[j][1] + b.y; v[j][2] = v[j][2] + b.z; v[j][3] = v[j][3] + b.w;
       }
     }
+    // the draws need no loaded data: they run while the loads are in flight
+    float u[kRounds][4];
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j)
+      uniforms4_t<ALIGNED>(seed, (uint64_t)(index_base + base + j * (kBlock * 4) + threadIdx.x * 4), u[j]);
+    // keep the compiler from sinking the second round's draw into the code after the
+    // first round's wait (an empty asm that takes the draws as operands pins them here)
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) asm volatile("" : "+v"(u[j][m]));
     // every round's results before the first store: the wait for a later round's load
     // would otherwise also wait for the earlier stores (the counter retires in order)
     uint32_t cw[kRounds];
@@ -61,13 +72,10 @@ __global__ __launch_bounds__(kBlock) void k_qsgd(const float* __restrict__ x, fl
     f32x4 rr[kRounds];
 #pragma unroll
     for (int j = 0; j < kRounds; ++j) {
-      const int64_t e0 = base + j * (kBlock * 4) + threadIdx.x * 4;
       nus[j] = sqrtf(seg_tree_sum_c<LPG_LOG2>(quad_sumsq(v[j])));
-      float u[4];
-      uniforms4_t<ALIGNED>(seed, (uint64_t)(index_base + e0), u);
       int lev[4];
       float gh[4];
-      qsgd_quad(v[j], nus[j], s, ys, u, lev, gh);
+      qsgd_quad(v[j], nus[j], s, ys, u[j], lev, gh);
       cw[j] = pack_codes4(lev);
       if (EF) {
         rr[j].x = v[j][0] - gh[0]; rr[j].y = v[j][1] - gh[1];
