@@ -17,19 +17,25 @@ namespace gc {
 // floor(u) = floor(u') and (U < p) = (U < p'); a quad with any element outside that band
 // (or nu outside the range, or nu = 0) divides.  One reciprocal per quad replaces four
 // IEEE divisions on almost every quad.
+//
+// When the estimate is taken, nu lies in that range (so nu > 0), and the level needs no
+// clamp to s: |v| <= nu up to a few ulps, so u' <= s * (1 + 2^-21), and floor(u') = s
+// would leave p' < 2^-13, which divides.  A taken element is also nonzero and not NaN
+// (p' >= 2^-13), so its sign bit is the sign test v < 0; the divided path keeps both the
+// nu > 0 test and the clamp (a NaN or zero element, or nu = 0, gives level 0, and -0 as
+// well as 0 converts to code 0; -Inf gives -s through the sign bit, as v < 0 does).
 __device__ __forceinline__ void qsgd_quad(const float v[4], float nu, float s, float ys, const float u[4],
                                           int lev[4], float gh[4]) {
   const float rnu = __builtin_amdgcn_rcpf(nu);
   bool slow = !(nu >= 0x1p-126f && nu < 0x1p126f);
-  float lf[4], up[4];
+  float level[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const float uu = (fabsf(v[m]) * rnu) * s;
     const float l = floorf(uu);
     const float p = uu - l;
     slow |= !(p >= 0x1p-13f && p <= 1.0f - 0x1p-13f && fabsf(u[m] - p) >= 0x1p-13f);
-    lf[m] = l;
-    up[m] = u[m] < p ? 1.f : 0.f;
+    level[m] = l + (u[m] < p ? 1.f : 0.f);
   }
   if (slow) {
 #pragma unroll
@@ -41,15 +47,13 @@ __device__ __forceinline__ void qsgd_quad(const float v[4], float nu, float s, f
         l = floorf(uu);
         up1 = u[m] < (uu - l) ? 1.f : 0.f;
       }
-      lf[m] = l;
-      up[m] = up1;
+      level[m] = nu > 0.f ? fminf(l + up1, s) : 0.f;
     }
   }
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const float level = nu > 0.f ? fminf(lf[m] + up[m], s) : 0.f;
-    lev[m] = v[m] < 0.f ? -(int)level : (int)level;
-    gh[m] = nu * level;   // t, divided below
+    lev[m] = (int)__builtin_copysignf(level[m], v[m]);   // level 0 gives 0 for either sign
+    gh[m] = nu * level[m];   // t, divided below
   }
   // with nu >= 2^-100 every t = fl(nu * level) is 0 or >= 2^-100: div_level_count's domain
   float mag[4];
