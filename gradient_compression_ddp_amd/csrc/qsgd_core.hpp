@@ -11,9 +11,10 @@ namespace gc {
 // ys = fl(1/s); the division by s goes through div_level_count (the same quotient).
 //
 // The level needs floor(u) and the decision U < p of u = fl(fl(|v| / nu) * s).  An
-// estimate u' = fl(fl(|v| * rnu) * s) with rnu = v_rcp_f32(nu) (within 1 ulp of 1/nu, for
-// nu in [2^-126, 2^126)) lies within u * (2^-22 + 2^-23) < 2^-14 of u, since u <= s <= 127
-// (|v| <= nu).  So when p' = u' - floor(u') is at least 2^-13 from 0, from 1 and from U,
+// estimate u' = fl(|v| * fl(rnu * s)) with rnu = v_rcp_f32(nu) (within 1 ulp of 1/nu, for
+// nu in [2^-126, 2^126)) carries three relative errors (2^-23, 2^-24, 2^-24) against the
+// two roundings of u (2^-24 each), so it lies within (|v| / nu) * s * (2^-22 + 2^-23) <
+// 2^-14 of u, since s <= 127 and |v| <= nu up to a few ulps.  So when p' = u' - floor(u') is at least 2^-13 from 0, from 1 and from U,
 // floor(u) = floor(u') and (U < p) = (U < p'); a quad with any element outside that band
 // (or nu outside the range, or nu = 0) divides.  One reciprocal per quad replaces four
 // IEEE divisions on almost every quad.
@@ -26,12 +27,12 @@ namespace gc {
 // well as 0 converts to code 0; -Inf gives -s through the sign bit, as v < 0 does).
 __device__ __forceinline__ void qsgd_quad(const float v[4], float nu, float s, float ys, const float u[4],
                                           int lev[4], float gh[4]) {
-  const float rnu = __builtin_amdgcn_rcpf(nu);
+  const float rnus = __builtin_amdgcn_rcpf(nu) * s;
   bool slow = !(nu >= 0x1p-126f && nu < 0x1p126f);
   float level[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const float uu = (fabsf(v[m]) * rnu) * s;
+    const float uu = fabsf(v[m]) * rnus;
     const float l = floorf(uu);
     const float p = uu - l;
     slow |= !(p >= 0x1p-13f && p <= 1.0f - 0x1p-13f && fabsf(u[m] - p) >= 0x1p-13f);
