@@ -2199,6 +2199,71 @@ __global__ __launch_bounds__(kBlock) void k_qsgd_kept(const float* __restrict__ 
   }
 }
 
+// The same for the deferred record without the norm monitor, as a streaming pass: each
+// quad's residuals v - g_hat go to the record as one 16-byte store (four consecutive kept
+// entries never straddle a 64-entry chunk of the record), so no LDS pass-through and no
+// barrier is needed.  One 2048-entry tile per block (two quads per lane, the draws issued
+// under the loads, every round computed before the first store), as the bucket QSGD.
+template <int LPG_LOG2>
+__global__ __launch_bounds__(kBlock) void k_qsgd_kept_rec(const float* __restrict__ vals, int64_t k, float s,
+                                                          float ys, uint64_t seed, int8_t* __restrict__ codes,
+                                                          float* __restrict__ norms, Pending pd) {
+  constexpr int R = 2;
+  constexpr int lpg = 1 << LPG_LOG2;
+  const int lane = lane_id();
+  const int64_t base = (int64_t)blockIdx.x * (kBlock * 4 * R);
+  float v[R][4];
+  float u[R][4];
+  const bool whole = base + kBlock * 4 * R <= k;   // block-uniform
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int64_t e0 = base + j * (kBlock * 4) + threadIdx.x * 4;
+    if (whole) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(vals + e0);
+      v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) v[j][m] = e0 + m < k ? vals[e0 + m] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    uniforms4_t<true>(seed, (uint64_t)(base + j * (kBlock * 4) + threadIdx.x * 4), u[j]);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) asm volatile("" : "+v"(u[j][m]));
+  }
+  uint32_t cw[R];
+  float nus[R];
+  float rv[R][4];
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    nus[j] = sqrtf(seg_tree_sum_c<LPG_LOG2>(quad_sumsq(v[j])));
+    int lev[4];
+    float gh[4];
+    qsgd_quad(v[j], nus[j], s, ys, u[j], lev, gh);
+    cw[j] = pack_codes4(lev);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) rv[j][m] = v[j][m] - gh[m];
+  }
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const int64_t e0 = base + j * (kBlock * 4) + threadIdx.x * 4;
+    if (whole || e0 + 4 <= k) {
+      *reinterpret_cast<uint32_t*>(codes + e0) = cw[j];
+      *reinterpret_cast<f32x4*>(pend_val(pd.chunks, (unsigned long long)e0)) =
+          f32x4{rv[j][0], rv[j][1], rv[j][2], rv[j][3]};
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        if (e0 + m < k) {
+          codes[e0 + m] = (int8_t)(uint8_t)(cw[j] >> (8 * m));
+          *pend_val(pd.chunks, (unsigned long long)(e0 + m)) = rv[j][m];
+        }
+    }
+    if ((lane & (lpg - 1)) == 0 && e0 < k) norms[e0 >> (LPG_LOG2 + 2)] = nus[j];
+  }
+}
+
 // ---- norm monitor: float64 sums of squares in a fixed order --------------------------
 // Sum of v^2 over each kKeptChunk entries of v (the kept values of pure selection).
 __global__ __launch_bounds__(kBlock) void k_sq_chunks(const float* __restrict__ v, int64_t len,
@@ -2469,7 +2534,27 @@ hipError_t launch_select(const float* grad, float* res, int64_t n, int64_t k, in
     case 5: GC_QSGD_KEPT(M, 5); break;        \
     default: GC_QSGD_KEPT(M, 6); break;       \
   }
-    if (mon) { GC_QSGD_KEPT_W(true) } else { GC_QSGD_KEPT_W(false) }
+    if (DEFER && !mon) {
+      // the record takes the residuals in kept order: the streaming form
+      const unsigned rgrid = (unsigned)cdiv(k, (int64_t)kBlock * 8);
+#define GC_QSGD_REC(W)                                                                                  \
+  hipLaunchKernelGGL((k_qsgd_kept_rec<W>), rgrid, kBlock, 0, s, (const float*)vals, k, (float)qsgd_levels, \
+                     1.0f / (float)qsgd_levels, qsgd_seed, out_codes, out_norms, pd)
+      switch (lpg_log2) {
+        case 0: GC_QSGD_REC(0); break;
+        case 1: GC_QSGD_REC(1); break;
+        case 2: GC_QSGD_REC(2); break;
+        case 3: GC_QSGD_REC(3); break;
+        case 4: GC_QSGD_REC(4); break;
+        case 5: GC_QSGD_REC(5); break;
+        default: GC_QSGD_REC(6); break;
+      }
+#undef GC_QSGD_REC
+    } else if (mon) {
+      GC_QSGD_KEPT_W(true)
+    } else {
+      GC_QSGD_KEPT_W(false)
+    }
 #undef GC_QSGD_KEPT_W
 #undef GC_QSGD_KEPT
   } else if (mon) {
