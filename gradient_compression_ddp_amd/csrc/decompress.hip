@@ -305,7 +305,14 @@ __device__ __forceinline__ void decode16(const uint32_t cw[4], float m0, float m
     float t[kEpl];
 #pragma unroll
     for (int i = 0; i < kEpl; ++i) t[i] = m0 * (float)(int)(int8_t)(uint8_t)(cw[i >> 2] >> (8 * (i & 3)));
-    if (m0 >= 0x1p-100f) {
+    if (m0 >= 0x1p-100f && m0 <= 0x1p120f) {
+      // every t = fl(nu * code), |code| <= 127, is finite: no infinite-t select
+#pragma unroll
+      for (int i = 0; i < kEpl; ++i) {
+        const float q0 = t[i] * ys;
+        v[i] = __builtin_fmaf(__builtin_fmaf(-q0, s, t[i]), ys, q0);
+      }
+    } else if (m0 >= 0x1p-100f) {
 #pragma unroll
       for (int i = 0; i < kEpl; ++i) {
         const float q0 = t[i] * ys;
