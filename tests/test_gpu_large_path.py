@@ -95,6 +95,58 @@ def test_topk_deferred_with_qsgd_three_steps(gc):
     assert_bits_equal(host(rd), r, "flushed residual")
 
 
+def test_topk_deferred_qsgd_without_values_three_steps(gc):
+    # the call the metric path makes, at a size that takes the batch emit: no kept values
+    # requested (they only pass through the staging array to the streaming QSGD pass);
+    # codes, norms and the flushed residual must be the oracle's
+    import torch
+    n, k = N_LARGE, N_LARGE // 100
+    print(f"[large] deferred qsgd, no values n={n} k={k}", flush=True)
+    g, r = inputs(n, 47)
+    rd = dev(r)
+    pend = gc.pending_record(n, k, torch.device("cuda:0"))
+    ws = workspace(gc, gc.OP_EF_TOPK, n, k, 127)
+    for step in (1, 2, 3):
+        gs = (g * F32(1.0 + 0.25 * step)).astype(F32)
+        o_idx, o_codes, o_norms, o_res, _ = oracle.ef_topk_qsgd(gs, r, k, levels=127, group=64, seed=700 + step)
+        idx, codes, norms, val = gc.ef_topk_deferred(dev(gs), rd, k, pend, qsgd_levels=127, qsgd_group=64,
+                                                     qsgd_seed=700 + step, want_values=False, workspace=ws)
+        assert val is None
+        assert mode_of(ws) == 0
+        assert_bits_equal(host(idx), o_idx, f"step {step} idx")
+        assert_bits_equal(host(codes), o_codes, f"step {step} codes")
+        assert_bits_equal(host(norms), o_norms, f"step {step} norms")
+        r = o_res
+    gc.ef_flush(rd, pend)
+    assert_bits_equal(host(rd), r, "flushed residual")
+
+
+def test_topk_deferred_qsgd_without_values_fallback(gc):
+    # the same call when the selection falls back to the full c (the fallback emit stages
+    # the kept values for the streaming QSGD pass)
+    import torch
+    n, k = N_LARGE, N_LARGE // 5
+    print(f"[large] deferred qsgd fallback, no values n={n} k={k}", flush=True)
+    g = np.full(n, -0.5, F32)
+    g[::1001] = 0.75
+    g[::7919] = 1.25
+    r = np.zeros(n, F32)
+    rd = dev(r)
+    pend = gc.pending_record(n, k, torch.device("cuda:0"))
+    ws = workspace(gc, gc.OP_EF_TOPK, n, k, 127)
+    for step in (1, 2):
+        o_idx, o_codes, o_norms, o_res, _ = oracle.ef_topk_qsgd(g, r, k, levels=127, group=64, seed=900 + step)
+        idx, codes, norms, val = gc.ef_topk_deferred(dev(g), rd, k, pend, qsgd_levels=127, qsgd_group=64,
+                                                     qsgd_seed=900 + step, want_values=False, workspace=ws)
+        assert mode_of(ws) == 1
+        assert_bits_equal(host(idx), o_idx, f"step {step} idx")
+        assert_bits_equal(host(codes), o_codes, f"step {step} codes")
+        assert_bits_equal(host(norms), o_norms, f"step {step} norms")
+        r = o_res
+    gc.ef_flush(rd, pend)
+    assert_bits_equal(host(rd), r, "flushed residual")
+
+
 def test_topk_forced_fallback(gc):
     # a huge tie block defeats the sampled bound: every element is a candidate, the pool
     # overflows, and the selection and the emit run over the full c
