@@ -71,6 +71,14 @@ def test_deferred_sizes_three_steps(gc, n, k):
     pure_steps(gc, grads, k)
 
 
+def test_deferred_forced_fallback_small_call(gc):
+    # the same at 2^20 elements, where the one-block select runs over the full c
+    n = 1 << 20
+    g = np.full(n, 1.0, F32)
+    g[300_000:300_007] = 2.0
+    pure_steps(gc, [g, g], 100_000)
+
+
 def test_deferred_forced_fallback(gc):
     # a huge tie block: the candidates overflow and the exact fallback records the kept
     # offsets and per-tile counts itself

@@ -74,6 +74,15 @@ def test_randk_zero_k_and_seed_changes_choice(gc):
     assert not np.array_equal(host(a), host(b))
 
 
+@pytest.mark.parametrize("n,k_minus", [(1 << 20, 0), (1 << 20, 2), ((1 << 21) - 5, 1)])
+def test_randk_k_close_to_n_small_call(gc, n, k_minus):
+    # k close to n on calls small enough for the one-block select: whether the candidates
+    # hold the answer or the selection falls back to all n keys, the result is the oracle's
+    k = n - k_minus
+    g = workloads.bucket(n, seed=19)
+    check_randk(gc, g, np.zeros(n, F32), k, seed=3 + k_minus)
+
+
 @pytest.mark.parametrize("seed,k_minus", [(1, 0), (8, 1), (7, 0), (7, 3000)])
 def test_randk_k_close_to_n(gc, seed, k_minus):
     # k close to n at n = 3e6: the sampled bound L is at or near the smallest sample key,
