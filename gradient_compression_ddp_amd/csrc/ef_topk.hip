@@ -576,16 +576,13 @@ __device__ __forceinline__ void pick_body(TopkCtrl* __restrict__ ctrl, int shift
     c[i] = ctrl->hist[hi_bin - i];
     local += c[i];
   }
-  s_sum[t] = local;
+  // exclusive prefix of the chunk sums in thread order (= descending bins): a wave scan,
+  // then the sums of the waves before (two barriers, not two per doubling step)
+  const unsigned long long inc = wave_incl_scan_u64(local);
+  if (lane_id() == kWave - 1) s_sum[t / kWave] = inc;
   __syncthreads();
-  // exclusive prefix of the chunk sums in thread order (= descending bins)
-  for (int d = 1; d < kBlock; d <<= 1) {
-    const unsigned long long o = t >= d ? s_sum[t - d] : 0ull;
-    __syncthreads();
-    s_sum[t] += o;
-    __syncthreads();
-  }
-  unsigned long long before = s_sum[t] - local;
+  unsigned long long before = inc - local;
+  for (int v = 0; v < t / kWave; ++v) before += s_sum[v];
   const unsigned long long krem = ctrl->krem;
   __syncthreads();
 #pragma unroll
