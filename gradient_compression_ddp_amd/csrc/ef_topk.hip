@@ -59,7 +59,9 @@ constexpr int64_t kTile = (int64_t)kBlock * 4 * kRounds;   // 4096 elements
 constexpr int kRegions = 32;                 // candidate-pool regions (tile % 32)
 // At 7e9 elements a draw of 2^20 points (about ten random 64-byte sectors each, with the
 // record lookup) took 0.10 ms; 2^19 points took the sample and its select 0.145 -> 0.100 ms
-// while the looser bound grew the pool passes and the emit by about 0.015 ms.
+// while the looser bound grew the pool passes and the emit by about 0.015 ms.  2^18 points
+// took it to 0.06 ms, but the after-pass grew by 0.04 ms and the streaming pass, writing
+// more candidates, by 0.1-0.2 ms (step medians 15.18-15.20 against 15.02-15.13 ms).
 constexpr int kSampleMax = 1 << 19;
 constexpr int kScanChunk = 1024;             // items per block in the multi-block scan
 constexpr int kBins = 2048;
