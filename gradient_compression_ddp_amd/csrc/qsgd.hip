@@ -70,9 +70,25 @@ __global__ __launch_bounds__(kBlock) void k_qsgd(const float* __restrict__ x, fl
     uint32_t cw[kRounds];
     float nus[kRounds];
     f32x4 rr[kRounds];
+    {
+      float ss[kRounds];
+#pragma unroll
+      for (int j = 0; j < kRounds; ++j) ss[j] = seg_tree_sum_c<LPG_LOG2>(quad_sumsq(v[j]));
+      if constexpr (LPG_LOG2 >= 1 && kRounds == 2) {
+        // both lanes of a pair hold both rounds' group sums: each takes one root, and the
+        // pair swaps them (one correctly rounded square root per lane instead of two)
+        const bool odd = (lane & 1) != 0;
+        const float mine = sqrtf(odd ? ss[1] : ss[0]);
+        const float other = __uint_as_float(bfly_u32<0>(__float_as_uint(mine)));
+        nus[0] = odd ? other : mine;
+        nus[1] = odd ? mine : other;
+      } else {
+#pragma unroll
+        for (int j = 0; j < kRounds; ++j) nus[j] = sqrtf(ss[j]);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < kRounds; ++j) {
-      nus[j] = sqrtf(seg_tree_sum_c<LPG_LOG2>(quad_sumsq(v[j])));
       int lev[4];
       float gh[4];
       qsgd_quad(v[j], nus[j], s, ys, u[j], lev, gh);

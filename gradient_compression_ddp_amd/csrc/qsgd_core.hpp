@@ -10,21 +10,23 @@ namespace gc {
 
 // ys = fl(1/s); the division by s goes through div_level_count (the same quotient).
 //
-// The level needs floor(u) and the decision U < p of u = fl(fl(|v| / nu) * s).  An
-// estimate u' = fl(|v| * fl(rnu * s)) with rnu = v_rcp_f32(nu) (within 1 ulp of 1/nu, for
-// nu in [2^-126, 2^126)) carries three relative errors (2^-23, 2^-24, 2^-24) against the
-// two roundings of u (2^-24 each), so it lies within (|v| / nu) * s * (2^-22 + 2^-23) <
-// 2^-14 of u, since s <= 127 and |v| <= nu up to a few ulps.  So when p' = u' - floor(u') is at least 2^-13 from 0, from 1 and from U,
-// floor(u) = floor(u') and (U < p) = (U < p'); a quad with any element outside that band
-// (or nu outside the range, or nu = 0) divides.  One reciprocal per quad replaces four
-// IEEE divisions on almost every quad.
+// The level l + (U < p), with u = fl(fl(|v| / nu) * s), l = floor(u) and p = u - l, equals
+// ceil(u - U) for U in [0, 1): U < p puts u - U in (l, l + 1), U >= p puts it in (l - 1, l].
+// An estimate u' = fl(|v| * fl(rnu * s)) with rnu = v_rcp_f32(nu) (within 1 ulp of 1/nu,
+// for nu in [2^-126, 2^126)) carries three relative errors (2^-23, 2^-24, 2^-24) against
+// the two roundings of u (2^-24 each), so it lies within (|v| / nu) * s * (2^-22 + 2^-23)
+// < 2^-14 of u, since s <= 127 and |v| <= nu up to a few ulps; d' = fl(u' - U) adds at most
+// 2^-18.  So when ceil(d') - d' is at least 2^-13 from 0 and from 1, ceil(u - U) =
+// ceil(d'); a quad with any element outside that band (or nu outside the range, or nu =
+// 0) divides.  One reciprocal per quad replaces four IEEE divisions on almost every quad.
 //
 // When the estimate is taken, nu lies in that range (so nu > 0), and the level needs no
-// clamp to s: |v| <= nu up to a few ulps, so u' <= s * (1 + 2^-21), and floor(u') = s
-// would leave p' < 2^-13, which divides.  A taken element is also nonzero and not NaN
-// (p' >= 2^-13), so its sign bit is the sign test v < 0; the divided path keeps both the
-// nu > 0 test and the clamp (a NaN or zero element, or nu = 0, gives level 0, and -0 as
-// well as 0 converts to code 0; -Inf gives -s through the sign bit, as v < 0 does).
+// clamp to s: u' <= s * (1 + 2^-21), and d' above s would leave ceil(d') - d' within 2^-14
+// of 1, which divides.  A NaN element fails the band and divides.  A zero element (and
+// any d' in (-1, 0)) takes the level -0, which converts to code 0 and enters the
+// dequantization as +0; the divided path keeps both the nu > 0 test and the clamp (a NaN
+// or zero element, or nu = 0, gives level 0; -Inf gives -s through the sign bit, as v < 0
+// does).
 __device__ __forceinline__ void qsgd_quad(const float v[4], float nu, float s, float ys, const float u[4],
                                           int lev[4], float gh[4]) {
   const float rnus = __builtin_amdgcn_rcpf(nu) * s;
@@ -32,11 +34,11 @@ __device__ __forceinline__ void qsgd_quad(const float v[4], float nu, float s, f
   float level[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const float uu = fabsf(v[m]) * rnus;
-    const float l = floorf(uu);
-    const float p = uu - l;
-    slow |= !(p >= 0x1p-13f && p <= 1.0f - 0x1p-13f && fabsf(u[m] - p) >= 0x1p-13f);
-    level[m] = l + (u[m] < p ? 1.f : 0.f);
+    const float d = fabsf(v[m]) * rnus - u[m];
+    const float c = ceilf(d);
+    const float e = c - d;
+    slow |= !(e >= 0x1p-13f && e <= 1.0f - 0x1p-13f);
+    level[m] = c;
   }
   if (slow) {
 #pragma unroll
@@ -54,7 +56,7 @@ __device__ __forceinline__ void qsgd_quad(const float v[4], float nu, float s, f
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     lev[m] = (int)__builtin_copysignf(level[m], v[m]);   // level 0 gives 0 for either sign
-    gh[m] = nu * level[m];   // t, divided below
+    gh[m] = nu * fabsf(level[m]);   // t, divided below (|.| turns an estimated -0 level into +0)
   }
   // with nu >= 2^-100 every t = fl(nu * level) is 0 or >= 2^-100: div_level_count's domain
   float mag[4];
