@@ -39,7 +39,7 @@ HBM_PEAK_GBS = 8000.0
 VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
 # VALU lane-instructions per element of the quantizer kernels (SQ_INSTS_VALU x 64 /
 # elements, rocprofv3 counters of bench.py --rows; profiles/compressor_rows_valu_and_traffic.md).
-VALU_LANE_OPS_PER_ELEMENT = {"minmax8": 20.4, "minmax4": 20.7, "qsgd": 40.5, "terngrad": 23.0}
+VALU_LANE_OPS_PER_ELEMENT = {"minmax8": 20.4, "minmax4": 20.7, "qsgd": 33.9, "terngrad": 23.0}
 # Issue slots beyond one per instruction: v_mad_u64_u32 (the Philox4x32-10 multiplies, 20
 # of the about 66 instructions of a block of 4 draws) occupies a SIMD for two full-rate
 # slots (a kernel of Philox blocks alone measured 5.4 cycles per wave instruction against
